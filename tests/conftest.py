@@ -1,0 +1,35 @@
+import os
+import sys
+
+import pytest
+
+ROOT = os.path.dirname(os.path.dirname(os.path.abspath(__file__)))
+if ROOT not in sys.path:
+    sys.path.insert(0, ROOT)
+
+
+def pytest_configure(config):
+    config.addinivalue_line("markers", "gpu: needs an MI355X (gfx950) GPU and the built HIP library")
+    config.addinivalue_line("markers", "slow: full-size workload checks")
+
+
+def golden_path(name: str) -> str:
+    return os.path.join(ROOT, "tests", "golden", name)
+
+
+def read_golden(name: str) -> dict:
+    """Parse a ``key: values`` golden fixture (``#`` lines are comments)."""
+    out = {}
+    with open(golden_path(name)) as f:
+        for line in f:
+            line = line.strip()
+            if not line or line.startswith("#"):
+                continue
+            k, v = line.split(":", 1)
+            out[k.strip()] = v.split()
+    return out
+
+
+@pytest.fixture
+def golden():
+    return read_golden
