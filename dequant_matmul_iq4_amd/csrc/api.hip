@@ -1,0 +1,161 @@
+// api.hip -- the extern "C" entry points declared in include/iq4.h: argument
+// validation on the host, then the launchers.  Nothing here allocates device memory
+// or synchronises a stream.
+#include <stdarg.h>
+#include <stdio.h>
+
+#include "../../include/iq4.h"
+#include "common.hpp"
+#include "launch.hpp"
+
+namespace iq4 {
+
+static thread_local char g_err[512];
+
+int set_error(int code, const char* fmt, ...) {
+  va_list ap;
+  va_start(ap, fmt);
+  vsnprintf(g_err, sizeof(g_err), fmt, ap);
+  va_end(ap);
+  return code;
+}
+
+int check_launch(const char* what) {
+  hipError_t e = hipGetLastError();
+  if (e != hipSuccess)
+    return set_error(IQ4_E_HIP, "%s: launch failed: %s", what, hipGetErrorString(e));
+  return IQ4_OK;
+}
+
+static inline void clear_error() { g_err[0] = '\0'; }
+static inline hipStream_t as_stream(void* s) { return static_cast<hipStream_t>(s); }
+
+}  // namespace iq4
+
+using namespace iq4;
+
+extern "C" {
+
+const char* iq4_last_error(void) { return g_err; }
+
+int iq4_abi_version(void) { return IQ4_ABI_VERSION; }
+
+int iq4_quantize_blocks(const float* src, int64_t n_blocks, void* blocks, void* stream) {
+  clear_error();
+  if (n_blocks < 0) return set_error(IQ4_E_ARG, "iq4_quantize_blocks: n_blocks < 0");
+  if (n_blocks == 0) return IQ4_OK;
+  if (!src || !blocks) return set_error(IQ4_E_ARG, "iq4_quantize_blocks: null pointer");
+  if (!aligned(src, 16) || !aligned(blocks, 2))
+    return set_error(IQ4_E_ALIGN, "iq4_quantize_blocks: src must be 16-byte and blocks 2-byte aligned");
+  return launch_quantize(src, n_blocks, blocks, as_stream(stream));
+}
+
+int iq4_dequant_blocks(const void* blocks, int64_t n_blocks, int32_t out_dtype, void* out,
+                       void* stream) {
+  clear_error();
+  if (n_blocks < 0) return set_error(IQ4_E_ARG, "iq4_dequant_blocks: n_blocks < 0");
+  if (out_dtype != IQ4_F32 && out_dtype != IQ4_F16)
+    return set_error(IQ4_E_ARG, "iq4_dequant_blocks: out_dtype must be IQ4_F32 or IQ4_F16");
+  if (n_blocks == 0) return IQ4_OK;
+  if (!blocks || !out) return set_error(IQ4_E_ARG, "iq4_dequant_blocks: null pointer");
+  if (!aligned(blocks, 2) || !aligned(out, 16))
+    return set_error(IQ4_E_ALIGN, "iq4_dequant_blocks: blocks must be 2-byte and out 16-byte aligned");
+  return launch_dequant(blocks, n_blocks, out_dtype == IQ4_F16, out, as_stream(stream));
+}
+
+int64_t iq4_packed_bytes(int64_t n, int64_t k) {
+  if (n <= 0 || k <= 0 || n % kTileRows || k % kTileK) return -1;
+  return n * (k / kQK) * kBlockBytes;
+}
+
+static int check_matrix(const char* fn, int64_t n, int64_t k) {
+  if (n <= 0 || k <= 0) return set_error(IQ4_E_ARG, "%s: n and k must be positive", fn);
+  if (n % kTileRows || k % kTileK)
+    return set_error(IQ4_E_UNSUPPORTED, "%s: n must be a multiple of 16 and k of 128 (n=%lld k=%lld)",
+                     fn, (long long)n, (long long)k);
+  if (n > (int64_t)1 << 24 || k > (int64_t)1 << 20)
+    return set_error(IQ4_E_UNSUPPORTED, "%s: n or k too large", fn);
+  return IQ4_OK;
+}
+
+int iq4_pack_weights(const void* blocks, int64_t n, int64_t k, void* packed, void* stream) {
+  clear_error();
+  if (int e = check_matrix("iq4_pack_weights", n, k)) return e;
+  if (!blocks || !packed) return set_error(IQ4_E_ARG, "iq4_pack_weights: null pointer");
+  if (!aligned(blocks, 2) || !aligned(packed, 256))
+    return set_error(IQ4_E_ALIGN, "iq4_pack_weights: blocks must be 2-byte and packed 256-byte aligned");
+  const uint8_t* b = static_cast<const uint8_t*>(blocks);
+  const uint8_t* p = static_cast<const uint8_t*>(packed);
+  const int64_t bytes = iq4_packed_bytes(n, k);
+  if (b < p + bytes && p < b + bytes)
+    return set_error(IQ4_E_ARG, "iq4_pack_weights: blocks and packed overlap");
+  return launch_pack(blocks, n, k, packed, as_stream(stream));
+}
+
+int iq4_qmv_multi(const void* packed, int64_t n, int64_t k, const float* x, int64_t ldx,
+                  int32_t T, float* y, int64_t ldy, void* stream) {
+  clear_error();
+  if (int e = check_matrix("iq4_qmv_multi", n, k)) return e;
+  if (T < 1 || T > 8) return set_error(IQ4_E_ARG, "iq4_qmv_multi: T must be in 1..8 (got %d)", T);
+  if (ldx < k || ldx % 4) return set_error(IQ4_E_ARG, "iq4_qmv_multi: ldx must be >= k and a multiple of 4");
+  if (ldy < n) return set_error(IQ4_E_ARG, "iq4_qmv_multi: ldy must be >= n");
+  if (!packed || !x || !y) return set_error(IQ4_E_ARG, "iq4_qmv_multi: null pointer");
+  if (!aligned(packed, 256) || !aligned(x, 16) || !aligned(y, 4))
+    return set_error(IQ4_E_ALIGN, "iq4_qmv_multi: packed must be 256-byte, x 16-byte, y 4-byte aligned");
+  return launch_qmv(static_cast<const uint8_t*>(packed), n, k, x, ldx, T, y, ldy, as_stream(stream));
+}
+
+int iq4_route_topk(const float* logits, int64_t n_tok, int32_t n_expert, int32_t top_k,
+                   int32_t* ids, float* w, void* stream) {
+  clear_error();
+  if (n_tok < 0 || n_expert < 1 || n_expert > 1024 || top_k < 1 || top_k > 16 || top_k > n_expert)
+    return set_error(IQ4_E_ARG, "iq4_route_topk: need n_tok >= 0, 1 <= top_k <= min(n_expert, 16), n_expert <= 1024");
+  if (n_tok == 0) return IQ4_OK;
+  if (!logits || !ids || !w) return set_error(IQ4_E_ARG, "iq4_route_topk: null pointer");
+  if (!aligned(logits, 4) || !aligned(ids, 4) || !aligned(w, 4))
+    return set_error(IQ4_E_ALIGN, "iq4_route_topk: pointers must be 4-byte aligned");
+  return launch_route_topk(logits, n_tok, n_expert, top_k, ids, w, as_stream(stream));
+}
+
+int iq4_moe_gather(const int32_t* ids, int64_t n_pairs, int32_t n_expert, int32_t* counts,
+                   int32_t* offsets, int32_t* pairs, int32_t* slot_row, void* stream) {
+  clear_error();
+  if (n_pairs < 0 || n_pairs > ((int64_t)1 << 24) || n_expert < 1 || n_expert > 1024)
+    return set_error(IQ4_E_ARG, "iq4_moe_gather: need 0 <= n_pairs <= 2^24, 1 <= n_expert <= 1024");
+  if (!counts || !offsets || (n_pairs > 0 && (!ids || !pairs || !slot_row)))
+    return set_error(IQ4_E_ARG, "iq4_moe_gather: null pointer");
+  if (!aligned(ids, 4) || !aligned(counts, 4) || !aligned(offsets, 4) || !aligned(pairs, 4) ||
+      !aligned(slot_row, 4))
+    return set_error(IQ4_E_ALIGN, "iq4_moe_gather: pointers must be 4-byte aligned");
+  return launch_gather(ids, n_pairs, n_expert, counts, offsets, pairs, slot_row, as_stream(stream));
+}
+
+int iq4_moe_workspace_size(int64_t n_tok, int32_t top_k, int32_t n_expert, int64_t hidden,
+                           int64_t inter, int32_t act_dtype, size_t* bytes) {
+  clear_error();
+  (void)n_tok; (void)top_k; (void)n_expert; (void)hidden; (void)inter; (void)act_dtype;
+  if (bytes) *bytes = 0;
+  return set_error(IQ4_E_UNSUPPORTED, "iq4_moe_workspace_size: not available in this build");
+}
+
+int iq4_moe_expert_gemm(const void* x, int32_t act_dtype, int64_t n_tok, int64_t ldx,
+                        const int32_t* ids, const float* w, int32_t top_k, int32_t n_expert,
+                        int64_t hidden, int64_t inter, const void* w_gate, const void* w_up,
+                        const void* w_down, float* out, int64_t ldo, void* workspace,
+                        size_t ws_bytes, uint32_t flags, void* stream) {
+  clear_error();
+  (void)x; (void)act_dtype; (void)n_tok; (void)ldx; (void)ids; (void)w; (void)top_k;
+  (void)n_expert; (void)hidden; (void)inter; (void)w_gate; (void)w_up; (void)w_down; (void)out;
+  (void)ldo; (void)workspace; (void)ws_bytes; (void)flags; (void)stream;
+  return set_error(IQ4_E_UNSUPPORTED, "iq4_moe_expert_gemm: not available in this build");
+}
+
+int iq4_qgemm(const void* packed, int64_t n, int64_t k, const void* x, int64_t m, int64_t ldx,
+              float* y, int64_t ldy, int64_t chunk, void* stream) {
+  clear_error();
+  (void)packed; (void)n; (void)k; (void)x; (void)m; (void)ldx; (void)y; (void)ldy; (void)chunk;
+  (void)stream;
+  return set_error(IQ4_E_UNSUPPORTED, "iq4_qgemm: not available in this build");
+}
+
+}  // extern "C"

@@ -1,0 +1,66 @@
+// common.hpp -- types, constants and helpers shared by the HIP sources of the IQ4
+// library (gfx950 / CDNA4 only).
+#pragma once
+
+#include <hip/hip_runtime.h>
+#include <hip/hip_fp16.h>
+#include <stdint.h>
+#include <stddef.h>
+
+namespace iq4 {
+
+// ---------------------------------------------------------------------------------
+// Block format: 32 weights, 18 bytes (binary16 scale + 16 bytes of 4-bit indices).
+constexpr int kQK = 32;
+constexpr int kBlockBytes = 18;
+constexpr int kNibbleBytes = 16;
+
+// The fixed 16-level codebook of the format.
+constexpr int8_t kCodebook[16] = {-127, -104, -83, -65, -49, -35, -22, -10,
+                                  1,    13,   25,  38,  53,  69,  89,  113};
+
+// Packed layout: 16-row x 4-block tiles, 1 KiB of indices + 128 B of scales each.
+constexpr int kTileRows = 16;
+constexpr int kTileBlocks = 4;
+constexpr int kTileK = kTileBlocks * kQK;  // 128
+constexpr int kTileNibbleBytes = 1024;
+constexpr int kTileScaleBytes = 128;
+
+// ---------------------------------------------------------------------------------
+// Matrix-core operand types (v_mfma_f32_16x16x32_{bf16,f16}).
+typedef __bf16 bf16x8 __attribute__((ext_vector_type(8)));
+typedef _Float16 f16x8 __attribute__((ext_vector_type(8)));
+typedef float f32x4 __attribute__((ext_vector_type(4)));
+typedef uint32_t u32x4 __attribute__((ext_vector_type(4)));
+typedef uint32_t u32x2 __attribute__((ext_vector_type(2)));
+typedef _Float16 f16x2 __attribute__((ext_vector_type(2)));
+
+// 16x16 output, K = 32, fp32 accumulate.  Lane l (g = l / 16, c = l % 16) supplies
+// A[c][8g .. 8g+7] and B[8g .. 8g+7][c]; it receives D[4g + i][c], i = 0..3.
+__device__ __forceinline__ f32x4 mfma_bf16(u32x4 a, u32x4 b, f32x4 c) {
+  return __builtin_amdgcn_mfma_f32_16x16x32_bf16(__builtin_bit_cast(bf16x8, a),
+                                                 __builtin_bit_cast(bf16x8, b), c, 0, 0, 0);
+}
+__device__ __forceinline__ f32x4 mfma_f16(u32x4 a, u32x4 b, f32x4 c) {
+  return __builtin_amdgcn_mfma_f32_16x16x32_f16(__builtin_bit_cast(f16x8, a),
+                                                __builtin_bit_cast(f16x8, b), c, 0, 0, 0);
+}
+
+// Packed pair of binary16 values: lo in bits 0-15.
+__device__ __forceinline__ uint32_t pk_mul_f16(uint32_t a, uint32_t b) {
+  f16x2 r = __builtin_bit_cast(f16x2, a) * __builtin_bit_cast(f16x2, b);
+  return __builtin_bit_cast(uint32_t, r);
+}
+
+__device__ __forceinline__ float h2f(uint16_t h) {
+  return __half2float(__ushort_as_half(h));
+}
+
+// ---------------------------------------------------------------------------------
+// Host-side status handling.
+int set_error(int code, const char* fmt, ...);
+int check_launch(const char* what);
+
+inline bool aligned(const void* p, size_t a) { return (reinterpret_cast<uintptr_t>(p) % a) == 0; }
+
+}  // namespace iq4

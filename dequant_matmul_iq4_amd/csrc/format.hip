@@ -1,0 +1,152 @@
+// format.hip -- the block format on the device: encode (quantise), decode, and the
+// one-time rearrangement into the packed tile layout read by the product kernels.
+#include "common.hpp"
+#include "launch.hpp"
+
+namespace iq4 {
+
+// Codebook midpoints (c_j + c_{j+1}) / 2: a value above the j-th midpoint is nearer
+// to level j+1 than to level j.
+__constant__ float kMid[15] = {-115.5f, -93.5f, -74.0f, -57.0f, -42.0f, -28.5f, -16.0f, -4.5f,
+                               7.0f,    19.0f,  31.5f,  45.5f,  61.0f,  79.0f,  101.0f};
+
+// One thread per block.  d = f16(f32(max|w|) / 127) (IEEE division, round to
+// nearest even); index = number of midpoints strictly below w/d, computed as
+// w > mid_j * d.  mid_j * d is exact in binary32 (at most 9 x 11 significant bits),
+// so the comparison is the exact nearest-level decision with ties to the lower
+// index.  d == 0 gives index 8 (the level nearest zero) for every element.
+__global__ void __launch_bounds__(256) quantize_kernel(const float* __restrict__ src, int64_t nb,
+                                                       uint16_t* __restrict__ dst) {
+  int64_t b = (int64_t)blockIdx.x * blockDim.x + threadIdx.x;
+  if (b >= nb) return;
+  const float4* s = reinterpret_cast<const float4*>(src + b * kQK);
+  float w[kQK];
+#pragma unroll
+  for (int i = 0; i < kQK / 4; ++i) {
+    float4 v = s[i];
+    w[4 * i + 0] = v.x;
+    w[4 * i + 1] = v.y;
+    w[4 * i + 2] = v.z;
+    w[4 * i + 3] = v.w;
+  }
+  float amax = 0.0f;
+#pragma unroll
+  for (int i = 0; i < kQK; ++i) amax = fmaxf(amax, fabsf(w[i]));
+  __half dh = __float2half_rn(amax / 127.0f);
+  float d = __half2float(dh);
+  int q[kQK];
+#pragma unroll
+  for (int i = 0; i < kQK; ++i) {
+    int c = 0;
+#pragma unroll
+    for (int j = 0; j < 15; ++j) c += (w[i] > kMid[j] * d) ? 1 : 0;
+    q[i] = (d == 0.0f) ? 8 : c;
+  }
+  uint16_t* o = dst + b * (kBlockBytes / 2);
+  o[0] = __half_as_ushort(dh);
+#pragma unroll
+  for (int i = 0; i < 8; ++i) {
+    uint32_t lo = (uint32_t)q[2 * i] | ((uint32_t)q[2 * i + 16] << 4);
+    uint32_t hi = (uint32_t)q[2 * i + 1] | ((uint32_t)q[2 * i + 17] << 4);
+    o[1 + i] = (uint16_t)(lo | (hi << 8));
+  }
+}
+
+// One thread per 8 consecutive outputs of a block: elements 8p .. 8p+7 are the low
+// (p < 2) or high (p >= 2) nibbles of index bytes 8(p % 2) .. 8(p % 2) + 7.
+template <bool F16>
+__global__ void __launch_bounds__(256) dequant_kernel(const uint16_t* __restrict__ blocks,
+                                                      int64_t nb, void* __restrict__ out) {
+  int64_t i = (int64_t)blockIdx.x * blockDim.x + threadIdx.x;
+  if (i >= nb * 4) return;
+  int64_t b = i >> 2;
+  int p = (int)(i & 3);
+  const uint16_t* blk = blocks + b * (kBlockBytes / 2);
+  float d = h2f(blk[0]);
+  uint32_t bytes[8];
+#pragma unroll
+  for (int j = 0; j < 4; ++j) {
+    uint16_t v = blk[1 + 4 * (p & 1) + j];
+    bytes[2 * j] = v & 0xFF;
+    bytes[2 * j + 1] = v >> 8;
+  }
+  float w[8];
+#pragma unroll
+  for (int j = 0; j < 8; ++j) {
+    uint32_t q = (p < 2) ? (bytes[j] & 0xF) : (bytes[j] >> 4);
+    w[j] = d * (float)kCodebook[q];
+  }
+  if (F16) {
+    uint32_t h[4];
+#pragma unroll
+    for (int j = 0; j < 4; ++j)
+      h[j] = (uint32_t)__half_as_ushort(__float2half_rn(w[2 * j])) |
+             ((uint32_t)__half_as_ushort(__float2half_rn(w[2 * j + 1])) << 16);
+    reinterpret_cast<uint4*>(out)[i] = make_uint4(h[0], h[1], h[2], h[3]);
+  } else {
+    float4* o = reinterpret_cast<float4*>(out) + 2 * i;
+    o[0] = make_float4(w[0], w[1], w[2], w[3]);
+    o[1] = make_float4(w[4], w[5], w[6], w[7]);
+  }
+}
+
+// One thread per packed entry (64 per tile).  Entry l = 16g + j of tile (rt, kq)
+// gathers index bytes 4g..4g+3 of the tile's four blocks of row 16rt + j; entries
+// with g == 0 also write that row's four scales.
+__global__ void __launch_bounds__(256) pack_kernel(const uint16_t* __restrict__ blocks, int64_t n,
+                                                   int64_t k, uint8_t* __restrict__ packed) {
+  const int64_t kq_n = k / kTileK;
+  const int64_t ntiles = (n / kTileRows) * kq_n;
+  int64_t gid = (int64_t)blockIdx.x * blockDim.x + threadIdx.x;
+  int64_t tile = gid >> 6;
+  if (tile >= ntiles) return;
+  int l = (int)(gid & 63);
+  int g = l >> 4, j = l & 15;
+  int64_t rt = tile / kq_n, kq = tile % kq_n;
+  int64_t row = rt * kTileRows + j;
+  const int64_t bpr = k / kQK;
+  uint32_t word[4];
+  uint16_t sc[4];
+#pragma unroll
+  for (int b = 0; b < 4; ++b) {
+    const uint16_t* blk = blocks + (row * bpr + kq * kTileBlocks + b) * (kBlockBytes / 2);
+    sc[b] = blk[0];
+    word[b] = (uint32_t)blk[1 + 2 * g] | ((uint32_t)blk[2 + 2 * g] << 16);
+  }
+  uint4* np = reinterpret_cast<uint4*>(packed + tile * kTileNibbleBytes) + l;
+  *np = make_uint4(word[0], word[1], word[2], word[3]);
+  if (g == 0) {
+    uint8_t* sp = packed + (n * bpr) * kNibbleBytes + tile * kTileScaleBytes + 8 * j;
+    *reinterpret_cast<uint2*>(sp) =
+        make_uint2((uint32_t)sc[0] | ((uint32_t)sc[1] << 16), (uint32_t)sc[2] | ((uint32_t)sc[3] << 16));
+  }
+}
+
+int launch_quantize(const float* src, int64_t nb, void* blocks, hipStream_t s) {
+  if (nb == 0) return 0;
+  int64_t grid = (nb + 255) / 256;
+  hipLaunchKernelGGL(quantize_kernel, dim3((unsigned)grid), dim3(256), 0, s, src, nb,
+                     static_cast<uint16_t*>(blocks));
+  return check_launch("quantize_kernel");
+}
+
+int launch_dequant(const void* blocks, int64_t nb, bool f16, void* out, hipStream_t s) {
+  if (nb == 0) return 0;
+  int64_t grid = (nb * 4 + 255) / 256;
+  const uint16_t* b = static_cast<const uint16_t*>(blocks);
+  if (f16)
+    hipLaunchKernelGGL(dequant_kernel<true>, dim3((unsigned)grid), dim3(256), 0, s, b, nb, out);
+  else
+    hipLaunchKernelGGL(dequant_kernel<false>, dim3((unsigned)grid), dim3(256), 0, s, b, nb, out);
+  return check_launch("dequant_kernel");
+}
+
+int launch_pack(const void* blocks, int64_t n, int64_t k, void* packed, hipStream_t s) {
+  int64_t threads = (n / kTileRows) * (k / kTileK) * 64;
+  int64_t grid = (threads + 255) / 256;
+  hipLaunchKernelGGL(pack_kernel, dim3((unsigned)grid), dim3(256), 0, s,
+                     static_cast<const uint16_t*>(blocks), n, k, static_cast<uint8_t*>(packed));
+  return check_launch("pack_kernel");
+}
+
+}  // namespace iq4

@@ -1,0 +1,125 @@
+// route.hip -- top-k routing from logits, and the bit-exact token gather of the
+// routed pairs (counts, exclusive offsets, pair list grouped by expert, inverse).
+#include "common.hpp"
+#include "launch.hpp"
+
+namespace iq4 {
+
+constexpr int kMaxTopK = 16;
+
+// One thread per token: a running top-k by insertion over experts in ascending id
+// order.  A logit displaces a kept one only if strictly larger, so equal logits keep
+// the lower expert id first.  Gate weights: softmax over the k kept logits in fp32.
+__global__ void __launch_bounds__(256) route_topk_kernel(const float* __restrict__ logits,
+                                                         int64_t n_tok, int n_expert, int top_k,
+                                                         int32_t* __restrict__ ids,
+                                                         float* __restrict__ w) {
+  int64_t t = (int64_t)blockIdx.x * blockDim.x + threadIdx.x;
+  if (t >= n_tok) return;
+  const float* row = logits + t * n_expert;
+  float val[kMaxTopK];
+  int id[kMaxTopK];
+  int kept = 0;
+  for (int e = 0; e < n_expert; ++e) {
+    const float v = row[e];
+    if (kept == top_k && !(v > val[top_k - 1])) continue;
+    int pos = kept < top_k ? kept : top_k - 1;
+    while (pos > 0 && v > val[pos - 1]) {
+      val[pos] = val[pos - 1];
+      id[pos] = id[pos - 1];
+      --pos;
+    }
+    val[pos] = v;
+    id[pos] = e;
+    if (kept < top_k) ++kept;
+  }
+  const float m = val[0];
+  float ex[kMaxTopK];
+  float sum = 0.0f;
+  for (int j = 0; j < top_k; ++j) {
+    ex[j] = expf(val[j] - m);
+    sum += ex[j];
+  }
+  for (int j = 0; j < top_k; ++j) {
+    ids[t * top_k + j] = id[j];
+    w[t * top_k + j] = ex[j] / sum;
+  }
+}
+
+// One workgroup per expert e.  Its waves own contiguous segments of the pair list.
+// Pass 1 counts, per wave, the pairs routed to e and to experts below e (so the
+// workgroup knows offsets[e] without a global scan); pass 2 walks each segment in
+// order, ranking matches with a ballot, so pairs of one expert keep ascending order.
+constexpr int kGatherThreads = 1024;
+
+__global__ void __launch_bounds__(kGatherThreads) gather_kernel(const int32_t* __restrict__ ids,
+                                                                int64_t n_pairs,
+                                                                int32_t* __restrict__ counts,
+                                                                int32_t* __restrict__ offsets,
+                                                                int32_t* __restrict__ pairs,
+                                                                int32_t* __restrict__ slot_row) {
+  constexpr int kWaves = kGatherThreads / 64;
+  __shared__ int eq_cnt[kWaves], lt_cnt[kWaves];
+  const int e = blockIdx.x;
+  const int lane = threadIdx.x & 63, wave = threadIdx.x >> 6;
+  const int64_t seg = ((n_pairs + kWaves - 1) / kWaves + 63) / 64 * 64;
+  const int64_t p0 = wave * seg;
+  const int64_t p1 = min(p0 + seg, n_pairs);
+
+  int eq = 0, lt = 0;
+  for (int64_t p = p0 + lane; p < p1; p += 64) {
+    const int v = ids[p];
+    eq += (v == e);
+    lt += (v < e);
+  }
+  for (int o = 32; o > 0; o >>= 1) {
+    eq += __shfl_xor(eq, o);
+    lt += __shfl_xor(lt, o);
+  }
+  if (lane == 0) {
+    eq_cnt[wave] = eq;
+    lt_cnt[wave] = lt;
+  }
+  __syncthreads();
+  int base = 0, total = 0;
+  for (int w2 = 0; w2 < kWaves; ++w2) {
+    base += lt_cnt[w2];
+    total += eq_cnt[w2];
+  }
+  int run = base;
+  for (int w2 = 0; w2 < wave; ++w2) run += eq_cnt[w2];
+  if (threadIdx.x == 0) {
+    counts[e] = total;
+    offsets[e] = base;
+    if (e == (int)gridDim.x - 1) offsets[e + 1] = (int32_t)n_pairs;
+  }
+  const uint64_t below = (lane == 0) ? 0ull : (~0ull >> (64 - lane));
+  for (int64_t pb = p0; pb < p1; pb += 64) {
+    const int64_t p = pb + lane;
+    const bool hit = (p < p1) && (ids[p] == e);
+    const uint64_t mask = __ballot(hit);
+    if (hit) {
+      const int pos = run + __popcll(mask & below);
+      pairs[pos] = (int32_t)p;
+      slot_row[p] = pos;
+    }
+    run += __popcll(mask);
+  }
+}
+
+int launch_route_topk(const float* logits, int64_t n_tok, int n_expert, int top_k, int32_t* ids,
+                      float* w, hipStream_t s) {
+  int64_t grid = (n_tok + 255) / 256;
+  hipLaunchKernelGGL(route_topk_kernel, dim3((unsigned)grid), dim3(256), 0, s, logits, n_tok,
+                     n_expert, top_k, ids, w);
+  return check_launch("route_topk_kernel");
+}
+
+int launch_gather(const int32_t* ids, int64_t n_pairs, int n_expert, int32_t* counts,
+                  int32_t* offsets, int32_t* pairs, int32_t* slot_row, hipStream_t s) {
+  hipLaunchKernelGGL(gather_kernel, dim3((unsigned)n_expert), dim3(kGatherThreads), 0, s, ids,
+                     n_pairs, counts, offsets, pairs, slot_row);
+  return check_launch("gather_kernel");
+}
+
+}  // namespace iq4

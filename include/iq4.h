@@ -1,0 +1,210 @@
+/*
+ * iq4.h -- C ABI of the MI355X (gfx950) library for matrix products against IQ4
+ * block-quantised weights decoded on the fly.
+ *
+ * Block format.  32 weights per block, stored in 18 bytes: an IEEE binary16 scale d
+ * (bytes 0-1, little-endian) and 32 four-bit indices into the fixed codebook
+ * {-127,-104,-83,-65,-49,-35,-22,-10,1,13,25,38,53,69,89,113}; byte 2+i holds index
+ * q_i in its low nibble and q_{i+16} in its high nibble.  The decoded weight is
+ * w = d * codebook[q], exact in binary32.  Page 2 of the sources (Strata pull request
+ * "sm_80 (GA100) tuning", PLE-compact commit message) fixes the block at 18 bytes per
+ * 32 values; the nibble order is this library's reading, shared with its CPU oracle.
+ *
+ * A weight matrix W has N rows and K columns (K a multiple of 32); row r is K/32
+ * consecutive blocks.  This "row-block" layout is what iq4_quantize_blocks writes and
+ * iq4_dequant_blocks / iq4_pack_weights read.  The product calls read the "packed"
+ * layout written by iq4_pack_weights (same 18 bytes per block, rearranged so that one
+ * 128-bit load feeds one matrix-core fragment; see iq4_pack_weights).
+ *
+ * Conventions shared by every call:
+ *  - All pointers are device pointers unless stated otherwise; the caller owns every
+ *    buffer.  The library never allocates device memory and never synchronises the
+ *    stream inside a call: work is enqueued on `stream` (a hipStream_t; NULL means the
+ *    legacy default stream) and inputs must stay valid and unmodified until the stream
+ *    has passed the call.  Outputs are overwritten, never accumulated into.
+ *  - Every call returns IQ4_OK (0) or a negative IQ4_E_* status.  Arguments are
+ *    validated on the host before anything is enqueued; on error nothing is enqueued
+ *    and iq4_last_error() describes the problem.
+ *  - Activations are token-major: X[t][k] at X + t*ldx + k (ldx in elements).
+ *  - Calls are safe from several host threads; the last-error text is per thread.
+ */
+#ifndef IQ4_H
+#define IQ4_H
+
+#include <stddef.h>
+#include <stdint.h>
+
+#ifdef __cplusplus
+extern "C" {
+#endif
+
+/* status codes */
+#define IQ4_OK 0
+#define IQ4_E_ARG (-1)         /* a size, count or dtype is out of range          */
+#define IQ4_E_ALIGN (-2)       /* a pointer or leading dimension is misaligned    */
+#define IQ4_E_UNSUPPORTED (-3) /* a shape this library does not implement         */
+#define IQ4_E_HIP (-4)         /* the HIP runtime reported an error at launch     */
+#define IQ4_E_WORKSPACE (-5)   /* the workspace is missing or too small           */
+
+/* element types */
+#define IQ4_F32 0
+#define IQ4_F16 1
+
+/* iq4_moe_expert_gemm flags */
+#define IQ4_MOE_ATOMIC_COMBINE 1u /* prefill: add slot rows into `out` with atomics
+                                     (faster, not bit-reproducible run to run)      */
+
+/* Text of the last error on the calling thread ("" if none).  Valid until the
+ * thread's next iq4_* call. */
+const char* iq4_last_error(void);
+
+/* ABI version of this header (incremented on incompatible change). */
+#define IQ4_ABI_VERSION 1
+int iq4_abi_version(void);
+
+/*
+ * Encode float32 weights into blocks (the quantiser of the block format).
+ *   src      [n_blocks][32] float32, finite, with max|w|/127 <= 65504.
+ *   blocks   [n_blocks][18] bytes (row-block layout; 2-byte aligned).
+ * Per block: d = f16_rne(f32(max|w|) / 127) (IEEE binary32 division); each element
+ * takes the codebook level nearest to w/d, ties to the lower index; d == 0 stores
+ * index 8 everywhere.  The index decision is exact, so the bytes are unique.
+ * Source: the workload definition of the format (scale absmax/127, nearest level).
+ * Errors: IQ4_E_ARG if n_blocks < 0; IQ4_E_ALIGN if src is not 16-byte aligned or
+ * blocks is not 2-byte aligned.
+ */
+int iq4_quantize_blocks(const float* src, int64_t n_blocks, void* blocks, void* stream);
+
+/*
+ * Decode blocks: out[b][i] = d_b * codebook[q_{b,i}], in block order.
+ *   blocks   [n_blocks][18] bytes (row-block layout; 2-byte aligned).
+ *   out      [n_blocks][32] of out_dtype: IQ4_F32 (exact) or IQ4_F16 (the exact
+ *            value rounded to nearest even, subnormals kept, overflow to inf).
+ * Bitwise equal to the host decode -- page 2 (pull request "sm_80 (GA100) tuning"),
+ * PLE-compact commit message: the device dequant yields the host dequant's floats
+ * bit for bit.
+ * Errors: IQ4_E_ARG (n_blocks < 0, bad dtype), IQ4_E_ALIGN (blocks not 2-byte or out
+ * not 16-byte aligned).
+ */
+int iq4_dequant_blocks(const void* blocks, int64_t n_blocks, int32_t out_dtype, void* out,
+                       void* stream);
+
+/*
+ * Size in bytes of the packed form of an n x k matrix (= n*k/32*18), or -1 if
+ * n % 16 != 0, k % 128 != 0 or either is not positive.
+ */
+int64_t iq4_packed_bytes(int64_t n, int64_t k);
+
+/*
+ * Rearrange an n x k matrix from the row-block layout into the packed layout read by
+ * the product calls (one-time, at weight-load time).
+ *   blocks   [n][k/32][18] bytes, 2-byte aligned.
+ *   packed   iq4_packed_bytes(n, k) bytes, 256-byte aligned, not overlapping blocks.
+ * Packed layout (16-row x 4-block tiles, tile (rt, kq) for rows 16rt..16rt+15 and
+ * blocks 4kq..4kq+3, tiles ordered rt-major):
+ *   nibble plane: tile at (rt*(k/128) + kq) * 1024 bytes; 64 entries of 16 bytes;
+ *     entry l = 16g + j (g = 0..3, j = 0..15) holds, for blocks b = 0..3 of the tile,
+ *     index bytes 4g..4g+3 of block (row 16rt+j, block 4kq+b) at bytes 4b..4b+3.
+ *   scale plane (after n*k/32*16 bytes of nibbles): tile at (rt*(k/128)+kq)*128 bytes;
+ *     row j's four scales (binary16) at bytes 8j..8j+7.
+ * Errors: IQ4_E_UNSUPPORTED (n % 16, k % 128), IQ4_E_ALIGN.
+ */
+int iq4_pack_weights(const void* blocks, int64_t n, int64_t k, void* packed, void* stream);
+
+/*
+ * T-column quantised matrix-vector product (the verify window's dense product):
+ *   Y[t][r] = sum_k W[r][k] * X[t][k],  t < T,  r < n,
+ * fp32 activations, fp32 result.  Page 1 (Strata commit "wire multi-token kernels
+ * into Verifier and MtpDrafter CUDA graphs", verify.hpp header): T tokens read the
+ * dense weights once, and each token's column is the single-token result bit for bit.
+ * This call guarantees that: column t of a T-column call is bitwise equal to a 1-column
+ * call on X[t], for every T, and results are run-to-run deterministic.
+ *   packed   W in the packed layout (iq4_pack_weights), 256-byte aligned.
+ *   x        [T][ldx] float32, 16-byte aligned, ldx >= k, ldx % 4 == 0.
+ *   y        [T][ldy] float32, ldy >= n.
+ *   T        1..8.
+ * Errors: IQ4_E_ARG (T, ldx, ldy), IQ4_E_UNSUPPORTED (n % 16, k % 128),
+ * IQ4_E_ALIGN.
+ */
+int iq4_qmv_multi(const void* packed, int64_t n, int64_t k, const float* x, int64_t ldx,
+                  int32_t T, float* y, int64_t ldy, void* stream);
+
+/*
+ * Top-k routing from router logits: ids[t] = the top_k experts with the largest
+ * logits, in descending logit order, ties to the lower expert id (page 3, DSpark
+ * tp2.py: both the TP-2 layout notes and markov_local_argmax resolve ties toward the
+ * smaller index); w[t][j] = softmax over the top_k selected logits (binary32 math).
+ *   logits   [n_tok][n_expert] float32.   ids [n_tok][top_k] int32.
+ *   w        [n_tok][top_k] float32.      1 <= top_k <= min(n_expert, 16), n_expert <= 1024.
+ * Errors: IQ4_E_ARG.
+ */
+int iq4_route_topk(const float* logits, int64_t n_tok, int32_t n_expert, int32_t top_k,
+                   int32_t* ids, float* w, void* stream);
+
+/*
+ * Token gather of routed pairs (pair p = t*top_k + j).  Bit-exact:
+ *   counts[e]    number of pairs routed to expert e                  [n_expert]
+ *   offsets[e]   exclusive prefix sum of counts                      [n_expert+1]
+ *   pairs[i]     pair ids grouped by expert, ascending within one    [n_pairs]
+ *   slot_row[p]  position of pair p in `pairs`                       [n_pairs]
+ * This is the per-expert count / start / token list of page 1's expert plan block.
+ * ids must lie in [0, n_expert) (not checked on the device).  n_pairs <= 2^24,
+ * n_expert <= 1024.  Errors: IQ4_E_ARG.
+ */
+int iq4_moe_gather(const int32_t* ids, int64_t n_pairs, int32_t n_expert, int32_t* counts,
+                   int32_t* offsets, int32_t* pairs, int32_t* slot_row, void* stream);
+
+/*
+ * Workspace bytes needed by iq4_moe_expert_gemm for these sizes (written to *bytes).
+ */
+int iq4_moe_workspace_size(int64_t n_tok, int32_t top_k, int32_t n_expert, int64_t hidden,
+                           int64_t inter, int32_t act_dtype, size_t* bytes);
+
+/*
+ * Mixture-of-experts FFN over routed tokens (SwiGLU experts, gate-weighted sum):
+ *   for token t, slot j, e = ids[t][j]:  g = Wg_e x_t, u = Wu_e x_t,
+ *   h = silu(g) * u,  y_tj = Wd_e h,  out[t] = sum_j w[t][j] * y_tj (added in j order).
+ * Page 1 (verify.hpp, PoolMultiFn): x (n_tok, n_embd) and ids (n_tok, k) give
+ * per-slot rows (n_tok*k, n_embd) that are then summed per token.
+ *   x           [n_tok][ldx] activations: IQ4_F32 (decode path, n_tok <= 8: every
+ *               product in fp32 through the T-column matvec) or IQ4_F16 (prefill path:
+ *               grouped GEMM on the matrix cores, weights decoded to f16, fp32
+ *               accumulation, h rounded to f16 for the down product).
+ *   ids, w      [n_tok][top_k] int32 / float32 (ids in [0, n_expert), not checked).
+ *   w_gate, w_up  n_expert packed inter x hidden matrices, expert e at
+ *               e * iq4_packed_bytes(inter, hidden) bytes.
+ *   w_down      n_expert packed hidden x inter matrices, expert e at
+ *               e * iq4_packed_bytes(hidden, inter).
+ *   out         [n_tok][ldo] float32, overwritten.
+ *   workspace   >= iq4_moe_workspace_size(...) bytes, 256-byte aligned; the call
+ *               leaves the gather (counts, offsets, pairs, slot_row) at its start.
+ *   flags       0 (deterministic) or IQ4_MOE_ATOMIC_COMBINE (prefill only).
+ * Errors: IQ4_E_ARG, IQ4_E_ALIGN, IQ4_E_UNSUPPORTED (hidden or inter not multiples of
+ * 256 / 128), IQ4_E_WORKSPACE.
+ */
+int iq4_moe_expert_gemm(const void* x, int32_t act_dtype, int64_t n_tok, int64_t ldx,
+                        const int32_t* ids, const float* w, int32_t top_k, int32_t n_expert,
+                        int64_t hidden, int64_t inter, const void* w_gate, const void* w_up,
+                        const void* w_down, float* out, int64_t ldo, void* workspace,
+                        size_t ws_bytes, uint32_t flags, void* stream);
+
+/*
+ * Dense dequant-fused GEMM over a prompt in chunks of `chunk` rows:
+ *   Y[m][r] = sum_k X[m][k] * W[r][k]  (X f16, W decoded to f16, fp32 accumulation),
+ * one launch per chunk of `chunk` consecutive rows of X (the last chunk may be short),
+ * each launch decoding the weights again -- page 2 (pull request "sm_80 (GA100)
+ * tuning"), wide-dequant commit: the prompt path decodes the dense weights for every
+ * chunk; here the decode is fused into the product instead of a separate pass.
+ * Results do not depend on `chunk` (bitwise).
+ *   packed  W (n x k) in the packed layout.   x [m][ldx] binary16, ldx % 8 == 0.
+ *   y       [m][ldy] float32.                  chunk >= 1 (0 means one launch).
+ * Errors: IQ4_E_ARG, IQ4_E_ALIGN, IQ4_E_UNSUPPORTED (n % 16, k % 128).
+ */
+int iq4_qgemm(const void* packed, int64_t n, int64_t k, const void* x, int64_t m, int64_t ldx,
+              float* y, int64_t ldy, int64_t chunk, void* stream);
+
+#ifdef __cplusplus
+}
+#endif
+
+#endif /* IQ4_H */

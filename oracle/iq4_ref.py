@@ -85,6 +85,9 @@ def decode_blocks_f16(blocks) -> np.ndarray:
     return decode_blocks(blocks).astype(np.float16)
 
 
+_ENCODE_CHUNK = 1 << 15
+
+
 def encode_blocks(w) -> np.ndarray:
     """Quantise float32 weights ``[nb, 32]`` to 18-byte blocks ``[nb, 18]`` (uint8).
 
@@ -94,6 +97,9 @@ def encode_blocks(w) -> np.ndarray:
     """
     w32 = np.ascontiguousarray(np.asarray(w, dtype=np.float32)).reshape(-1, QK)
     nb = w32.shape[0]
+    if nb > _ENCODE_CHUNK:  # bound the [blocks, 32, 16] distance array; same result
+        return np.concatenate([encode_blocks(w32[i:i + _ENCODE_CHUNK])
+                               for i in range(0, nb, _ENCODE_CHUNK)])
     amax = np.max(np.abs(w32), axis=1)
     d16 = (amax / np.float32(127.0)).astype(np.float32).astype(np.float16)
     d = d16.astype(np.float64)

@@ -1,0 +1,81 @@
+"""The C ABI on the CPU: the library loads, exports every entry point that
+include/iq4.h declares, and rejects bad arguments on the host before touching a GPU.
+(No call here reaches a launch.)"""
+import ctypes
+import os
+import re
+
+import pytest
+
+import dequant_matmul_iq4_amd as iq4
+from conftest import ROOT
+
+HEADER = os.path.join(ROOT, "include", "iq4.h")
+
+
+def declared_functions():
+    text = open(HEADER).read()
+    text = re.sub(r"/\*.*?\*/", "", text, flags=re.S)
+    return sorted(set(re.findall(r"\b(iq4_\w+)\s*\(", text)))
+
+
+def test_library_exports_every_declared_symbol():
+    lib = iq4.lib()
+    names = declared_functions()
+    assert len(names) >= 11
+    missing = [n for n in names if not hasattr(lib, n)]
+    assert not missing, missing
+    assert set(names) == set(iq4.SIGNATURES), "binding and header disagree"
+
+
+def test_abi_version():
+    assert iq4.iq4_abi_version() == 1
+
+
+def test_packed_bytes():
+    assert iq4.iq4_packed_bytes(4096, 4096) == 4096 * 4096 // 32 * 18
+    assert iq4.iq4_packed_bytes(768, 2048) == 768 * 2048 // 32 * 18
+    assert iq4.iq4_packed_bytes(15, 128) == -1
+    assert iq4.iq4_packed_bytes(16, 96) == -1
+    assert iq4.iq4_packed_bytes(0, 128) == -1
+
+
+def _rc(name, *args):
+    return getattr(iq4.lib(), name)(*args)
+
+
+FAKE = 1 << 20  # a 256-byte-aligned non-null address that no call may dereference
+
+
+def test_validation_errors_never_launch():
+    assert _rc("iq4_qmv_multi", FAKE, 16, 128, FAKE, 128, 0, FAKE, 16, None) == iq4.IQ4_E_ARG
+    assert "T must be" in iq4.iq4_last_error()
+    assert _rc("iq4_qmv_multi", FAKE, 16, 128, FAKE, 128, 9, FAKE, 16, None) == iq4.IQ4_E_ARG
+    assert _rc("iq4_qmv_multi", FAKE, 17, 128, FAKE, 128, 1, FAKE, 17, None) == iq4.IQ4_E_UNSUPPORTED
+    assert _rc("iq4_qmv_multi", FAKE, 16, 96, FAKE, 128, 1, FAKE, 16, None) == iq4.IQ4_E_UNSUPPORTED
+    assert _rc("iq4_qmv_multi", FAKE, 16, 128, FAKE, 127, 1, FAKE, 16, None) == iq4.IQ4_E_ARG
+    assert _rc("iq4_qmv_multi", FAKE, 16, 128, FAKE + 4, 128, 1, FAKE, 16, None) == iq4.IQ4_E_ALIGN
+    assert _rc("iq4_qmv_multi", FAKE + 16, 16, 128, FAKE, 128, 1, FAKE, 16, None) == iq4.IQ4_E_ALIGN
+    assert _rc("iq4_qmv_multi", None, 16, 128, FAKE, 128, 1, FAKE, 16, None) == iq4.IQ4_E_ARG
+    assert _rc("iq4_dequant_blocks", FAKE, 4, 7, FAKE, None) == iq4.IQ4_E_ARG
+    assert _rc("iq4_dequant_blocks", FAKE + 1, 4, 0, FAKE, None) == iq4.IQ4_E_ALIGN
+    assert _rc("iq4_dequant_blocks", FAKE, -1, 0, FAKE, None) == iq4.IQ4_E_ARG
+    assert _rc("iq4_quantize_blocks", FAKE + 4, 4, FAKE, None) == iq4.IQ4_E_ALIGN
+    assert _rc("iq4_pack_weights", FAKE, 16, 128, FAKE, None) == iq4.IQ4_E_ARG  # overlap
+    assert _rc("iq4_pack_weights", FAKE, 16, 100, FAKE * 2, None) == iq4.IQ4_E_UNSUPPORTED
+    assert _rc("iq4_route_topk", FAKE, 4, 8, 9, FAKE, FAKE, None) == iq4.IQ4_E_ARG
+    assert _rc("iq4_route_topk", FAKE, 4, 2000, 8, FAKE, FAKE, None) == iq4.IQ4_E_ARG
+    assert _rc("iq4_moe_gather", FAKE, -1, 8, FAKE, FAKE, FAKE, FAKE, None) == iq4.IQ4_E_ARG
+    assert _rc("iq4_moe_gather", FAKE, 8, 0, FAKE, FAKE, FAKE, FAKE, None) == iq4.IQ4_E_ARG
+
+
+def test_zero_sized_calls_are_no_ops():
+    assert _rc("iq4_quantize_blocks", None, 0, None, None) == iq4.IQ4_OK
+    assert _rc("iq4_dequant_blocks", None, 0, 0, None, None) == iq4.IQ4_OK
+    assert _rc("iq4_route_topk", None, 0, 8, 2, None, None, None) == iq4.IQ4_OK
+
+
+def test_binding_raises_with_message():
+    with pytest.raises(iq4.IQ4Error) as ei:
+        iq4.iq4_qmv_multi(FAKE, 16, 128, FAKE, 128, 0, FAKE, 16, stream=0)
+    assert ei.value.code == iq4.IQ4_E_ARG and "T must be" in str(ei.value)

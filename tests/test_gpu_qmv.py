@@ -1,0 +1,137 @@
+"""T-column quantised matvec on the GPU against the oracle.
+
+Tolerance: fp32 activations and accumulation, normwise max|y - r| / max|r| <= 1e-3
+(the stated tolerance for the fp32 paths).  Exact cases (one-hot columns, power-of-two
+scales with small-integer activations) must match bitwise, and every column of a
+T-column call must equal the 1-column call on that column bitwise (page 1, verify.hpp
+header: each window token reproduces single-token decode bit for bit).
+"""
+import numpy as np
+import pytest
+import torch
+
+import dequant_matmul_iq4_amd as iq4
+import oracle
+from gpu_util import bits_equal, dev, host, normwise, note, pack
+from test_oracle_pins import integer_exact_blocks
+import workloads
+
+pytestmark = pytest.mark.gpu
+
+TOL = 1e-3
+
+
+def run_qmv(packed, n, k, x: np.ndarray, ldx=None, ldy=None) -> np.ndarray:
+    T = x.shape[0]
+    ldx = ldx or k
+    ldy = ldy or n
+    xb = np.zeros((T, ldx), dtype=np.float32)
+    xb[:, :k] = x
+    xd = dev(xb)
+    y = torch.full((T, ldy), float("nan"), dtype=torch.float32, device="cuda")
+    iq4.iq4_qmv_multi(packed, n, k, xd, ldx, T, y, ldy)
+    out = host(y)
+    if ldy > n:
+        assert np.all(np.isnan(out[:, n:])), "wrote outside [0, n)"
+    return out[:, :n]
+
+
+def test_plumbing_matvec():
+    note("qmv: plumbing 512 x 2048, T = 1")
+    b, n, k, x = workloads.cfg1()
+    y = run_qmv(pack(b, n, k), n, k, x)
+    r = oracle.qmv(b, n, k, x)
+    assert normwise(y, r) <= TOL
+
+
+@pytest.mark.parametrize("T", [1, 2, 3, 4, 8])
+def test_verify_window_matvec(T):
+    note(f"qmv: verify window 4096 x 4096, T = {T}")
+    b, n, k, x = workloads.cfg2(T)
+    y = run_qmv(pack(b, n, k), n, k, x)
+    r = oracle.qmv(b, n, k, x)
+    err = normwise(y, r)
+    assert err <= TOL, err
+    # also every column on its own scale
+    for t in range(T):
+        assert normwise(y[t], r[t]) <= TOL
+
+
+def test_columns_equal_single_column_bitwise():
+    note("qmv: T-column vs 1-column bitwise, T = 1..8")
+    b, n, k, x8 = workloads.cfg2(8)
+    packed = pack(b, n, k)
+    single = [run_qmv(packed, n, k, x8[t:t + 1]) for t in range(8)]
+    for T in range(1, 9):
+        y = run_qmv(packed, n, k, x8[:T])
+        for t in range(T):
+            assert bits_equal(y[t], single[t][0]), (T, t)
+
+
+def test_column_position_does_not_matter():
+    note("qmv: the same column in every slot of an 8-column call")
+    b, n, k, x8 = workloads.cfg2(8)
+    packed = pack(b, n, k)
+    one = run_qmv(packed, n, k, x8[3:4])[0]
+    rep = run_qmv(packed, n, k, np.repeat(x8[3:4], 8, axis=0))
+    for t in range(8):
+        assert bits_equal(rep[t], one)
+
+
+def test_one_hot_columns_exact():
+    note("qmv: one-hot columns read back the decoded matrix exactly")
+    b, n, k, _ = workloads.cfg2(1)
+    packed = pack(b, n, k)
+    W = oracle.decode_blocks(b).reshape(n, k)
+    cols = [0, 1, 15, 16, 17, 31, 32, 127, 128, 2047, 4095]
+    for i in range(0, len(cols), 8):
+        cs = cols[i:i + 8]
+        x = np.zeros((len(cs), k), dtype=np.float32)
+        for t, c in enumerate(cs):
+            x[t, c] = 1.0
+        y = run_qmv(packed, n, k, x)
+        for t, c in enumerate(cs):
+            assert bits_equal(y[t], W[:, c]), c
+
+
+@pytest.mark.parametrize("n,k,T", [(16, 128, 1), (48, 384, 3), (64, 768, 5), (32, 1152, 8), (160, 2048, 2)])
+def test_integer_exact_bitwise(n, k, T):
+    """Power-of-two scales and integer activations: every partial sum is exact, so the
+    GPU must equal the oracle bitwise whatever its summation order."""
+    note(f"qmv: integer-exact n={n} k={k} T={T}")
+    rng = np.random.default_rng(n * 7 + k + T)
+    b = integer_exact_blocks(rng, n * k // 32, 6)
+    x = rng.integers(-8, 9, (T, k)).astype(np.float32)
+    y = run_qmv(pack(b, n, k), n, k, x)
+    assert bits_equal(y, oracle.qmv(b, n, k, x))
+
+
+@pytest.mark.parametrize("n,k,T", [(16, 128, 1), (48, 384, 4), (64, 768, 2), (32, 1152, 7), (256, 14336, 3)])
+def test_ragged_shapes(n, k, T):
+    """Tile-edge shapes: one tile, uneven K split over the waves, a long K."""
+    note(f"qmv: ragged n={n} k={k} T={T}")
+    rng = np.random.default_rng(n + k)
+    w = (rng.standard_normal((n, k)) * 0.02).astype(np.float32)
+    b = oracle.encode_blocks(w.reshape(-1, 32))
+    x = rng.standard_normal((T, k)).astype(np.float32)
+    y = run_qmv(pack(b, n, k), n, k, x, ldx=k + 4 * (T % 3), ldy=n + 16 * (T % 2))
+    assert normwise(y, oracle.qmv(b, n, k, x)) <= TOL
+
+
+def test_wide_dynamic_range_activations():
+    """Activations spanning many binades (exercises the exact three-part split)."""
+    note("qmv: wide dynamic range")
+    rng = np.random.default_rng(5)
+    n, k = 64, 1024
+    b = oracle.encode_blocks((rng.standard_normal((n * k // 32, 32)) * 0.02).astype(np.float32))
+    x = (rng.standard_normal((4, k)) * 2.0 ** rng.integers(-60, 60, (4, k))).astype(np.float32)
+    y = run_qmv(pack(b, n, k), n, k, x)
+    r = oracle.qmv(b, n, k, x)
+    assert normwise(y, r) <= 1e-5
+
+
+def test_deterministic():
+    note("qmv: run-to-run determinism")
+    b, n, k, x = workloads.cfg2(4)
+    packed = pack(b, n, k)
+    assert bits_equal(run_qmv(packed, n, k, x), run_qmv(packed, n, k, x))
