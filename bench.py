@@ -45,8 +45,10 @@ def build_verify_inputs(torch, iq4, synth, copies: int):
         p.copy_(packed[0])
     x = torch.from_numpy(synth.acts_f32(synth.SEED_VERIFY, synth.TAG_X, 4, k)).cuda()
     y = torch.empty((4, n), dtype=torch.float32, device="cuda")
+    wsb = iq4.iq4_qmv_workspace_size(n, k)
+    ws = torch.zeros(max(wsb, 256), dtype=torch.uint8, device="cuda")
     del w
-    return dict(n=n, k=k, packed=packed, x=x, y=y, wbytes=nbytes)
+    return dict(n=n, k=k, packed=packed, x=x, y=y, wbytes=nbytes, ws=ws, wsb=wsb)
 
 
 def cpu_baseline(min_seconds: float = 10.0):
@@ -106,44 +108,54 @@ def main():
 
     it = [0]
 
-    def mmvq(T, ev=None):
+    def mmvq(T):
         p = V["packed"][it[0] % len(V["packed"])]
         it[0] += 1
-        if ev is not None:
-            ev[0].record(stream)
-        iq4.iq4_qmv_multi(p, n, k, V["x"], k, T, V["y"], n, stream)
-        if ev is not None:
-            ev[1].record(stream)
+        iq4.iq4_qmv_multi(p, n, k, V["x"], k, T, V["y"], n, V["ws"], V["wsb"], stream)
 
-    def step(evs=None):
-        for i, T in enumerate((1, 2, 3, 4)):
-            mmvq(T, None if evs is None else evs[i])
+    def step():
+        for T in (1, 2, 3, 4):
+            mmvq(T)
 
     log(f"warmup {args.warmup} steps")
     for _ in range(args.warmup):
         step()
     torch.cuda.synchronize()
 
-    # timed region: K whole steps, bracketed by synchronisation
-    start, end = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+    # The timed region replays HIP graphs of the step's launches: per-launch CPU
+    # overhead (several us) would otherwise hide kernels that take a few us.
+    # One graph per T: R launches, each on the next weight copy (cold weights).
+    R = len(V["packed"])
+    graphs = {}
+    for T in (1, 2, 3, 4):
+        g = torch.cuda.CUDAGraph()
+        with torch.cuda.graph(g, stream=torch.cuda.Stream()):
+            s2 = torch.cuda.current_stream()
+            for r in range(R):
+                iq4.iq4_qmv_multi(V["packed"][r], n, k, V["x"], k, T, V["y"], n, V["ws"], V["wsb"], s2)
+        graphs[T] = g
+    for T in (1, 2, 3, 4):  # warm replays
+        graphs[T].replay()
     torch.cuda.synchronize()
-    start.record(stream)
-    for _ in range(args.steps):
-        step()
-    end.record(stream)
-    torch.cuda.synchronize()
-    ms_step = start.elapsed_time(end) / args.steps
 
-    # per-launch kernel durations (events around each launch, same stream)
-    evs = [[[torch.cuda.Event(enable_timing=True) for _ in range(2)] for _ in range(4)]
-           for _ in range(args.steps)]
-    for s in range(args.steps):
-        step(evs[s])
-    torch.cuda.synchronize()
+    # K steps = K x (T = 1..4) launches, timed per T with events around graph replays
+    reps = max(1, args.steps // R) if args.steps >= R else 1
     per_T = {}
-    for i, T in enumerate((1, 2, 3, 4)):
-        d = sorted(evs[s][i][0].elapsed_time(evs[s][i][1]) for s in range(args.steps))
-        per_T[T] = sum(d) / len(d)  # ms, mean
+    start, end = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+    total_ms, total_launches = 0.0, 0
+    for T in (1, 2, 3, 4):
+        torch.cuda.synchronize()
+        start.record(stream)
+        for _ in range(reps):
+            graphs[T].replay()
+        end.record(stream)
+        torch.cuda.synchronize()
+        ms = start.elapsed_time(end)
+        per_T[T] = ms / (reps * R)  # ms per launch
+        total_ms += ms
+        total_launches += reps * R
+    steps_timed = total_launches // 4
+    ms_step = total_ms / steps_timed
     tot_ms = sum(per_T.values())
     wb = V["wbytes"]
     value = 4 * wb / (tot_ms * 1e-3) / 1e9
@@ -155,7 +167,7 @@ def main():
         "value": round(value, 2),
         "unit": "GB/s",
         "n_gpus": 1,
-        "steps": args.steps,
+        "steps": steps_timed,
         "warmup": args.warmup,
         "ms_per_step": round(ms_step, 5),
         "higher_is_better": True,

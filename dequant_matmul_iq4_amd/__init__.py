@@ -35,7 +35,9 @@ SIGNATURES = {
     "iq4_dequant_blocks": (ctypes.c_int, [_c_p, _c_i64, _c_i32, _c_p, _c_p]),
     "iq4_packed_bytes": (_c_i64, [_c_i64, _c_i64]),
     "iq4_pack_weights": (ctypes.c_int, [_c_p, _c_i64, _c_i64, _c_p, _c_p]),
-    "iq4_qmv_multi": (ctypes.c_int, [_c_p, _c_i64, _c_i64, _c_p, _c_i64, _c_i32, _c_p, _c_i64, _c_p]),
+    "iq4_qmv_workspace_size": (ctypes.c_int, [_c_i64, _c_i64, ctypes.POINTER(_c_sz)]),
+    "iq4_qmv_multi": (ctypes.c_int, [_c_p, _c_i64, _c_i64, _c_p, _c_i64, _c_i32, _c_p, _c_i64, _c_p, _c_sz,
+                                     _c_p]),
     "iq4_route_topk": (ctypes.c_int, [_c_p, _c_i64, _c_i32, _c_i32, _c_p, _c_p, _c_p]),
     "iq4_moe_gather": (ctypes.c_int, [_c_p, _c_i64, _c_i32, _c_p, _c_p, _c_p, _c_p, _c_p]),
     "iq4_moe_workspace_size": (ctypes.c_int, [_c_i64, _c_i32, _c_i32, _c_i64, _c_i64, _c_i32,
@@ -118,8 +120,15 @@ def iq4_pack_weights(blocks, n, k, packed, stream=None):
     _call("iq4_pack_weights", _ptr(blocks), n, k, _ptr(packed), _stream(stream))
 
 
-def iq4_qmv_multi(packed, n, k, x, ldx, T, y, ldy, stream=None):
-    _call("iq4_qmv_multi", _ptr(packed), n, k, _ptr(x), ldx, T, _ptr(y), ldy, _stream(stream))
+def iq4_qmv_workspace_size(n, k) -> int:
+    out = _c_sz(0)
+    _call("iq4_qmv_workspace_size", n, k, ctypes.byref(out))
+    return out.value
+
+
+def iq4_qmv_multi(packed, n, k, x, ldx, T, y, ldy, workspace=None, ws_bytes=0, stream=None):
+    _call("iq4_qmv_multi", _ptr(packed), n, k, _ptr(x), ldx, T, _ptr(y), ldy, _ptr(workspace), ws_bytes,
+          _stream(stream))
 
 
 def iq4_route_topk(logits, n_tok, n_expert, top_k, ids, w, stream=None):

@@ -4,9 +4,10 @@
 #include <stdarg.h>
 #include <stdio.h>
 
-#include "../../include/iq4.h"
+#include "iq4.h"
 #include "common.hpp"
 #include "launch.hpp"
+#include "qmv.hpp"
 
 namespace iq4 {
 
@@ -92,8 +93,18 @@ int iq4_pack_weights(const void* blocks, int64_t n, int64_t k, void* packed, voi
   return launch_pack(blocks, n, k, packed, as_stream(stream));
 }
 
+int iq4_qmv_workspace_size(int64_t n, int64_t k, size_t* bytes) {
+  clear_error();
+  if (!bytes) return set_error(IQ4_E_ARG, "iq4_qmv_workspace_size: null bytes");
+  *bytes = 0;
+  if (int e = check_matrix("iq4_qmv_workspace_size", n, k)) return e;
+  *bytes = (size_t)qmv_workspace_bytes(n, k);
+  return IQ4_OK;
+}
+
 int iq4_qmv_multi(const void* packed, int64_t n, int64_t k, const float* x, int64_t ldx,
-                  int32_t T, float* y, int64_t ldy, void* stream) {
+                  int32_t T, float* y, int64_t ldy, void* workspace, size_t ws_bytes,
+                  void* stream) {
   clear_error();
   if (int e = check_matrix("iq4_qmv_multi", n, k)) return e;
   if (T < 1 || T > 8) return set_error(IQ4_E_ARG, "iq4_qmv_multi: T must be in 1..8 (got %d)", T);
@@ -102,7 +113,14 @@ int iq4_qmv_multi(const void* packed, int64_t n, int64_t k, const float* x, int6
   if (!packed || !x || !y) return set_error(IQ4_E_ARG, "iq4_qmv_multi: null pointer");
   if (!aligned(packed, 256) || !aligned(x, 16) || !aligned(y, 4))
     return set_error(IQ4_E_ALIGN, "iq4_qmv_multi: packed must be 256-byte, x 16-byte, y 4-byte aligned");
-  return launch_qmv(static_cast<const uint8_t*>(packed), n, k, x, ldx, T, y, ldy, as_stream(stream));
+  const int64_t need = qmv_workspace_bytes(n, k);
+  if (need > 0) {
+    if (!workspace || ws_bytes < (size_t)need)
+      return set_error(IQ4_E_WORKSPACE, "iq4_qmv_multi: needs a workspace of %lld bytes", (long long)need);
+    if (!aligned(workspace, 256)) return set_error(IQ4_E_ALIGN, "iq4_qmv_multi: workspace must be 256-byte aligned");
+  }
+  return launch_qmv(static_cast<const uint8_t*>(packed), n, k, x, ldx, T, y, ldy, workspace,
+                    as_stream(stream));
 }
 
 int iq4_route_topk(const float* logits, int64_t n_tok, int32_t n_expert, int32_t top_k,

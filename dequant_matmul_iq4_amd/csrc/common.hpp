@@ -19,6 +19,22 @@ constexpr int kNibbleBytes = 16;
 constexpr int8_t kCodebook[16] = {-127, -104, -83, -65, -49, -35, -22, -10,
                                   1,    13,   25,  38,  53,  69,  89,  113};
 
+// Register-only level lookup (no memory access): the 16 levels as int8 bytes in four
+// 32-bit immediates, one byte picked with v_perm_b32.
+constexpr uint32_t pack_levels(int i) {
+  return (uint32_t)(uint8_t)kCodebook[i] | ((uint32_t)(uint8_t)kCodebook[i + 1] << 8) |
+         ((uint32_t)(uint8_t)kCodebook[i + 2] << 16) | ((uint32_t)(uint8_t)kCodebook[i + 3] << 24);
+}
+constexpr uint32_t kLevels0 = pack_levels(0), kLevels1 = pack_levels(4);
+constexpr uint32_t kLevels2 = pack_levels(8), kLevels3 = pack_levels(12);
+
+__device__ __forceinline__ int level_of(uint32_t q) {
+  const uint32_t sel = q & 7u;  // byte 0..3 of the second operand, 4..7 of the first
+  const uint32_t b = (q < 8u) ? __builtin_amdgcn_perm(kLevels1, kLevels0, sel)
+                              : __builtin_amdgcn_perm(kLevels3, kLevels2, sel);
+  return (int)(int8_t)(b & 0xFFu);
+}
+
 // Packed layout: 16-row x 4-block tiles, 1 KiB of indices + 128 B of scales each.
 constexpr int kTileRows = 16;
 constexpr int kTileBlocks = 4;

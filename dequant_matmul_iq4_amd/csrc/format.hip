@@ -62,7 +62,7 @@ __global__ void __launch_bounds__(256) dequant_kernel(const uint16_t* __restrict
   int64_t b = i >> 2;
   int p = (int)(i & 3);
   const uint16_t* blk = blocks + b * (kBlockBytes / 2);
-  float d = h2f(blk[0]);
+  const uint16_t dbits = blk[0];
   uint32_t bytes[8];
 #pragma unroll
   for (int j = 0; j < 4; ++j) {
@@ -70,20 +70,27 @@ __global__ void __launch_bounds__(256) dequant_kernel(const uint16_t* __restrict
     bytes[2 * j] = v & 0xFF;
     bytes[2 * j + 1] = v >> 8;
   }
-  float w[8];
+  uint32_t q[8];
 #pragma unroll
-  for (int j = 0; j < 8; ++j) {
-    uint32_t q = (p < 2) ? (bytes[j] & 0xF) : (bytes[j] >> 4);
-    w[j] = d * (float)kCodebook[q];
-  }
+  for (int j = 0; j < 8; ++j) q[j] = (p < 2) ? (bytes[j] & 0xF) : (bytes[j] >> 4);
   if (F16) {
+    // One binary16 multiply d * c (both exact in binary16) rounds the exact product
+    // once to nearest even: the binary16 rounding of the exact fp32 decode, with
+    // subnormals and signed zeros kept.
+    const uint32_t dd = (uint32_t)dbits | ((uint32_t)dbits << 16);
     uint32_t h[4];
 #pragma unroll
-    for (int j = 0; j < 4; ++j)
-      h[j] = (uint32_t)__half_as_ushort(__float2half_rn(w[2 * j])) |
-             ((uint32_t)__half_as_ushort(__float2half_rn(w[2 * j + 1])) << 16);
+    for (int j = 0; j < 4; ++j) {
+      const uint32_t cc = (uint32_t)__half_as_ushort(__int2half_rn(level_of(q[2 * j]))) |
+                          ((uint32_t)__half_as_ushort(__int2half_rn(level_of(q[2 * j + 1]))) << 16);
+      h[j] = pk_mul_f16(dd, cc);
+    }
     reinterpret_cast<uint4*>(out)[i] = make_uint4(h[0], h[1], h[2], h[3]);
   } else {
+    const float d = h2f(dbits);
+    float w[8];
+#pragma unroll
+    for (int j = 0; j < 8; ++j) w[j] = d * (float)level_of(q[j]);  // exact
     float4* o = reinterpret_cast<float4*>(out) + 2 * i;
     o[0] = make_float4(w[0], w[1], w[2], w[3]);
     o[1] = make_float4(w[4], w[5], w[6], w[7]);

@@ -1,0 +1,37 @@
+// gemm.hpp -- arguments of the dequant-fused GEMM kernel (gemm.hip).
+#pragma once
+#include "common.hpp"
+
+namespace iq4 {
+
+enum GemmMode { kGemmDense = 0, kGemmGateUp = 1, kGemmDown = 2 };
+
+struct GemmArgs {
+  const uint16_t* A;        // binary16 activations, rows of lda elements
+  int64_t lda;
+  const uint8_t* W0;        // packed weights (DENSE: W; GATEUP: gate bank; DOWN: down bank)
+  const uint8_t* W1;        // GATEUP: up bank
+  int64_t w_expert_stride;  // bytes between experts' packed matrices
+  int64_t N, K;             // weight rows and reduction length of one matrix
+  int64_t M;                // DENSE: rows of A in this launch
+  float* C;                 // DENSE: output [M][ldc]; DOWN: per-pair rows [pairs][ldc]
+  int64_t ldc;
+  uint16_t* H;              // GATEUP: h = silu(g) * u as binary16 [pairs][ldh] (sorted order)
+  int64_t ldh;
+  const int32_t* tiles;     // grouped: (expert, m tile) pairs
+  const int32_t* num_tiles; // grouped: number of valid entries in `tiles`
+  int64_t n_tiles_n;        // grouped: workgroups per m tile along N
+  const int32_t* offsets;   // grouped: per-expert start in the sorted pair list [E+1]
+  const int32_t* pairs;     // grouped: sorted pair ids
+  const float* gate_w;      // DOWN: gate weight of each pair (indexed by pair id)
+  int top_k;
+  float* out;               // DOWN with atomic combine: [n_tok][ldo]
+  int64_t ldo;
+  int atomic;
+};
+
+int launch_qgemm_dense(const uint8_t* packed, int64_t n, int64_t k, const uint16_t* x, int64_t m,
+                       int64_t ldx, float* y, int64_t ldy, int64_t chunk, hipStream_t s);
+int launch_qgemm_grouped(int mode, const GemmArgs& a, int64_t max_tiles, hipStream_t s);
+
+}  // namespace iq4

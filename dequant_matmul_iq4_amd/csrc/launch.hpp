@@ -10,7 +10,7 @@ int launch_dequant(const void* blocks, int64_t nb, bool f16, void* out, hipStrea
 int launch_pack(const void* blocks, int64_t n, int64_t k, void* packed, hipStream_t s);
 
 int launch_qmv(const uint8_t* packed, int64_t n, int64_t k, const float* x, int64_t ldx, int T,
-               float* y, int64_t ldy, hipStream_t s);
+               float* y, int64_t ldy, void* workspace, hipStream_t s);
 
 int launch_route_topk(const float* logits, int64_t n_tok, int n_expert, int top_k, int32_t* ids,
                       float* w, hipStream_t s);

@@ -19,24 +19,42 @@
 //    three parts are added (hi + mid) + lo.
 //
 // Column invariance.  Token t's value never meets another token's: it sits in matrix
-// row 4s + (t mod 4) of MFMA group t / 4, the per-block scaling and the reductions run
-// the same instruction sequence for every t, and the wave / K-slice split depends on K
-// only.  Column t of a T-column call is therefore bitwise the 1-column call on token t
+// row 4s + (t mod 4) of the pass that holds it, the per-block scaling and the
+// reductions run the same instruction sequence for every t, and the wave / K-slice
+// split depends on K only.  Column t of a T-column call is therefore bitwise the 1-column call on token t
 // (the property page 1's verify window relies on: each window token reproduces plain
 // greedy decode bit for bit).
 //
+// Work split.  A workgroup (up to 8 waves) owns RG row tiles (16 rows each) and a slice
+// of K of at most 128 blocks; each wave owns a contiguous run of at most 4 quads
+// (16 blocks) of the slice and issues every weight load of that run at kernel entry,
+// so all of the matrix is in flight from the start (the pages' lesson from their
+// interleaved matvec: one block in flight per warp starved it).  The slice's
+// activations are staged once in LDS, already split and in fragment order (a wave's
+// fragment read is one conflict-free ds_read_b128), up to 4 columns per pass.  A K
+// above 4096 is cut into S slices handled by S workgroups, whose partial sums go to
+// a caller workspace; the last workgroup to arrive adds them in slice order
+// (deterministic).  RG, S and the wave runs depend on the matrix shape only, never
+// on T.
+//
 // Memory.  Weights come in the packed tile layout: per 16-row x 4-block tile each lane
 // issues one 128-bit load of indices (coalesced 1 KiB per wave) and one 64-bit load
-// of its row's four scales; all loads of a wave's chunk are issued before any decode
-// (page 2 found one weight block in flight per warp to be the bottleneck of its
-// interleaved matvec).  The index-to-level decode is a byte-indexed table in LDS
-// (one byte = two 4-bit indices -> two bf16 levels).
+// of its row's four scales.  The index-to-level decode is a byte-indexed table in LDS
+// (one byte = two 4-bit indices -> two bf16 levels), built from register immediates.
 #include "common.hpp"
 #include "launch.hpp"
+#include "qmv.hpp"
 
 namespace iq4 {
 
-constexpr int kQmvMaxWaves = 8;
+constexpr int kWaves = 8;              // waves per workgroup (at most)
+constexpr int kMaxWaveQuads = 4;       // quads per wave: all of a wave's weights in registers
+constexpr int kSliceQuads = kWaves * kMaxWaveQuads;  // 32 quads = 128 blocks = K 4096
+constexpr int kSliceBlocks = 4 * kSliceQuads;
+constexpr int kCols = 4;               // columns per pass (rows 4s + t of the A operand)
+constexpr int kMaxTasks = 4;           // staging tasks per thread (see qmv_plan)
+constexpr int kDenseRG = 1;            // row tiles per workgroup (dense, down)
+constexpr int kGateUpRG = 1;           // row tiles per matrix (gate + up)
 
 __device__ __forceinline__ uint32_t bf16_of_level(int c) {
   return __float_as_uint((float)c) >> 16;  // exact: |c| <= 127
@@ -53,119 +71,312 @@ __device__ __forceinline__ uint32_t split_part(float v, int s) {
   return __float_as_uint(r2) >> 16;
 }
 
-// A fragment of one block for lane (g, row 4s + tt) of token group `grp`: the 8 values
-// x[32kb + 4g + j] (low half of VGPR j) and x[32kb + 16 + 4g + j] (high half), part s.
-__device__ __forceinline__ u32x4 x_fragment(const float* __restrict__ x, int64_t ldx, int T,
-                                            int grp, int s, int tt, int g, int64_t kb) {
-  const int t = 4 * grp + tt;
-  u32x4 a = {0u, 0u, 0u, 0u};
-  if (s < 3 && t < T) {
-    const float* p = x + (int64_t)t * ldx + kb * kQK + 4 * g;
-    float4 xa = *reinterpret_cast<const float4*>(p);
-    float4 xb = *reinterpret_cast<const float4*>(p + 16);
-    a[0] = split_part(xa.x, s) | (split_part(xb.x, s) << 16);
-    a[1] = split_part(xa.y, s) | (split_part(xb.y, s) << 16);
-    a[2] = split_part(xa.z, s) | (split_part(xb.z, s) << 16);
-    a[3] = split_part(xa.w, s) | (split_part(xb.w, s) << 16);
-  }
-  return a;
+// Column t of the call: where its activations live.
+__device__ __forceinline__ const float* column_ptr(const QmvArgs& a, int mode, int64_t seg0,
+                                                   int64_t t) {
+  if (mode == kQmvDense) return a.x + t * a.ldx;
+  if (mode == kQmvGateUp) return a.x + (int64_t)(a.pairs[seg0 + t] / a.top_k) * a.ldx;
+  return a.x + (seg0 + t) * a.ldx;  // kQmvDown: h rows in pair-sorted order
 }
 
-// One workgroup per 16-row tile; its waves split K into runs of whole 4-block quads.
-template <bool TWO>
-__global__ void __launch_bounds__(512) qmv_kernel(const uint8_t* __restrict__ packed, int kq_n,
-                                                  int64_t nibble_bytes, const float* __restrict__ x,
-                                                  int64_t ldx, int T, float* __restrict__ y,
-                                                  int64_t ldy, int quads_per_wave) {
+// A-fragment store of the slice in LDS: [block][k-group g][row 4s+t], padding rows
+// (s = 3) omitted, 16 bytes each.
+constexpr int kFragRows = 12;
+constexpr int kFragBytes = 4 * kFragRows * 16;  // 768 B per block
+
+// One workgroup per RG row tiles (and per expert in the grouped modes) and K slice.
+template <int MODE, int RG>
+__global__ void __launch_bounds__(512) qmv_kernel(QmvArgs a) {
+  constexpr int NMAT = (MODE == kQmvGateUp) ? 2 : 1;
+  constexpr int ROWS = RG * kTileRows;
+  constexpr int XBYTES = kSliceBlocks * kFragBytes;
+  static_assert(kWaves * NMAT * RG * 64 * 16 <= XBYTES, "reduction scratch does not fit");
   __shared__ uint32_t lut[256];
-  __shared__ f32x4 red[kQmvMaxWaves][TWO ? 2 : 1][64];
+  __shared__ __attribute__((aligned(16))) uint8_t xs[XBYTES + 256];  // + room for padding-row reads
+  __shared__ int s_last;
 
   const int tid = threadIdx.x;
-  const int lane = tid & 63, wave = tid >> 6, nwaves = blockDim.x >> 6;
-  for (int i = tid; i < 256; i += blockDim.x)
-    lut[i] = bf16_of_level(kCodebook[i & 15]) | (bf16_of_level(kCodebook[i >> 4]) << 16);
-
-  const int64_t rt = blockIdx.x;
-  const int g = lane >> 4, c = lane & 15;
+  const int lane = tid & 63, wave = tid >> 6, nwaves = (int)(blockDim.x >> 6);
+  const int c = lane & 15, g = lane >> 4;
   const int s = c >> 2, tt = c & 3;
-  const int q0 = wave * quads_per_wave;
-  const int q1 = min(q0 + quads_per_wave, kq_n);
-  const uint8_t* tiles = packed + rt * kq_n * kTileNibbleBytes + lane * 16;
-  const uint8_t* scales = packed + nibble_bytes + rt * kq_n * kTileScaleBytes + c * 8;
 
-  f32x4 acc0 = {0.f, 0.f, 0.f, 0.f}, acc1 = {0.f, 0.f, 0.f, 0.f};
-  __syncthreads();
+  // ---- tile of this workgroup ---------------------------------------------------------
+  int64_t rg, seg0 = 0, ncols;
+  int slice = 0;
+  const uint8_t* W[2] = {a.W0, a.W1};
+  if (MODE == kQmvDense) {
+    rg = blockIdx.x / a.S;
+    slice = (int)(blockIdx.x % a.S);
+    ncols = a.T;
+  } else {
+    const int64_t e = blockIdx.x / a.rg_n;
+    rg = blockIdx.x % a.rg_n;
+    seg0 = a.offsets[e];
+    ncols = a.offsets[e + 1] - seg0;
+    if (ncols == 0) return;
+    W[0] += e * a.w_expert_stride;
+    W[1] += e * a.w_expert_stride;
+  }
+  const int kq_n = a.kq_n;
+  const int kqa = slice * a.slice_quads;                 // first quad of the slice
+  const int nq_slice = min(a.slice_quads, kq_n - kqa);   // quads in the slice
+  const int wq0 = wave * a.wave_quads;                   // this wave's quads (slice-relative)
+  const int wq1 = min(wq0 + a.wave_quads, nq_slice);
 
-  for (int qc = q0; qc < q1; qc += 4) {
-    const int nq = min(4, q1 - qc);
-    uint4 nib[4];
-    uint2 sc[4];
+  // This wave's activations: blocks [4 * wq0, 4 * wq1) of the slice, staged by the wave
+  // itself into its own LDS region (no workgroup barrier before the products).
+  const int wblk = 4 * (wq1 - wq0);  // blocks of this wave (0 for an idle wave)
+  uint8_t* xw = xs + wave * (4 * kMaxWaveQuads) * kFragBytes;
+  float4 xr[kMaxTasks][2];
+  auto load_x = [&](int64_t t0, int T) {  // tasks (column t, block, k-group gg), 64 lanes
+    const int ntask = T * wblk * 4;
 #pragma unroll
-    for (int u = 0; u < 4; ++u) {  // every load of the chunk first (tail clamped)
-      const int q = qc + min(u, nq - 1);
-      nib[u] = *reinterpret_cast<const uint4*>(tiles + (int64_t)q * kTileNibbleBytes);
-      sc[u] = *reinterpret_cast<const uint2*>(scales + (int64_t)q * kTileScaleBytes);
+    for (int i = 0; i < kMaxTasks; ++i) {
+      const int task = lane + 64 * i;
+      if (task < ntask) {
+        const int gg = task & 3, bl = (task >> 2) % wblk, t = (task >> 2) / wblk;
+        const float* p = column_ptr(a, MODE, seg0, t0 + t) + ((int64_t)(kqa + wq0) * 4 + bl) * kQK + 4 * gg;
+        xr[i][0] = *reinterpret_cast<const float4*>(p);
+        xr[i][1] = *reinterpret_cast<const float4*>(p + 16);
+      }
     }
+  };
+  auto store_x = [&](int T) {  // split and store in fragment order
+    const int ntask = T * wblk * 4;
 #pragma unroll
-    for (int u = 0; u < 4; ++u) {
-      if (u >= nq) break;
-      const int64_t kb0 = (int64_t)(qc + u) * kTileBlocks;
-      const uint32_t words[4] = {nib[u].x, nib[u].y, nib[u].z, nib[u].w};
-      const uint32_t sw[2] = {sc[u].x, sc[u].y};
+    for (int i = 0; i < kMaxTasks; ++i) {
+      const int task = lane + 64 * i;
+      if (task < ntask) {
+        const int gg = task & 3, bl = (task >> 2) % wblk, t = (task >> 2) / wblk;
+        const float4 xa = xr[i][0], xb = xr[i][1];
+        uint8_t* dst = xw + (bl * 4 + gg) * (kFragRows * 16) + t * 16;
 #pragma unroll
-      for (int j = 0; j < 4; ++j) {
-        const uint32_t w = words[j];
-        u32x4 b;
-        b[0] = lut[w & 0xFF];
-        b[1] = lut[(w >> 8) & 0xFF];
-        b[2] = lut[(w >> 16) & 0xFF];
-        b[3] = lut[w >> 24];
-        const float d = h2f((uint16_t)(sw[j >> 1] >> (16 * (j & 1))));
-        const f32x4 zero = {0.f, 0.f, 0.f, 0.f};
-        f32x4 r0 = mfma_bf16(x_fragment(x, ldx, T, 0, s, tt, g, kb0 + j), b, zero);
-#pragma unroll
-        for (int i = 0; i < 4; ++i) acc0[i] = __builtin_fmaf(d, r0[i], acc0[i]);
-        if (TWO) {
-          f32x4 r1 = mfma_bf16(x_fragment(x, ldx, T, 1, s, tt, g, kb0 + j), b, zero);
-#pragma unroll
-          for (int i = 0; i < 4; ++i) acc1[i] = __builtin_fmaf(d, r1[i], acc1[i]);
+        for (int sp = 0; sp < 3; ++sp) {
+          uint4 f;
+          f.x = split_part(xa.x, sp) | (split_part(xb.x, sp) << 16);
+          f.y = split_part(xa.y, sp) | (split_part(xb.y, sp) << 16);
+          f.z = split_part(xa.z, sp) | (split_part(xb.z, sp) << 16);
+          f.w = split_part(xa.w, sp) | (split_part(xb.w, sp) << 16);
+          *reinterpret_cast<uint4*>(dst + sp * 4 * 16) = f;
         }
       }
     }
-  }
+    // LDS accesses of one wave execute in order: the wave's reads below see these
+    // writes; this only keeps the compiler from moving them.
+    __builtin_amdgcn_fence(__ATOMIC_RELEASE, "wavefront");
+    __builtin_amdgcn_wave_barrier();
+    __builtin_amdgcn_fence(__ATOMIC_ACQUIRE, "wavefront");
+  };
 
-  // Lane (g, c) holds D[4g + i][c]: part s = g, token 4 * grp + i, weight row c.
-  red[wave][0][lane] = acc0;
-  if (TWO) red[wave][TWO ? 1 : 0][lane] = acc1;
-  __syncthreads();
-  if (tid < T * 16) {
-    const int t = tid >> 4, r = tid & 15;
-    const int grp = TWO ? (t >> 2) : 0, i = t & 3;
-    float part[3];
+  // The first pass's activations go out first (small), then every weight load.
+  load_x(0, (int)min((int64_t)kCols, ncols));
+  uint4 nib[kMaxWaveQuads][NMAT][RG];
+  uint2 scl[kMaxWaveQuads][NMAT][RG];
 #pragma unroll
-    for (int p = 0; p < 3; ++p) {
-      float a = red[0][grp][16 * p + r][i];
-      for (int w2 = 1; w2 < nwaves; ++w2) a += red[w2][grp][16 * p + r][i];
-      part[p] = a;
+  for (int r = 0; r < RG; ++r) {
+    const int64_t rt = min(rg * RG + r, a.nt - 1);  // clamped: rows past n are dropped
+#pragma unroll
+    for (int m = 0; m < NMAT; ++m) {
+      const uint8_t* tp = W[m] + (rt * kq_n + kqa) * kTileNibbleBytes + lane * 16;
+      const uint8_t* sp = W[m] + a.nibble_bytes + (rt * kq_n + kqa) * kTileScaleBytes + c * 8;
+#pragma unroll
+      for (int u = 0; u < kMaxWaveQuads; ++u) {
+        const int q = min(wq0 + u, max(wq1 - 1, 0));  // clamped; unused when past the range
+        nib[u][m][r] = *reinterpret_cast<const uint4*>(tp + (int64_t)q * kTileNibbleBytes);
+        scl[u][m][r] = *reinterpret_cast<const uint2*>(sp + (int64_t)q * kTileScaleBytes);
+      }
     }
-    y[(int64_t)t * ldy + rt * kTileRows + r] = (part[0] + part[1]) + part[2];
+  }
+  for (int i = tid; i < 256; i += blockDim.x)
+    lut[i] = bf16_of_level(level_of(i & 15)) | (bf16_of_level(level_of(i >> 4)) << 16);
+  __syncthreads();  // the table (LDS only: no wait on the loads in flight)
+
+  for (int64_t t0 = 0; t0 < ncols; t0 += kCols) {  // passes of up to 4 columns
+    const int T = (int)min((int64_t)kCols, ncols - t0);
+    if (t0 > 0) load_x(t0, T);
+    store_x(T);
+
+    // ---- the wave's quads: per quad, every LDS read first, then 4 x NMAT x RG
+    // independent MFMAs, then the scale FMAs.  Lanes of padding rows (s = 3 or a
+    // column >= T) read whatever lies there: an MFMA output row depends on its own A row
+    // only, and those rows are never used.
+    f32x4 acc[NMAT][RG];
+#pragma unroll
+    for (int m = 0; m < NMAT; ++m)
+#pragma unroll
+      for (int r = 0; r < RG; ++r) acc[m][r] = f32x4{0.f, 0.f, 0.f, 0.f};
+#pragma unroll
+    for (int u = 0; u < kMaxWaveQuads; ++u) {
+      if (wq0 + u >= wq1) break;
+      u32x4 xf[4];
+      u32x4 bf[4][NMAT][RG];
+#pragma unroll
+      for (int j = 0; j < 4; ++j) {
+        const int bl = 4 * u + j;  // block within this wave's run
+        xf[j] = *reinterpret_cast<const u32x4*>(xw + (bl * 4 + g) * (kFragRows * 16) + c * 16);
+#pragma unroll
+        for (int m = 0; m < NMAT; ++m)
+#pragma unroll
+          for (int r = 0; r < RG; ++r) {
+            const uint4 nb = nib[u][m][r];
+            const uint32_t w = (j == 0) ? nb.x : (j == 1) ? nb.y : (j == 2) ? nb.z : nb.w;
+            bf[j][m][r][0] = lut[w & 0xFF];
+            bf[j][m][r][1] = lut[(w >> 8) & 0xFF];
+            bf[j][m][r][2] = lut[(w >> 16) & 0xFF];
+            bf[j][m][r][3] = lut[w >> 24];
+          }
+      }
+      f32x4 prod[4][NMAT][RG];
+#pragma unroll
+      for (int j = 0; j < 4; ++j)
+#pragma unroll
+        for (int m = 0; m < NMAT; ++m)
+#pragma unroll
+          for (int r = 0; r < RG; ++r) prod[j][m][r] = mfma_bf16(xf[j], bf[j][m][r], f32x4{0.f, 0.f, 0.f, 0.f});
+#pragma unroll
+      for (int j = 0; j < 4; ++j)
+#pragma unroll
+        for (int m = 0; m < NMAT; ++m)
+#pragma unroll
+          for (int r = 0; r < RG; ++r) {
+            const uint2 sc = scl[u][m][r];
+            const uint32_t sw = (j < 2) ? sc.x : sc.y;
+            const float d = h2f((uint16_t)(sw >> (16 * (j & 1))));
+#pragma unroll
+            for (int i = 0; i < 4; ++i) acc[m][r][i] = __builtin_fmaf(d, prod[j][m][r][i], acc[m][r][i]);
+          }
+    }
+    __syncthreads();  // every wave is done reading the staged activations
+
+    // ---- reduction over the waves' K runs, then the three parts ---------------------
+    // Lane (g, c) holds D[4g + i][c]: part s = g, column i, weight row c.
+    f32x4* red = reinterpret_cast<f32x4*>(xs);
+#pragma unroll
+    for (int m = 0; m < NMAT; ++m)
+#pragma unroll
+      for (int r = 0; r < RG; ++r) red[((wave * NMAT + m) * RG + r) * 64 + lane] = acc[m][r];
+    __syncthreads();
+    const int nout = T * ROWS;
+    const int t = tid / ROWS, rr = tid % ROWS;
+    const int r = rr >> 4, row = rr & 15;
+    float v[NMAT];
+    if (tid < nout) {
+#pragma unroll
+      for (int m = 0; m < NMAT; ++m) {
+        float part[3];
+#pragma unroll
+        for (int p = 0; p < 3; ++p) {
+          float sum = red[((0 * NMAT + m) * RG + r) * 64 + 16 * p + row][t];
+          for (int w2 = 1; w2 < nwaves; ++w2) sum += red[((w2 * NMAT + m) * RG + r) * 64 + 16 * p + row][t];
+          part[p] = sum;
+        }
+        v[m] = (part[0] + part[1]) + part[2];
+      }
+    }
+    const int64_t col = rg * ROWS + rr;  // output row index (weight row)
+    const bool col_ok = col < a.n;
+    if (MODE == kQmvDense) {
+      if (a.S == 1) {
+        if (tid < nout && col_ok) a.y[(t0 + t) * a.ldy + col] = v[0];
+      } else {
+        // split K: partial sums to the workspace; the last of the S workgroups of this
+        // row group adds them in slice order.  The partials are written and read with
+        // agent-scope atomic stores / loads, which go to the device coherence point
+        // one access at a time, so no cache-wide writeback or invalidate is needed;
+        // s_waitcnt(0) makes every store complete before this workgroup's arrival is
+        // counted, and the last arriver issues its loads only after seeing the count.
+        float* part = a.partials + (rg * a.S + slice) * (kCols * ROWS);
+        if (tid < nout)
+          __hip_atomic_store(part + t * ROWS + rr, v[0], __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
+        __builtin_amdgcn_s_waitcnt(0);
+        __syncthreads();
+        if (tid == 0)
+          s_last = __hip_atomic_fetch_add(a.counters + rg, 1, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT) ==
+                   a.S - 1;
+        __syncthreads();
+        if (s_last) {
+          if (tid < nout && col_ok) {
+            const float* p0 = a.partials + rg * a.S * (kCols * ROWS) + t * ROWS + rr;
+            float sum = __hip_atomic_load(p0, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
+            for (int sl = 1; sl < a.S; ++sl)
+              sum += __hip_atomic_load(p0 + sl * (kCols * ROWS), __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
+            a.y[(t0 + t) * a.ldy + col] = sum;
+          }
+          // leaves the workspace ready for the next call
+          if (tid == 0) __hip_atomic_store(a.counters + rg, 0, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
+        }
+      }
+    } else if (MODE == kQmvGateUp) {
+      if (tid < nout && col_ok) {
+        const float gv = v[0], uv = v[NMAT - 1];
+        a.y[(seg0 + t0 + t) * a.ldy + col] = gv / (1.0f + expf(-gv)) * uv;  // SwiGLU
+      }
+    } else {
+      if (tid < nout && col_ok) {
+        const int p = a.pairs[seg0 + t0 + t];
+        a.y[(int64_t)p * a.ldy + col] = a.gate_w[p] * v[0];
+      }
+    }
+    if (t0 + kCols < ncols) __syncthreads();  // LDS is reused by the next pass
   }
 }
 
-int launch_qmv(const uint8_t* packed, int64_t n, int64_t k, const float* x, int64_t ldx, int T,
-               float* y, int64_t ldy, hipStream_t s) {
-  const int kq_n = (int)(k / kTileK);
-  const int nwaves = kq_n < kQmvMaxWaves ? kq_n : kQmvMaxWaves;
-  const int qpw = (kq_n + nwaves - 1) / nwaves;
-  const int64_t nibble_bytes = n * (k / kQK) * kNibbleBytes;
-  dim3 grid((unsigned)(n / kTileRows)), block(64 * nwaves);
-  if (T > 4)
-    hipLaunchKernelGGL(qmv_kernel<true>, grid, block, 0, s, packed, kq_n, nibble_bytes, x, ldx, T,
-                       y, ldy, qpw);
-  else
-    hipLaunchKernelGGL(qmv_kernel<false>, grid, block, 0, s, packed, kq_n, nibble_bytes, x, ldx,
-                       T, y, ldy, qpw);
+// Shape-only launch plan (never depends on T): K is cut into slices of at most
+// kSliceQuads quads (more than one slice only for K > 4096), each wave of a workgroup
+// owns a contiguous run of at most kMaxWaveQuads quads of the slice.
+static void qmv_plan(QmvArgs& a, int64_t n, int64_t k, int rg_rows) {
+  a.n = n;
+  a.nt = n / kTileRows;
+  a.kq_n = (int)(k / kTileK);
+  a.nibble_bytes = n * (k / kQK) * kNibbleBytes;
+  a.rg_n = (a.nt + rg_rows - 1) / rg_rows;
+  a.S = (a.kq_n + kSliceQuads - 1) / kSliceQuads;
+  a.slice_quads = (a.kq_n + a.S - 1) / a.S;
+  a.wave_quads = (a.slice_quads + kWaves - 1) / kWaves;
+  a.nwaves = (a.slice_quads + a.wave_quads - 1) / a.wave_quads;
+}
+
+int64_t qmv_workspace_bytes(int64_t n, int64_t k) {
+  QmvArgs a{};
+  qmv_plan(a, n, k, kDenseRG);
+  if (a.S == 1) return 0;
+  return a.rg_n * a.S * kCols * kDenseRG * kTileRows * (int64_t)sizeof(float) + 256 + a.rg_n * 4;
+}
+
+template <int MODE, int RG>
+static int launch_mode(const QmvArgs& a, int64_t grid) {
+  hipLaunchKernelGGL((qmv_kernel<MODE, RG>), dim3((unsigned)grid), dim3(64 * a.nwaves), 0, a.stream, a);
   return check_launch("qmv_kernel");
+}
+
+int launch_qmv(const uint8_t* packed, int64_t n, int64_t k, const float* x, int64_t ldx, int T,
+               float* y, int64_t ldy, void* workspace, hipStream_t s) {
+  QmvArgs a{};
+  a.W0 = packed;
+  a.x = x;
+  a.ldx = ldx;
+  a.T = T;
+  a.y = y;
+  a.ldy = ldy;
+  a.stream = s;
+  qmv_plan(a, n, k, kDenseRG);
+  if (a.S > 1) {
+    const int64_t pbytes = a.rg_n * a.S * kCols * kDenseRG * kTileRows * (int64_t)sizeof(float);
+    a.partials = static_cast<float*>(workspace);
+    a.counters = reinterpret_cast<int*>(static_cast<uint8_t*>(workspace) + ((pbytes + 255) / 256) * 256);
+  }
+  return launch_mode<kQmvDense, kDenseRG>(a, a.rg_n * a.S);
+}
+
+int launch_qmv_grouped(int mode, QmvArgs a, int64_t n, int64_t k, int n_expert) {
+  if (mode == kQmvGateUp) {
+    qmv_plan(a, n, k, kGateUpRG);
+    if (a.S != 1) return set_error(-3, "grouped matvec: K above 4096 is not supported");
+    return launch_mode<kQmvGateUp, kGateUpRG>(a, (int64_t)n_expert * a.rg_n);
+  }
+  qmv_plan(a, n, k, kDenseRG);
+  if (a.S != 1) return set_error(-3, "grouped matvec: K above 4096 is not supported");
+  return launch_mode<kQmvDown, kDenseRG>(a, (int64_t)n_expert * a.rg_n);
 }
 
 }  // namespace iq4

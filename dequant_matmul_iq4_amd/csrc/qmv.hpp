@@ -1,0 +1,33 @@
+// qmv.hpp -- arguments of the T-column matvec kernel (qmv.hip).
+#pragma once
+#include "common.hpp"
+
+namespace iq4 {
+
+enum QmvMode { kQmvDense = 0, kQmvGateUp = 1, kQmvDown = 2 };
+
+struct QmvArgs {
+  const uint8_t* W0;        // packed weights (DENSE: W; GATEUP: gate bank; DOWN: down bank)
+  const uint8_t* W1;        // GATEUP: up bank
+  int64_t w_expert_stride;  // bytes between experts' packed matrices
+  const float* x;           // DENSE: X [T][ldx]; GATEUP: X [n_tok][ldx]; DOWN: h [pairs][ldx]
+  int64_t ldx;
+  int T;                    // DENSE: columns
+  float* y;                 // DENSE: Y [T][ldy]; GATEUP: h [pairs][ldy]; DOWN: rows [pairs][ldy]
+  int64_t ldy;
+  const int32_t* offsets;   // grouped: per-expert start in the sorted pair list [E+1]
+  const int32_t* pairs;     // grouped: sorted pair ids
+  const float* gate_w;      // DOWN: gate weight per pair id
+  int top_k;
+  float* partials;          // DENSE split K: per-slice partial sums (workspace)
+  int* counters;            // DENSE split K: arrival counters per row group (workspace)
+  // launch plan (qmv_plan)
+  int64_t n, nt, rg_n, nibble_bytes;
+  int kq_n, S, slice_quads, wave_quads, nwaves;
+  hipStream_t stream;
+};
+
+int64_t qmv_workspace_bytes(int64_t n, int64_t k);
+int launch_qmv_grouped(int mode, QmvArgs a, int64_t n, int64_t k, int n_expert);
+
+}  // namespace iq4

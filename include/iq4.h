@@ -112,22 +112,33 @@ int64_t iq4_packed_bytes(int64_t n, int64_t k);
 int iq4_pack_weights(const void* blocks, int64_t n, int64_t k, void* packed, void* stream);
 
 /*
+ * Workspace bytes iq4_qmv_multi needs for an n x k matrix (written to *bytes; 0 when
+ * the shape is covered without splitting K over workgroups).  Depends on n and k only.
+ */
+int iq4_qmv_workspace_size(int64_t n, int64_t k, size_t* bytes);
+
+/*
  * T-column quantised matrix-vector product (the verify window's dense product):
  *   Y[t][r] = sum_k W[r][k] * X[t][k],  t < T,  r < n,
  * fp32 activations, fp32 result.  Page 1 (Strata commit "wire multi-token kernels
  * into Verifier and MtpDrafter CUDA graphs", verify.hpp header): T tokens read the
  * dense weights once, and each token's column is the single-token result bit for bit.
  * This call guarantees that: column t of a T-column call is bitwise equal to a 1-column
- * call on X[t], for every T, and results are run-to-run deterministic.
- *   packed   W in the packed layout (iq4_pack_weights), 256-byte aligned.
- *   x        [T][ldx] float32, 16-byte aligned, ldx >= k, ldx % 4 == 0.
- *   y        [T][ldy] float32, ldy >= n.
- *   T        1..8.
+ * call on X[t] (same n, k), for every T, and results are run-to-run deterministic.
+ *   packed     W in the packed layout (iq4_pack_weights), 256-byte aligned.
+ *   x          [T][ldx] float32, 16-byte aligned, ldx >= k, ldx % 4 == 0.
+ *   y          [T][ldy] float32, ldy >= n.
+ *   T          1..8.
+ *   workspace  >= iq4_qmv_workspace_size(n, k) bytes, 256-byte aligned (may be NULL
+ *              when that size is 0).  It must be zero-filled before its first use;
+ *              each call leaves it ready for the next one (its arrival counters back
+ *              at zero).  Calls that overlap in time must not share a workspace.
  * Errors: IQ4_E_ARG (T, ldx, ldy), IQ4_E_UNSUPPORTED (n % 16, k % 128),
- * IQ4_E_ALIGN.
+ * IQ4_E_ALIGN, IQ4_E_WORKSPACE.
  */
 int iq4_qmv_multi(const void* packed, int64_t n, int64_t k, const float* x, int64_t ldx,
-                  int32_t T, float* y, int64_t ldy, void* stream);
+                  int32_t T, float* y, int64_t ldy, void* workspace, size_t ws_bytes,
+                  void* stream);
 
 /*
  * Top-k routing from router logits: ids[t] = the top_k experts with the largest

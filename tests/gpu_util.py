@@ -46,3 +46,16 @@ def bits_equal(a: np.ndarray, b: np.ndarray) -> bool:
     a = np.ascontiguousarray(a)
     b = np.ascontiguousarray(b)
     return a.dtype == b.dtype and a.shape == b.shape and a.tobytes() == b.tobytes()
+
+
+_WS = {}
+
+
+def qmv_workspace(n: int, k: int):
+    """A zero-filled workspace for iq4_qmv_multi on an n x k matrix (cached per shape)."""
+    nbytes = iq4.iq4_qmv_workspace_size(n, k)
+    if nbytes == 0:
+        return None, 0
+    if (n, k) not in _WS:
+        _WS[(n, k)] = torch.zeros(nbytes, dtype=torch.uint8, device=DEV)
+    return _WS[(n, k)], nbytes

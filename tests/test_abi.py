@@ -48,15 +48,15 @@ FAKE = 1 << 20  # a 256-byte-aligned non-null address that no call may dereferen
 
 
 def test_validation_errors_never_launch():
-    assert _rc("iq4_qmv_multi", FAKE, 16, 128, FAKE, 128, 0, FAKE, 16, None) == iq4.IQ4_E_ARG
+    assert _rc("iq4_qmv_multi", FAKE, 16, 128, FAKE, 128, 0, FAKE, 16, None, 0, None) == iq4.IQ4_E_ARG
     assert "T must be" in iq4.iq4_last_error()
-    assert _rc("iq4_qmv_multi", FAKE, 16, 128, FAKE, 128, 9, FAKE, 16, None) == iq4.IQ4_E_ARG
-    assert _rc("iq4_qmv_multi", FAKE, 17, 128, FAKE, 128, 1, FAKE, 17, None) == iq4.IQ4_E_UNSUPPORTED
-    assert _rc("iq4_qmv_multi", FAKE, 16, 96, FAKE, 128, 1, FAKE, 16, None) == iq4.IQ4_E_UNSUPPORTED
-    assert _rc("iq4_qmv_multi", FAKE, 16, 128, FAKE, 127, 1, FAKE, 16, None) == iq4.IQ4_E_ARG
-    assert _rc("iq4_qmv_multi", FAKE, 16, 128, FAKE + 4, 128, 1, FAKE, 16, None) == iq4.IQ4_E_ALIGN
-    assert _rc("iq4_qmv_multi", FAKE + 16, 16, 128, FAKE, 128, 1, FAKE, 16, None) == iq4.IQ4_E_ALIGN
-    assert _rc("iq4_qmv_multi", None, 16, 128, FAKE, 128, 1, FAKE, 16, None) == iq4.IQ4_E_ARG
+    assert _rc("iq4_qmv_multi", FAKE, 16, 128, FAKE, 128, 9, FAKE, 16, None, 0, None) == iq4.IQ4_E_ARG
+    assert _rc("iq4_qmv_multi", FAKE, 17, 128, FAKE, 128, 1, FAKE, 17, None, 0, None) == iq4.IQ4_E_UNSUPPORTED
+    assert _rc("iq4_qmv_multi", FAKE, 16, 96, FAKE, 128, 1, FAKE, 16, None, 0, None) == iq4.IQ4_E_UNSUPPORTED
+    assert _rc("iq4_qmv_multi", FAKE, 16, 128, FAKE, 127, 1, FAKE, 16, None, 0, None) == iq4.IQ4_E_ARG
+    assert _rc("iq4_qmv_multi", FAKE, 16, 128, FAKE + 4, 128, 1, FAKE, 16, None, 0, None) == iq4.IQ4_E_ALIGN
+    assert _rc("iq4_qmv_multi", FAKE + 16, 16, 128, FAKE, 128, 1, FAKE, 16, None, 0, None) == iq4.IQ4_E_ALIGN
+    assert _rc("iq4_qmv_multi", None, 16, 128, FAKE, 128, 1, FAKE, 16, None, 0, None) == iq4.IQ4_E_ARG
     assert _rc("iq4_dequant_blocks", FAKE, 4, 7, FAKE, None) == iq4.IQ4_E_ARG
     assert _rc("iq4_dequant_blocks", FAKE + 1, 4, 0, FAKE, None) == iq4.IQ4_E_ALIGN
     assert _rc("iq4_dequant_blocks", FAKE, -1, 0, FAKE, None) == iq4.IQ4_E_ARG
@@ -69,6 +69,15 @@ def test_validation_errors_never_launch():
     assert _rc("iq4_moe_gather", FAKE, 8, 0, FAKE, FAKE, FAKE, FAKE, None) == iq4.IQ4_E_ARG
 
 
+def test_qmv_workspace_rules():
+    assert iq4.iq4_qmv_workspace_size(768, 768) == 0        # one round of K: no split
+    need = iq4.iq4_qmv_workspace_size(4096, 4096)
+    assert need > 0
+    assert _rc("iq4_qmv_multi", FAKE, 4096, 4096, FAKE, 4096, 1, FAKE, 4096, None, 0, None) == iq4.IQ4_E_WORKSPACE
+    assert _rc("iq4_qmv_multi", FAKE, 4096, 4096, FAKE, 4096, 1, FAKE, 4096, FAKE, need - 1, None) == iq4.IQ4_E_WORKSPACE
+    assert _rc("iq4_qmv_multi", FAKE, 4096, 4096, FAKE, 4096, 1, FAKE, 4096, FAKE + 64, need, None) == iq4.IQ4_E_ALIGN
+
+
 def test_zero_sized_calls_are_no_ops():
     assert _rc("iq4_quantize_blocks", None, 0, None, None) == iq4.IQ4_OK
     assert _rc("iq4_dequant_blocks", None, 0, 0, None, None) == iq4.IQ4_OK
@@ -77,5 +86,5 @@ def test_zero_sized_calls_are_no_ops():
 
 def test_binding_raises_with_message():
     with pytest.raises(iq4.IQ4Error) as ei:
-        iq4.iq4_qmv_multi(FAKE, 16, 128, FAKE, 128, 0, FAKE, 16, stream=0)
+        iq4.iq4_qmv_multi(FAKE, 16, 128, FAKE, 128, 0, FAKE, 16, None, 0, stream=0)
     assert ei.value.code == iq4.IQ4_E_ARG and "T must be" in str(ei.value)

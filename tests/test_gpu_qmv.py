@@ -12,7 +12,7 @@ import torch
 
 import dequant_matmul_iq4_amd as iq4
 import oracle
-from gpu_util import bits_equal, dev, host, normwise, note, pack
+from gpu_util import bits_equal, dev, host, normwise, note, pack, qmv_workspace
 from test_oracle_pins import integer_exact_blocks
 import workloads
 
@@ -29,7 +29,8 @@ def run_qmv(packed, n, k, x: np.ndarray, ldx=None, ldy=None) -> np.ndarray:
     xb[:, :k] = x
     xd = dev(xb)
     y = torch.full((T, ldy), float("nan"), dtype=torch.float32, device="cuda")
-    iq4.iq4_qmv_multi(packed, n, k, xd, ldx, T, y, ldy)
+    ws, wsb = qmv_workspace(n, k)
+    iq4.iq4_qmv_multi(packed, n, k, xd, ldx, T, y, ldy, ws, wsb)
     out = host(y)
     if ldy > n:
         assert np.all(np.isnan(out[:, n:])), "wrote outside [0, n)"
@@ -135,3 +136,23 @@ def test_deterministic():
     b, n, k, x = workloads.cfg2(4)
     packed = pack(b, n, k)
     assert bits_equal(run_qmv(packed, n, k, x), run_qmv(packed, n, k, x))
+
+
+def test_split_k_workspace_is_reusable():
+    """A shape whose K is split over workgroups leaves its workspace ready: back-to-back
+    calls (different T) through one workspace match fresh ones bitwise, and the result
+    matches the oracle."""
+    note("qmv: split-K workspace reuse across calls")
+    n, k = 256, 14336
+    assert iq4.iq4_qmv_workspace_size(n, k) > 0
+    rng = np.random.default_rng(9)
+    b = oracle.encode_blocks((rng.standard_normal((n * k // 32, 32)) * 0.02).astype(np.float32))
+    x = rng.standard_normal((4, k)).astype(np.float32)
+    packed = pack(b, n, k)
+    first = [run_qmv(packed, n, k, x[:T]) for T in (1, 4, 2, 3)]
+    again = [run_qmv(packed, n, k, x[:T]) for T in (1, 4, 2, 3)]
+    for a_, b_ in zip(first, again):
+        assert bits_equal(a_, b_)
+    assert normwise(first[1], oracle.qmv(b, n, k, x)) <= TOL
+    for t in range(4):
+        assert bits_equal(first[1][t], first[0][0] if t == 0 else run_qmv(packed, n, k, x[t:t + 1])[0])
