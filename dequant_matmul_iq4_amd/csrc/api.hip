@@ -8,6 +8,8 @@
 #include "common.hpp"
 #include "launch.hpp"
 #include "qmv.hpp"
+#include "gemm.hpp"
+#include "moe.hpp"
 
 namespace iq4 {
 
@@ -148,12 +150,32 @@ int iq4_moe_gather(const int32_t* ids, int64_t n_pairs, int32_t n_expert, int32_
   return launch_gather(ids, n_pairs, n_expert, counts, offsets, pairs, slot_row, as_stream(stream));
 }
 
+static int check_moe_sizes(const char* fn, int64_t n_tok, int32_t top_k, int32_t n_expert,
+                           int64_t hidden, int64_t inter, int32_t act_dtype) {
+  if (n_tok < 0 || n_tok > ((int64_t)1 << 24) / (top_k > 0 ? top_k : 1))
+    return set_error(IQ4_E_ARG, "%s: n_tok out of range", fn);
+  if (n_expert < 1 || n_expert > 1024 || top_k < 1 || top_k > n_expert)
+    return set_error(IQ4_E_ARG, "%s: need 1 <= top_k <= n_expert <= 1024", fn);
+  if (act_dtype != IQ4_F32 && act_dtype != IQ4_F16)
+    return set_error(IQ4_E_ARG, "%s: act_dtype must be IQ4_F32 or IQ4_F16", fn);
+  if (hidden <= 0 || inter <= 0 || hidden % kTileK || inter % kTileK)
+    return set_error(IQ4_E_UNSUPPORTED, "%s: hidden and inter must be positive multiples of 128", fn);
+  if (act_dtype == IQ4_F32 && (hidden > 4096 || inter > 4096))
+    return set_error(IQ4_E_UNSUPPORTED, "%s: the fp32 path supports hidden, inter <= 4096", fn);
+  if (hidden > ((int64_t)1 << 16) || inter > ((int64_t)1 << 16))
+    return set_error(IQ4_E_UNSUPPORTED, "%s: hidden or inter too large", fn);
+  return IQ4_OK;
+}
+
 int iq4_moe_workspace_size(int64_t n_tok, int32_t top_k, int32_t n_expert, int64_t hidden,
                            int64_t inter, int32_t act_dtype, size_t* bytes) {
   clear_error();
-  (void)n_tok; (void)top_k; (void)n_expert; (void)hidden; (void)inter; (void)act_dtype;
-  if (bytes) *bytes = 0;
-  return set_error(IQ4_E_UNSUPPORTED, "iq4_moe_workspace_size: not available in this build");
+  if (!bytes) return set_error(IQ4_E_ARG, "iq4_moe_workspace_size: null bytes");
+  *bytes = 0;
+  if (int e = check_moe_sizes("iq4_moe_workspace_size", n_tok, top_k, n_expert, hidden, inter, act_dtype))
+    return e;
+  *bytes = (size_t)moe_layout(n_tok, top_k, n_expert, hidden, inter, act_dtype == IQ4_F16).total;
+  return IQ4_OK;
 }
 
 int iq4_moe_expert_gemm(const void* x, int32_t act_dtype, int64_t n_tok, int64_t ldx,
@@ -162,18 +184,55 @@ int iq4_moe_expert_gemm(const void* x, int32_t act_dtype, int64_t n_tok, int64_t
                         const void* w_down, float* out, int64_t ldo, void* workspace,
                         size_t ws_bytes, uint32_t flags, void* stream) {
   clear_error();
-  (void)x; (void)act_dtype; (void)n_tok; (void)ldx; (void)ids; (void)w; (void)top_k;
-  (void)n_expert; (void)hidden; (void)inter; (void)w_gate; (void)w_up; (void)w_down; (void)out;
-  (void)ldo; (void)workspace; (void)ws_bytes; (void)flags; (void)stream;
-  return set_error(IQ4_E_UNSUPPORTED, "iq4_moe_expert_gemm: not available in this build");
+  const char* fn = "iq4_moe_expert_gemm";
+  if (int e = check_moe_sizes(fn, n_tok, top_k, n_expert, hidden, inter, act_dtype)) return e;
+  if (flags & ~IQ4_MOE_ATOMIC_COMBINE) return set_error(IQ4_E_ARG, "%s: unknown flags", fn);
+  if (ldx < hidden || ldo < hidden) return set_error(IQ4_E_ARG, "%s: ldx and ldo must be >= hidden", fn);
+  if (n_tok == 0) return IQ4_OK;
+  if (!x || !ids || !w || !w_gate || !w_up || !w_down || !out)
+    return set_error(IQ4_E_ARG, "%s: null pointer", fn);
+  const bool f16 = act_dtype == IQ4_F16;
+  if (!aligned(x, 16) || ldx % (f16 ? 8 : 4) || !aligned(out, 16) || ldo % 4 || !aligned(ids, 4) ||
+      !aligned(w, 4) || !aligned(w_gate, 256) || !aligned(w_up, 256) || !aligned(w_down, 256))
+    return set_error(IQ4_E_ALIGN, "%s: x/out 16-byte aligned with ldx %% %d == 0 and ldo %% 4 == 0, "
+                     "weights 256-byte aligned", fn, f16 ? 8 : 4);
+  const MoeLayout L = moe_layout(n_tok, top_k, n_expert, hidden, inter, f16);
+  if (!workspace || ws_bytes < (size_t)L.total)
+    return set_error(IQ4_E_WORKSPACE, "%s: needs a workspace of %lld bytes", fn, (long long)L.total);
+  if (!aligned(workspace, 256)) return set_error(IQ4_E_ALIGN, "%s: workspace must be 256-byte aligned", fn);
+  MoeCall m{};
+  m.x = x;
+  m.f16 = f16;
+  m.n_tok = n_tok;
+  m.ldx = ldx;
+  m.ids = ids;
+  m.w = w;
+  m.top_k = top_k;
+  m.n_expert = n_expert;
+  m.hidden = hidden;
+  m.inter = inter;
+  m.w_gate = w_gate;
+  m.w_up = w_up;
+  m.w_down = w_down;
+  m.out = out;
+  m.ldo = ldo;
+  m.workspace = workspace;
+  m.atomic = (flags & IQ4_MOE_ATOMIC_COMBINE) != 0;
+  return launch_moe(m, as_stream(stream));
 }
 
 int iq4_qgemm(const void* packed, int64_t n, int64_t k, const void* x, int64_t m, int64_t ldx,
               float* y, int64_t ldy, int64_t chunk, void* stream) {
   clear_error();
-  (void)packed; (void)n; (void)k; (void)x; (void)m; (void)ldx; (void)y; (void)ldy; (void)chunk;
-  (void)stream;
-  return set_error(IQ4_E_UNSUPPORTED, "iq4_qgemm: not available in this build");
+  if (int e = check_matrix("iq4_qgemm", n, k)) return e;
+  if (m < 0 || chunk < 0) return set_error(IQ4_E_ARG, "iq4_qgemm: m and chunk must be >= 0");
+  if (ldx < k || ldy < n) return set_error(IQ4_E_ARG, "iq4_qgemm: ldx must be >= k and ldy >= n");
+  if (m == 0) return IQ4_OK;
+  if (!packed || !x || !y) return set_error(IQ4_E_ARG, "iq4_qgemm: null pointer");
+  if (!aligned(packed, 256) || !aligned(x, 16) || ldx % 8 || !aligned(y, 4))
+    return set_error(IQ4_E_ALIGN, "iq4_qgemm: packed 256-byte, x 16-byte aligned with ldx %% 8 == 0, y 4-byte");
+  return launch_qgemm_dense(static_cast<const uint8_t*>(packed), n, k, static_cast<const uint16_t*>(x), m,
+                            ldx, y, ldy, chunk, as_stream(stream));
 }
 
 }  // extern "C"

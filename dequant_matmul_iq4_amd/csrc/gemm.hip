@@ -121,13 +121,10 @@ __global__ void __launch_bounds__(256) qgemm_kernel(GemmArgs a) {
   // [16 + 8h, 16 + 8h + 8) of the block and writes fragments g = 2h and 2h + 1.
   const uint16_t* arow[4];
   int a_lds_off[4];
-  int a_blk[4], a_half[4];
 #pragma unroll
   for (int it = 0; it < 4; ++it) {
     const int item = tid + 256 * it;
     const int half = item & 1, blk = (item >> 1) & 3, r = item >> 3;  // r = 0..127
-    a_blk[it] = blk;
-    a_half[it] = half;
     const uint16_t* p = nullptr;
     if (r < rows) {
       int64_t src_row;

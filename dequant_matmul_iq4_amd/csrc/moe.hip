@@ -1,0 +1,203 @@
+// moe.hip -- the mixture-of-experts path around the products: the per-expert tile list,
+// the gate-weighted combine, and the orchestration of one MoE layer call.
+//
+// Prefill (binary16 activations):
+//   gather -> tile list -> GEMM gate|up (+SwiGLU, h binary16) -> GEMM down (x gate
+//   weight) -> combine.
+// Decode (fp32 activations, few tokens):
+//   gather -> grouped matvec gate|up (+SwiGLU, h fp32) -> grouped matvec down (x gate
+//   weight) -> combine.
+// The combine adds each token's top_k weighted slot rows in slot order j = 0..k-1, so
+// the result does not depend on how pairs were scheduled (page 1's PoolMultiFn:
+// per-slot rows (n_tok * k, n_embd), then summed per token).  The atomic variant adds
+// the slot rows into the output as they are produced instead.
+#include "common.hpp"
+#include "gemm.hpp"
+#include "launch.hpp"
+#include "moe.hpp"
+#include "qmv.hpp"
+
+namespace iq4 {
+
+constexpr int kTileM = 128;  // rows per GEMM tile (gemm.hip kBM)
+
+// One workgroup: m tiles per expert (ceil(count / 128)), exclusive scan over experts,
+// then each expert writes its (expert, m tile) entries.
+__global__ void __launch_bounds__(1024) tiles_kernel(const int32_t* __restrict__ counts, int n_expert,
+                                                     int32_t* __restrict__ tiles,
+                                                     int32_t* __restrict__ num_tiles) {
+  __shared__ int scan[1024];
+  const int e = threadIdx.x;
+  const int nt = (e < n_expert) ? (counts[e] + kTileM - 1) / kTileM : 0;
+  scan[e] = nt;
+  __syncthreads();
+  for (int off = 1; off < 1024; off <<= 1) {  // inclusive Hillis-Steele scan
+    const int v = (e >= off) ? scan[e - off] : 0;
+    __syncthreads();
+    scan[e] += v;
+    __syncthreads();
+  }
+  const int base = scan[e] - nt;
+  for (int i = 0; i < nt; ++i) {
+    tiles[2 * (base + i)] = e;
+    tiles[2 * (base + i) + 1] = i;
+  }
+  if (e == 1023) *num_tiles = scan[1023];
+}
+
+// out[t][h] = sum_j rows[t * k + j][h], j ascending; one thread per 4 outputs.
+__global__ void __launch_bounds__(256) combine_kernel(const float* __restrict__ rows, int64_t ldr,
+                                                      int64_t n_tok, int top_k, int64_t hidden,
+                                                      float* __restrict__ out, int64_t ldo) {
+  const int64_t per_tok = hidden / 4;
+  const int64_t i = (int64_t)blockIdx.x * blockDim.x + threadIdx.x;
+  if (i >= n_tok * per_tok) return;
+  const int64_t t = i / per_tok, h = (i % per_tok) * 4;
+  const float* r = rows + t * top_k * ldr + h;
+  float4 acc = *reinterpret_cast<const float4*>(r);
+  for (int j = 1; j < top_k; ++j) {
+    const float4 v = *reinterpret_cast<const float4*>(r + j * ldr);
+    acc.x += v.x;
+    acc.y += v.y;
+    acc.z += v.z;
+    acc.w += v.w;
+  }
+  *reinterpret_cast<float4*>(out + t * ldo + h) = acc;
+}
+
+// Zero-fill (a kernel rather than a memset node, so the call stays graph-safe).
+__global__ void __launch_bounds__(256) zero_rows_kernel(float* __restrict__ out, int64_t n_tok,
+                                                        int64_t hidden, int64_t ldo) {
+  const int64_t per_tok = hidden / 4;
+  const int64_t i = (int64_t)blockIdx.x * blockDim.x + threadIdx.x;
+  if (i >= n_tok * per_tok) return;
+  const int64_t t = i / per_tok, h = (i % per_tok) * 4;
+  *reinterpret_cast<float4*>(out + t * ldo + h) = make_float4(0.f, 0.f, 0.f, 0.f);
+}
+
+static inline int64_t align256(int64_t b) { return (b + 255) / 256 * 256; }
+
+MoeLayout moe_layout(int64_t n_tok, int top_k, int n_expert, int64_t hidden, int64_t inter,
+                     bool f16) {
+  MoeLayout L{};
+  const int64_t P = n_tok * top_k;
+  int64_t off = 0;
+  L.counts = off;    off += align256(4 * (int64_t)n_expert);
+  L.offsets = off;   off += align256(4 * ((int64_t)n_expert + 1));
+  L.pairs = off;     off += align256(4 * P);
+  L.slot_row = off;  off += align256(4 * P);
+  L.max_tiles = (P + kTileM - 1) / kTileM + n_expert;
+  L.num_tiles = off; off += 256;
+  L.tiles = off;     off += align256(8 * L.max_tiles);
+  L.h = off;         off += align256(P * inter * (f16 ? 2 : 4));
+  L.rows = off;      off += align256(P * hidden * 4);
+  L.total = off;
+  return L;
+}
+
+int launch_moe(const MoeCall& m, hipStream_t s) {
+  const MoeLayout L = moe_layout(m.n_tok, m.top_k, m.n_expert, m.hidden, m.inter, m.f16);
+  uint8_t* ws = static_cast<uint8_t*>(m.workspace);
+  int32_t* counts = reinterpret_cast<int32_t*>(ws + L.counts);
+  int32_t* offsets = reinterpret_cast<int32_t*>(ws + L.offsets);
+  int32_t* pairs = reinterpret_cast<int32_t*>(ws + L.pairs);
+  int32_t* slot_row = reinterpret_cast<int32_t*>(ws + L.slot_row);
+  int32_t* num_tiles = reinterpret_cast<int32_t*>(ws + L.num_tiles);
+  int32_t* tiles = reinterpret_cast<int32_t*>(ws + L.tiles);
+  float* rows = reinterpret_cast<float*>(ws + L.rows);
+  const int64_t P = m.n_tok * m.top_k;
+  if (m.n_tok == 0) return 0;
+
+  if (int e = launch_gather(m.ids, P, m.n_expert, counts, offsets, pairs, slot_row, s)) return e;
+
+  const int64_t gate_stride = m.inter * (m.hidden / kQK) * kBlockBytes;
+  const int64_t down_stride = m.hidden * (m.inter / kQK) * kBlockBytes;
+  const bool atomic = m.f16 && m.atomic;
+  if (atomic) {
+    const int64_t n4 = m.n_tok * (m.hidden / 4);
+    hipLaunchKernelGGL(zero_rows_kernel, dim3((unsigned)((n4 + 255) / 256)), dim3(256), 0, s, m.out,
+                       m.n_tok, m.hidden, m.ldo);
+    if (int e = check_launch("zero_rows_kernel")) return e;
+  }
+
+  if (m.f16) {
+    hipLaunchKernelGGL(tiles_kernel, dim3(1), dim3(1024), 0, s, counts, m.n_expert, tiles, num_tiles);
+    if (int e = check_launch("tiles_kernel")) return e;
+    uint16_t* h = reinterpret_cast<uint16_t*>(ws + L.h);
+    GemmArgs g{};
+    g.A = static_cast<const uint16_t*>(m.x);
+    g.lda = m.ldx;
+    g.W0 = static_cast<const uint8_t*>(m.w_gate);
+    g.W1 = static_cast<const uint8_t*>(m.w_up);
+    g.w_expert_stride = gate_stride;
+    g.N = m.inter;
+    g.K = m.hidden;
+    g.H = h;
+    g.ldh = m.inter;
+    g.tiles = tiles;
+    g.num_tiles = num_tiles;
+    g.n_tiles_n = (m.inter + 127) / 128;
+    g.offsets = offsets;
+    g.pairs = pairs;
+    g.top_k = m.top_k;
+    if (int e = launch_qgemm_grouped(kGemmGateUp, g, L.max_tiles, s)) return e;
+    GemmArgs d{};
+    d.A = h;
+    d.lda = m.inter;
+    d.W0 = static_cast<const uint8_t*>(m.w_down);
+    d.w_expert_stride = down_stride;
+    d.N = m.hidden;
+    d.K = m.inter;
+    d.C = rows;
+    d.ldc = m.hidden;
+    d.tiles = tiles;
+    d.num_tiles = num_tiles;
+    d.n_tiles_n = (m.hidden + 255) / 256;
+    d.offsets = offsets;
+    d.pairs = pairs;
+    d.gate_w = m.w;
+    d.top_k = m.top_k;
+    d.out = m.out;
+    d.ldo = m.ldo;
+    d.atomic = atomic ? 1 : 0;
+    if (int e = launch_qgemm_grouped(kGemmDown, d, L.max_tiles, s)) return e;
+  } else {
+    float* h = reinterpret_cast<float*>(ws + L.h);
+    QmvArgs g{};
+    g.W0 = static_cast<const uint8_t*>(m.w_gate);
+    g.W1 = static_cast<const uint8_t*>(m.w_up);
+    g.w_expert_stride = gate_stride;
+    g.x = static_cast<const float*>(m.x);
+    g.ldx = m.ldx;
+    g.y = h;
+    g.ldy = m.inter;
+    g.offsets = offsets;
+    g.pairs = pairs;
+    g.top_k = m.top_k;
+    g.stream = s;
+    if (int e = launch_qmv_grouped(kQmvGateUp, g, m.inter, m.hidden, m.n_expert)) return e;
+    QmvArgs d{};
+    d.W0 = static_cast<const uint8_t*>(m.w_down);
+    d.w_expert_stride = down_stride;
+    d.x = h;
+    d.ldx = m.inter;
+    d.y = rows;
+    d.ldy = m.hidden;
+    d.offsets = offsets;
+    d.pairs = pairs;
+    d.gate_w = m.w;
+    d.top_k = m.top_k;
+    d.stream = s;
+    if (int e = launch_qmv_grouped(kQmvDown, d, m.hidden, m.inter, m.n_expert)) return e;
+  }
+
+  if (!atomic) {
+    const int64_t n4 = m.n_tok * (m.hidden / 4);
+    hipLaunchKernelGGL(combine_kernel, dim3((unsigned)((n4 + 255) / 256)), dim3(256), 0, s, rows,
+                       m.hidden, m.n_tok, m.top_k, m.hidden, m.out, m.ldo);
+    if (int e = check_launch("combine_kernel")) return e;
+  }
+  return 0;
+}
+
+}  // namespace iq4

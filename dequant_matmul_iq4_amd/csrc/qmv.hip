@@ -98,7 +98,6 @@ __global__ void __launch_bounds__(512) qmv_kernel(QmvArgs a) {
   const int tid = threadIdx.x;
   const int lane = tid & 63, wave = tid >> 6, nwaves = (int)(blockDim.x >> 6);
   const int c = lane & 15, g = lane >> 4;
-  const int s = c >> 2, tt = c & 3;
 
   // ---- tile of this workgroup ---------------------------------------------------------
   int64_t rg, seg0 = 0, ncols;

@@ -1,0 +1,85 @@
+"""Dense dequant-fused GEMM (prompt projection in chunks) on the GPU vs the oracle.
+
+Tolerance: binary16 activations, weights decoded to binary16, fp32 accumulation:
+normwise max|y - r| / max|r| <= 5e-3 (the stated tolerance for the f16 matrix-core
+paths).  Power-of-two scales with small-integer activations make every product and
+partial sum exact, so those cases must match bitwise; results must not depend on the
+chunk size (bitwise).
+"""
+import numpy as np
+import pytest
+import torch
+
+import dequant_matmul_iq4_amd as iq4
+import oracle
+import synth
+from gpu_util import bits_equal, dev, host, normwise, note, pack
+from test_oracle_pins import integer_exact_blocks
+import workloads
+
+pytestmark = pytest.mark.gpu
+
+TOL = 5e-3
+
+
+def run_qgemm(packed, n, k, x16: np.ndarray, chunk=512, ldy=None) -> np.ndarray:
+    m = x16.shape[0]
+    ldy = ldy or n
+    xd = dev(x16.astype(np.float16))
+    y = torch.full((m, ldy), float("nan"), dtype=torch.float32, device="cuda")
+    iq4.iq4_qgemm(packed, n, k, xd, m, k, y, ldy, chunk)
+    out = host(y)
+    if ldy > n:
+        assert np.all(np.isnan(out[:, n:])), "wrote outside [0, n)"
+    return out[:, :n]
+
+
+@pytest.mark.parametrize("n,k,m", [(256, 256, 200), (48, 128, 5), (272, 384, 129), (512, 768, 640)])
+def test_small_shapes(n, k, m):
+    note(f"qgemm: n={n} k={k} m={m}")
+    rng = np.random.default_rng(n + k + m)
+    b = oracle.encode_blocks((rng.standard_normal((n * k // 32, 32)) * 0.02).astype(np.float32))
+    x = rng.standard_normal((m, k)).astype(np.float16)
+    y = run_qgemm(pack(b, n, k), n, k, x, ldy=n + 16)
+    assert normwise(y, oracle.gemm(b, n, k, x)) <= TOL
+
+
+@pytest.mark.parametrize("n,k,m", [(256, 256, 130), (48, 384, 17)])
+def test_integer_exact_bitwise(n, k, m):
+    note(f"qgemm: integer-exact n={n} k={k} m={m}")
+    rng = np.random.default_rng(7 * n + k)
+    b = integer_exact_blocks(rng, n * k // 32, 4)
+    x = rng.integers(-8, 9, (m, k)).astype(np.float16)
+    y = run_qgemm(pack(b, n, k), n, k, x)
+    assert bits_equal(y, oracle.gemm(b, n, k, x))
+
+
+def test_chunk_invariance_bitwise():
+    note("qgemm: chunk 512 / 256 / 100 / one launch, bitwise")
+    n, k, m = 512, 512, 1100
+    rng = np.random.default_rng(11)
+    b = oracle.encode_blocks((rng.standard_normal((n * k // 32, 32)) * 0.02).astype(np.float32))
+    x = rng.standard_normal((m, k)).astype(np.float16)
+    packed = pack(b, n, k)
+    ref = run_qgemm(packed, n, k, x, chunk=512)
+    for chunk in (256, 100, 0):
+        assert bits_equal(run_qgemm(packed, n, k, x, chunk=chunk), ref), chunk
+
+
+def test_long_prompt_projection_sampled():
+    """The full long-prompt workload: W 14,336 x 4,096 (seed 105), 13,056 f16 tokens in
+    512-token chunks; every output column checked on a sample of rows (first and last
+    chunk, the 256-token tail, and rows spread over the prompt)."""
+    note("qgemm: long prompt 13056 x 4096 x 14336, chunk 512")
+    n, k, m = 14336, 4096, 13056
+    _, b = workloads.dense_weights(synth.SEED_LONG, n, k)
+    x = workloads.acts16(synth.SEED_LONG, m, k)
+    packed = pack(b, n, k)
+    xd = dev(x)
+    y = torch.empty((m, n), dtype=torch.float32, device="cuda")
+    iq4.iq4_qgemm(packed, n, k, xd, m, k, y, n, 512)
+    rows = np.unique(np.concatenate([np.arange(0, 8), np.arange(12800, 12808), np.arange(13048, 13056),
+                                     np.linspace(0, m - 1, 40).astype(int)]))
+    got = host(y[torch.from_numpy(rows).cuda()])
+    ref = oracle.gemm(b, n, k, x[rows])
+    assert normwise(got, ref) <= TOL

@@ -1,0 +1,163 @@
+"""Mixture-of-experts path on the GPU vs the oracle: routing, the bit-exact gather, the
+fp32 decode path (tolerance 1e-3) and the binary16 prefill path (tolerance 5e-3)."""
+import numpy as np
+import pytest
+import torch
+
+import dequant_matmul_iq4_amd as iq4
+import oracle
+import synth
+from gpu_util import bits_equal, dev, host, normwise, note, pack
+
+pytestmark = pytest.mark.gpu
+
+
+def make_bank(rng, E, H, I, scale=0.02):
+    gate = [oracle.encode_blocks((rng.standard_normal((I * H // 32, 32)) * scale).astype(np.float32)) for _ in range(E)]
+    up = [oracle.encode_blocks((rng.standard_normal((I * H // 32, 32)) * scale).astype(np.float32)) for _ in range(E)]
+    down = [oracle.encode_blocks((rng.standard_normal((H * I // 32, 32)) * scale).astype(np.float32)) for _ in range(E)]
+    return gate, up, down
+
+
+def pack_bank(blocks, n, k):
+    return torch.cat([pack(b, n, k) for b in blocks])
+
+
+def run_moe(x, ids, w, banks, H, I, E, flags=0, dtype="f16"):
+    n_tok, top_k = ids.shape
+    f16 = dtype == "f16"
+    xd = dev(x.astype(np.float16 if f16 else np.float32))
+    out = torch.full((n_tok, H), float("nan"), dtype=torch.float32, device="cuda")
+    act = iq4.IQ4_F16 if f16 else iq4.IQ4_F32
+    wsb = iq4.iq4_moe_workspace_size(n_tok, top_k, E, H, I, act)
+    ws = torch.empty(max(wsb, 256), dtype=torch.uint8, device="cuda")
+    g, u, d = banks
+    iq4.iq4_moe_expert_gemm(xd, act, n_tok, H, dev(ids.astype(np.int32)), dev(w.astype(np.float32)), top_k, E,
+                            H, I, g, u, d, out, H, ws, wsb, flags)
+    return host(out), ws
+
+
+def routing(rng, n_tok, E, k):
+    logits = rng.standard_normal((n_tok, E)).astype(np.float32)
+    return oracle.route_topk(logits, k)
+
+
+def test_route_topk_matches_oracle():
+    note("route: top-8 of 128, ties")
+    rng = np.random.default_rng(1)
+    L = rng.standard_normal((300, 128)).astype(np.float32)
+    L[::7, 5] = L[::7, 9]  # ties
+    L[3] = 0.25  # a fully tied row
+    ids_r, w_r = oracle.route_topk(L, 8)
+    ids = torch.empty((300, 8), dtype=torch.int32, device="cuda")
+    w = torch.empty((300, 8), dtype=torch.float32, device="cuda")
+    iq4.iq4_route_topk(dev(L), 300, 128, 8, ids, w)
+    assert bits_equal(host(ids), ids_r)
+    assert np.allclose(host(w), w_r, rtol=2e-6, atol=1e-7)
+
+
+@pytest.mark.parametrize("n_tok,k,E", [(3256, 8, 128), (4, 8, 128), (1, 1, 1), (37, 3, 7)])
+def test_gather_bit_exact(n_tok, k, E):
+    note(f"gather: n_tok={n_tok} k={k} E={E}")
+    rng = np.random.default_rng(n_tok + E)
+    if E == 128 and n_tok > 100:
+        L = synth.logits_zipf_gumbel(synth.SEED_PREFILL, synth.TAG_GUMBEL, n_tok, E)
+        ids, _ = oracle.route_topk(L, k)
+    else:
+        ids = np.stack([rng.permutation(E)[:k] for _ in range(n_tok)]).astype(np.int32)
+    P = n_tok * k
+    c = torch.empty(E, dtype=torch.int32, device="cuda")
+    o = torch.empty(E + 1, dtype=torch.int32, device="cuda")
+    p = torch.empty(P, dtype=torch.int32, device="cuda")
+    s = torch.empty(P, dtype=torch.int32, device="cuda")
+    iq4.iq4_moe_gather(dev(ids), P, E, c, o, p, s)
+    rc, ro, rp, rs = oracle.gather(ids, E)
+    assert bits_equal(host(c), rc) and bits_equal(host(o), ro)
+    assert bits_equal(host(p), rp) and bits_equal(host(s), rs)
+
+
+@pytest.fixture(scope="module")
+def small_bank():
+    rng = np.random.default_rng(42)
+    E, H, I = 8, 256, 128
+    gate, up, down = make_bank(rng, E, H, I)
+    banks = (pack_bank(gate, I, H), pack_bank(up, I, H), pack_bank(down, H, I))
+    return dict(E=E, H=H, I=I, gate=gate, up=up, down=down, banks=banks)
+
+
+@pytest.mark.parametrize("n_tok,k", [(300, 2), (129, 3), (5, 8), (1, 1)])
+def test_prefill_small(small_bank, n_tok, k):
+    note(f"moe prefill: n_tok={n_tok} k={k}")
+    B = small_bank
+    rng = np.random.default_rng(n_tok * 10 + k)
+    ids, w = routing(rng, n_tok, B["E"], k)
+    x = rng.standard_normal((n_tok, B["H"])).astype(np.float16)
+    got, ws = run_moe(x, ids, w, B["banks"], B["H"], B["I"], B["E"])
+    ref = oracle.moe(x, ids, w, B["gate"], B["up"], B["down"], B["H"], B["I"])
+    assert normwise(got, ref) <= 5e-3
+    # the call leaves the gather at the start of its workspace
+    rc, ro, rp, rs = oracle.gather(ids, B["E"])
+    wsn = host(ws)
+    cnt = wsn[:4 * B["E"]].view(np.int32)
+    assert bits_equal(cnt, rc)
+
+
+@pytest.mark.parametrize("n_tok,k", [(4, 2), (8, 8), (1, 3), (13, 4)])
+def test_decode_small(small_bank, n_tok, k):
+    note(f"moe decode: n_tok={n_tok} k={k}")
+    B = small_bank
+    rng = np.random.default_rng(n_tok * 100 + k)
+    ids, w = routing(rng, n_tok, B["E"], k)
+    x = rng.standard_normal((n_tok, B["H"])).astype(np.float32)
+    got, _ = run_moe(x, ids, w, B["banks"], B["H"], B["I"], B["E"], dtype="f32")
+    ref = oracle.moe(x, ids, w, B["gate"], B["up"], B["down"], B["H"], B["I"])
+    assert normwise(got, ref) <= 1e-3
+
+
+def test_decode_batch_invariance(small_bank):
+    """Each token of a 4-token decode step equals that token run alone, bitwise (the
+    verify window's per-token property, for the expert path)."""
+    note("moe decode: batch invariance")
+    B = small_bank
+    rng = np.random.default_rng(5)
+    ids, w = routing(rng, 4, B["E"], 4)
+    ids[1] = ids[0]  # two tokens sharing all their experts
+    x = rng.standard_normal((4, B["H"])).astype(np.float32)
+    full, _ = run_moe(x, ids, w, B["banks"], B["H"], B["I"], B["E"], dtype="f32")
+    for t in range(4):
+        one, _ = run_moe(x[t:t + 1], ids[t:t + 1], w[t:t + 1], B["banks"], B["H"], B["I"], B["E"], dtype="f32")
+        assert bits_equal(full[t], one[0]), t
+
+
+def test_prefill_batch_invariance(small_bank):
+    note("moe prefill: batch invariance")
+    B = small_bank
+    rng = np.random.default_rng(6)
+    ids, w = routing(rng, 200, B["E"], 2)
+    x = rng.standard_normal((200, B["H"])).astype(np.float16)
+    full, _ = run_moe(x, ids, w, B["banks"], B["H"], B["I"], B["E"])
+    sub = [0, 77, 199]
+    part, _ = run_moe(x[sub], ids[sub], w[sub], B["banks"], B["H"], B["I"], B["E"])
+    assert bits_equal(full[sub], part)
+
+
+def test_prefill_atomic_combine(small_bank):
+    note("moe prefill: atomic combine")
+    B = small_bank
+    rng = np.random.default_rng(8)
+    ids, w = routing(rng, 150, B["E"], 3)
+    x = rng.standard_normal((150, B["H"])).astype(np.float16)
+    det, _ = run_moe(x, ids, w, B["banks"], B["H"], B["I"], B["E"])
+    atom, _ = run_moe(x, ids, w, B["banks"], B["H"], B["I"], B["E"], flags=iq4.IQ4_MOE_ATOMIC_COMBINE)
+    assert normwise(atom, det) <= 1e-5
+
+
+def test_prefill_deterministic(small_bank):
+    note("moe prefill: run-to-run determinism")
+    B = small_bank
+    rng = np.random.default_rng(9)
+    ids, w = routing(rng, 300, B["E"], 2)
+    x = rng.standard_normal((300, B["H"])).astype(np.float16)
+    a, _ = run_moe(x, ids, w, B["banks"], B["H"], B["I"], B["E"])
+    b, _ = run_moe(x, ids, w, B["banks"], B["H"], B["I"], B["E"])
+    assert bits_equal(a, b)
