@@ -70,12 +70,34 @@ def test_validation_errors_never_launch():
 
 
 def test_qmv_workspace_rules():
-    assert iq4.iq4_qmv_workspace_size(768, 768) == 0        # one round of K: no split
-    need = iq4.iq4_qmv_workspace_size(4096, 4096)
+    # K up to 4096 is one slice per workgroup: no workspace
+    assert iq4.iq4_qmv_workspace_size(768, 768) == 0
+    assert iq4.iq4_qmv_workspace_size(4096, 4096) == 0
+    need = iq4.iq4_qmv_workspace_size(256, 14336)  # K split over workgroups
     assert need > 0
-    assert _rc("iq4_qmv_multi", FAKE, 4096, 4096, FAKE, 4096, 1, FAKE, 4096, None, 0, None) == iq4.IQ4_E_WORKSPACE
-    assert _rc("iq4_qmv_multi", FAKE, 4096, 4096, FAKE, 4096, 1, FAKE, 4096, FAKE, need - 1, None) == iq4.IQ4_E_WORKSPACE
-    assert _rc("iq4_qmv_multi", FAKE, 4096, 4096, FAKE, 4096, 1, FAKE, 4096, FAKE + 64, need, None) == iq4.IQ4_E_ALIGN
+    assert _rc("iq4_qmv_multi", FAKE, 256, 14336, FAKE, 14336, 1, FAKE, 256, None, 0, None) == iq4.IQ4_E_WORKSPACE
+    assert _rc("iq4_qmv_multi", FAKE, 256, 14336, FAKE, 14336, 1, FAKE, 256, FAKE, need - 1, None) == iq4.IQ4_E_WORKSPACE
+    assert _rc("iq4_qmv_multi", FAKE, 256, 14336, FAKE, 14336, 1, FAKE, 256, FAKE + 64, need, None) == iq4.IQ4_E_ALIGN
+
+
+def test_moe_and_gemm_validation():
+    ws = iq4.iq4_moe_workspace_size(3256, 8, 128, 2048, 768, iq4.IQ4_F16)
+    assert ws > 3256 * 8 * 2048 * 4
+    rc = _rc("iq4_moe_expert_gemm", FAKE, iq4.IQ4_F16, 16, 2048, FAKE, FAKE, 8, 128, 2048, 768,
+             FAKE, FAKE, FAKE, FAKE, 2048, FAKE, 16, 0, None)
+    assert rc == iq4.IQ4_E_WORKSPACE
+    rc = _rc("iq4_moe_expert_gemm", FAKE, iq4.IQ4_F32, 16, 2048, FAKE, FAKE, 8, 128, 2048, 5000,
+             FAKE, FAKE, FAKE, FAKE, 2048, FAKE, 1 << 30, 0, None)
+    assert rc == iq4.IQ4_E_UNSUPPORTED  # fp32 path: inter above 4096
+    rc = _rc("iq4_moe_expert_gemm", FAKE, iq4.IQ4_F16, 16, 2048, FAKE, FAKE, 9, 8, 2048, 768,
+             FAKE, FAKE, FAKE, FAKE, 2048, FAKE, 1 << 30, 0, None)
+    assert rc == iq4.IQ4_E_ARG  # top_k > n_expert
+    rc = _rc("iq4_moe_expert_gemm", FAKE, iq4.IQ4_F16, 16, 2048, FAKE, FAKE, 8, 128, 2048, 768,
+             FAKE, FAKE, FAKE, FAKE, 2048, FAKE, 1 << 30, 4, None)
+    assert rc == iq4.IQ4_E_ARG  # unknown flag
+    assert _rc("iq4_qgemm", FAKE, 256, 256, FAKE, 10, 252, FAKE, 256, 512, None) == iq4.IQ4_E_ARG
+    assert _rc("iq4_qgemm", FAKE, 256, 256, FAKE + 8, 10, 256, FAKE, 256, 512, None) == iq4.IQ4_E_ALIGN
+    assert _rc("iq4_qgemm", FAKE, 256, 256, FAKE, 0, 256, FAKE, 256, 512, None) == iq4.IQ4_OK
 
 
 def test_zero_sized_calls_are_no_ops():
