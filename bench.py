@@ -2,15 +2,21 @@
 
     python bench.py [--gpus 1] [--steps K] [--warmup W]
 
-One step = one pass of the hot path over resident synthetic inputs:
-  * the verify-window matvec, W 4096 x 4096 in IQ4 blocks, one call at each of
-    T = 1, 2, 3, 4 fp32 columns, each call on a different one of R weight copies
-    (R * 9.4 MB > 2 x the 256 MB Infinity Cache, so the weights stream from HBM).
+One step = one pass over every step of the hot path, on resident synthetic inputs:
+  1. verify-window matvec: W 4096 x 4096 IQ4, one call at each T = 1, 2, 3, 4 fp32
+     columns, each call on the next of R weight copies (R x 9.4 MB > 2 x the 256 MB
+     Infinity Cache, so weights stream from HBM);
+  2. block decode of that matrix to binary16 (iq4_dequant_blocks);
+  3. MoE decode step: 4 fp32 tokens, top-8 of 128 experts (hidden 2048, inter 768),
+     alternating between two expert banks (2 x 340 MB, cold);
+  4. MoE prefill layer: 3,256 f16 tokens, Zipf(1.1)-skewed top-8 routing, same bank;
+  5. long-prompt projection: 13,056 f16 tokens x W 14,336 x 4,096, 512-token chunks.
 
-Prints ONE JSON line.  ``value`` = effective weight GB/s of the matvec calls
-(total weight bytes / total kernel time, T = 1..4).  The roofline object is measured
-live with HIP events on the launch stream; ``cpu_baseline`` times the CPU oracle on a
-bounded sample of the same workload.
+Prints ONE JSON line.  ``value`` = effective weight GB/s of the verify-window matvec
+(total weight bytes of the T = 1..4 calls / their total time).  Launch times come from
+HIP events around graph replays on the launch stream (many launches per replay, so
+per-launch CPU overhead does not enter).  ``cpu_baseline`` times the CPU oracle on a
+bounded sample of the matvec workload.
 """
 from __future__ import annotations
 
@@ -24,37 +30,52 @@ ROOT = os.path.dirname(os.path.abspath(__file__))
 if ROOT not in sys.path:
     sys.path.insert(0, ROOT)
 
-HBM_PEAK_GBS = 8000.0  # MI355X HBM3E, published
+HBM_PEAK_GBS = 8000.0       # MI355X HBM3E, published
+F16_MFMA_PEAK_TFS = 2500.0  # MI355X dense f16 matrix throughput, published
+
+HIDDEN, INTER, N_EXPERT, TOP_K = 2048, 768, 128, 8
 
 
 def log(msg):
     print(f"[bench] {msg}", file=sys.stderr, flush=True)
 
 
-def build_verify_inputs(torch, iq4, synth, copies: int):
-    """W 4096 x 4096 quantised on the GPU (seed 102), packed, replicated `copies`
-    times; X = 4 fp32 columns (seed 102)."""
-    n = k = 4096
-    w = torch.from_numpy(synth.weights_f32(synth.SEED_VERIFY, synth.TAG_WEIGHT, n, k)).cuda()
+def quantize_pack(torch, iq4, w32, n, k):
+    """float32 [n, k] on the GPU -> packed IQ4 tensor (and the row-block bytes)."""
     blocks = torch.empty(n * k // 32 * 18, dtype=torch.uint8, device="cuda")
-    iq4.iq4_quantize_blocks(w, n * k // 32, blocks)
-    nbytes = iq4.iq4_packed_bytes(n, k)
-    packed = [torch.empty(nbytes, dtype=torch.uint8, device="cuda") for _ in range(copies)]
-    iq4.iq4_pack_weights(blocks, n, k, packed[0])
-    for p in packed[1:]:
-        p.copy_(packed[0])
-    x = torch.from_numpy(synth.acts_f32(synth.SEED_VERIFY, synth.TAG_X, 4, k)).cuda()
-    y = torch.empty((4, n), dtype=torch.float32, device="cuda")
-    wsb = iq4.iq4_qmv_workspace_size(n, k)
-    ws = torch.zeros(max(wsb, 256), dtype=torch.uint8, device="cuda")
-    del w
-    return dict(n=n, k=k, packed=packed, x=x, y=y, wbytes=nbytes, ws=ws, wsb=wsb)
+    iq4.iq4_quantize_blocks(w32.contiguous(), n * k // 32, blocks)
+    packed = torch.empty(iq4.iq4_packed_bytes(n, k), dtype=torch.uint8, device="cuda")
+    iq4.iq4_pack_weights(blocks, n, k, packed)
+    return packed, blocks
+
+
+def build_bank(torch, iq4, synth, seed):
+    """128 experts x (gate, up: 768 x 2048; down: 2048 x 768), packed, expert-major."""
+    sg = iq4.iq4_packed_bytes(INTER, HIDDEN)
+    sd = iq4.iq4_packed_bytes(HIDDEN, INTER)
+    gate = torch.empty(N_EXPERT * sg, dtype=torch.uint8, device="cuda")
+    up = torch.empty(N_EXPERT * sg, dtype=torch.uint8, device="cuda")
+    down = torch.empty(N_EXPERT * sd, dtype=torch.uint8, device="cuda")
+    for e in range(N_EXPERT):
+        for which, dst, n, k, size in (("gate", gate, INTER, HIDDEN, sg), ("up", up, INTER, HIDDEN, sg),
+                                       ("down", down, HIDDEN, INTER, sd)):
+            w = synth.weights_f32_torch(seed, synth.tag_expert(e, which), n, k, device="cuda")
+            p, _ = quantize_pack(torch, iq4, w, n, k)
+            dst[e * size:(e + 1) * size].copy_(p)
+    return gate, up, down
+
+
+def route(torch, iq4, logits):
+    n = logits.shape[0]
+    ids = torch.empty((n, TOP_K), dtype=torch.int32, device="cuda")
+    w = torch.empty((n, TOP_K), dtype=torch.float32, device="cuda")
+    iq4.iq4_route_topk(logits.contiguous(), n, N_EXPERT, TOP_K, ids, w)
+    return ids, w
 
 
 def cpu_baseline(min_seconds: float = 10.0):
     """The CPU oracle on the verify-window matvec, T = 1..4 per pass, repeated until
-    `min_seconds` of work; returns GB/s of weight bytes like the GPU value."""
-    import numpy as np
+    `min_seconds` of work; GB/s of weight bytes like the GPU value."""
     import oracle
     import synth
     try:
@@ -77,16 +98,21 @@ def cpu_baseline(min_seconds: float = 10.0):
         el = time.perf_counter() - t0
         if el >= min_seconds or passes >= 50:
             break
-    return {"value": done_bytes / el / 1e9, "unit": "GB/s", "cores": int(cores), "kind": "oracle",
-            "sample": f"{passes} passes of the verify-window matvec (W 4096x4096, T=1..4), "
-                      f"numpy float64, {el:.1f} s"}
+    return {"value": round(done_bytes / el / 1e9, 4), "unit": "GB/s", "cores": int(cores), "kind": "oracle",
+            "sample": f"{passes} passes of the verify-window matvec (W 4096x4096, T=1..4): oracle decode + "
+                      f"float64 product, {el:.1f} s"}
+
+
+def roof(bound, achieved, peak, unit, kernel, traffic=None):
+    return {"bound": bound, "achieved": round(achieved, 2), "peak": peak, "unit": unit,
+            "frac": round(achieved / peak, 4), "traffic": traffic, "kernel": kernel}
 
 
 def main():
     ap = argparse.ArgumentParser()
     ap.add_argument("--gpus", type=int, default=1)
-    ap.add_argument("--steps", type=int, default=200)
-    ap.add_argument("--warmup", type=int, default=50)
+    ap.add_argument("--steps", type=int, default=20)
+    ap.add_argument("--warmup", type=int, default=3)
     ap.add_argument("--copies", type=int, default=64)
     ap.add_argument("--no-cpu-baseline", action="store_true")
     args = ap.parse_args()
@@ -101,87 +127,198 @@ def main():
     import synth
 
     torch.cuda.set_device(0)
-    log("building inputs")
-    V = build_verify_inputs(torch, iq4, synth, args.copies)
     stream = torch.cuda.current_stream()
-    n, k = V["n"], V["k"]
+    Ev = lambda: torch.cuda.Event(enable_timing=True)  # noqa: E731
 
-    it = [0]
+    # ---- inputs ------------------------------------------------------------------------
+    log("verify-window matvec inputs")
+    n = k = 4096
+    w = synth.weights_f32_torch(synth.SEED_VERIFY, synth.TAG_WEIGHT, n, k, device="cuda")
+    p0, vblocks = quantize_pack(torch, iq4, w, n, k)
+    del w
+    R = args.copies
+    vcopies = [p0] + [p0.clone() for _ in range(R - 1)]
+    wb = iq4.iq4_packed_bytes(n, k)
+    vx = synth.acts_f32_torch(synth.SEED_VERIFY, synth.TAG_X, 4, k, device="cuda")
+    vy = torch.empty((4, n), dtype=torch.float32, device="cuda")
+    vwsb = iq4.iq4_qmv_workspace_size(n, k)
+    vws = torch.zeros(max(vwsb, 256), dtype=torch.uint8, device="cuda")
+    deq_out = torch.empty(n * k, dtype=torch.float16, device="cuda")
 
-    def mmvq(T):
-        p = V["packed"][it[0] % len(V["packed"])]
-        it[0] += 1
-        iq4.iq4_qmv_multi(p, n, k, V["x"], k, T, V["y"], n, V["ws"], V["wsb"], stream)
+    log("expert banks (2 x 128 experts)")
+    bank_a = build_bank(torch, iq4, synth, synth.SEED_EXPERTS)
+    bank_b = build_bank(torch, iq4, synth, synth.SEED_EXPERTS + 1000)
 
-    def step():
-        for T in (1, 2, 3, 4):
-            mmvq(T)
+    log("MoE decode and prefill inputs")
+    dx = synth.acts_f32_torch(synth.SEED_DECODE, synth.TAG_X, 4, HIDDEN, device="cuda")
+    dlog = synth.acts_f32_torch(synth.SEED_DECODE, synth.TAG_LOGITS, 4, N_EXPERT, device="cuda")
+    d_ids, d_w = route(torch, iq4, dlog)
+    d_out = torch.empty((4, HIDDEN), dtype=torch.float32, device="cuda")
+    d_wsb = iq4.iq4_moe_workspace_size(4, TOP_K, N_EXPERT, HIDDEN, INTER, iq4.IQ4_F32)
+    d_ws = torch.empty(d_wsb, dtype=torch.uint8, device="cuda")
+    n_unique = int(torch.unique(d_ids).numel())
+
+    NP = 3256
+    px = synth.acts_f16_torch(synth.SEED_PREFILL, synth.TAG_X, NP, HIDDEN, device="cuda")
+    plog = torch.from_numpy(synth.logits_zipf_gumbel(synth.SEED_PREFILL, synth.TAG_GUMBEL, NP, N_EXPERT)).cuda()
+    p_ids, p_w = route(torch, iq4, plog)
+    p_out = torch.empty((NP, HIDDEN), dtype=torch.float32, device="cuda")
+    p_wsb = iq4.iq4_moe_workspace_size(NP, TOP_K, N_EXPERT, HIDDEN, INTER, iq4.IQ4_F16)
+    p_ws = torch.empty(p_wsb, dtype=torch.uint8, device="cuda")
+    counts = torch.bincount(p_ids.reshape(-1).long(), minlength=N_EXPERT)
+
+    log("long-prompt projection inputs")
+    LN, LK, LM, CH = 14336, 4096, 13056, 512
+    lw = synth.weights_f32_torch(synth.SEED_LONG, synth.TAG_WEIGHT, LN, LK, device="cuda")
+    lpacked, _ = quantize_pack(torch, iq4, lw, LN, LK)
+    del lw
+    lx = synth.acts_f16_torch(synth.SEED_LONG, synth.TAG_X, LM, LK, device="cuda")
+    ly = torch.empty((LM, LN), dtype=torch.float32, device="cuda")
+    torch.cuda.synchronize()
+
+    # ---- the step's calls ----------------------------------------------------------------
+    def mmvq(copy, T, s):
+        iq4.iq4_qmv_multi(vcopies[copy % R], n, k, vx, k, T, vy, n, vws, vwsb, s)
+
+    def dequant(s):
+        iq4.iq4_dequant_blocks(vblocks, n * k // 32, iq4.IQ4_F16, deq_out, s)
+
+    def moe_decode(bank, s):
+        g, u, d = bank
+        iq4.iq4_moe_expert_gemm(dx, iq4.IQ4_F32, 4, HIDDEN, d_ids, d_w, TOP_K, N_EXPERT, HIDDEN, INTER,
+                                g, u, d, d_out, HIDDEN, d_ws, d_wsb, 0, s)
+
+    def moe_prefill(s):
+        g, u, d = bank_a
+        iq4.iq4_moe_expert_gemm(px, iq4.IQ4_F16, NP, HIDDEN, p_ids, p_w, TOP_K, N_EXPERT, HIDDEN, INTER,
+                                g, u, d, p_out, HIDDEN, p_ws, p_wsb, 0, s)
+
+    def dense(s):
+        iq4.iq4_qgemm(lpacked, LN, LK, lx, LM, LK, ly, LN, CH, s)
+
+    # The small calls are replayed from HIP graphs (their CPU launch cost would otherwise
+    # exceed their GPU time); each step advances through the weight copies.
+    def capture(fn):
+        g = torch.cuda.CUDAGraph()
+        side = torch.cuda.Stream()
+        side.wait_stream(stream)
+        with torch.cuda.graph(g, stream=side):
+            fn(torch.cuda.current_stream())
+        stream.wait_stream(side)
+        return g
+
+    steps_per_cycle = R // 4
+    mm_graphs = [capture(lambda s, i=i: [mmvq(4 * i + T - 1, T, s) for T in (1, 2, 3, 4)])
+                 for i in range(steps_per_cycle)]
+    dec_graphs = [capture(lambda s: moe_decode(bank_a, s)), capture(lambda s: moe_decode(bank_b, s))]
+
+    def step(i, ev=None):
+        if ev:
+            ev[0].record(stream)
+        mm_graphs[i % steps_per_cycle].replay()
+        if ev:
+            ev[1].record(stream)
+        dequant(stream)
+        if ev:
+            ev[2].record(stream)
+        dec_graphs[i % 2].replay()
+        if ev:
+            ev[3].record(stream)
+        moe_prefill(stream)
+        if ev:
+            ev[4].record(stream)
+        dense(stream)
+        if ev:
+            ev[5].record(stream)
 
     log(f"warmup {args.warmup} steps")
-    for _ in range(args.warmup):
-        step()
+    for i in range(args.warmup):
+        step(i)
     torch.cuda.synchronize()
 
-    # The timed region replays HIP graphs of the step's launches: per-launch CPU
-    # overhead (several us) would otherwise hide kernels that take a few us.
-    # One graph per T: R launches, each on the next weight copy (cold weights).
-    R = len(V["packed"])
-    graphs = {}
-    for T in (1, 2, 3, 4):
-        g = torch.cuda.CUDAGraph()
-        with torch.cuda.graph(g, stream=torch.cuda.Stream()):
-            s2 = torch.cuda.current_stream()
-            for r in range(R):
-                iq4.iq4_qmv_multi(V["packed"][r], n, k, V["x"], k, T, V["y"], n, V["ws"], V["wsb"], s2)
-        graphs[T] = g
-    for T in (1, 2, 3, 4):  # warm replays
-        graphs[T].replay()
+    # ---- timed region: exactly K steps ---------------------------------------------------
+    log(f"timing {args.steps} steps")
+    evs = [[Ev() for _ in range(6)] for _ in range(args.steps)]
+    start, end = Ev(), Ev()
     torch.cuda.synchronize()
+    start.record(stream)
+    for i in range(args.steps):
+        step(i, evs[i])
+    end.record(stream)
+    torch.cuda.synchronize()
+    ms_step = start.elapsed_time(end) / args.steps
+    comp = {name: sum(evs[i][j].elapsed_time(evs[i][j + 1]) for i in range(args.steps)) / args.steps
+            for j, name in enumerate(("mmvq_4_calls", "dequant", "moe_decode", "moe_prefill", "dense"))}
 
-    # K steps = K x (T = 1..4) launches, timed per T with events around graph replays
-    reps = max(1, args.steps // R) if args.steps >= R else 1
+    # ---- per-launch matvec durations: graphs of R launches per T ------------------------
     per_T = {}
-    start, end = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
-    total_ms, total_launches = 0.0, 0
     for T in (1, 2, 3, 4):
+        g = capture(lambda s, T=T: [mmvq(c, T, s) for c in range(R)])
+        g.replay()
         torch.cuda.synchronize()
-        start.record(stream)
+        a, b = Ev(), Ev()
+        reps = 4
+        a.record(stream)
         for _ in range(reps):
-            graphs[T].replay()
-        end.record(stream)
+            g.replay()
+        b.record(stream)
         torch.cuda.synchronize()
-        ms = start.elapsed_time(end)
-        per_T[T] = ms / (reps * R)  # ms per launch
-        total_ms += ms
-        total_launches += reps * R
-    steps_timed = total_launches // 4
-    ms_step = total_ms / steps_timed
+        per_T[T] = a.elapsed_time(b) / (reps * R)  # ms per launch
     tot_ms = sum(per_T.values())
-    wb = V["wbytes"]
     value = 4 * wb / (tot_ms * 1e-3) / 1e9
-    alg = sum(wb + 2 * 4 * T * k for T in (1, 2, 3, 4))  # weights + X + Y
-    achieved = alg / (tot_ms * 1e-3) / 1e9
+    mm_alg = sum(wb + 2 * 4 * T * k for T in (1, 2, 3, 4))  # weights + X + Y per four calls
+    mm_achieved = mm_alg / (tot_ms * 1e-3) / 1e9
+
+    prefill_flop = NP * TOP_K * 3 * 2 * HIDDEN * INTER  # 245,819,768,832
+    dense_flop = 2 * LM * LN * LK
+    unique_bytes = n_unique * 3 * iq4.iq4_packed_bytes(INTER, HIDDEN)
+    deq_bytes = n * k // 32 * 18 + n * k * 2
 
     res = {
         "metric": "MMVQ effective weight GB/s at T=1..4; ms per 3,256-token MoE layer",
         "value": round(value, 2),
         "unit": "GB/s",
         "n_gpus": 1,
-        "steps": steps_timed,
+        "steps": args.steps,
         "warmup": args.warmup,
-        "ms_per_step": round(ms_step, 5),
+        "ms_per_step": round(ms_step, 4),
         "higher_is_better": True,
         "scaling": "weak",
         "vs_baseline": None,
         "dtype": "f32",
         "data": "synthetic",
-        "config": {"workload": "verify-window MMVQ W 4096x4096 IQ4 (18 B/32 w), X fp32 T=1..4, "
-                               f"{args.copies} rotating weight copies (cold)",
-                   "mmvq_us_per_T": {str(T): round(per_T[T] * 1e3, 3) for T in per_T},
-                   "mmvq_weight_gbs_per_T": {str(T): round(wb / (per_T[T] * 1e-3) / 1e9, 1) for T in per_T}},
-        "roofline": {"bound": "hbm", "achieved": round(achieved, 1), "peak": HBM_PEAK_GBS, "unit": "GB/s",
-                     "frac": round(achieved / HBM_PEAK_GBS, 4), "traffic": None,
-                     "kernel": "qmv_kernel (verify-window matvec, T=1..4 mean)"},
+        "config": {
+            "workload": "verify-window MMVQ (W 4096x4096 IQ4, 18 B per 32 weights; fp32 X, T=1..4; "
+                        f"{R} rotating weight copies) + IQ4 decode + MoE decode (4 tokens) + MoE prefill "
+                        "(3256 tokens, Zipf 1.1, top-8 of 128, hidden 2048, inter 768) + long-prompt "
+                        "projection (13056 x 4096 x 14336, 512-token chunks)",
+            "mmvq_us_per_call": {str(T): round(per_T[T] * 1e3, 3) for T in per_T},
+            "mmvq_weight_gbs_per_T": {str(T): round(wb / (per_T[T] * 1e-3) / 1e9, 1) for T in per_T},
+            "moe_prefill_ms_per_layer": round(comp["moe_prefill"], 4),
+            "moe_prefill_tflops": round(prefill_flop / (comp["moe_prefill"] * 1e-3) / 1e12, 2),
+            "moe_decode_us_per_step": round(comp["moe_decode"] * 1e3, 2),
+            "moe_decode_unique_experts": n_unique,
+            "dense_ms_26_chunks": round(comp["dense"], 4),
+            "dense_tflops": round(dense_flop / (comp["dense"] * 1e-3) / 1e12, 2),
+            "dequant_us": round(comp["dequant"] * 1e3, 2),
+            "prefill_expert_tokens_max_min": [int(counts.max()), int(counts.min())],
+            "component_ms_per_step": {kk: round(v, 4) for kk, v in comp.items()},
+        },
+        "roofline": roof("hbm", mm_achieved, HBM_PEAK_GBS, "GB/s",
+                         "qmv_kernel<dense>: verify-window matvec, bytes = W + X + Y per call, "
+                         "mean over T=1..4"),
+        "rooflines": {
+            "moe_prefill_layer": roof("mfma", prefill_flop / (comp["moe_prefill"] * 1e-3) / 1e12,
+                                      F16_MFMA_PEAK_TFS, "TFLOP/s",
+                                      "gather + qgemm<gateup> + qgemm<down> + combine, f16 MFMA"),
+            "dense_projection": roof("mfma", dense_flop / (comp["dense"] * 1e-3) / 1e12, F16_MFMA_PEAK_TFS,
+                                     "TFLOP/s", "qgemm<dense> x 26 chunks"),
+            "moe_decode_step": roof("hbm", unique_bytes / (comp["moe_decode"] * 1e-3) / 1e9, HBM_PEAK_GBS,
+                                    "GB/s", f"gather + qmv<gateup> + qmv<down> + combine, {n_unique} "
+                                    "unique experts' weights"),
+            "dequant": roof("hbm", deq_bytes / (comp["dequant"] * 1e-3) / 1e9, HBM_PEAK_GBS, "GB/s",
+                            "dequant_kernel<f16>: 9.4 MB of blocks in, 33.5 MB of f16 out"),
+        },
     }
     if not args.no_cpu_baseline:
         log("cpu baseline (oracle)")

@@ -196,6 +196,8 @@ int iq4_moe_expert_gemm(const void* x, int32_t act_dtype, int64_t n_tok, int64_t
       !aligned(w, 4) || !aligned(w_gate, 256) || !aligned(w_up, 256) || !aligned(w_down, 256))
     return set_error(IQ4_E_ALIGN, "%s: x/out 16-byte aligned with ldx %% %d == 0 and ldo %% 4 == 0, "
                      "weights 256-byte aligned", fn, f16 ? 8 : 4);
+  if (n_tok * ldx >= ((int64_t)1 << 31) || n_tok * top_k * inter >= ((int64_t)1 << 31))
+    return set_error(IQ4_E_UNSUPPORTED, "%s: x and the intermediate rows must span fewer than 2^31 elements", fn);
   const MoeLayout L = moe_layout(n_tok, top_k, n_expert, hidden, inter, f16);
   if (!workspace || ws_bytes < (size_t)L.total)
     return set_error(IQ4_E_WORKSPACE, "%s: needs a workspace of %lld bytes", fn, (long long)L.total);
@@ -231,6 +233,8 @@ int iq4_qgemm(const void* packed, int64_t n, int64_t k, const void* x, int64_t m
   if (!packed || !x || !y) return set_error(IQ4_E_ARG, "iq4_qgemm: null pointer");
   if (!aligned(packed, 256) || !aligned(x, 16) || ldx % 8 || !aligned(y, 4))
     return set_error(IQ4_E_ALIGN, "iq4_qgemm: packed 256-byte, x 16-byte aligned with ldx %% 8 == 0, y 4-byte");
+  if ((chunk > 0 ? (chunk < m ? chunk : m) : m) * ldx >= ((int64_t)1 << 31))
+    return set_error(IQ4_E_UNSUPPORTED, "iq4_qgemm: a chunk of x must span fewer than 2^31 elements");
   return launch_qgemm_dense(static_cast<const uint8_t*>(packed), n, k, static_cast<const uint16_t*>(x), m,
                             ldx, y, ldy, chunk, as_stream(stream));
 }

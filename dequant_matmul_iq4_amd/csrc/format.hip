@@ -97,8 +97,10 @@ __global__ void __launch_bounds__(256) dequant_kernel(const uint16_t* __restrict
   }
 }
 
-// One thread per packed entry (64 per tile).  Entry l = 16g + j of tile (rt, kq)
-// gathers index bytes 4g..4g+3 of the tile's four blocks of row 16rt + j; entries
+// One thread per packed entry (64 per tile).  Entry l = 16g + j of tile (rt, kq) holds,
+// for each of the tile's four blocks of row 16rt + j, the indices of elements
+// 8g .. 8g+7 as four bytes, element 8g + 2i in the low and 8g + 2i + 1 in the high
+// nibble of byte i (a row-block byte i holds elements i and i + 16 instead); entries
 // with g == 0 also write that row's four scales.
 __global__ void __launch_bounds__(256) pack_kernel(const uint16_t* __restrict__ blocks, int64_t n,
                                                    int64_t k, uint8_t* __restrict__ packed) {
@@ -112,13 +114,23 @@ __global__ void __launch_bounds__(256) pack_kernel(const uint16_t* __restrict__ 
   int64_t rt = tile / kq_n, kq = tile % kq_n;
   int64_t row = rt * kTileRows + j;
   const int64_t bpr = k / kQK;
+  const int shift = (g >> 1) * 4;  // elements 0..15: low nibbles; 16..31: high nibbles
   uint32_t word[4];
   uint16_t sc[4];
 #pragma unroll
   for (int b = 0; b < 4; ++b) {
     const uint16_t* blk = blocks + (row * bpr + kq * kTileBlocks + b) * (kBlockBytes / 2);
     sc[b] = blk[0];
-    word[b] = (uint32_t)blk[1 + 2 * g] | ((uint32_t)blk[2 + 2 * g] << 16);
+    // row-block bytes 8(g & 1) .. 8(g & 1) + 7 carry elements 8g .. 8g+7 (in one nibble half)
+    uint32_t w = 0;
+#pragma unroll
+    for (int i = 0; i < 4; ++i) {
+      const uint16_t two = blk[1 + 4 * (g & 1) + i];  // bytes 2i, 2i+1 of that run
+      const uint32_t e0 = ((uint32_t)(two & 0xFF) >> shift) & 0xF;
+      const uint32_t e1 = ((uint32_t)(two >> 8) >> shift) & 0xF;
+      w |= (e0 | (e1 << 4)) << (8 * i);
+    }
+    word[b] = w;
   }
   uint4* np = reinterpret_cast<uint4*>(packed + tile * kTileNibbleBytes) + l;
   *np = make_uint4(word[0], word[1], word[2], word[3]);

@@ -11,24 +11,29 @@
 //           scales by the pair's gate weight and writes the pair's row (or adds it
 //           atomically into the token's output).
 //
-// Tiling (workgroup = 4 waves, 128 x 256 outputs):
-//   * the 128 x 128 activation tile of one 4-block quad is staged in LDS, already in
-//     matrix-core fragment order (a fragment read is one conflict-free 1 KiB
-//     ds_read_b128 per wave), double-buffered across quads;
-//   * each wave owns 64 weight rows (4 packed row tiles) and decodes them itself,
-//     straight from the packed tiles into B fragments: one 128-bit load of indices and
-//     one 64-bit load of scales per row tile and quad, a byte-indexed LDS table giving
-//     two binary16 levels per byte, and one packed binary16 multiply by the block
-//     scale -- the binary16 rounding of the exact decoded weight.  No decoded weight
-//     goes through LDS or HBM;
-//   * per block a wave issues 8 x 4 MFMAs against 8 A-fragment reads.
-//
-// Within a fragment the 32 weights of a block are visited in the order
-// 0,16,1,17,...,15,31 (low/high nibble of each index byte); the activation tile is
-// written to LDS in the same order, so each MFMA still sums one block's products.
+// Tiling (workgroup = 4 waves, 128 x 256 outputs, K walked in 4-block quads):
+//   * a ring of 3 LDS stages, each holding one quad of the workgroup's operands and
+//     filled two quads ahead, straight from global memory with global_load_lds (no
+//     operand passes through VGPRs on its way in):
+//       activations  32 KiB: every 16-row x 32-k fragment in matrix-core A order
+//                    (lane l = 16g + r holds row r, elements 8g..8g+7), one
+//                    dwordx4 copy per fragment; wave w copies block w of the quad;
+//       weights      4 x 4.5 KiB: each wave copies its own 4 packed row tiles
+//                    (1 KiB of indices + 128 B of scales each) as they are in HBM;
+//   * each wave decodes its 64 weight rows into B fragments: a byte-indexed LDS table
+//     gives two binary16 levels per index byte, one packed binary16 multiply by the
+//     block scale gives the binary16 rounding of the exact decoded weight.  No decoded
+//     weight goes through LDS or HBM;
+//   * per block a wave issues 8 x 4 MFMAs against 8 A-fragment reads; the next block's
+//     16 table reads are issued under the current block's MFMAs.
+// The copies are issued from inline assembly so that the compiler, which cannot tell
+// the ring stages apart, does not drain every copy in flight before each LDS read; the
+// kernel waits for them itself: per quad one s_waitcnt for this wave's copies of the
+// quad, then one workgroup barrier (the quad is complete for everyone, and the stage
+// filled next is no longer read by anyone).
 #include "common.hpp"
-#include "launch.hpp"
 #include "gemm.hpp"
+#include "launch.hpp"
 
 namespace iq4 {
 
@@ -37,10 +42,50 @@ constexpr int kWaveRT = 4;               // packed row tiles (16 rows) per wave
 constexpr int kWaves = 4;
 constexpr int kBN = kWaves * kWaveRT * kTileRows;  // 256 weight rows per workgroup
 constexpr int kMT = kBM / 16;            // 8 fragment rows of A
-constexpr int kALdsQuad = kTileBlocks * kMT * 64 * 16;  // 32 KiB per quad
+constexpr int kStages = 3;               // quads in the ring
+constexpr int kABytes = kTileBlocks * kMT * 1024;                        // 32 KiB
+constexpr int kWaveBBytes = kWaveRT * (kTileNibbleBytes + kTileScaleBytes);  // 4.5 KiB
+constexpr int kStageBytes = kABytes + kWaves * kWaveBBytes;              // 50 KiB
+constexpr int kCopiesPerQuad = kMT + kWaveRT + 2;  // per wave: A fragments, index tiles, 2 scale copies
 
 __device__ __forceinline__ uint32_t f16_of_level(int c) {
   return (uint32_t)__half_as_ushort(__int2half_rn(c));  // exact: |c| <= 127
+}
+
+// s_waitcnt vmcnt(n) (gfx9 encoding, other counters left alone).
+template <int N>
+__device__ __forceinline__ void wait_vmcnt() {
+  static_assert(N >= 0 && N < 64, "vmcnt range");
+  __builtin_amdgcn_s_waitcnt((N & 15) | ((N >> 4) << 14) | (7 << 4) | (15 << 8));
+}
+
+// LDS byte address of a pointer into a __shared__ array.
+__device__ __forceinline__ uint32_t lds_addr(const void* p) {
+  return (uint32_t)(uintptr_t)(const __attribute__((address_space(3))) uint8_t*)p;
+}
+
+// Global -> LDS copies (saddr form): lane l reads base + voff_l and its bytes land at
+// LDS address lds + 16 l (dwordx4) or lds + 4 l (dword).  M0 carries the LDS address
+// (written by the compiler); one wait state separates that write from the copy.
+__device__ __forceinline__ void copy16(const void* base, uint32_t voff, uint32_t lds) {
+  asm volatile("s_nop 0\n\tglobal_load_lds_dwordx4 %0, %1"
+               :
+               : "v"(voff), "s"(base), "{m0}"(lds)
+               : "memory");
+}
+__device__ __forceinline__ void copy4(const void* base, uint32_t voff, uint32_t lds) {
+  asm volatile("s_nop 0\n\tglobal_load_lds_dword %0, %1"
+               :
+               : "v"(voff), "s"(base), "{m0}"(lds)
+               : "memory");
+}
+
+// Workgroup barrier ordering LDS only: the copies are waited for explicitly, so the
+// barrier must not wait for every global load in flight.
+__device__ __forceinline__ void lds_barrier() {
+  __builtin_amdgcn_fence(__ATOMIC_RELEASE, "workgroup", "local");
+  __builtin_amdgcn_s_barrier();
+  __builtin_amdgcn_fence(__ATOMIC_ACQUIRE, "workgroup", "local");
 }
 
 // XCD-aware order of the workgroups: hardware deals workgroup b to XCD b mod 8, so
@@ -53,24 +98,23 @@ __device__ __forceinline__ int64_t xcd_swizzle(int64_t b, int64_t G) {
 
 template <int MODE>
 __global__ void __launch_bounds__(256) qgemm_kernel(GemmArgs a) {
-  __shared__ __attribute__((aligned(16))) uint8_t lds_a[2][kALdsQuad];
+  __shared__ __attribute__((aligned(1024))) uint8_t ring[kStages][kStageBytes];
   __shared__ uint32_t lut[256];
 
   const int tid = threadIdx.x;
-  const int lane = tid & 63, wave = tid >> 6;
+  const int lane = tid & 63;
+  const int wave = __builtin_amdgcn_readfirstlane(tid >> 6);
   const int g = lane >> 4, c = lane & 15;
   lut[tid] = f16_of_level(level_of(tid & 15)) | (f16_of_level(level_of(tid >> 4)) << 16);
 
   // ---- which tile ------------------------------------------------------------------
   int64_t m0, rows;          // first A row (in the launch's row space) and valid rows
   int64_t n0;                // first weight row of the workgroup
-  int e = 0;                 // expert (grouped modes)
   int64_t seg0 = 0;          // first sorted pair of the expert (grouped modes)
   const uint8_t* W0 = a.W0;
   const uint8_t* W1 = a.W1;
   if (MODE == kGemmDense) {
-    const int64_t G = (int64_t)gridDim.x;
-    const int64_t L = xcd_swizzle(blockIdx.x, G);
+    const int64_t L = xcd_swizzle(blockIdx.x, (int64_t)gridDim.x);
     const int64_t mt_n = (a.M + kBM - 1) / kBM;
     const int64_t mt = L % mt_n, nt = L / mt_n;
     m0 = mt * kBM;
@@ -81,7 +125,7 @@ __global__ void __launch_bounds__(256) qgemm_kernel(GemmArgs a) {
     const int64_t L = xcd_swizzle(blockIdx.x, (int64_t)gridDim.x);
     const int64_t ti = L / ntl, nt = L % ntl;
     if (ti >= *a.num_tiles) return;
-    e = a.tiles[2 * ti];
+    const int e = a.tiles[2 * ti];
     const int mt = a.tiles[2 * ti + 1];
     seg0 = a.offsets[e];
     const int64_t cnt = a.offsets[e + 1] - seg0;
@@ -93,12 +137,29 @@ __global__ void __launch_bounds__(256) qgemm_kernel(GemmArgs a) {
     W0 += (int64_t)e * a.w_expert_stride;
     if (MODE == kGemmGateUp) W1 += (int64_t)e * a.w_expert_stride;
   }
-  const int64_t kq_n = a.K / kTileK;
+  const int kq_n = (int)(a.K / kTileK);
   const int64_t nib_bytes = a.N * (a.K / kQK) * kNibbleBytes;
+  const uint32_t ring0 = lds_addr(&ring[0][0]);
+
+  // ---- activation rows of this lane: row r = c of each of the 8 fragment rows ------
+  // (rows past the tile's valid rows repeat its last row: read in bounds, never stored)
+  uint32_t a_off[kMT];  // byte offsets from A (the launcher checks they fit in 32 bits)
+#pragma unroll
+  for (int mt = 0; mt < kMT; ++mt) {
+    const int64_t r = min((int64_t)(16 * mt + c), rows - 1);
+    int64_t src_row;
+    if (MODE == kGemmDense) src_row = m0 + r;
+    else if (MODE == kGemmGateUp) src_row = a.pairs[seg0 + m0 + r] / a.top_k;  // token of the pair
+    else src_row = seg0 + m0 + r;                                             // h in sorted order
+    // this wave copies block `wave` of each quad
+    a_off[mt] = (uint32_t)(2 * (src_row * a.lda + 32 * wave + 8 * g));
+  }
 
   // ---- weight row tiles of this wave -------------------------------------------------
   // DENSE / DOWN: rows n0 + 64w + 16r, r = 0..3 of W0.
   // GATEUP: r = 0,1 -> gate rows n0 + 32w + 16r;  r = 2,3 -> up rows n0 + 32w + 16(r-2).
+  // Row tiles past N are replaced by the last row tile (read in bounds, never stored),
+  // so the two tiles of each scale copy are equal or ascending in memory.
   const uint8_t* wbase[kWaveRT];
   int64_t wtile0[kWaveRT];
   bool rt_ok[kWaveRT];
@@ -113,76 +174,28 @@ __global__ void __launch_bounds__(256) qgemm_kernel(GemmArgs a) {
       wbase[r] = W0;
     }
     rt_ok[r] = row0 < a.N;
-    wtile0[r] = (rt_ok[r] ? row0 / kTileRows : 0) * kq_n;  // tile index of quad 0
+    wtile0[r] = (min(row0, a.N - kTileRows) / kTileRows) * kq_n;  // tile index of quad 0
   }
+  // scale copy i brings row tiles 2i (lanes 0..31) and 2i+1 (lanes 32..63)
+  uint32_t s_off[2];
+#pragma unroll
+  for (int i = 0; i < 2; ++i)
+    s_off[i] = (uint32_t)(4 * (lane & 31) + (lane >> 5) * (wtile0[2 * i + 1] - wtile0[2 * i]) * kTileScaleBytes);
 
-  // ---- A staging: 1024 items of (row, block, half) per quad, 4 per thread ----------
-  // item = ((row * 4) + block) * 2 + half; reads physical k chunks [8h, 8h+8) and
-  // [16 + 8h, 16 + 8h + 8) of the block and writes fragments g = 2h and 2h + 1.
-  const uint16_t* arow[4];
-  int a_lds_off[4];
+  // copy quad q into its stage: A block `wave` (8 fragments), then this wave's tiles
+  auto copy_quad = [&](int q) {
+    const uint32_t st = ring0 + (uint32_t)((q % kStages) * kStageBytes);
 #pragma unroll
-  for (int it = 0; it < 4; ++it) {
-    const int item = tid + 256 * it;
-    const int half = item & 1, blk = (item >> 1) & 3, r = item >> 3;  // r = 0..127
-    const uint16_t* p = nullptr;
-    if (r < rows) {
-      int64_t src_row;
-      if (MODE == kGemmDense) {
-        src_row = m0 + r;
-      } else if (MODE == kGemmGateUp) {
-        src_row = a.pairs[seg0 + m0 + r] / a.top_k;  // token of the pair
-      } else {
-        src_row = seg0 + m0 + r;  // h is stored in pair-sorted order
-      }
-      p = a.A + src_row * a.lda + blk * kQK + 8 * half;
-    }
-    arow[it] = p;
-    const int mt = r >> 4, rr = r & 15;
-    a_lds_off[it] = ((blk * kMT + mt) * 64 + (2 * half) * 16 + rr) * 16;
-  }
-
-  uint4 a_reg[4][2];
-  auto load_a = [&](int64_t q) {
+    for (int mt = 0; mt < kMT; ++mt)
+      copy16(a.A + (int64_t)q * kTileK, a_off[mt], st + (uint32_t)((wave * kMT + mt) * 1024));
+    const uint32_t sb = st + kABytes + wave * kWaveBBytes;
 #pragma unroll
-    for (int it = 0; it < 4; ++it) {
-      if (arow[it]) {
-        const uint4* p = reinterpret_cast<const uint4*>(arow[it] + q * kTileK);
-        a_reg[it][0] = p[0];
-        a_reg[it][1] = p[2];  // + 16 elements
-      } else {
-        a_reg[it][0] = make_uint4(0, 0, 0, 0);
-        a_reg[it][1] = make_uint4(0, 0, 0, 0);
-      }
-    }
-  };
-  auto store_a = [&](int buf) {
+    for (int r = 0; r < kWaveRT; ++r)
+      copy16(wbase[r] + (wtile0[r] + q) * kTileNibbleBytes, 16 * lane, sb + r * kTileNibbleBytes);
 #pragma unroll
-    for (int it = 0; it < 4; ++it) {
-      const uint4 L = a_reg[it][0], H = a_reg[it][1];
-      const uint32_t lo[4] = {L.x, L.y, L.z, L.w};
-      const uint32_t hi[4] = {H.x, H.y, H.z, H.w};
-      uint32_t f[8];
-#pragma unroll
-      for (int d = 0; d < 4; ++d) {
-        f[2 * d] = __builtin_amdgcn_perm(hi[d], lo[d], 0x05040100u);
-        f[2 * d + 1] = __builtin_amdgcn_perm(hi[d], lo[d], 0x07060302u);
-      }
-      uint8_t* dst = &lds_a[buf][a_lds_off[it]];
-      *reinterpret_cast<uint4*>(dst) = make_uint4(f[0], f[1], f[2], f[3]);
-      *reinterpret_cast<uint4*>(dst + 16 * 16) = make_uint4(f[4], f[5], f[6], f[7]);
-    }
-  };
-
-  uint4 nib[kWaveRT];
-  uint2 scl[kWaveRT];
-  auto load_b = [&](int64_t q) {
-#pragma unroll
-    for (int r = 0; r < kWaveRT; ++r) {
-      const int64_t tile = wtile0[r] + q;
-      nib[r] = *reinterpret_cast<const uint4*>(wbase[r] + tile * kTileNibbleBytes + lane * 16);
-      scl[r] = *reinterpret_cast<const uint2*>(wbase[r] + nib_bytes + tile * kTileScaleBytes + c * 8);
-    }
+    for (int i = 0; i < 2; ++i)
+      copy4(wbase[2 * i] + nib_bytes + (wtile0[2 * i] + q) * kTileScaleBytes, s_off[i],
+            sb + kWaveRT * kTileNibbleBytes + i * 2 * kTileScaleBytes);
   };
 
   f32x4 acc[kMT][kWaveRT];
@@ -191,47 +204,57 @@ __global__ void __launch_bounds__(256) qgemm_kernel(GemmArgs a) {
 #pragma unroll
     for (int r = 0; r < kWaveRT; ++r) acc[i][r] = f32x4{0.f, 0.f, 0.f, 0.f};
 
-  load_a(0);
-  load_b(0);
-  store_a(0);
-  __syncthreads();
-
-  for (int64_t q = 0; q < kq_n; ++q) {
-    const int buf = (int)(q & 1);
-    uint4 cur_nib[kWaveRT];
-    uint2 cur_scl[kWaveRT];
+  // LUT values of one block: 16 independent LDS reads.
+  auto lut_reads = [&](const uint4 (&nib)[kWaveRT], int j, uint32_t (&lv)[kWaveRT][4]) {
 #pragma unroll
     for (int r = 0; r < kWaveRT; ++r) {
-      cur_nib[r] = nib[r];
-      cur_scl[r] = scl[r];
+      const uint32_t w = (j == 0) ? nib[r].x : (j == 1) ? nib[r].y : (j == 2) ? nib[r].z : nib[r].w;
+      lv[r][0] = lut[w & 0xFF];
+      lv[r][1] = lut[(w >> 8) & 0xFF];
+      lv[r][2] = lut[(w >> 16) & 0xFF];
+      lv[r][3] = lut[w >> 24];
     }
-    if (q + 1 < kq_n) {
-      load_a(q + 1);
-      load_b(q + 1);
+  };
+
+  copy_quad(0);
+  if (kq_n > 1) copy_quad(1);
+
+  for (int q = 0; q < kq_n; ++q) {
+    // this wave's copies of quad q are done once only quad q+1's may still be in flight
+    if (q + 1 < kq_n) wait_vmcnt<kCopiesPerQuad>();
+    else wait_vmcnt<0>();
+    lds_barrier();  // quad q is in LDS for everyone; quad q-1's stage is free
+    if (q + 2 < kq_n) copy_quad(q + 2);
+
+    const uint8_t* st = &ring[q % kStages][0];
+    const uint8_t* sb = st + kABytes + (tid >> 6) * kWaveBBytes;
+    uint4 nib[kWaveRT];
+    uint2 scl[kWaveRT];
+#pragma unroll
+    for (int r = 0; r < kWaveRT; ++r) {
+      nib[r] = *reinterpret_cast<const uint4*>(sb + r * kTileNibbleBytes + lane * 16);
+      scl[r] = *reinterpret_cast<const uint2*>(sb + kWaveRT * kTileNibbleBytes + r * kTileScaleBytes + c * 8);
     }
+    uint32_t lv[kWaveRT][4];
+    lut_reads(nib, 0, lv);
 #pragma unroll
     for (int j = 0; j < kTileBlocks; ++j) {
       u32x4 bf[kWaveRT];
 #pragma unroll
       for (int r = 0; r < kWaveRT; ++r) {
-        const uint32_t w = (j == 0) ? cur_nib[r].x : (j == 1) ? cur_nib[r].y : (j == 2) ? cur_nib[r].z : cur_nib[r].w;
-        const uint32_t sw = (j < 2) ? cur_scl[r].x : cur_scl[r].y;
+        const uint32_t sw = (j < 2) ? scl[r].x : scl[r].y;
         const uint32_t dd = __builtin_amdgcn_perm(sw, sw, (j & 1) ? 0x03020302u : 0x01000100u);
-        bf[r][0] = pk_mul_f16(lut[w & 0xFF], dd);
-        bf[r][1] = pk_mul_f16(lut[(w >> 8) & 0xFF], dd);
-        bf[r][2] = pk_mul_f16(lut[(w >> 16) & 0xFF], dd);
-        bf[r][3] = pk_mul_f16(lut[w >> 24], dd);
+#pragma unroll
+        for (int i = 0; i < 4; ++i) bf[r][i] = pk_mul_f16(lv[r][i], dd);
       }
+      if (j + 1 < kTileBlocks) lut_reads(nib, j + 1, lv);  // next block's reads under these MFMAs
 #pragma unroll
       for (int mt = 0; mt < kMT; ++mt) {
-        const u32x4 af =
-            *reinterpret_cast<const u32x4*>(&lds_a[buf][((j * kMT + mt) * 64 + lane) * 16]);
+        const u32x4 af = *reinterpret_cast<const u32x4*>(st + (j * kMT + mt) * 1024 + lane * 16);
 #pragma unroll
         for (int r = 0; r < kWaveRT; ++r) acc[mt][r] = mfma_f16(af, bf[r], acc[mt][r]);
       }
     }
-    if (q + 1 < kq_n) store_a(buf ^ 1);
-    __syncthreads();
   }
 
   // ---- epilogue: lane holds D[4g + i][c] of each (mt, r) fragment -------------------

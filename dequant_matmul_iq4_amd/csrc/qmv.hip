@@ -40,7 +40,8 @@
 // Memory.  Weights come in the packed tile layout: per 16-row x 4-block tile each lane
 // issues one 128-bit load of indices (coalesced 1 KiB per wave) and one 64-bit load
 // of its row's four scales.  The index-to-level decode is a byte-indexed table in LDS
-// (one byte = two 4-bit indices -> two bf16 levels), built from register immediates.
+// (one byte = two 4-bit indices of consecutive elements -> two bf16 levels), built from
+// register immediates.
 #include "common.hpp"
 #include "launch.hpp"
 #include "qmv.hpp"
@@ -80,7 +81,8 @@ __device__ __forceinline__ const float* column_ptr(const QmvArgs& a, int mode, i
 }
 
 // A-fragment store of the slice in LDS: [block][k-group g][row 4s+t], padding rows
-// (s = 3) omitted, 16 bytes each.
+// (s = 3) omitted, 16 bytes each: part s of elements 8g .. 8g+7 of the block (element
+// 8g+2i in the low, 8g+2i+1 in the high half of word i, the weights' index order).
 constexpr int kFragRows = 12;
 constexpr int kFragBytes = 4 * kFragRows * 16;  // 768 B per block
 
@@ -134,9 +136,9 @@ __global__ void __launch_bounds__(512) qmv_kernel(QmvArgs a) {
       const int task = lane + 64 * i;
       if (task < ntask) {
         const int gg = task & 3, bl = (task >> 2) % wblk, t = (task >> 2) / wblk;
-        const float* p = column_ptr(a, MODE, seg0, t0 + t) + ((int64_t)(kqa + wq0) * 4 + bl) * kQK + 4 * gg;
+        const float* p = column_ptr(a, MODE, seg0, t0 + t) + ((int64_t)(kqa + wq0) * 4 + bl) * kQK + 8 * gg;
         xr[i][0] = *reinterpret_cast<const float4*>(p);
-        xr[i][1] = *reinterpret_cast<const float4*>(p + 16);
+        xr[i][1] = *reinterpret_cast<const float4*>(p + 4);
       }
     }
   };
@@ -152,10 +154,10 @@ __global__ void __launch_bounds__(512) qmv_kernel(QmvArgs a) {
 #pragma unroll
         for (int sp = 0; sp < 3; ++sp) {
           uint4 f;
-          f.x = split_part(xa.x, sp) | (split_part(xb.x, sp) << 16);
-          f.y = split_part(xa.y, sp) | (split_part(xb.y, sp) << 16);
-          f.z = split_part(xa.z, sp) | (split_part(xb.z, sp) << 16);
-          f.w = split_part(xa.w, sp) | (split_part(xb.w, sp) << 16);
+          f.x = split_part(xa.x, sp) | (split_part(xa.y, sp) << 16);
+          f.y = split_part(xa.z, sp) | (split_part(xa.w, sp) << 16);
+          f.z = split_part(xb.x, sp) | (split_part(xb.y, sp) << 16);
+          f.w = split_part(xb.z, sp) | (split_part(xb.w, sp) << 16);
           *reinterpret_cast<uint4*>(dst + sp * 4 * 16) = f;
         }
       }

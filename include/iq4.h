@@ -104,7 +104,8 @@ int64_t iq4_packed_bytes(int64_t n, int64_t k);
  * blocks 4kq..4kq+3, tiles ordered rt-major):
  *   nibble plane: tile at (rt*(k/128) + kq) * 1024 bytes; 64 entries of 16 bytes;
  *     entry l = 16g + j (g = 0..3, j = 0..15) holds, for blocks b = 0..3 of the tile,
- *     index bytes 4g..4g+3 of block (row 16rt+j, block 4kq+b) at bytes 4b..4b+3.
+ *     the indices of elements 8g..8g+7 of block (row 16rt+j, block 4kq+b) at bytes
+ *     4b..4b+3: element 8g+2i in the low and 8g+2i+1 in the high nibble of byte 4b+i.
  *   scale plane (after n*k/32*16 bytes of nibbles): tile at (rt*(k/128)+kq)*128 bytes;
  *     row j's four scales (binary16) at bytes 8j..8j+7.
  * Errors: IQ4_E_UNSUPPORTED (n % 16, k % 128), IQ4_E_ALIGN.

@@ -168,3 +168,69 @@ def logits_zipf_gumbel(seed: int, tag: int, n_tok: int, n_expert: int, s: float 
     u = uniform(seed, tag, n_tok * n_expert, open_interval=True).reshape(n_tok, n_expert)
     g = -np.log(-np.log(u))
     return (lp[None, :] + g).astype(np.float32)
+
+
+# ----------------------------------------------------------------------------------
+# The same streams produced with torch (CPU or GPU), for large inputs.  The 64-bit
+# integer stream is bit-identical to the numpy version; the float64 Box-Muller step may
+# differ from it in the last bit (device libm), which leaves the float32/float16
+# results equal except, rarely, at a rounding boundary.  Parity tests use the numpy
+# version; the benchmark uses this one to build its 600M-weight expert bank quickly.
+
+def _as_i64(v: int) -> int:
+    v &= _MASK64
+    return v - (1 << 64) if v >= (1 << 63) else v
+
+
+def _lsr(z, s: int):
+    import torch
+    return torch.bitwise_and(torch.bitwise_right_shift(z, s), (1 << (64 - s)) - 1)
+
+
+def _mix64_t(z):
+    z = torch_bitxor(z, _lsr(z, 30)) * _as_i64(0xBF58476D1CE4E5B9)
+    z = torch_bitxor(z, _lsr(z, 27)) * _as_i64(0x94D049BB133111EB)
+    return torch_bitxor(z, _lsr(z, 31))
+
+
+def torch_bitxor(a, b):
+    import torch
+    return torch.bitwise_xor(a, b)
+
+
+def raw_u64_torch(seed: int, tag: int, start: int, count: int, device="cpu"):
+    """Same values as ``raw_u64`` as a torch int64 tensor (two's complement bits)."""
+    import torch
+    s0 = _as_i64(stream_key(seed, tag))
+    i = torch.arange(start + 1, start + count + 1, dtype=torch.int64, device=device)
+    return _mix64_t(i * _as_i64(int(GAMMA)) + s0)
+
+
+def normal_torch(seed: int, tag: int, count: int, device="cpu"):
+    """``count`` standard normals (float64 torch tensor), Box-Muller as in ``normal``."""
+    import torch
+    npair = (count + 1) // 2
+    out = torch.empty(2 * npair, dtype=torch.float64, device=device)
+    chunk = 1 << 24
+    for a in range(0, npair, chunk):
+        b = min(npair, a + chunk)
+        x = raw_u64_torch(seed, tag, 2 * a, 2 * (b - a), device)
+        u = _lsr(x, 11).to(torch.float64) * (2.0 ** -53)
+        u1, u2 = u[0::2], u[1::2]
+        r = torch.sqrt(-2.0 * torch.log1p(-u1))
+        th = (2.0 * torch.pi) * u2
+        out[2 * a:2 * b:2] = r * torch.cos(th)
+        out[2 * a + 1:2 * b:2] = r * torch.sin(th)
+    return out[:count]
+
+
+def weights_f32_torch(seed: int, tag: int, rows: int, cols: int, device="cpu"):
+    return (0.02 * normal_torch(seed, tag, rows * cols, device)).to(__import__("torch").float32).reshape(rows, cols)
+
+
+def acts_f32_torch(seed: int, tag: int, rows: int, cols: int, device="cpu"):
+    return normal_torch(seed, tag, rows * cols, device).to(__import__("torch").float32).reshape(rows, cols)
+
+
+def acts_f16_torch(seed: int, tag: int, rows: int, cols: int, device="cpu"):
+    return normal_torch(seed, tag, rows * cols, device).to(__import__("torch").float16).reshape(rows, cols)

@@ -47,3 +47,16 @@ def test_zipf_gumbel_logits_skew():
     assert counts.sum() == 3256 * 8
     assert counts[0] > counts[10] > counts[100]
     assert counts.max() <= 3256
+
+
+def test_torch_stream_matches_numpy():
+    import torch
+    a = synth.raw_u64(103, 7, 100, 5000)
+    b = synth.raw_u64_torch(103, 7, 100, 5000).numpy().view(np.uint64)
+    assert np.array_equal(a, b)
+    z = synth.normal(103, 7, 10001)
+    zt = synth.normal_torch(103, 7, 10001).numpy()
+    assert np.allclose(z, zt, rtol=1e-13, atol=1e-13)
+    w = synth.weights_f32(104, 3, 64, 128)
+    wt = synth.weights_f32_torch(104, 3, 64, 128).numpy()
+    assert np.mean(w == wt) > 0.9999
