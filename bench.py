@@ -35,6 +35,32 @@ F16_MFMA_PEAK_TFS = 2500.0  # MI355X dense f16 matrix throughput, published
 
 HIDDEN, INTER, N_EXPERT, TOP_K = 2048, 768, 128, 8
 
+# HBM bytes per launch from rocprofv3 FETCH_SIZE and WRITE_SIZE passes (each scaled by what
+# the counter reads for a 256 MiB device copy), kept with a digest of the kernel's sources
+# at the time: a kernel changed since then reports traffic null.  Commands and raw
+# figures: profiles/<name>.txt.
+MEASURED_TRAFFIC = {
+    "qmv_dense_4096x4096_T1-4": (9971758, "dbef0314edda513c", ("qmv.hip", "qmv.hpp", "common.hpp")),
+    "qgemm_gateup_moe_prefill_3256tok": (434470556, "05fc183f95bdbd3a", ("gemm.hip", "gemm.hpp", "common.hpp")),
+    "qgemm_down_moe_prefill_3256tok": (385754943, "05fc183f95bdbd3a", ("gemm.hip", "gemm.hpp", "common.hpp")),
+    "qgemm_dense_13056x4096x14336_chunk512": (94976366, "05fc183f95bdbd3a", ("gemm.hip", "gemm.hpp", "common.hpp")),
+}
+
+
+def measured_traffic(name):
+    import hashlib
+    nbytes, digest, files = MEASURED_TRAFFIC[name]
+    h = hashlib.sha256()
+    for f in files:
+        with open(os.path.join(ROOT, "dequant_matmul_iq4_amd", "csrc", f), "rb") as fh:
+            h.update(fh.read())
+    return nbytes if h.hexdigest()[:16] == digest else None
+
+
+def sum_traffic(*names):
+    parts = [measured_traffic(nm) for nm in names]
+    return None if any(p is None for p in parts) else sum(parts)
+
 
 def log(msg):
     print(f"[bench] {msg}", file=sys.stderr, flush=True)
@@ -115,6 +141,9 @@ def main():
     ap.add_argument("--warmup", type=int, default=3)
     ap.add_argument("--copies", type=int, default=64)
     ap.add_argument("--no-cpu-baseline", action="store_true")
+    ap.add_argument("--copy-calibration", type=int, default=0, metavar="MIB",
+                    help="only copy a float32 buffer of MIB MiB three times (the known-size "
+                         "kernel that scales the FETCH_SIZE / WRITE_SIZE counters), then exit")
     args = ap.parse_args()
     if args.gpus != 1 or int(os.environ.get("WORLD_SIZE", "1")) > 1:
         print("bench.py measures one GPU only: this library has no multi-GPU path "
@@ -128,6 +157,15 @@ def main():
 
     torch.cuda.set_device(0)
     stream = torch.cuda.current_stream()
+    if args.copy_calibration:
+        nel = args.copy_calibration * (1 << 20) // 4
+        src = torch.ones(nel, dtype=torch.float32, device="cuda")
+        dst = torch.empty_like(src)
+        for _ in range(3):
+            dst.copy_(src)
+        torch.cuda.synchronize()
+        log(f"copied {args.copy_calibration} MiB three times")
+        return
     Ev = lambda: torch.cuda.Event(enable_timing=True)  # noqa: E731
 
     # ---- inputs ------------------------------------------------------------------------
@@ -306,13 +344,18 @@ def main():
         },
         "roofline": roof("hbm", mm_achieved, HBM_PEAK_GBS, "GB/s",
                          "qmv_kernel<dense>: verify-window matvec, bytes = W + X + Y per call, "
-                         "mean over T=1..4"),
+                         "mean over T=1..4; traffic = HBM bytes per launch",
+                         traffic=measured_traffic("qmv_dense_4096x4096_T1-4")),
         "rooflines": {
             "moe_prefill_layer": roof("mfma", prefill_flop / (comp["moe_prefill"] * 1e-3) / 1e12,
                                       F16_MFMA_PEAK_TFS, "TFLOP/s",
-                                      "gather + qgemm<gateup> + qgemm<down> + combine, f16 MFMA"),
+                                      "gather + qgemm<gateup> + qgemm<down> + combine, f16 MFMA; "
+                                      "traffic = HBM bytes of the two GEMM launches",
+                                      traffic=sum_traffic("qgemm_gateup_moe_prefill_3256tok",
+                                                          "qgemm_down_moe_prefill_3256tok")),
             "dense_projection": roof("mfma", dense_flop / (comp["dense"] * 1e-3) / 1e12, F16_MFMA_PEAK_TFS,
-                                     "TFLOP/s", "qgemm<dense> x 26 chunks"),
+                                     "TFLOP/s", "qgemm<dense> x 26 chunks; traffic = HBM bytes of the 26 launches",
+                                     traffic=sum_traffic(*["qgemm_dense_13056x4096x14336_chunk512"] * 26)),
             "moe_decode_step": roof("hbm", unique_bytes / (comp["moe_decode"] * 1e-3) / 1e9, HBM_PEAK_GBS,
                                     "GB/s", f"gather + qmv<gateup> + qmv<down> + combine, {n_unique} "
                                     "unique experts' weights"),
