@@ -8,7 +8,7 @@ One step = one pass over every step of the hot path, on resident synthetic input
      Infinity Cache, so weights stream from HBM);
   2. block decode of that matrix to binary16 (iq4_dequant_blocks);
   3. MoE decode step: 4 fp32 tokens, top-8 of 128 experts (hidden 2048, inter 768),
-     alternating between two expert banks (2 x 340 MB, cold);
+     rotating over eight expert banks (8 x 340 MB, cold);
   4. MoE prefill layer: 3,256 f16 tokens, Zipf(1.1)-skewed top-8 routing, same bank;
   5. long-prompt projection: 13,056 f16 tokens x W 14,336 x 4,096, 512-token chunks.
 
@@ -34,6 +34,7 @@ HBM_PEAK_GBS = 8000.0       # MI355X HBM3E, published
 F16_MFMA_PEAK_TFS = 2500.0  # MI355X dense f16 matrix throughput, published
 
 HIDDEN, INTER, N_EXPERT, TOP_K = 2048, 768, 128, 8
+N_BANKS = 8                 # expert banks the decode step rotates over
 
 # HBM bytes per launch from rocprofv3 FETCH_SIZE and WRITE_SIZE passes (each scaled by what
 # the counter reads for a 256 MiB device copy), kept with a digest of the kernel's sources
@@ -183,9 +184,11 @@ def main():
     vws = torch.zeros(max(vwsb, 256), dtype=torch.uint8, device="cuda")
     deq_out = torch.empty(n * k, dtype=torch.float16, device="cuda")
 
-    log("expert banks (2 x 128 experts)")
-    bank_a = build_bank(torch, iq4, synth, synth.SEED_EXPERTS)
-    bank_b = build_bank(torch, iq4, synth, synth.SEED_EXPERTS + 1000)
+    # The decode step reads ~80 MB of one bank; rotating over 8 banks (2.7 GB) puts 7
+    # other steps' reads between two uses of a bank, well past the 256 MB Infinity Cache.
+    log(f"expert banks ({N_BANKS} x 128 experts)")
+    banks = [build_bank(torch, iq4, synth, synth.SEED_EXPERTS + 1000 * i) for i in range(N_BANKS)]
+    bank_a = banks[0]
 
     log("MoE decode and prefill inputs")
     dx = synth.acts_f32_torch(synth.SEED_DECODE, synth.TAG_X, 4, HIDDEN, device="cuda")
@@ -248,7 +251,7 @@ def main():
     steps_per_cycle = R // 4
     mm_graphs = [capture(lambda s, i=i: [mmvq(4 * i + T - 1, T, s) for T in (1, 2, 3, 4)])
                  for i in range(steps_per_cycle)]
-    dec_graphs = [capture(lambda s: moe_decode(bank_a, s)), capture(lambda s: moe_decode(bank_b, s))]
+    dec_graphs = [capture(lambda s, b=b: moe_decode(b, s)) for b in banks]
 
     def step(i, ev=None):
         if ev:
@@ -259,7 +262,7 @@ def main():
         dequant(stream)
         if ev:
             ev[2].record(stream)
-        dec_graphs[i % 2].replay()
+        dec_graphs[i % N_BANKS].replay()
         if ev:
             ev[3].record(stream)
         moe_prefill(stream)

@@ -175,7 +175,7 @@ int launch_moe(const MoeCall& m, hipStream_t s) {
     g.pairs = pairs;
     g.top_k = m.top_k;
     g.stream = s;
-    if (int e = launch_qmv_grouped(kQmvGateUp, g, m.inter, m.hidden, m.n_expert)) return e;
+    if (int e = launch_qmv_grouped(kQmvGateUp, g, m.inter, m.hidden, m.n_expert, P)) return e;
     QmvArgs d{};
     d.W0 = static_cast<const uint8_t*>(m.w_down);
     d.w_expert_stride = down_stride;
@@ -188,7 +188,7 @@ int launch_moe(const MoeCall& m, hipStream_t s) {
     d.gate_w = m.w;
     d.top_k = m.top_k;
     d.stream = s;
-    if (int e = launch_qmv_grouped(kQmvDown, d, m.hidden, m.inter, m.n_expert)) return e;
+    if (int e = launch_qmv_grouped(kQmvDown, d, m.hidden, m.inter, m.n_expert, P)) return e;
   }
 
   if (!atomic) {

@@ -53,9 +53,9 @@ constexpr int kMaxWaveQuads = 4;       // quads per wave: all of a wave's weight
 constexpr int kSliceQuads = kWaves * kMaxWaveQuads;  // 32 quads = 128 blocks = K 4096
 constexpr int kSliceBlocks = 4 * kSliceQuads;
 constexpr int kCols = 4;               // columns per pass (rows 4s + t of the A operand)
-constexpr int kMaxTasks = 4;           // staging tasks per thread (see qmv_plan)
-constexpr int kDenseRG = 1;            // row tiles per workgroup (dense, down)
+constexpr int kDenseRG = 1;            // row tiles per workgroup (dense)
 constexpr int kGateUpRG = 1;           // row tiles per matrix (gate + up)
+constexpr int kDownRG = 2;             // row tiles per workgroup (down)
 
 __device__ __forceinline__ uint32_t bf16_of_level(int c) {
   return __float_as_uint((float)c) >> 16;  // exact: |c| <= 127
@@ -72,11 +72,18 @@ __device__ __forceinline__ uint32_t split_part(float v, int s) {
   return __float_as_uint(r2) >> 16;
 }
 
-// Column t of the call: where its activations live.
+// Column t of the call: where its activations live.  The pair list is read through the
+// constant address space (it is not written during the call), so a uniform lookup is a
+// scalar load, counted apart from the weight loads in flight.
 __device__ __forceinline__ const float* column_ptr(const QmvArgs& a, int mode, int64_t seg0,
                                                    int64_t t) {
   if (mode == kQmvDense) return a.x + t * a.ldx;
-  if (mode == kQmvGateUp) return a.x + (int64_t)(a.pairs[seg0 + t] / a.top_k) * a.ldx;
+  if (mode == kQmvGateUp) {
+    const __attribute__((address_space(4))) int32_t* pairs =
+        (const __attribute__((address_space(4))) int32_t*)a.pairs;
+    const int idx = __builtin_amdgcn_readfirstlane((int)(seg0 + t));  // uniform by construction
+    return a.x + (int64_t)(pairs[idx] / a.top_k) * a.ldx;
+  }
   return a.x + (seg0 + t) * a.ldx;  // kQmvDown: h rows in pair-sorted order
 }
 
@@ -86,12 +93,13 @@ __device__ __forceinline__ const float* column_ptr(const QmvArgs& a, int mode, i
 constexpr int kFragRows = 12;
 constexpr int kFragBytes = 4 * kFragRows * 16;  // 768 B per block
 
-// One workgroup per RG row tiles (and per expert in the grouped modes) and K slice.
-template <int MODE, int RG>
+// One workgroup per RG row tiles (and per routed expert in the grouped modes) and K
+// slice; each wave owns WQ quads of the slice (registers and LDS sized to K).
+template <int MODE, int RG, int WQ>
 __global__ void __launch_bounds__(512) qmv_kernel(QmvArgs a) {
   constexpr int NMAT = (MODE == kQmvGateUp) ? 2 : 1;
   constexpr int ROWS = RG * kTileRows;
-  constexpr int XBYTES = kSliceBlocks * kFragBytes;
+  constexpr int XBYTES = kWaves * WQ * 4 * kFragBytes;
   static_assert(kWaves * NMAT * RG * 64 * 16 <= XBYTES, "reduction scratch does not fit");
   __shared__ uint32_t lut[256];
   __shared__ __attribute__((aligned(16))) uint8_t xs[XBYTES + 256];  // + room for padding-row reads
@@ -110,11 +118,30 @@ __global__ void __launch_bounds__(512) qmv_kernel(QmvArgs a) {
     slice = (int)(blockIdx.x % a.S);
     ncols = a.T;
   } else {
-    const int64_t e = blockIdx.x / a.rg_n;
+    // The grid covers at most min(pairs, experts) experts: workgroup slot i takes the
+    // i-th expert (ascending id) that has pairs, found by a ballot over the offsets in
+    // every wave (no LDS, no barrier); slots past the routed experts exit.
+    const int64_t slot = blockIdx.x / a.rg_n;
     rg = blockIdx.x % a.rg_n;
-    seg0 = a.offsets[e];
-    ncols = a.offsets[e + 1] - seg0;
-    if (ncols == 0) return;
+    int64_t e = -1, before = 0;
+    for (int e0 = 0; e0 < a.n_expert && e < 0; e0 += 64) {
+      const int ee = e0 + lane;
+      const int lo = (ee < a.n_expert) ? a.offsets[ee] : 0;
+      const int hi = (ee < a.n_expert) ? a.offsets[ee + 1] : 0;
+      const bool act = hi > lo;
+      const uint64_t m = __ballot(act);
+      const int64_t cnt = __popcll(m);
+      if (slot < before + cnt) {
+        const uint64_t below = (lane == 0) ? 0ull : (~0ull >> (64 - lane));
+        const uint64_t hit = __ballot(act && before + __popcll(m & below) == slot);
+        const int L = __ffsll((unsigned long long)hit) - 1;
+        e = e0 + L;
+        seg0 = __shfl(lo, L);
+        ncols = __shfl(hi, L) - seg0;
+      }
+      before += cnt;
+    }
+    if (e < 0) return;
     W[0] += e * a.w_expert_stride;
     W[1] += e * a.w_expert_stride;
   }
@@ -127,16 +154,21 @@ __global__ void __launch_bounds__(512) qmv_kernel(QmvArgs a) {
   // This wave's activations: blocks [4 * wq0, 4 * wq1) of the slice, staged by the wave
   // itself into its own LDS region (no workgroup barrier before the products).
   const int wblk = 4 * (wq1 - wq0);  // blocks of this wave (0 for an idle wave)
-  uint8_t* xw = xs + wave * (4 * kMaxWaveQuads) * kFragBytes;
-  float4 xr[kMaxTasks][2];
+  uint8_t* xw = xs + wave * (4 * WQ) * kFragBytes;
+  float4 xr[WQ][2];  // staging tasks: at most T * 16 WQ blocks-groups = 64 WQ, i.e. WQ per lane
   auto load_x = [&](int64_t t0, int T) {  // tasks (column t, block, k-group gg), 64 lanes
     const int ntask = T * wblk * 4;
+    // the pass's column rows first, one uniform load per column (not one per task)
+    const float* col[kCols];
 #pragma unroll
-    for (int i = 0; i < kMaxTasks; ++i) {
+    for (int t = 0; t < kCols; ++t) col[t] = column_ptr(a, MODE, seg0, t0 + min(t, T - 1));
+#pragma unroll
+    for (int i = 0; i < WQ; ++i) {
       const int task = lane + 64 * i;
       if (task < ntask) {
         const int gg = task & 3, bl = (task >> 2) % wblk, t = (task >> 2) / wblk;
-        const float* p = column_ptr(a, MODE, seg0, t0 + t) + ((int64_t)(kqa + wq0) * 4 + bl) * kQK + 8 * gg;
+        const float* cp = (t == 0) ? col[0] : (t == 1) ? col[1] : (t == 2) ? col[2] : col[3];
+        const float* p = cp + ((int64_t)(kqa + wq0) * 4 + bl) * kQK + 8 * gg;
         xr[i][0] = *reinterpret_cast<const float4*>(p);
         xr[i][1] = *reinterpret_cast<const float4*>(p + 4);
       }
@@ -145,7 +177,7 @@ __global__ void __launch_bounds__(512) qmv_kernel(QmvArgs a) {
   auto store_x = [&](int T) {  // split and store in fragment order
     const int ntask = T * wblk * 4;
 #pragma unroll
-    for (int i = 0; i < kMaxTasks; ++i) {
+    for (int i = 0; i < WQ; ++i) {
       const int task = lane + 64 * i;
       if (task < ntask) {
         const int gg = task & 3, bl = (task >> 2) % wblk, t = (task >> 2) / wblk;
@@ -169,10 +201,12 @@ __global__ void __launch_bounds__(512) qmv_kernel(QmvArgs a) {
     __builtin_amdgcn_fence(__ATOMIC_ACQUIRE, "wavefront");
   };
 
-  // The first pass's activations go out first (small), then every weight load.
-  load_x(0, (int)min((int64_t)kCols, ncols));
-  uint4 nib[kMaxWaveQuads][NMAT][RG];
-  uint2 scl[kMaxWaveQuads][NMAT][RG];
+  // Dense: the first pass's activations go out first (small, no dependent load), then
+  // every weight load.  Grouped: the weights go out as soon as the expert is known,
+  // ahead of the column-row lookups the activations depend on.
+  if (MODE == kQmvDense) load_x(0, (int)min((int64_t)kCols, ncols));
+  uint4 nib[WQ][NMAT][RG];
+  uint2 scl[WQ][NMAT][RG];
 #pragma unroll
   for (int r = 0; r < RG; ++r) {
     const int64_t rt = min(rg * RG + r, a.nt - 1);  // clamped: rows past n are dropped
@@ -181,13 +215,14 @@ __global__ void __launch_bounds__(512) qmv_kernel(QmvArgs a) {
       const uint8_t* tp = W[m] + (rt * kq_n + kqa) * kTileNibbleBytes + lane * 16;
       const uint8_t* sp = W[m] + a.nibble_bytes + (rt * kq_n + kqa) * kTileScaleBytes + c * 8;
 #pragma unroll
-      for (int u = 0; u < kMaxWaveQuads; ++u) {
+      for (int u = 0; u < WQ; ++u) {
         const int q = min(wq0 + u, max(wq1 - 1, 0));  // clamped; unused when past the range
         nib[u][m][r] = *reinterpret_cast<const uint4*>(tp + (int64_t)q * kTileNibbleBytes);
         scl[u][m][r] = *reinterpret_cast<const uint2*>(sp + (int64_t)q * kTileScaleBytes);
       }
     }
   }
+  if (MODE != kQmvDense) load_x(0, (int)min((int64_t)kCols, ncols));
   for (int i = tid; i < 256; i += blockDim.x)
     lut[i] = bf16_of_level(level_of(i & 15)) | (bf16_of_level(level_of(i >> 4)) << 16);
   __syncthreads();  // the table (LDS only: no wait on the loads in flight)
@@ -207,8 +242,40 @@ __global__ void __launch_bounds__(512) qmv_kernel(QmvArgs a) {
 #pragma unroll
       for (int r = 0; r < RG; ++r) acc[m][r] = f32x4{0.f, 0.f, 0.f, 0.f};
 #pragma unroll
-    for (int u = 0; u < kMaxWaveQuads; ++u) {
+    for (int u = 0; u < WQ; ++u) {
       if (wq0 + u >= wq1) break;
+      if constexpr (MODE != kQmvDense) {
+        // grouped modes (several workgroups per CU): one block at a time, same order
+#pragma unroll
+        for (int j = 0; j < 4; ++j) {
+          const int bl = 4 * u + j;
+          const u32x4 xf = *reinterpret_cast<const u32x4*>(xw + (bl * 4 + g) * (kFragRows * 16) + c * 16);
+          u32x4 bf[NMAT][RG];
+#pragma unroll
+          for (int m = 0; m < NMAT; ++m)
+#pragma unroll
+            for (int r = 0; r < RG; ++r) {
+              const uint4 nb = nib[u][m][r];
+              const uint32_t w = (j == 0) ? nb.x : (j == 1) ? nb.y : (j == 2) ? nb.z : nb.w;
+              bf[m][r][0] = lut[w & 0xFF];
+              bf[m][r][1] = lut[(w >> 8) & 0xFF];
+              bf[m][r][2] = lut[(w >> 16) & 0xFF];
+              bf[m][r][3] = lut[w >> 24];
+            }
+#pragma unroll
+          for (int m = 0; m < NMAT; ++m)
+#pragma unroll
+            for (int r = 0; r < RG; ++r) {
+              const f32x4 pr = mfma_bf16(xf, bf[m][r], f32x4{0.f, 0.f, 0.f, 0.f});
+              const uint2 sc = scl[u][m][r];
+              const uint32_t sw = (j < 2) ? sc.x : sc.y;
+              const float d = h2f((uint16_t)(sw >> (16 * (j & 1))));
+#pragma unroll
+              for (int i = 0; i < 4; ++i) acc[m][r][i] = __builtin_fmaf(d, pr[i], acc[m][r][i]);
+            }
+        }
+        continue;
+      }
       u32x4 xf[4];
       u32x4 bf[4][NMAT][RG];
 #pragma unroll
@@ -258,64 +325,69 @@ __global__ void __launch_bounds__(512) qmv_kernel(QmvArgs a) {
       for (int r = 0; r < RG; ++r) red[((wave * NMAT + m) * RG + r) * 64 + lane] = acc[m][r];
     __syncthreads();
     const int nout = T * ROWS;
-    const int t = tid / ROWS, rr = tid % ROWS;
-    const int r = rr >> 4, row = rr & 15;
-    float v[NMAT];
-    if (tid < nout) {
+    // one round unless a narrow workgroup holds more outputs than threads (grouped
+    // modes with two row tiles and a short K); the trip count is uniform
+    for (int idx0 = 0; idx0 < nout; idx0 += (int)blockDim.x) {
+      const int idx = idx0 + tid;
+      const int t = idx / ROWS, rr = idx % ROWS;
+      const int r = rr >> 4, row = rr & 15;
+      float v[NMAT];
+      if (idx < nout) {
 #pragma unroll
-      for (int m = 0; m < NMAT; ++m) {
-        float part[3];
+        for (int m = 0; m < NMAT; ++m) {
+          float part[3];
 #pragma unroll
-        for (int p = 0; p < 3; ++p) {
-          float sum = red[((0 * NMAT + m) * RG + r) * 64 + 16 * p + row][t];
-          for (int w2 = 1; w2 < nwaves; ++w2) sum += red[((w2 * NMAT + m) * RG + r) * 64 + 16 * p + row][t];
-          part[p] = sum;
-        }
-        v[m] = (part[0] + part[1]) + part[2];
-      }
-    }
-    const int64_t col = rg * ROWS + rr;  // output row index (weight row)
-    const bool col_ok = col < a.n;
-    if (MODE == kQmvDense) {
-      if (a.S == 1) {
-        if (tid < nout && col_ok) a.y[(t0 + t) * a.ldy + col] = v[0];
-      } else {
-        // split K: partial sums to the workspace; the last of the S workgroups of this
-        // row group adds them in slice order.  The partials are written and read with
-        // agent-scope atomic stores / loads, which go to the device coherence point
-        // one access at a time, so no cache-wide writeback or invalidate is needed;
-        // s_waitcnt(0) makes every store complete before this workgroup's arrival is
-        // counted, and the last arriver issues its loads only after seeing the count.
-        float* part = a.partials + (rg * a.S + slice) * (kCols * ROWS);
-        if (tid < nout)
-          __hip_atomic_store(part + t * ROWS + rr, v[0], __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
-        __builtin_amdgcn_s_waitcnt(0);
-        __syncthreads();
-        if (tid == 0)
-          s_last = __hip_atomic_fetch_add(a.counters + rg, 1, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT) ==
-                   a.S - 1;
-        __syncthreads();
-        if (s_last) {
-          if (tid < nout && col_ok) {
-            const float* p0 = a.partials + rg * a.S * (kCols * ROWS) + t * ROWS + rr;
-            float sum = __hip_atomic_load(p0, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
-            for (int sl = 1; sl < a.S; ++sl)
-              sum += __hip_atomic_load(p0 + sl * (kCols * ROWS), __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
-            a.y[(t0 + t) * a.ldy + col] = sum;
+          for (int p = 0; p < 3; ++p) {
+            float sum = red[((0 * NMAT + m) * RG + r) * 64 + 16 * p + row][t];
+            for (int w2 = 1; w2 < nwaves; ++w2) sum += red[((w2 * NMAT + m) * RG + r) * 64 + 16 * p + row][t];
+            part[p] = sum;
           }
-          // leaves the workspace ready for the next call
-          if (tid == 0) __hip_atomic_store(a.counters + rg, 0, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
+          v[m] = (part[0] + part[1]) + part[2];
         }
       }
-    } else if (MODE == kQmvGateUp) {
-      if (tid < nout && col_ok) {
-        const float gv = v[0], uv = v[NMAT - 1];
-        a.y[(seg0 + t0 + t) * a.ldy + col] = gv / (1.0f + expf(-gv)) * uv;  // SwiGLU
-      }
-    } else {
-      if (tid < nout && col_ok) {
-        const int p = a.pairs[seg0 + t0 + t];
-        a.y[(int64_t)p * a.ldy + col] = a.gate_w[p] * v[0];
+      const int64_t col = rg * ROWS + rr;  // output row index (weight row)
+      const bool col_ok = col < a.n;
+      if (MODE == kQmvDense) {
+        if (a.S == 1) {
+          if (idx < nout && col_ok) a.y[(t0 + t) * a.ldy + col] = v[0];
+        } else {
+          // split K: partial sums to the workspace; the last of the S workgroups of this
+          // row group adds them in slice order.  The partials are written and read with
+          // agent-scope atomic stores / loads, which go to the device coherence point
+          // one access at a time, so no cache-wide writeback or invalidate is needed;
+          // s_waitcnt(0) makes every store complete before this workgroup's arrival is
+          // counted, and the last arriver issues its loads only after seeing the count.
+          float* part = a.partials + (rg * a.S + slice) * (kCols * ROWS);
+          if (idx < nout)
+            __hip_atomic_store(part + t * ROWS + rr, v[0], __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
+          __builtin_amdgcn_s_waitcnt(0);
+          __syncthreads();
+          if (tid == 0)
+            s_last = __hip_atomic_fetch_add(a.counters + rg, 1, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT) ==
+                     a.S - 1;
+          __syncthreads();
+          if (s_last) {
+            if (idx < nout && col_ok) {
+              const float* p0 = a.partials + rg * a.S * (kCols * ROWS) + t * ROWS + rr;
+              float sum = __hip_atomic_load(p0, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
+              for (int sl = 1; sl < a.S; ++sl)
+                sum += __hip_atomic_load(p0 + sl * (kCols * ROWS), __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
+              a.y[(t0 + t) * a.ldy + col] = sum;
+            }
+            // leaves the workspace ready for the next call
+            if (tid == 0) __hip_atomic_store(a.counters + rg, 0, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
+          }
+        }
+      } else if (MODE == kQmvGateUp) {
+        if (idx < nout && col_ok) {
+          const float gv = v[0], uv = v[NMAT - 1];
+          a.y[(seg0 + t0 + t) * a.ldy + col] = gv / (1.0f + expf(-gv)) * uv;  // SwiGLU
+        }
+      } else {
+        if (idx < nout && col_ok) {
+          const int p = a.pairs[seg0 + t0 + t];
+          a.y[(int64_t)p * a.ldy + col] = a.gate_w[p] * v[0];
+        }
       }
     }
     if (t0 + kCols < ncols) __syncthreads();  // LDS is reused by the next pass
@@ -344,10 +416,22 @@ int64_t qmv_workspace_bytes(int64_t n, int64_t k) {
   return a.rg_n * a.S * kCols * kDenseRG * kTileRows * (int64_t)sizeof(float) + 256 + a.rg_n * 4;
 }
 
-template <int MODE, int RG>
+template <int MODE, int RG, int XQ>
 static int launch_mode(const QmvArgs& a, int64_t grid) {
-  hipLaunchKernelGGL((qmv_kernel<MODE, RG>), dim3((unsigned)grid), dim3(64 * a.nwaves), 0, a.stream, a);
+  if (grid == 0) return 0;
+  hipLaunchKernelGGL((qmv_kernel<MODE, RG, XQ>), dim3((unsigned)grid), dim3(64 * a.nwaves), 0, a.stream, a);
   return check_launch("qmv_kernel");
+}
+
+// Instantiation by quads per wave (the plan gives 1..4).
+template <int MODE, int RG>
+static int launch_sized(const QmvArgs& a, int64_t grid) {
+  switch (a.wave_quads) {
+    case 1: return launch_mode<MODE, RG, 1>(a, grid);
+    case 2: return launch_mode<MODE, RG, 2>(a, grid);
+    case 3: return launch_mode<MODE, RG, 3>(a, grid);
+    default: return launch_mode<MODE, RG, kMaxWaveQuads>(a, grid);
+  }
 }
 
 int launch_qmv(const uint8_t* packed, int64_t n, int64_t k, const float* x, int64_t ldx, int T,
@@ -366,18 +450,20 @@ int launch_qmv(const uint8_t* packed, int64_t n, int64_t k, const float* x, int6
     a.partials = static_cast<float*>(workspace);
     a.counters = reinterpret_cast<int*>(static_cast<uint8_t*>(workspace) + ((pbytes + 255) / 256) * 256);
   }
-  return launch_mode<kQmvDense, kDenseRG>(a, a.rg_n * a.S);
+  return launch_sized<kQmvDense, kDenseRG>(a, a.rg_n * a.S);
 }
 
-int launch_qmv_grouped(int mode, QmvArgs a, int64_t n, int64_t k, int n_expert) {
+int launch_qmv_grouped(int mode, QmvArgs a, int64_t n, int64_t k, int n_expert, int64_t n_pairs) {
+  a.n_expert = n_expert;
+  const int64_t slots = (n_pairs < n_expert) ? n_pairs : n_expert;  // routed experts at most
   if (mode == kQmvGateUp) {
     qmv_plan(a, n, k, kGateUpRG);
     if (a.S != 1) return set_error(-3, "grouped matvec: K above 4096 is not supported");
-    return launch_mode<kQmvGateUp, kGateUpRG>(a, (int64_t)n_expert * a.rg_n);
+    return launch_sized<kQmvGateUp, kGateUpRG>(a, slots * a.rg_n);
   }
-  qmv_plan(a, n, k, kDenseRG);
+  qmv_plan(a, n, k, kDownRG);
   if (a.S != 1) return set_error(-3, "grouped matvec: K above 4096 is not supported");
-  return launch_mode<kQmvDown, kDenseRG>(a, (int64_t)n_expert * a.rg_n);
+  return launch_sized<kQmvDown, kDownRG>(a, slots * a.rg_n);
 }
 
 }  // namespace iq4

@@ -19,6 +19,7 @@ struct QmvArgs {
   const int32_t* pairs;     // grouped: sorted pair ids
   const float* gate_w;      // DOWN: gate weight per pair id
   int top_k;
+  int n_expert;             // grouped: experts in the bank
   float* partials;          // DENSE split K: per-slice partial sums (workspace)
   int* counters;            // DENSE split K: arrival counters per row group (workspace)
   // launch plan (qmv_plan)
@@ -28,6 +29,6 @@ struct QmvArgs {
 };
 
 int64_t qmv_workspace_bytes(int64_t n, int64_t k);
-int launch_qmv_grouped(int mode, QmvArgs a, int64_t n, int64_t k, int n_expert);
+int launch_qmv_grouped(int mode, QmvArgs a, int64_t n, int64_t k, int n_expert, int64_t n_pairs);
 
 }  // namespace iq4

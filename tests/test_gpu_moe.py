@@ -161,3 +161,66 @@ def test_prefill_deterministic(small_bank):
     a, _ = run_moe(x, ids, w, B["banks"], B["H"], B["I"], B["E"])
     b, _ = run_moe(x, ids, w, B["banks"], B["H"], B["I"], B["E"])
     assert bits_equal(a, b)
+
+
+# ---- full-size workloads: the 128-expert bank (hidden 2048, inter 768, seed 103) ----------
+
+H_FULL, I_FULL, E_FULL, K_FULL = 2048, 768, 128, 8
+
+
+@pytest.fixture(scope="module")
+def full_bank():
+    """Every expert of the bank encoded by the oracle, and the same bank packed on the
+    GPU (expert-major), as the benchmark lays it out."""
+    import workloads
+    blocks = workloads.expert_blocks(synth.SEED_EXPERTS, tuple(range(E_FULL)), H_FULL, I_FULL)
+    gate = {e: b[0] for e, b in blocks.items()}
+    up = {e: b[1] for e, b in blocks.items()}
+    down = {e: b[2] for e, b in blocks.items()}
+    banks = (pack_bank([gate[e] for e in range(E_FULL)], I_FULL, H_FULL),
+             pack_bank([up[e] for e in range(E_FULL)], I_FULL, H_FULL),
+             pack_bank([down[e] for e in range(E_FULL)], H_FULL, I_FULL))
+    return dict(gate=gate, up=up, down=down, banks=banks)
+
+
+def test_decode_step_full_size(full_bank):
+    """The decode step at its real shape: 4 fp32 tokens, top-8 of 128 experts with softmax
+    gate weights from N(0,1) logits; every output against the oracle (1e-3), and the
+    on-device router bit-exact against the oracle's."""
+    note("moe decode full size: 4 tokens, top-8 of 128, hidden 2048, inter 768")
+    logits = synth.logits_normal(synth.SEED_DECODE, synth.TAG_LOGITS, 4, E_FULL)
+    ids, w = oracle.route_topk(logits, K_FULL)
+    ids_d = torch.empty((4, K_FULL), dtype=torch.int32, device="cuda")
+    w_d = torch.empty((4, K_FULL), dtype=torch.float32, device="cuda")
+    iq4.iq4_route_topk(dev(logits), 4, E_FULL, K_FULL, ids_d, w_d)
+    assert bits_equal(host(ids_d), ids.astype(np.int32))
+    x = synth.acts_f32(synth.SEED_DECODE, synth.TAG_X, 4, H_FULL)
+    B = full_bank
+    got, _ = run_moe(x, ids, w, B["banks"], H_FULL, I_FULL, E_FULL, dtype="f32")
+    ref = oracle.moe(x, ids, w, B["gate"], B["up"], B["down"], H_FULL, I_FULL)
+    err = normwise(got, ref)
+    note(f"  unique experts {len(np.unique(ids))}, normwise {err:.2e}")
+    assert err <= 1e-3
+
+
+def test_prefill_layer_full_size_sampled(full_bank):
+    """The prefill layer at its real shape and launch configuration: 3,256 f16 tokens with
+    Zipf(1.1)-skewed top-8 routing; sampled tokens against the oracle (5e-3)."""
+    n_tok = 3256
+    note("moe prefill full size: 3256 tokens, Zipf 1.1, top-8 of 128")
+    logits = synth.logits_zipf_gumbel(synth.SEED_PREFILL, synth.TAG_GUMBEL, n_tok, E_FULL)
+    ids, w = oracle.route_topk(logits, K_FULL)
+    x = synth.acts_f16(synth.SEED_PREFILL, synth.TAG_X, n_tok, H_FULL)
+    B = full_bank
+    got, _ = run_moe(x, ids, w, B["banks"], H_FULL, I_FULL, E_FULL, dtype="f16")
+    assert np.isfinite(got).all()
+    rng = np.random.default_rng(7)
+    # first, last, and tokens routed to the least and the most popular experts
+    counts = np.bincount(ids.reshape(-1), minlength=E_FULL)
+    rare = np.argmin(counts)
+    toks = sorted({0, n_tok - 1, int(np.nonzero((ids == rare).any(1))[0][0]),
+                   *rng.choice(n_tok, 29, replace=False).tolist()})
+    ref = oracle.moe(x, ids, w, B["gate"], B["up"], B["down"], H_FULL, I_FULL, tokens=toks)
+    err = normwise(got[toks], ref)
+    note(f"  {len(toks)} sampled tokens, normwise {err:.2e}")
+    assert err <= 5e-3

@@ -37,3 +37,21 @@ def cfg2(T: int = 4):
     """Verify-window matvec: W 4096 x 4096 (seed 102), T fp32 columns."""
     w, b = dense_weights(synth.SEED_VERIFY, 4096, 4096)
     return b, 4096, 4096, acts32(synth.SEED_VERIFY, 8, 4096)[:T]
+
+
+def _expert_matrix(seed: int, e: int, which: str, n: int, k: int) -> np.ndarray:
+    w = synth.weights_f32(seed, synth.tag_expert(e, which), n, k)
+    return oracle.encode_blocks(w.reshape(-1, 32))
+
+
+@functools.lru_cache(maxsize=None)
+def expert_blocks(seed: int, experts: tuple, hidden: int, inter: int):
+    """Oracle-encoded blocks of the listed experts of a bank: {e: (gate, up, down)},
+    gate/up inter x hidden, down hidden x inter.  Encoded in a thread pool (numpy
+    releases the GIL in the heavy loops)."""
+    from concurrent.futures import ThreadPoolExecutor
+    jobs = [(e, which, inter if which != "down" else hidden, hidden if which != "down" else inter)
+            for e in experts for which in ("gate", "up", "down")]
+    with ThreadPoolExecutor(max_workers=16) as ex:
+        mats = list(ex.map(lambda j: _expert_matrix(seed, *j), jobs))
+    return {e: tuple(mats[3 * i:3 * i + 3]) for i, e in enumerate(experts)}
