@@ -39,14 +39,22 @@ namespace iq4 {
 
 constexpr int kBM = 128;                 // rows of A per workgroup
 constexpr int kWaveRT = 4;               // packed row tiles (16 rows) per wave
-constexpr int kWaves = 4;
-constexpr int kBN = kWaves * kWaveRT * kTileRows;  // 256 weight rows per workgroup
 constexpr int kMT = kBM / 16;            // 8 fragment rows of A
-constexpr int kStages = 3;               // quads in the ring
+constexpr int kStages = 2;               // quads in the ring (filled kStages - 1 ahead)
 constexpr int kABytes = kTileBlocks * kMT * 1024;                        // 32 KiB
 constexpr int kWaveBBytes = kWaveRT * (kTileNibbleBytes + kTileScaleBytes);  // 4.5 KiB
-constexpr int kStageBytes = kABytes + kWaves * kWaveBBytes;              // 50 KiB
-constexpr int kCopiesPerQuad = kMT + kWaveRT + 2;  // per wave: A fragments, index tiles, 2 scale copies
+
+// Shape of a workgroup of NW waves: NW x 64 weight rows, one A quad shared by all.
+template <int NW>
+struct Shape {
+  static constexpr int kBN = NW * kWaveRT * kTileRows;                 // weight rows per workgroup
+  static constexpr int kStageBytes = kABytes + NW * kWaveBBytes;       // one quad of operands
+  static constexpr int kAPerWave = kTileBlocks * kMT / NW;             // A fragments each wave copies
+  static constexpr int kCopiesPerQuad = kAPerWave + kWaveRT + 2;       // + index tiles + 2 scale copies
+  // replicas of the level table (fewer bank conflicts), as many as the LDS left allows
+  static constexpr int kLutCopies = (NW == 4) ? 32 : 16;
+  static_assert(kStages * kStageBytes + 256 * 4 * kLutCopies + 2048 <= 160 * 1024, "LDS budget");
+};
 
 __device__ __forceinline__ uint32_t f16_of_level(int c) {
   return (uint32_t)__half_as_ushort(__int2half_rn(c));  // exact: |c| <= 127
@@ -96,16 +104,26 @@ __device__ __forceinline__ int64_t xcd_swizzle(int64_t b, int64_t G) {
   return (b % 8) * (G / 8) + b / 8;
 }
 
-template <int MODE>
-__global__ void __launch_bounds__(256) qgemm_kernel(GemmArgs a) {
+template <int MODE, int NW>
+__global__ void __launch_bounds__(NW * 64) qgemm_kernel(GemmArgs a) {
+  using S = Shape<NW>;
+  constexpr int kBN = S::kBN, kStageBytes = S::kStageBytes, kLutCopies = S::kLutCopies;
+  constexpr int kAPerWave = S::kAPerWave, kCopiesPerQuad = S::kCopiesPerQuad;
   __shared__ __attribute__((aligned(1024))) uint8_t ring[kStages][kStageBytes];
-  __shared__ uint32_t lut[256];
+  __shared__ uint32_t lut[256 * kLutCopies];  // entry e of copy c at e * kLutCopies + c
+  __shared__ int32_t tile_pair[kBM];          // DOWN: pair id and gate weight of each row
+  __shared__ float tile_gw[kBM];
 
   const int tid = threadIdx.x;
   const int lane = tid & 63;
   const int wave = __builtin_amdgcn_readfirstlane(tid >> 6);
   const int g = lane >> 4, c = lane & 15;
-  lut[tid] = f16_of_level(level_of(tid & 15)) | (f16_of_level(level_of(tid >> 4)) << 16);
+  if (tid < 256) {
+    const uint32_t v = f16_of_level(level_of(tid & 15)) | (f16_of_level(level_of(tid >> 4)) << 16);
+#pragma unroll
+    for (int cc = 0; cc < kLutCopies; ++cc) lut[tid * kLutCopies + cc] = v;
+  }
+  const uint32_t* lutc = lut + (lane % kLutCopies);  // this lane's copy
 
   // ---- which tile ------------------------------------------------------------------
   int64_t m0, rows;          // first A row (in the launch's row space) and valid rows
@@ -141,18 +159,22 @@ __global__ void __launch_bounds__(256) qgemm_kernel(GemmArgs a) {
   const int64_t nib_bytes = a.N * (a.K / kQK) * kNibbleBytes;
   const uint32_t ring0 = lds_addr(&ring[0][0]);
 
-  // ---- activation rows of this lane: row r = c of each of the 8 fragment rows ------
+  // ---- activation rows this lane copies ---------------------------------------------
+  // The quad's 32 fragments f = 8 j + mt (block j, fragment row mt) are split evenly over
+  // the waves: wave w copies f = w * kAPerWave .. +kAPerWave-1 (one block), lane l = 16g + r
+  // bringing row r of the fragment row, elements 8g .. 8g+7.
   // (rows past the tile's valid rows repeat its last row: read in bounds, never stored)
-  uint32_t a_off[kMT];  // byte offsets from A (the launcher checks they fit in 32 bits)
+  const int f0 = wave * kAPerWave, ablk = f0 / kMT;
+  uint32_t a_off[kAPerWave];  // byte offsets from A (the launcher checks they fit in 32 bits)
 #pragma unroll
-  for (int mt = 0; mt < kMT; ++mt) {
+  for (int i = 0; i < kAPerWave; ++i) {
+    const int mt = (f0 + i) % kMT;
     const int64_t r = min((int64_t)(16 * mt + c), rows - 1);
     int64_t src_row;
     if (MODE == kGemmDense) src_row = m0 + r;
     else if (MODE == kGemmGateUp) src_row = a.pairs[seg0 + m0 + r] / a.top_k;  // token of the pair
     else src_row = seg0 + m0 + r;                                             // h in sorted order
-    // this wave copies block `wave` of each quad
-    a_off[mt] = (uint32_t)(2 * (src_row * a.lda + 32 * wave + 8 * g));
+    a_off[i] = (uint32_t)(2 * (src_row * a.lda + 32 * ablk + 8 * g));
   }
 
   // ---- weight row tiles of this wave -------------------------------------------------
@@ -183,19 +205,25 @@ __global__ void __launch_bounds__(256) qgemm_kernel(GemmArgs a) {
     s_off[i] = (uint32_t)(4 * (lane & 31) + (lane >> 5) * (wtile0[2 * i + 1] - wtile0[2 * i]) * kTileScaleBytes);
 
   // copy quad q into its stage: A block `wave` (8 fragments), then this wave's tiles
-  auto copy_quad = [&](int q) {
+  // copy number `idx` (0 .. kCopiesPerQuad-1) of quad q into its stage: this wave's A
+  // fragments, then its 4 index tiles, then its 2 scale copies
+  auto copy_piece = [&](int q, int idx) {
     const uint32_t st = ring0 + (uint32_t)((q % kStages) * kStageBytes);
-#pragma unroll
-    for (int mt = 0; mt < kMT; ++mt)
-      copy16(a.A + (int64_t)q * kTileK, a_off[mt], st + (uint32_t)((wave * kMT + mt) * 1024));
     const uint32_t sb = st + kABytes + wave * kWaveBBytes;
-#pragma unroll
-    for (int r = 0; r < kWaveRT; ++r)
+    if (idx < kAPerWave) {
+      copy16(a.A + (int64_t)q * kTileK, a_off[idx], st + (uint32_t)((f0 + idx) * 1024));
+    } else if (idx < kAPerWave + kWaveRT) {
+      const int r = idx - kAPerWave;
       copy16(wbase[r] + (wtile0[r] + q) * kTileNibbleBytes, 16 * lane, sb + r * kTileNibbleBytes);
-#pragma unroll
-    for (int i = 0; i < 2; ++i)
+    } else {
+      const int i = idx - kAPerWave - kWaveRT;
       copy4(wbase[2 * i] + nib_bytes + (wtile0[2 * i] + q) * kTileScaleBytes, s_off[i],
             sb + kWaveRT * kTileNibbleBytes + i * 2 * kTileScaleBytes);
+    }
+  };
+  auto copy_quad = [&](int q) {
+#pragma unroll
+    for (int idx = 0; idx < kCopiesPerQuad; ++idx) copy_piece(q, idx);
   };
 
   f32x4 acc[kMT][kWaveRT];
@@ -209,22 +237,34 @@ __global__ void __launch_bounds__(256) qgemm_kernel(GemmArgs a) {
 #pragma unroll
     for (int r = 0; r < kWaveRT; ++r) {
       const uint32_t w = (j == 0) ? nib[r].x : (j == 1) ? nib[r].y : (j == 2) ? nib[r].z : nib[r].w;
-      lv[r][0] = lut[w & 0xFF];
-      lv[r][1] = lut[(w >> 8) & 0xFF];
-      lv[r][2] = lut[(w >> 16) & 0xFF];
-      lv[r][3] = lut[w >> 24];
+      lv[r][0] = lutc[(w & 0xFF) * kLutCopies];
+      lv[r][1] = lutc[((w >> 8) & 0xFF) * kLutCopies];
+      lv[r][2] = lutc[((w >> 16) & 0xFF) * kLutCopies];
+      lv[r][3] = lutc[(w >> 24) * kLutCopies];
     }
   };
 
-  copy_quad(0);
-  if (kq_n > 1) copy_quad(1);
+#pragma unroll
+  for (int i = 0; i < kStages - 1; ++i)
+    if (i < kq_n) copy_quad(i);
+  if (MODE == kGemmDown && tid < rows) {
+    // the epilogue's per-row pair id and gate weight, fetched once per tile (after the
+    // first copies are in flight) instead of as two dependent loads per stored row
+    const int p = a.pairs[seg0 + m0 + tid];
+    tile_pair[tid] = p;
+    tile_gw[tid] = a.gate_w[p];
+  }
 
   for (int q = 0; q < kq_n; ++q) {
     // this wave's copies of quad q are done once only quad q+1's may still be in flight
-    if (q + 1 < kq_n) wait_vmcnt<kCopiesPerQuad>();
+    // quads issued after q that may stay in flight: min(kStages - 2, kq_n - 1 - q)
+    const int later = min(kStages - 2, kq_n - 1 - q);
+    static_assert(kStages >= 2 && kStages <= 4, "ring depth");
+    if (later >= 2) wait_vmcnt<2 * kCopiesPerQuad>();
+    else if (later == 1) wait_vmcnt<kCopiesPerQuad>();
     else wait_vmcnt<0>();
     lds_barrier();  // quad q is in LDS for everyone; quad q-1's stage is free
-    if (q + 2 < kq_n) copy_quad(q + 2);
+    if (q + kStages - 1 < kq_n) copy_quad(q + kStages - 1);
 
     const uint8_t* st = &ring[q % kStages][0];
     const uint8_t* sb = st + kABytes + (tid >> 6) * kWaveBBytes;
@@ -293,8 +333,8 @@ __global__ void __launch_bounds__(256) qgemm_kernel(GemmArgs a) {
       for (int i = 0; i < 4; ++i) {
         const int rr = 16 * mt + 4 * g + i;
         if (rr >= rows) continue;
-        const int p = a.pairs[seg0 + m0 + rr];
-        const float gw = a.gate_w[p];
+        const int p = tile_pair[rr];
+        const float gw = tile_gw[rr];
         if (a.atomic) {
           float* orow = a.out + (int64_t)(p / a.top_k) * a.ldo + n0 + 64 * wave + c;
 #pragma unroll
@@ -310,8 +350,12 @@ __global__ void __launch_bounds__(256) qgemm_kernel(GemmArgs a) {
   }
 }
 
+constexpr int kDenseWaves = 4;    // long prompt: 128 x 256 tiles keep a 512-token chunk on ~224 CUs
+constexpr int kGroupedWaves = 8;  // MoE: 128 x 512 tiles (two waves per SIMD)
+
 int launch_qgemm_dense(const uint8_t* packed, int64_t n, int64_t k, const uint16_t* x, int64_t m,
                        int64_t ldx, float* y, int64_t ldy, int64_t chunk, hipStream_t s) {
+  constexpr int kBN = Shape<kDenseWaves>::kBN;
   if (chunk <= 0) chunk = m;
   for (int64_t c0 = 0; c0 < m; c0 += chunk) {
     GemmArgs a{};
@@ -324,19 +368,25 @@ int launch_qgemm_dense(const uint8_t* packed, int64_t n, int64_t k, const uint16
     a.C = y + c0 * ldy;
     a.ldc = ldy;
     const int64_t grid = ((a.M + kBM - 1) / kBM) * ((n + kBN - 1) / kBN);
-    hipLaunchKernelGGL(qgemm_kernel<kGemmDense>, dim3((unsigned)grid), dim3(256), 0, s, a);
+    hipLaunchKernelGGL((qgemm_kernel<kGemmDense, kDenseWaves>), dim3((unsigned)grid), dim3(64 * kDenseWaves), 0,
+                       s, a);
     if (int e = check_launch("qgemm_kernel<dense>")) return e;
   }
   return 0;
 }
 
-int launch_qgemm_grouped(int mode, const GemmArgs& a, int64_t max_tiles, hipStream_t s) {
+int launch_qgemm_grouped(int mode, GemmArgs a, int64_t max_tiles, hipStream_t s) {
+  constexpr int kBN = Shape<kGroupedWaves>::kBN;
+  // GATEUP: a workgroup covers kBN/2 intermediate columns (gate and up rows side by side)
+  a.n_tiles_n = (mode == kGemmGateUp) ? (a.N + kBN / 2 - 1) / (kBN / 2) : (a.N + kBN - 1) / kBN;
   const int64_t grid = max_tiles * a.n_tiles_n;
   if (grid == 0) return 0;
   if (mode == kGemmGateUp)
-    hipLaunchKernelGGL(qgemm_kernel<kGemmGateUp>, dim3((unsigned)grid), dim3(256), 0, s, a);
+    hipLaunchKernelGGL((qgemm_kernel<kGemmGateUp, kGroupedWaves>), dim3((unsigned)grid), dim3(64 * kGroupedWaves),
+                       0, s, a);
   else
-    hipLaunchKernelGGL(qgemm_kernel<kGemmDown>, dim3((unsigned)grid), dim3(256), 0, s, a);
+    hipLaunchKernelGGL((qgemm_kernel<kGemmDown, kGroupedWaves>), dim3((unsigned)grid), dim3(64 * kGroupedWaves), 0,
+                       s, a);
   return check_launch(mode == kGemmGateUp ? "qgemm_kernel<gateup>" : "qgemm_kernel<down>");
 }
 

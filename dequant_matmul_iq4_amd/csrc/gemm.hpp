@@ -20,7 +20,7 @@ struct GemmArgs {
   int64_t ldh;
   const int32_t* tiles;     // grouped: (expert, m tile) pairs
   const int32_t* num_tiles; // grouped: number of valid entries in `tiles`
-  int64_t n_tiles_n;        // grouped: workgroups per m tile along N
+  int64_t n_tiles_n;        // grouped: workgroups per m tile along N (set by the launcher)
   const int32_t* offsets;   // grouped: per-expert start in the sorted pair list [E+1]
   const int32_t* pairs;     // grouped: sorted pair ids
   const float* gate_w;      // DOWN: gate weight of each pair (indexed by pair id)
@@ -32,6 +32,7 @@ struct GemmArgs {
 
 int launch_qgemm_dense(const uint8_t* packed, int64_t n, int64_t k, const uint16_t* x, int64_t m,
                        int64_t ldx, float* y, int64_t ldy, int64_t chunk, hipStream_t s);
-int launch_qgemm_grouped(int mode, const GemmArgs& a, int64_t max_tiles, hipStream_t s);
+// Sets a.n_tiles_n (workgroups per m tile along N) itself.
+int launch_qgemm_grouped(int mode, GemmArgs a, int64_t max_tiles, hipStream_t s);
 
 }  // namespace iq4

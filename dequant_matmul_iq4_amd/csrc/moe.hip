@@ -136,7 +136,6 @@ int launch_moe(const MoeCall& m, hipStream_t s) {
     g.ldh = m.inter;
     g.tiles = tiles;
     g.num_tiles = num_tiles;
-    g.n_tiles_n = (m.inter + 127) / 128;
     g.offsets = offsets;
     g.pairs = pairs;
     g.top_k = m.top_k;
@@ -152,7 +151,6 @@ int launch_moe(const MoeCall& m, hipStream_t s) {
     d.ldc = m.hidden;
     d.tiles = tiles;
     d.num_tiles = num_tiles;
-    d.n_tiles_n = (m.hidden + 255) / 256;
     d.offsets = offsets;
     d.pairs = pairs;
     d.gate_w = m.w;
