@@ -31,6 +31,8 @@
 // kernel waits for them itself: per quad one s_waitcnt for this wave's copies of the
 // quad, then one workgroup barrier (the quad is complete for everyone, and the stage
 // filled next is no longer read by anyone).
+#include <type_traits>
+
 #include "common.hpp"
 #include "gemm.hpp"
 #include "launch.hpp"
@@ -156,6 +158,9 @@ __global__ void __launch_bounds__(NW * 64) qgemm_kernel(GemmArgs a) {
     if (MODE == kGemmGateUp) W1 += (int64_t)e * a.w_expert_stride;
   }
   const int kq_n = (int)(a.K / kTileK);
+  // fragment rows holding valid rows (a partial last tile of an expert, or of a chunk,
+  // multiplies only these; the copies still bring all rows so the wait counts hold)
+  const int nfr = __builtin_amdgcn_readfirstlane((int)((rows + 15) / 16));
   const int64_t nib_bytes = a.N * (a.K / kQK) * kNibbleBytes;
   const uint32_t ring0 = lds_addr(&ring[0][0]);
 
@@ -255,47 +260,57 @@ __global__ void __launch_bounds__(NW * 64) qgemm_kernel(GemmArgs a) {
     tile_gw[tid] = a.gate_w[p];
   }
 
-  for (int q = 0; q < kq_n; ++q) {
-    // this wave's copies of quad q are done once only quad q+1's may still be in flight
-    // quads issued after q that may stay in flight: min(kStages - 2, kq_n - 1 - q)
-    const int later = min(kStages - 2, kq_n - 1 - q);
-    static_assert(kStages >= 2 && kStages <= 4, "ring depth");
-    if (later >= 2) wait_vmcnt<2 * kCopiesPerQuad>();
-    else if (later == 1) wait_vmcnt<kCopiesPerQuad>();
-    else wait_vmcnt<0>();
-    lds_barrier();  // quad q is in LDS for everyone; quad q-1's stage is free
-    if (q + kStages - 1 < kq_n) copy_quad(q + kStages - 1);
+  // The main loop, instantiated twice: full tiles multiply all fragment rows with no
+  // branch in the unrolled body; a partial tile (an expert's or a chunk's last) skips the
+  // fragment rows wholly past its rows (the copies still bring them, so the wait counts
+  // hold).
+  auto main_loop = [&](auto partial_tag) {
+    constexpr bool PARTIAL = decltype(partial_tag)::value;
+    for (int q = 0; q < kq_n; ++q) {
+      // this wave's copies of quad q are done once only quad q+1's may still be in flight
+      // quads issued after q that may stay in flight: min(kStages - 2, kq_n - 1 - q)
+      const int later = min(kStages - 2, kq_n - 1 - q);
+      static_assert(kStages >= 2 && kStages <= 4, "ring depth");
+      if (later >= 2) wait_vmcnt<2 * kCopiesPerQuad>();
+      else if (later == 1) wait_vmcnt<kCopiesPerQuad>();
+      else wait_vmcnt<0>();
+      lds_barrier();  // quad q is in LDS for everyone; quad q-1's stage is free
+      if (q + kStages - 1 < kq_n) copy_quad(q + kStages - 1);
 
-    const uint8_t* st = &ring[q % kStages][0];
-    const uint8_t* sb = st + kABytes + (tid >> 6) * kWaveBBytes;
-    uint4 nib[kWaveRT];
-    uint2 scl[kWaveRT];
-#pragma unroll
-    for (int r = 0; r < kWaveRT; ++r) {
-      nib[r] = *reinterpret_cast<const uint4*>(sb + r * kTileNibbleBytes + lane * 16);
-      scl[r] = *reinterpret_cast<const uint2*>(sb + kWaveRT * kTileNibbleBytes + r * kTileScaleBytes + c * 8);
-    }
-    uint32_t lv[kWaveRT][4];
-    lut_reads(nib, 0, lv);
-#pragma unroll
-    for (int j = 0; j < kTileBlocks; ++j) {
-      u32x4 bf[kWaveRT];
+      const uint8_t* st = &ring[q % kStages][0];
+      const uint8_t* sb = st + kABytes + (tid >> 6) * kWaveBBytes;
+      uint4 nib[kWaveRT];
+      uint2 scl[kWaveRT];
 #pragma unroll
       for (int r = 0; r < kWaveRT; ++r) {
-        const uint32_t sw = (j < 2) ? scl[r].x : scl[r].y;
-        const uint32_t dd = __builtin_amdgcn_perm(sw, sw, (j & 1) ? 0x03020302u : 0x01000100u);
-#pragma unroll
-        for (int i = 0; i < 4; ++i) bf[r][i] = pk_mul_f16(lv[r][i], dd);
+        nib[r] = *reinterpret_cast<const uint4*>(sb + r * kTileNibbleBytes + lane * 16);
+        scl[r] = *reinterpret_cast<const uint2*>(sb + kWaveRT * kTileNibbleBytes + r * kTileScaleBytes + c * 8);
       }
-      if (j + 1 < kTileBlocks) lut_reads(nib, j + 1, lv);  // next block's reads under these MFMAs
+      uint32_t lv[kWaveRT][4];
+      lut_reads(nib, 0, lv);
 #pragma unroll
-      for (int mt = 0; mt < kMT; ++mt) {
-        const u32x4 af = *reinterpret_cast<const u32x4*>(st + (j * kMT + mt) * 1024 + lane * 16);
+      for (int j = 0; j < kTileBlocks; ++j) {
+        u32x4 bf[kWaveRT];
 #pragma unroll
-        for (int r = 0; r < kWaveRT; ++r) acc[mt][r] = mfma_f16(af, bf[r], acc[mt][r]);
+        for (int r = 0; r < kWaveRT; ++r) {
+          const uint32_t sw = (j < 2) ? scl[r].x : scl[r].y;
+          const uint32_t dd = __builtin_amdgcn_perm(sw, sw, (j & 1) ? 0x03020302u : 0x01000100u);
+#pragma unroll
+          for (int i = 0; i < 4; ++i) bf[r][i] = pk_mul_f16(lv[r][i], dd);
+        }
+        if (j + 1 < kTileBlocks) lut_reads(nib, j + 1, lv);  // next block's reads under these MFMAs
+#pragma unroll
+        for (int mt = 0; mt < kMT; ++mt) {
+          if (PARTIAL && mt >= nfr) break;  // fragment rows wholly past the tile's rows
+          const u32x4 af = *reinterpret_cast<const u32x4*>(st + (j * kMT + mt) * 1024 + lane * 16);
+#pragma unroll
+          for (int r = 0; r < kWaveRT; ++r) acc[mt][r] = mfma_f16(af, bf[r], acc[mt][r]);
+        }
       }
     }
-  }
+  };
+  if (nfr == kMT) main_loop(std::false_type{});
+  else main_loop(std::true_type{});
 
   // ---- epilogue: lane holds D[4g + i][c] of each (mt, r) fragment -------------------
   if (MODE == kGemmDense) {
