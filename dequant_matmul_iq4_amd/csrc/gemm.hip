@@ -42,7 +42,8 @@ namespace iq4 {
 constexpr int kBM = 128;                 // rows of A per workgroup
 constexpr int kWaveRT = 4;               // packed row tiles (16 rows) per wave
 constexpr int kMT = kBM / 16;            // 8 fragment rows of A
-constexpr int kStages = 2;               // quads in the ring (filled kStages - 1 ahead)
+constexpr int kStages = 2;               // quads in the ring (filled one quad ahead)
+constexpr int kPrefetch = 3;             // quads ahead whose weight lines are touched into L2
 constexpr int kABytes = kTileBlocks * kMT * 1024;                        // 32 KiB
 constexpr int kWaveBBytes = kWaveRT * (kTileNibbleBytes + kTileScaleBytes);  // 4.5 KiB
 
@@ -90,6 +91,15 @@ __device__ __forceinline__ void copy4(const void* base, uint32_t voff, uint32_t 
                : "memory");
 }
 
+// Global -> LDS copy with a per-lane 64-bit address, 4 bytes per lane (used to touch
+// cache lines ahead of their copy; the bytes land in a sink nobody reads).
+__device__ __forceinline__ void touch4(const void* addr, uint32_t lds) {
+  asm volatile("s_nop 0\n\tglobal_load_lds_dword %0, off"
+               :
+               : "v"(addr), "{m0}"(lds)
+               : "memory");
+}
+
 // Workgroup barrier ordering LDS only: the copies are waited for explicitly, so the
 // barrier must not wait for every global load in flight.
 __device__ __forceinline__ void lds_barrier() {
@@ -99,12 +109,19 @@ __device__ __forceinline__ void lds_barrier() {
 }
 
 // XCD-aware order of the workgroups: hardware deals workgroup b to XCD b mod 8, so
-// logical tile L = (b mod 8) * (G / 8) + b / 8 keeps runs of consecutive logical tiles
-// (which share weight row tiles) inside one XCD and its L2.
+// logical tile L = (b mod 8) * ceil(G / 8) + b / 8 gives each XCD a run of consecutive
+// logical tiles (which share activation tiles and weight row tiles) in its own L2.
+// G is the number of logical tiles (for the grouped products, known only on the device);
+// the grid holds at least 8 * ceil(G / 8) workgroups; -1 = nothing to do.
 __device__ __forceinline__ int64_t xcd_swizzle(int64_t b, int64_t G) {
-  if (G % 8) return b;
-  return (b % 8) * (G / 8) + b / 8;
+  const int64_t per = (G + 7) / 8;
+  const int64_t i = b / 8;
+  if (i >= per) return -1;
+  const int64_t L = (b % 8) * per + i;
+  return (L < G) ? L : -1;
 }
+
+static inline int64_t round8(int64_t g) { return (g + 7) / 8 * 8; }
 
 template <int MODE, int NW>
 __global__ void __launch_bounds__(NW * 64) qgemm_kernel(GemmArgs a) {
@@ -113,6 +130,7 @@ __global__ void __launch_bounds__(NW * 64) qgemm_kernel(GemmArgs a) {
   constexpr int kAPerWave = S::kAPerWave, kCopiesPerQuad = S::kCopiesPerQuad;
   __shared__ __attribute__((aligned(1024))) uint8_t ring[kStages][kStageBytes];
   __shared__ uint32_t lut[256 * kLutCopies];  // entry e of copy c at e * kLutCopies + c
+  __shared__ uint32_t touch_sink[64];         // destination of the prefetch touches (never read)
   __shared__ int32_t tile_pair[kBM];          // DOWN: pair id and gate weight of each row
   __shared__ float tile_gw[kBM];
 
@@ -134,17 +152,18 @@ __global__ void __launch_bounds__(NW * 64) qgemm_kernel(GemmArgs a) {
   const uint8_t* W0 = a.W0;
   const uint8_t* W1 = a.W1;
   if (MODE == kGemmDense) {
-    const int64_t L = xcd_swizzle(blockIdx.x, (int64_t)gridDim.x);
     const int64_t mt_n = (a.M + kBM - 1) / kBM;
+    const int64_t L = xcd_swizzle(blockIdx.x, mt_n * ((a.N + kBN - 1) / kBN));
+    if (L < 0) return;
     const int64_t mt = L % mt_n, nt = L / mt_n;
     m0 = mt * kBM;
     rows = min((int64_t)kBM, a.M - m0);
     n0 = nt * kBN;
   } else {
     const int64_t ntl = a.n_tiles_n;
-    const int64_t L = xcd_swizzle(blockIdx.x, (int64_t)gridDim.x);
+    const int64_t L = xcd_swizzle(blockIdx.x, (int64_t)(*a.num_tiles) * ntl);
+    if (L < 0) return;
     const int64_t ti = L / ntl, nt = L % ntl;
-    if (ti >= *a.num_tiles) return;
     const int e = a.tiles[2 * ti];
     const int mt = a.tiles[2 * ti + 1];
     seg0 = a.offsets[e];
@@ -210,6 +229,24 @@ __global__ void __launch_bounds__(NW * 64) qgemm_kernel(GemmArgs a) {
     s_off[i] = (uint32_t)(4 * (lane & 31) + (lane >> 5) * (wtile0[2 * i + 1] - wtile0[2 * i]) * kTileScaleBytes);
 
   // copy quad q into its stage: A block `wave` (8 fragments), then this wave's tiles
+  // Prefetch: lane l touches one 128-byte line of this wave's weight tiles of a later
+  // quad (lanes 0..31: the 4 index tiles, 8 lines each; 32..35: the 4 scale tiles; the
+  // others repeat lane 0), so that quad's copy finds its weights in L2.
+  const uint8_t* touch_ptr;
+  int64_t touch_stride;
+  {
+    const int l = (lane < 36) ? lane : 0;
+    const int r = (l < 32) ? (l >> 3) : (l - 32);
+    const uint8_t* wb = (r == 0) ? wbase[0] : (r == 1) ? wbase[1] : (r == 2) ? wbase[2] : wbase[3];
+    const int64_t t0 = (r == 0) ? wtile0[0] : (r == 1) ? wtile0[1] : (r == 2) ? wtile0[2] : wtile0[3];
+    touch_ptr = (l < 32) ? wb + t0 * kTileNibbleBytes + (l & 7) * 128 : wb + nib_bytes + t0 * kTileScaleBytes;
+    touch_stride = (l < 32) ? kTileNibbleBytes : kTileScaleBytes;
+  }
+  const uint32_t sink = lds_addr(&touch_sink[0]);
+  auto prefetch = [&](int q) {  // exactly one load per call (the quad is clamped)
+    touch4(touch_ptr + (int64_t)min(q, kq_n - 1) * touch_stride, sink);
+  };
+
   // copy number `idx` (0 .. kCopiesPerQuad-1) of quad q into its stage: this wave's A
   // fragments, then its 4 index tiles, then its 2 scale copies
   auto copy_piece = [&](int q, int idx) {
@@ -259,6 +296,8 @@ __global__ void __launch_bounds__(NW * 64) qgemm_kernel(GemmArgs a) {
     tile_pair[tid] = p;
     tile_gw[tid] = a.gate_w[p];
   }
+#pragma unroll
+  for (int i = 1; i < kPrefetch; ++i) prefetch(i);
 
   // The main loop, instantiated twice: full tiles multiply all fragment rows with no
   // branch in the unrolled body; a partial tile (an expert's or a chunk's last) skips the
@@ -267,15 +306,15 @@ __global__ void __launch_bounds__(NW * 64) qgemm_kernel(GemmArgs a) {
   auto main_loop = [&](auto partial_tag) {
     constexpr bool PARTIAL = decltype(partial_tag)::value;
     for (int q = 0; q < kq_n; ++q) {
-      // this wave's copies of quad q are done once only quad q+1's may still be in flight
-      // quads issued after q that may stay in flight: min(kStages - 2, kq_n - 1 - q)
-      const int later = min(kStages - 2, kq_n - 1 - q);
-      static_assert(kStages >= 2 && kStages <= 4, "ring depth");
-      if (later >= 2) wait_vmcnt<2 * kCopiesPerQuad>();
-      else if (later == 1) wait_vmcnt<kCopiesPerQuad>();
-      else wait_vmcnt<0>();
+      // this wave's copies of quad q are done once only the prefetch touches issued after
+      // them may still be in flight: kPrefetch - 1 of the prologue before quad 0, then the
+      // one issued with the previous quad's copies
+      static_assert(kStages == 2, "the wait counts assume a ring filled one quad ahead");
+      if (q == 0) wait_vmcnt<kPrefetch - 1>();
+      else wait_vmcnt<1>();
       lds_barrier();  // quad q is in LDS for everyone; quad q-1's stage is free
-      if (q + kStages - 1 < kq_n) copy_quad(q + kStages - 1);
+      if (q + 1 < kq_n) copy_quad(q + 1);
+      prefetch(q + kPrefetch);
 
       const uint8_t* st = &ring[q % kStages][0];
       const uint8_t* sb = st + kABytes + (tid >> 6) * kWaveBBytes;
@@ -382,7 +421,7 @@ int launch_qgemm_dense(const uint8_t* packed, int64_t n, int64_t k, const uint16
     a.M = (m - c0 < chunk) ? (m - c0) : chunk;
     a.C = y + c0 * ldy;
     a.ldc = ldy;
-    const int64_t grid = ((a.M + kBM - 1) / kBM) * ((n + kBN - 1) / kBN);
+    const int64_t grid = round8(((a.M + kBM - 1) / kBM) * ((n + kBN - 1) / kBN));
     hipLaunchKernelGGL((qgemm_kernel<kGemmDense, kDenseWaves>), dim3((unsigned)grid), dim3(64 * kDenseWaves), 0,
                        s, a);
     if (int e = check_launch("qgemm_kernel<dense>")) return e;
@@ -394,7 +433,7 @@ int launch_qgemm_grouped(int mode, GemmArgs a, int64_t max_tiles, hipStream_t s)
   constexpr int kBN = Shape<kGroupedWaves>::kBN;
   // GATEUP: a workgroup covers kBN/2 intermediate columns (gate and up rows side by side)
   a.n_tiles_n = (mode == kGemmGateUp) ? (a.N + kBN / 2 - 1) / (kBN / 2) : (a.N + kBN - 1) / kBN;
-  const int64_t grid = max_tiles * a.n_tiles_n;
+  const int64_t grid = round8(max_tiles * a.n_tiles_n);
   if (grid == 0) return 0;
   if (mode == kGemmGateUp)
     hipLaunchKernelGGL((qgemm_kernel<kGemmGateUp, kGroupedWaves>), dim3((unsigned)grid), dim3(64 * kGroupedWaves),
