@@ -100,7 +100,7 @@ __global__ void __launch_bounds__(512) qmv_kernel(QmvArgs a) {
   constexpr int NMAT = (MODE == kQmvGateUp) ? 2 : 1;
   constexpr int ROWS = RG * kTileRows;
   constexpr int XBYTES = kWaves * WQ * 4 * kFragBytes;
-  static_assert(kWaves * NMAT * RG * 64 * 16 <= XBYTES, "reduction scratch does not fit");
+  static_assert(kWaves * NMAT * RG * 64 * 16 <= XBYTES, "reduction scratch does not fit");  // every wave's slot
   __shared__ uint32_t lut[256];
   __shared__ __attribute__((aligned(16))) uint8_t xs[XBYTES + 256];  // + room for padding-row reads
   __shared__ int s_last;
@@ -336,10 +336,20 @@ __global__ void __launch_bounds__(512) qmv_kernel(QmvArgs a) {
 #pragma unroll
         for (int m = 0; m < NMAT; ++m) {
           float part[3];
+          // every partial slot is read at once (slots of absent waves lie inside the
+          // staging buffer; their values are not used), then added in wave order
+          const float* redf = reinterpret_cast<const float*>(red);
+          float pv[3][kWaves];
+#pragma unroll
+          for (int p = 0; p < 3; ++p)
+#pragma unroll
+            for (int w2 = 0; w2 < kWaves; ++w2)
+              pv[p][w2] = redf[(((w2 * NMAT + m) * RG + r) * 64 + 16 * p + row) * 4 + t];
 #pragma unroll
           for (int p = 0; p < 3; ++p) {
-            float sum = red[((0 * NMAT + m) * RG + r) * 64 + 16 * p + row][t];
-            for (int w2 = 1; w2 < nwaves; ++w2) sum += red[((w2 * NMAT + m) * RG + r) * 64 + 16 * p + row][t];
+            float sum = pv[p][0];
+#pragma unroll
+            for (int w2 = 1; w2 < kWaves; ++w2) sum = (w2 < nwaves) ? sum + pv[p][w2] : sum;
             part[p] = sum;
           }
           v[m] = (part[0] + part[1]) + part[2];
