@@ -154,8 +154,8 @@ static int check_moe_sizes(const char* fn, int64_t n_tok, int32_t top_k, int32_t
                            int64_t hidden, int64_t inter, int32_t act_dtype) {
   if (n_tok < 0 || n_tok > ((int64_t)1 << 24) / (top_k > 0 ? top_k : 1))
     return set_error(IQ4_E_ARG, "%s: n_tok out of range", fn);
-  if (n_expert < 1 || n_expert > 1024 || top_k < 1 || top_k > n_expert)
-    return set_error(IQ4_E_ARG, "%s: need 1 <= top_k <= n_expert <= 1024", fn);
+  if (n_expert < 1 || n_expert > 1024 || top_k < 1 || top_k > 16 || top_k > n_expert)
+    return set_error(IQ4_E_ARG, "%s: need 1 <= top_k <= min(n_expert, 16), n_expert <= 1024", fn);
   if (act_dtype != IQ4_F32 && act_dtype != IQ4_F16)
     return set_error(IQ4_E_ARG, "%s: act_dtype must be IQ4_F32 or IQ4_F16", fn);
   if (hidden <= 0 || inter <= 0 || hidden % kTileK || inter % kTileK)

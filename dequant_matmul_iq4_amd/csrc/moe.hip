@@ -20,6 +20,7 @@
 namespace iq4 {
 
 constexpr int kTileM = 128;  // rows per GEMM tile (gemm.hip kBM)
+constexpr int kMaxTopK = 16;  // the largest top_k the call accepts
 
 // One workgroup: m tiles per expert (ceil(count / 128)), exclusive scan over experts,
 // then each expert writes its (expert, m tile) entries.
@@ -54,13 +55,20 @@ __global__ void __launch_bounds__(256) combine_kernel(const float* __restrict__ 
   if (i >= n_tok * per_tok) return;
   const int64_t t = i / per_tok, h = (i % per_tok) * 4;
   const float* r = rows + t * top_k * ldr + h;
-  float4 acc = *reinterpret_cast<const float4*>(r);
-  for (int j = 1; j < top_k; ++j) {
-    const float4 v = *reinterpret_cast<const float4*>(r + j * ldr);
-    acc.x += v.x;
-    acc.y += v.y;
-    acc.z += v.z;
-    acc.w += v.w;
+  // every slot row is read at once (indices past top_k repeat the last one: in bounds,
+  // not added), then added in slot order
+  float4 v[kMaxTopK];
+#pragma unroll
+  for (int j = 0; j < kMaxTopK; ++j) v[j] = *reinterpret_cast<const float4*>(r + min(j, top_k - 1) * ldr);
+  float4 acc = v[0];
+#pragma unroll
+  for (int j = 1; j < kMaxTopK; ++j) {
+    if (j < top_k) {
+      acc.x += v[j].x;
+      acc.y += v[j].y;
+      acc.z += v[j].z;
+      acc.w += v[j].w;
+    }
   }
   *reinterpret_cast<float4*>(out + t * ldo + h) = acc;
 }

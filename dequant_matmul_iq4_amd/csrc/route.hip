@@ -1,5 +1,7 @@
 // route.hip -- top-k routing from logits, and the bit-exact token gather of the
 // routed pairs (counts, exclusive offsets, pair list grouped by expert, inverse).
+#include <climits>
+
 #include "common.hpp"
 #include "launch.hpp"
 
@@ -66,11 +68,22 @@ __global__ void __launch_bounds__(kGatherThreads) gather_kernel(const int32_t* _
   const int64_t p0 = wave * seg;
   const int64_t p1 = min(p0 + seg, n_pairs);
 
+  // ids are read 8 x 64 at a time (independent loads in flight; out of range -> never equal
+  // to, nor below, any expert)
+  constexpr int kBatch = 8;
   int eq = 0, lt = 0;
-  for (int64_t p = p0 + lane; p < p1; p += 64) {
-    const int v = ids[p];
-    eq += (v == e);
-    lt += (v < e);
+  for (int64_t pb = p0; pb < p1; pb += 64 * kBatch) {
+    int v[kBatch];
+#pragma unroll
+    for (int u = 0; u < kBatch; ++u) {
+      const int64_t p = pb + 64 * u + lane;
+      v[u] = (p < p1) ? ids[p] : INT_MAX;
+    }
+#pragma unroll
+    for (int u = 0; u < kBatch; ++u) {
+      eq += (v[u] == e);
+      lt += (v[u] < e);
+    }
   }
   for (int o = 32; o > 0; o >>= 1) {
     eq += __shfl_xor(eq, o);
@@ -94,16 +107,25 @@ __global__ void __launch_bounds__(kGatherThreads) gather_kernel(const int32_t* _
     if (e == (int)gridDim.x - 1) offsets[e + 1] = (int32_t)n_pairs;
   }
   const uint64_t below = (lane == 0) ? 0ull : (~0ull >> (64 - lane));
-  for (int64_t pb = p0; pb < p1; pb += 64) {
-    const int64_t p = pb + lane;
-    const bool hit = (p < p1) && (ids[p] == e);
-    const uint64_t mask = __ballot(hit);
-    if (hit) {
-      const int pos = run + __popcll(mask & below);
-      pairs[pos] = (int32_t)p;
-      slot_row[p] = pos;
+  for (int64_t pb = p0; pb < p1; pb += 64 * kBatch) {
+    int v[kBatch];
+#pragma unroll
+    for (int u = 0; u < kBatch; ++u) {
+      const int64_t p = pb + 64 * u + lane;
+      v[u] = (p < p1) ? ids[p] : INT_MAX;
     }
-    run += __popcll(mask);
+#pragma unroll
+    for (int u = 0; u < kBatch; ++u) {  // in pair order: u, then lane
+      const int64_t p = pb + 64 * u + lane;
+      const bool hit = v[u] == e;
+      const uint64_t mask = __ballot(hit);
+      if (hit) {
+        const int pos = run + __popcll(mask & below);
+        pairs[pos] = (int32_t)p;
+        slot_row[p] = pos;
+      }
+      run += __popcll(mask);
+    }
   }
 }
 

@@ -182,7 +182,8 @@ int iq4_moe_workspace_size(int64_t n_tok, int32_t top_k, int32_t n_expert, int64
  *               product in fp32 through the T-column matvec) or IQ4_F16 (prefill path:
  *               grouped GEMM on the matrix cores, weights decoded to f16, fp32
  *               accumulation, h rounded to f16 for the down product).
- *   ids, w      [n_tok][top_k] int32 / float32 (ids in [0, n_expert), not checked).
+ *   ids, w      [n_tok][top_k] int32 / float32 (ids in [0, n_expert), not checked);
+ *               1 <= top_k <= min(n_expert, 16), n_expert <= 1024.
  *   w_gate, w_up  n_expert packed inter x hidden matrices, expert e at
  *               e * iq4_packed_bytes(inter, hidden) bytes.
  *   w_down      n_expert packed hidden x inter matrices, expert e at

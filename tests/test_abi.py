@@ -92,6 +92,11 @@ def test_moe_and_gemm_validation():
     rc = _rc("iq4_moe_expert_gemm", FAKE, iq4.IQ4_F16, 16, 2048, FAKE, FAKE, 9, 8, 2048, 768,
              FAKE, FAKE, FAKE, FAKE, 2048, FAKE, 1 << 30, 0, None)
     assert rc == iq4.IQ4_E_ARG  # top_k > n_expert
+    rc = _rc("iq4_moe_expert_gemm", FAKE, iq4.IQ4_F16, 16, 2048, FAKE, FAKE, 17, 128, 2048, 768,
+             FAKE, FAKE, FAKE, FAKE, 2048, FAKE, 1 << 30, 0, None)
+    assert rc == iq4.IQ4_E_ARG  # top_k > 16
+    nb = ctypes.c_size_t(0)
+    assert iq4.lib().iq4_moe_workspace_size(16, 17, 128, 2048, 768, iq4.IQ4_F16, ctypes.byref(nb)) == iq4.IQ4_E_ARG
     rc = _rc("iq4_moe_expert_gemm", FAKE, iq4.IQ4_F16, 16, 2048, FAKE, FAKE, 8, 128, 2048, 768,
              FAKE, FAKE, FAKE, FAKE, 2048, FAKE, 1 << 30, 4, None)
     assert rc == iq4.IQ4_E_ARG  # unknown flag
