@@ -43,7 +43,6 @@ constexpr int kBM = 128;                 // rows of A per workgroup
 constexpr int kWaveRT = 4;               // packed row tiles (16 rows) per wave
 constexpr int kMT = kBM / 16;            // 8 fragment rows of A
 constexpr int kStages = 2;               // quads in the ring (filled one quad ahead)
-constexpr int kPrefetch = 3;             // quads ahead whose weight lines are touched into L2
 constexpr int kABytes = kTileBlocks * kMT * 1024;                        // 32 KiB
 constexpr int kWaveBBytes = kWaveRT * (kTileNibbleBytes + kTileScaleBytes);  // 4.5 KiB
 
@@ -91,15 +90,6 @@ __device__ __forceinline__ void copy4(const void* base, uint32_t voff, uint32_t 
                : "memory");
 }
 
-// Global -> LDS copy with a per-lane 64-bit address, 4 bytes per lane (used to touch
-// cache lines ahead of their copy; the bytes land in a sink nobody reads).
-__device__ __forceinline__ void touch4(const void* addr, uint32_t lds) {
-  asm volatile("s_nop 0\n\tglobal_load_lds_dword %0, off"
-               :
-               : "v"(addr), "{m0}"(lds)
-               : "memory");
-}
-
 // Workgroup barrier ordering LDS only: the copies are waited for explicitly, so the
 // barrier must not wait for every global load in flight.
 __device__ __forceinline__ void lds_barrier() {
@@ -130,7 +120,6 @@ __global__ void __launch_bounds__(NW * 64) qgemm_kernel(GemmArgs a) {
   constexpr int kAPerWave = S::kAPerWave, kCopiesPerQuad = S::kCopiesPerQuad;
   __shared__ __attribute__((aligned(1024))) uint8_t ring[kStages][kStageBytes];
   __shared__ uint32_t lut[256 * kLutCopies];  // entry e of copy c at e * kLutCopies + c
-  __shared__ uint32_t touch_sink[64];         // destination of the prefetch touches (never read)
   __shared__ int32_t tile_pair[kBM];          // DOWN: pair id and gate weight of each row
   __shared__ float tile_gw[kBM];
 
@@ -229,24 +218,6 @@ __global__ void __launch_bounds__(NW * 64) qgemm_kernel(GemmArgs a) {
     s_off[i] = (uint32_t)(4 * (lane & 31) + (lane >> 5) * (wtile0[2 * i + 1] - wtile0[2 * i]) * kTileScaleBytes);
 
   // copy quad q into its stage: A block `wave` (8 fragments), then this wave's tiles
-  // Prefetch: lane l touches one 128-byte line of this wave's weight tiles of a later
-  // quad (lanes 0..31: the 4 index tiles, 8 lines each; 32..35: the 4 scale tiles; the
-  // others repeat lane 0), so that quad's copy finds its weights in L2.
-  const uint8_t* touch_ptr;
-  int64_t touch_stride;
-  {
-    const int l = (lane < 36) ? lane : 0;
-    const int r = (l < 32) ? (l >> 3) : (l - 32);
-    const uint8_t* wb = (r == 0) ? wbase[0] : (r == 1) ? wbase[1] : (r == 2) ? wbase[2] : wbase[3];
-    const int64_t t0 = (r == 0) ? wtile0[0] : (r == 1) ? wtile0[1] : (r == 2) ? wtile0[2] : wtile0[3];
-    touch_ptr = (l < 32) ? wb + t0 * kTileNibbleBytes + (l & 7) * 128 : wb + nib_bytes + t0 * kTileScaleBytes;
-    touch_stride = (l < 32) ? kTileNibbleBytes : kTileScaleBytes;
-  }
-  const uint32_t sink = lds_addr(&touch_sink[0]);
-  auto prefetch = [&](int q) {  // exactly one load per call (the quad is clamped)
-    touch4(touch_ptr + (int64_t)min(q, kq_n - 1) * touch_stride, sink);
-  };
-
   // copy number `idx` (0 .. kCopiesPerQuad-1) of quad q into its stage: this wave's A
   // fragments, then its 4 index tiles, then its 2 scale copies
   auto copy_piece = [&](int q, int idx) {
@@ -296,8 +267,6 @@ __global__ void __launch_bounds__(NW * 64) qgemm_kernel(GemmArgs a) {
     tile_pair[tid] = p;
     tile_gw[tid] = a.gate_w[p];
   }
-#pragma unroll
-  for (int i = 1; i < kPrefetch; ++i) prefetch(i);
 
   // The main loop, instantiated twice: full tiles multiply all fragment rows with no
   // branch in the unrolled body; a partial tile (an expert's or a chunk's last) skips the
@@ -306,15 +275,11 @@ __global__ void __launch_bounds__(NW * 64) qgemm_kernel(GemmArgs a) {
   auto main_loop = [&](auto partial_tag) {
     constexpr bool PARTIAL = decltype(partial_tag)::value;
     for (int q = 0; q < kq_n; ++q) {
-      // this wave's copies of quad q are done once only the prefetch touches issued after
-      // them may still be in flight: kPrefetch - 1 of the prologue before quad 0, then the
-      // one issued with the previous quad's copies
-      static_assert(kStages == 2, "the wait counts assume a ring filled one quad ahead");
-      if (q == 0) wait_vmcnt<kPrefetch - 1>();
-      else wait_vmcnt<1>();
+      // this wave's copies of quad q are the last it issued: wait for all of them
+      static_assert(kStages == 2, "the wait count assumes a ring filled one quad ahead");
+      wait_vmcnt<0>();
       lds_barrier();  // quad q is in LDS for everyone; quad q-1's stage is free
       if (q + 1 < kq_n) copy_quad(q + 1);
-      prefetch(q + kPrefetch);
 
       const uint8_t* st = &ring[q % kStages][0];
       const uint8_t* sb = st + kABytes + (tid >> 6) * kWaveBBytes;
