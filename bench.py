@@ -41,10 +41,10 @@ N_BANKS = 8                 # expert banks the decode step rotates over
 # at the time: a kernel changed since then reports traffic null.  Commands and raw
 # figures: profiles/<name>.txt.
 MEASURED_TRAFFIC = {
-    "qmv_dense_4096x4096_T1-4": (9971758, "dbef0314edda513c", ("qmv.hip", "qmv.hpp", "common.hpp")),
-    "qgemm_gateup_moe_prefill_3256tok": (434470556, "05fc183f95bdbd3a", ("gemm.hip", "gemm.hpp", "common.hpp")),
-    "qgemm_down_moe_prefill_3256tok": (385754943, "05fc183f95bdbd3a", ("gemm.hip", "gemm.hpp", "common.hpp")),
-    "qgemm_dense_13056x4096x14336_chunk512": (94976366, "05fc183f95bdbd3a", ("gemm.hip", "gemm.hpp", "common.hpp")),
+    "qmv_dense_4096x4096_T1-4": (9968189, "9148a83eabf59afb", ("qmv.hip", "qmv.hpp", "common.hpp")),
+    "qgemm_gateup_moe_prefill_3256tok": (418056742, "ad7f045771126915", ("gemm.hip", "gemm.hpp", "common.hpp")),
+    "qgemm_down_moe_prefill_3256tok": (391365660, "ad7f045771126915", ("gemm.hip", "gemm.hpp", "common.hpp")),
+    "qgemm_dense_13056x4096x14336_chunk512": (95007150, "ad7f045771126915", ("gemm.hip", "gemm.hpp", "common.hpp")),
 }
 
 
