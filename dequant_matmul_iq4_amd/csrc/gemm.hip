@@ -111,6 +111,21 @@ __device__ __forceinline__ int64_t xcd_swizzle(int64_t b, int64_t G) {
   return (L < G) ? L : -1;
 }
 
+// Grouped products: the full tiles' logical range G1 in XCD-contiguous runs as above,
+// then the partial tiles (lighter, by descending rows) dealt round-robin over the XCDs,
+// so every XCD ends on light work.  The grid holds at least 8 * ceil(G1 / 8) + round8(G - G1)
+// workgroups.
+__device__ __forceinline__ int64_t xcd_swizzle_grouped(int64_t b, int64_t G1, int64_t G) {
+  const int64_t per = (G1 + 7) / 8;
+  const int64_t x = b % 8, i = b / 8;
+  if (i < per) {
+    const int64_t L = x * per + i;
+    return (L < G1) ? L : -1;
+  }
+  const int64_t L = G1 + (i - per) * 8 + x;
+  return (L < G) ? L : -1;
+}
+
 static inline int64_t round8(int64_t g) { return (g + 7) / 8 * 8; }
 
 template <int MODE, int NW>
@@ -150,7 +165,7 @@ __global__ void __launch_bounds__(NW * 64) qgemm_kernel(GemmArgs a) {
     n0 = nt * kBN;
   } else {
     const int64_t ntl = a.n_tiles_n;
-    const int64_t L = xcd_swizzle(blockIdx.x, (int64_t)(*a.num_tiles) * ntl);
+    const int64_t L = xcd_swizzle_grouped(blockIdx.x, (int64_t)a.num_tiles[1] * ntl, (int64_t)a.num_tiles[0] * ntl);
     if (L < 0) return;
     const int64_t ti = L / ntl, nt = L % ntl;
     const int e = a.tiles[2 * ti];
@@ -398,7 +413,7 @@ int launch_qgemm_grouped(int mode, GemmArgs a, int64_t max_tiles, hipStream_t s)
   constexpr int kBN = Shape<kGroupedWaves>::kBN;
   // GATEUP: a workgroup covers kBN/2 intermediate columns (gate and up rows side by side)
   a.n_tiles_n = (mode == kGemmGateUp) ? (a.N + kBN / 2 - 1) / (kBN / 2) : (a.N + kBN - 1) / kBN;
-  const int64_t grid = round8(max_tiles * a.n_tiles_n);
+  const int64_t grid = round8(max_tiles * a.n_tiles_n) + 8;  // + the rounding of the full-tile range
   if (grid == 0) return 0;
   if (mode == kGemmGateUp)
     hipLaunchKernelGGL((qgemm_kernel<kGemmGateUp, kGroupedWaves>), dim3((unsigned)grid), dim3(64 * kGroupedWaves),

@@ -19,7 +19,7 @@ struct GemmArgs {
   uint16_t* H;              // GATEUP: h = silu(g) * u as binary16 [pairs][ldh] (sorted order)
   int64_t ldh;
   const int32_t* tiles;     // grouped: (expert, m tile) pairs
-  const int32_t* num_tiles; // grouped: number of valid entries in `tiles`
+  const int32_t* num_tiles; // grouped: [0] valid entries in `tiles`, [1] of them full tiles (listed first)
   int64_t n_tiles_n;        // grouped: workgroups per m tile along N (set by the launcher)
   const int32_t* offsets;   // grouped: per-expert start in the sorted pair list [E+1]
   const int32_t* pairs;     // grouped: sorted pair ids

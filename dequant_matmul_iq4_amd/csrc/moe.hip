@@ -22,15 +22,21 @@ namespace iq4 {
 constexpr int kTileM = 128;  // rows per GEMM tile (gemm.hip kBM)
 constexpr int kMaxTopK = 16;  // the largest top_k the call accepts
 
-// One workgroup: m tiles per expert (ceil(count / 128)), exclusive scan over experts,
-// then each expert writes its (expert, m tile) entries.
+// One workgroup.  The tile list holds every expert's full 128-row tiles first
+// (expert-major, an expert's tiles adjacent), then the experts' partial last tiles by
+// descending row count (ties: lower expert first), so the products can run the lighter
+// tiles last.  num_tiles[0] = all tiles, num_tiles[1] = full tiles.
 __global__ void __launch_bounds__(1024) tiles_kernel(const int32_t* __restrict__ counts, int n_expert,
                                                      int32_t* __restrict__ tiles,
                                                      int32_t* __restrict__ num_tiles) {
   __shared__ int scan[1024];
+  __shared__ int part_rows[1024];
   const int e = threadIdx.x;
-  const int nt = (e < n_expert) ? (counts[e] + kTileM - 1) / kTileM : 0;
-  scan[e] = nt;
+  const int cnt = (e < n_expert) ? counts[e] : 0;
+  const int nf = cnt / kTileM;  // full tiles
+  const int pr = cnt % kTileM;  // rows of the partial tile (0: none)
+  scan[e] = nf;
+  part_rows[e] = pr;
   __syncthreads();
   for (int off = 1; off < 1024; off <<= 1) {  // inclusive Hillis-Steele scan
     const int v = (e >= off) ? scan[e - off] : 0;
@@ -38,12 +44,26 @@ __global__ void __launch_bounds__(1024) tiles_kernel(const int32_t* __restrict__
     scan[e] += v;
     __syncthreads();
   }
-  const int base = scan[e] - nt;
-  for (int i = 0; i < nt; ++i) {
+  const int full = scan[1023];
+  const int base = scan[e] - nf;
+  for (int i = 0; i < nf; ++i) {
     tiles[2 * (base + i)] = e;
     tiles[2 * (base + i) + 1] = i;
   }
-  if (e == 1023) *num_tiles = scan[1023];
+  if (pr > 0) {
+    int rank = 0;
+    for (int e2 = 0; e2 < n_expert; ++e2) {
+      const int p2 = part_rows[e2];
+      rank += (p2 > pr) || (p2 == pr && e2 < e);
+    }
+    tiles[2 * (full + rank)] = e;
+    tiles[2 * (full + rank) + 1] = nf;
+  }
+  const int partial = __syncthreads_count(pr > 0);
+  if (e == 0) {
+    num_tiles[0] = full + partial;
+    num_tiles[1] = full;
+  }
 }
 
 // out[t][h] = sum_j rows[t * k + j][h], j ascending; one thread per 4 outputs.

@@ -201,26 +201,35 @@ __global__ void __launch_bounds__(512) qmv_kernel(QmvArgs a) {
     __builtin_amdgcn_fence(__ATOMIC_ACQUIRE, "wavefront");
   };
 
-  // Dense: the first pass's activations go out first (small, no dependent load), then
-  // every weight load.  Grouped: the weights go out as soon as the expert is known,
-  // ahead of the column-row lookups the activations depend on.
-  if (MODE == kQmvDense) load_x(0, (int)min((int64_t)kCols, ncols));
   uint4 nib[WQ][NMAT][RG];
   uint2 scl[WQ][NMAT][RG];
+  auto load_w = [&](int u0, int u1) {
 #pragma unroll
-  for (int r = 0; r < RG; ++r) {
-    const int64_t rt = min(rg * RG + r, a.nt - 1);  // clamped: rows past n are dropped
+    for (int u = 0; u < WQ; ++u) {
+      if (u < u0 || u >= u1) continue;
 #pragma unroll
-    for (int m = 0; m < NMAT; ++m) {
-      const uint8_t* tp = W[m] + (rt * kq_n + kqa) * kTileNibbleBytes + lane * 16;
-      const uint8_t* sp = W[m] + a.nibble_bytes + (rt * kq_n + kqa) * kTileScaleBytes + c * 8;
+      for (int r = 0; r < RG; ++r) {
+        const int64_t rt = min(rg * RG + r, a.nt - 1);
 #pragma unroll
-      for (int u = 0; u < WQ; ++u) {
-        const int q = min(wq0 + u, max(wq1 - 1, 0));  // clamped; unused when past the range
-        nib[u][m][r] = *reinterpret_cast<const uint4*>(tp + (int64_t)q * kTileNibbleBytes);
-        scl[u][m][r] = *reinterpret_cast<const uint2*>(sp + (int64_t)q * kTileScaleBytes);
+        for (int m = 0; m < NMAT; ++m) {
+          const uint8_t* tp = W[m] + (rt * kq_n + kqa) * kTileNibbleBytes + lane * 16;
+          const uint8_t* sp = W[m] + a.nibble_bytes + (rt * kq_n + kqa) * kTileScaleBytes + c * 8;
+          const int q = min(wq0 + u, max(wq1 - 1, 0));
+          nib[u][m][r] = *reinterpret_cast<const uint4*>(tp + (int64_t)q * kTileNibbleBytes);
+          scl[u][m][r] = *reinterpret_cast<const uint2*>(sp + (int64_t)q * kTileScaleBytes);
+        }
       }
     }
+  };
+  // Dense: the first quad's weights, then the activations (L2-hot, staged while the
+  // rest streams in), then the other quads.  Grouped: the weights go out as soon as
+  // the expert is known, ahead of the column-row lookups the activations depend on.
+  if (MODE == kQmvDense) {
+    load_w(0, 1);
+    load_x(0, (int)min((int64_t)kCols, ncols));
+    load_w(1, WQ);
+  } else {
+    load_w(0, WQ);
   }
   if (MODE != kQmvDense) load_x(0, (int)min((int64_t)kCols, ncols));
   for (int i = tid; i < 256; i += blockDim.x)
