@@ -51,7 +51,6 @@ namespace iq4 {
 constexpr int kWaves = 8;              // waves per workgroup (at most)
 constexpr int kMaxWaveQuads = 4;       // quads per wave: all of a wave's weights in registers
 constexpr int kSliceQuads = kWaves * kMaxWaveQuads;  // 32 quads = 128 blocks = K 4096
-constexpr int kSliceBlocks = 4 * kSliceQuads;
 constexpr int kCols = 4;               // columns per pass (rows 4s + t of the A operand)
 constexpr int kDenseRG = 1;            // row tiles per workgroup (dense)
 constexpr int kGateUpRG = 1;           // row tiles per matrix (gate + up)
@@ -93,10 +92,11 @@ __device__ __forceinline__ const float* column_ptr(const QmvArgs& a, int mode, i
 constexpr int kFragRows = 12;
 constexpr int kFragBytes = 4 * kFragRows * 16;  // 768 B per block
 
-// One workgroup per RG row tiles (and per routed expert in the grouped modes) and K
-// slice; each wave owns WQ quads of the slice (registers and LDS sized to K).
+// Dense verify-window matvec: one workgroup per RG row tiles and K slice; each wave owns
+// WQ quads of the slice (registers and LDS sized to K).
 template <int MODE, int RG, int WQ>
 __global__ void __launch_bounds__(512) qmv_kernel(QmvArgs a) {
+  static_assert(MODE == kQmvDense, "the grouped modes have their own kernel");
   constexpr int NMAT = (MODE == kQmvGateUp) ? 2 : 1;
   constexpr int ROWS = RG * kTileRows;
   constexpr int XBYTES = kWaves * WQ * 4 * kFragBytes;
@@ -110,41 +110,10 @@ __global__ void __launch_bounds__(512) qmv_kernel(QmvArgs a) {
   const int c = lane & 15, g = lane >> 4;
 
   // ---- tile of this workgroup ---------------------------------------------------------
-  int64_t rg, seg0 = 0, ncols;
-  int slice = 0;
+  const int64_t rg = blockIdx.x / a.S;
+  const int slice = (int)(blockIdx.x % a.S);
+  const int64_t seg0 = 0, ncols = a.T;
   const uint8_t* W[2] = {a.W0, a.W1};
-  if (MODE == kQmvDense) {
-    rg = blockIdx.x / a.S;
-    slice = (int)(blockIdx.x % a.S);
-    ncols = a.T;
-  } else {
-    // The grid covers at most min(pairs, experts) experts: workgroup slot i takes the
-    // i-th expert (ascending id) that has pairs, found by a ballot over the offsets in
-    // every wave (no LDS, no barrier); slots past the routed experts exit.
-    const int64_t slot = blockIdx.x / a.rg_n;
-    rg = blockIdx.x % a.rg_n;
-    int64_t e = -1, before = 0;
-    for (int e0 = 0; e0 < a.n_expert && e < 0; e0 += 64) {
-      const int ee = e0 + lane;
-      const int lo = (ee < a.n_expert) ? a.offsets[ee] : 0;
-      const int hi = (ee < a.n_expert) ? a.offsets[ee + 1] : 0;
-      const bool act = hi > lo;
-      const uint64_t m = __ballot(act);
-      const int64_t cnt = __popcll(m);
-      if (slot < before + cnt) {
-        const uint64_t below = (lane == 0) ? 0ull : (~0ull >> (64 - lane));
-        const uint64_t hit = __ballot(act && before + __popcll(m & below) == slot);
-        const int L = __ffsll((unsigned long long)hit) - 1;
-        e = e0 + L;
-        seg0 = __shfl(lo, L);
-        ncols = __shfl(hi, L) - seg0;
-      }
-      before += cnt;
-    }
-    if (e < 0) return;
-    W[0] += e * a.w_expert_stride;
-    W[1] += e * a.w_expert_stride;
-  }
   const int kq_n = a.kq_n;
   const int kqa = slice * a.slice_quads;                 // first quad of the slice
   const int nq_slice = min(a.slice_quads, kq_n - kqa);   // quads in the slice
@@ -221,17 +190,11 @@ __global__ void __launch_bounds__(512) qmv_kernel(QmvArgs a) {
       }
     }
   };
-  // Dense: the first quad's weights, then the activations (L2-hot, staged while the
-  // rest streams in), then the other quads.  Grouped: the weights go out as soon as
-  // the expert is known, ahead of the column-row lookups the activations depend on.
-  if (MODE == kQmvDense) {
-    load_w(0, 1);
-    load_x(0, (int)min((int64_t)kCols, ncols));
-    load_w(1, WQ);
-  } else {
-    load_w(0, WQ);
-  }
-  if (MODE != kQmvDense) load_x(0, (int)min((int64_t)kCols, ncols));
+  // the first quad's weights, then the activations (L2-hot, staged while the rest
+  // streams in), then the other quads
+  load_w(0, 1);
+  load_x(0, (int)min((int64_t)kCols, ncols));
+  load_w(1, WQ);
   for (int i = tid; i < 256; i += blockDim.x)
     lut[i] = bf16_of_level(level_of(i & 15)) | (bf16_of_level(level_of(i >> 4)) << 16);
   __syncthreads();  // the table (LDS only: no wait on the loads in flight)
@@ -253,38 +216,6 @@ __global__ void __launch_bounds__(512) qmv_kernel(QmvArgs a) {
 #pragma unroll
     for (int u = 0; u < WQ; ++u) {
       if (wq0 + u >= wq1) break;
-      if constexpr (MODE != kQmvDense) {
-        // grouped modes (several workgroups per CU): one block at a time, same order
-#pragma unroll
-        for (int j = 0; j < 4; ++j) {
-          const int bl = 4 * u + j;
-          const u32x4 xf = *reinterpret_cast<const u32x4*>(xw + (bl * 4 + g) * (kFragRows * 16) + c * 16);
-          u32x4 bf[NMAT][RG];
-#pragma unroll
-          for (int m = 0; m < NMAT; ++m)
-#pragma unroll
-            for (int r = 0; r < RG; ++r) {
-              const uint4 nb = nib[u][m][r];
-              const uint32_t w = (j == 0) ? nb.x : (j == 1) ? nb.y : (j == 2) ? nb.z : nb.w;
-              bf[m][r][0] = lut[w & 0xFF];
-              bf[m][r][1] = lut[(w >> 8) & 0xFF];
-              bf[m][r][2] = lut[(w >> 16) & 0xFF];
-              bf[m][r][3] = lut[w >> 24];
-            }
-#pragma unroll
-          for (int m = 0; m < NMAT; ++m)
-#pragma unroll
-            for (int r = 0; r < RG; ++r) {
-              const f32x4 pr = mfma_bf16(xf, bf[m][r], f32x4{0.f, 0.f, 0.f, 0.f});
-              const uint2 sc = scl[u][m][r];
-              const uint32_t sw = (j < 2) ? sc.x : sc.y;
-              const float d = h2f((uint16_t)(sw >> (16 * (j & 1))));
-#pragma unroll
-              for (int i = 0; i < 4; ++i) acc[m][r][i] = __builtin_fmaf(d, pr[i], acc[m][r][i]);
-            }
-        }
-        continue;
-      }
       u32x4 xf[4];
       u32x4 bf[4][NMAT][RG];
 #pragma unroll
@@ -397,19 +328,264 @@ __global__ void __launch_bounds__(512) qmv_kernel(QmvArgs a) {
             if (tid == 0) __hip_atomic_store(a.counters + rg, 0, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
           }
         }
-      } else if (MODE == kQmvGateUp) {
-        if (idx < nout && col_ok) {
-          const float gv = v[0], uv = v[NMAT - 1];
-          a.y[(seg0 + t0 + t) * a.ldy + col] = gv / (1.0f + expf(-gv)) * uv;  // SwiGLU
-        }
-      } else {
-        if (idx < nout && col_ok) {
-          const int p = a.pairs[seg0 + t0 + t];
-          a.y[(int64_t)p * a.ldy + col] = a.gate_w[p] * v[0];
-        }
       }
     }
     if (t0 + kCols < ncols) __syncthreads();  // LDS is reused by the next pass
+  }
+}
+
+// ---------------------------------------------------------------------------------
+// Grouped matvec (MoE decode): one workgroup per (routed expert slot, run of row groups).
+// It finds its expert and stages the expert's columns once, then walks its row groups,
+// loading the next group's weights while the current one is multiplied and reduced
+// (two register sets).  Per output the arithmetic is the dense kernel's: the same plan
+// (a function of K only), block order, wave order and part order.
+template <int MODE, int RG, int WQ>
+__global__ void __launch_bounds__(512) qmv_grouped_kernel(QmvArgs a) {
+  constexpr int NMAT = (MODE == kQmvGateUp) ? 2 : 1;
+  constexpr int ROWS = RG * kTileRows;
+  constexpr int XBYTES = kWaves * WQ * 4 * kFragBytes;
+  constexpr int REDN = kWaves * NMAT * RG * 64;  // one f32x4 partial per (wave, matrix, tile, lane)
+  __shared__ uint32_t lut[256];
+  __shared__ __attribute__((aligned(16))) uint8_t xs[XBYTES + 256];  // + room for padding-row reads
+  __shared__ f32x4 red[REDN];
+
+  const int tid = threadIdx.x;
+  const int lane = tid & 63, wave = tid >> 6, nwaves = (int)(blockDim.x >> 6);
+  const int c = lane & 15, g = lane >> 4;
+
+  // ---- expert slot and row groups of this workgroup ---------------------------------
+  // Slot i takes the i-th expert (ascending id) that has pairs, found by a ballot over
+  // the offsets in every wave; slots past the routed experts exit.
+  const int64_t slot = blockIdx.x / a.rg_chunks;
+  const int64_t rg0 = (blockIdx.x % a.rg_chunks) * a.rg_per_wg;
+  const int64_t rg1 = min(rg0 + (int64_t)a.rg_per_wg, a.rg_n);
+  int64_t e = -1, before = 0, seg0 = 0, ncols = 0;
+  for (int e0 = 0; e0 < a.n_expert && e < 0; e0 += 64) {
+    const int ee = e0 + lane;
+    const int lo = (ee < a.n_expert) ? a.offsets[ee] : 0;
+    const int hi = (ee < a.n_expert) ? a.offsets[ee + 1] : 0;
+    const bool act = hi > lo;
+    const uint64_t m = __ballot(act);
+    const int64_t cnt = __popcll(m);
+    if (slot < before + cnt) {
+      const uint64_t below = (lane == 0) ? 0ull : (~0ull >> (64 - lane));
+      const uint64_t hit = __ballot(act && before + __popcll(m & below) == slot);
+      const int L = __ffsll((unsigned long long)hit) - 1;
+      e = e0 + L;
+      seg0 = __shfl(lo, L);
+      ncols = __shfl(hi, L) - seg0;
+    }
+    before += cnt;
+  }
+  if (e < 0 || rg0 >= rg1) return;
+  const uint8_t* W[2] = {a.W0 + e * a.w_expert_stride, a.W1 + e * a.w_expert_stride};
+  const int kq_n = a.kq_n;
+  const int wq0 = wave * a.wave_quads;  // this wave's quads (a single slice: K <= 4096)
+  const int wq1 = min(wq0 + a.wave_quads, kq_n);
+
+  // ---- this wave's activations (blocks [4 wq0, 4 wq1)), staged by the wave itself ----
+  const int wblk = 4 * (wq1 - wq0);
+  uint8_t* xw = xs + wave * (4 * WQ) * kFragBytes;
+  float4 xr[WQ][2];
+  auto load_x = [&](int64_t t0, int T) {  // tasks (column t, block, k-group gg), 64 lanes
+    const int ntask = T * wblk * 4;
+    const float* col[kCols];
+#pragma unroll
+    for (int t = 0; t < kCols; ++t) col[t] = column_ptr(a, MODE, seg0, t0 + min(t, T - 1));
+#pragma unroll
+    for (int i = 0; i < WQ; ++i) {
+      const int task = lane + 64 * i;
+      if (task < ntask) {
+        const int gg = task & 3, bl = (task >> 2) % wblk, t = (task >> 2) / wblk;
+        const float* cp = (t == 0) ? col[0] : (t == 1) ? col[1] : (t == 2) ? col[2] : col[3];
+        const float* p = cp + ((int64_t)wq0 * 4 + bl) * kQK + 8 * gg;
+        xr[i][0] = *reinterpret_cast<const float4*>(p);
+        xr[i][1] = *reinterpret_cast<const float4*>(p + 4);
+      }
+    }
+  };
+  auto store_x = [&](int T) {  // split and store in fragment order
+    const int ntask = T * wblk * 4;
+#pragma unroll
+    for (int i = 0; i < WQ; ++i) {
+      const int task = lane + 64 * i;
+      if (task < ntask) {
+        const int gg = task & 3, bl = (task >> 2) % wblk, t = (task >> 2) / wblk;
+        const float4 xa = xr[i][0], xb = xr[i][1];
+        uint8_t* dst = xw + (bl * 4 + gg) * (kFragRows * 16) + t * 16;
+#pragma unroll
+        for (int sp = 0; sp < 3; ++sp) {
+          uint4 f;
+          f.x = split_part(xa.x, sp) | (split_part(xa.y, sp) << 16);
+          f.y = split_part(xa.z, sp) | (split_part(xa.w, sp) << 16);
+          f.z = split_part(xb.x, sp) | (split_part(xb.y, sp) << 16);
+          f.w = split_part(xb.z, sp) | (split_part(xb.w, sp) << 16);
+          *reinterpret_cast<uint4*>(dst + sp * 4 * 16) = f;
+        }
+      }
+    }
+    // LDS accesses of one wave execute in order: the wave's reads below see these
+    // writes; this only keeps the compiler from moving them.
+    __builtin_amdgcn_fence(__ATOMIC_RELEASE, "wavefront");
+    __builtin_amdgcn_wave_barrier();
+    __builtin_amdgcn_fence(__ATOMIC_ACQUIRE, "wavefront");
+  };
+  // DOWN: each column's pair id and gate weight (scalar loads through the constant
+  // address space: the lists are not written during the call)
+  const __attribute__((address_space(4))) int32_t* cpairs = (const __attribute__((address_space(4))) int32_t*)a.pairs;
+  const __attribute__((address_space(4))) float* cgate = (const __attribute__((address_space(4))) float*)a.gate_w;
+  int32_t pcol[kCols];
+  float gwcol[kCols];
+  auto load_cols = [&](int64_t t0, int T) {
+    if (MODE != kQmvDown) return;
+#pragma unroll
+    for (int t = 0; t < kCols; ++t) {
+      const int idx = __builtin_amdgcn_readfirstlane((int)(seg0 + t0 + min(t, T - 1)));
+      pcol[t] = cpairs[idx];
+      gwcol[t] = cgate[pcol[t]];
+    }
+  };
+
+  // ---- weights of one row group (all of this wave's quads) -------------------------
+  struct WSet {
+    uint4 nib[WQ][NMAT][RG];
+    uint2 scl[WQ][NMAT][RG];
+  };
+  auto load_w = [&](WSet& ws, int64_t rg) {
+#pragma unroll
+    for (int u = 0; u < WQ; ++u)
+#pragma unroll
+      for (int r = 0; r < RG; ++r) {
+        const int64_t rt = min(rg * RG + r, a.nt - 1);  // clamped: rows past n are dropped
+#pragma unroll
+        for (int m = 0; m < NMAT; ++m) {
+          const uint8_t* tp = W[m] + rt * kq_n * kTileNibbleBytes + lane * 16;
+          const uint8_t* sp = W[m] + a.nibble_bytes + rt * kq_n * kTileScaleBytes + c * 8;
+          const int q = min(wq0 + u, max(wq1 - 1, 0));  // clamped; unused when past the range
+          ws.nib[u][m][r] = *reinterpret_cast<const uint4*>(tp + (int64_t)q * kTileNibbleBytes);
+          ws.scl[u][m][r] = *reinterpret_cast<const uint2*>(sp + (int64_t)q * kTileScaleBytes);
+        }
+      }
+  };
+  // the wave's quads, one block at a time; lanes of padding rows (s = 3 or a column
+  // >= T) read whatever lies there: an MFMA output row depends on its own A row only
+  auto multiply = [&](const WSet& ws, f32x4 (&acc)[NMAT][RG]) {
+#pragma unroll
+    for (int m = 0; m < NMAT; ++m)
+#pragma unroll
+      for (int r = 0; r < RG; ++r) acc[m][r] = f32x4{0.f, 0.f, 0.f, 0.f};
+#pragma unroll
+    for (int u = 0; u < WQ; ++u) {
+      if (wq0 + u >= wq1) break;
+#pragma unroll
+      for (int j = 0; j < 4; ++j) {
+        const int bl = 4 * u + j;
+        const u32x4 xf = *reinterpret_cast<const u32x4*>(xw + (bl * 4 + g) * (kFragRows * 16) + c * 16);
+        u32x4 bf[NMAT][RG];
+#pragma unroll
+        for (int m = 0; m < NMAT; ++m)
+#pragma unroll
+          for (int r = 0; r < RG; ++r) {
+            const uint4 nb = ws.nib[u][m][r];
+            const uint32_t w = (j == 0) ? nb.x : (j == 1) ? nb.y : (j == 2) ? nb.z : nb.w;
+            bf[m][r][0] = lut[w & 0xFF];
+            bf[m][r][1] = lut[(w >> 8) & 0xFF];
+            bf[m][r][2] = lut[(w >> 16) & 0xFF];
+            bf[m][r][3] = lut[w >> 24];
+          }
+#pragma unroll
+        for (int m = 0; m < NMAT; ++m)
+#pragma unroll
+          for (int r = 0; r < RG; ++r) {
+            const f32x4 pr = mfma_bf16(xf, bf[m][r], f32x4{0.f, 0.f, 0.f, 0.f});
+            const uint2 sc = ws.scl[u][m][r];
+            const uint32_t sw = (j < 2) ? sc.x : sc.y;
+            const float d = h2f((uint16_t)(sw >> (16 * (j & 1))));
+#pragma unroll
+            for (int i = 0; i < 4; ++i) acc[m][r][i] = __builtin_fmaf(d, pr[i], acc[m][r][i]);
+          }
+      }
+    }
+  };
+  // reduction over the waves' K runs, then the three parts, then the mode's epilogue.
+  // Lane (g, c) holds D[4g + i][c]: part s = g, column i, weight row c.
+  auto reduce_store = [&](int64_t rg, int64_t t0, int T, const f32x4 (&acc)[NMAT][RG]) {
+#pragma unroll
+    for (int m = 0; m < NMAT; ++m)
+#pragma unroll
+      for (int r = 0; r < RG; ++r) red[((wave * NMAT + m) * RG + r) * 64 + lane] = acc[m][r];
+    __syncthreads();
+    const float* redf = reinterpret_cast<const float*>(red);
+    const int nout = T * ROWS;
+    for (int idx0 = 0; idx0 < nout; idx0 += (int)blockDim.x) {  // uniform trip count
+      const int idx = idx0 + tid;
+      const int t = idx / ROWS, rr = idx % ROWS;
+      const int r = rr >> 4, row = rr & 15;
+      const int64_t col = rg * ROWS + rr;  // output row index (weight row)
+      if (idx < nout && col < a.n) {
+        float v[NMAT];
+#pragma unroll
+        for (int m = 0; m < NMAT; ++m) {
+          float pv[3][kWaves];  // every slot read at once (absent waves' slots unused)
+#pragma unroll
+          for (int p = 0; p < 3; ++p)
+#pragma unroll
+            for (int w2 = 0; w2 < kWaves; ++w2)
+              pv[p][w2] = redf[(((w2 * NMAT + m) * RG + r) * 64 + 16 * p + row) * 4 + t];
+          float part[3];
+#pragma unroll
+          for (int p = 0; p < 3; ++p) {
+            float sum = pv[p][0];
+#pragma unroll
+            for (int w2 = 1; w2 < kWaves; ++w2) sum = (w2 < nwaves) ? sum + pv[p][w2] : sum;
+            part[p] = sum;
+          }
+          v[m] = (part[0] + part[1]) + part[2];
+        }
+        if (MODE == kQmvGateUp) {
+          const float gv = v[0], uv = v[NMAT - 1];
+          a.y[(seg0 + t0 + t) * a.ldy + col] = gv / (1.0f + expf(-gv)) * uv;  // SwiGLU
+        } else {
+          const int pc = (t == 0) ? pcol[0] : (t == 1) ? pcol[1] : (t == 2) ? pcol[2] : pcol[3];
+          const float gw = (t == 0) ? gwcol[0] : (t == 1) ? gwcol[1] : (t == 2) ? gwcol[2] : gwcol[3];
+          a.y[(int64_t)pc * a.ldy + col] = gw * v[0];
+        }
+      }
+    }
+    __syncthreads();  // the partials are read; the slots can be reused
+  };
+
+  // ---- prologue: first row group's weights, then the columns, the table -------------
+  WSet wa, wb;
+  load_w(wa, rg0);
+  const bool one_pass = ncols <= kCols;
+  if (one_pass) {
+    load_x(0, (int)ncols);
+    load_cols(0, (int)ncols);
+  }
+  for (int i = tid; i < 256; i += blockDim.x)
+    lut[i] = bf16_of_level(level_of(i & 15)) | (bf16_of_level(level_of(i >> 4)) << 16);
+  __syncthreads();  // the table (LDS only: no wait on the loads in flight)
+  if (one_pass) store_x((int)ncols);
+
+  auto step = [&](const WSet& cur, WSet& nxt, int64_t rg) {
+    if (rg + 1 < rg1) load_w(nxt, rg + 1);  // in flight during this group's work
+    for (int64_t t0 = 0; t0 < ncols; t0 += kCols) {
+      const int T = (int)min((int64_t)kCols, ncols - t0);
+      if (!one_pass) {  // more than kCols columns: stage each pass (rare in decode)
+        load_x(t0, T);
+        load_cols(t0, T);
+        store_x(T);
+      }
+      f32x4 acc[NMAT][RG];
+      multiply(cur, acc);
+      reduce_store(rg, t0, T, acc);
+    }
+  };
+  for (int64_t rg = rg0; rg < rg1; rg += 2) {
+    step(wa, wb, rg);
+    if (rg + 1 < rg1) step(wb, wa, rg + 1);
   }
 }
 
@@ -472,17 +648,49 @@ int launch_qmv(const uint8_t* packed, int64_t n, int64_t k, const float* x, int6
   return launch_sized<kQmvDense, kDenseRG>(a, a.rg_n * a.S);
 }
 
+template <int MODE, int RG, int WQ>
+static int launch_grouped_mode(const QmvArgs& a, int64_t grid) {
+  if (grid == 0) return 0;
+  hipLaunchKernelGGL((qmv_grouped_kernel<MODE, RG, WQ>), dim3((unsigned)grid), dim3(64 * a.nwaves), 0, a.stream,
+                     a);
+  return check_launch("qmv_grouped_kernel");
+}
+
+template <int MODE, int RG>
+static int launch_grouped_sized(const QmvArgs& a, int64_t grid) {
+  switch (a.wave_quads) {
+    case 1: return launch_grouped_mode<MODE, RG, 1>(a, grid);
+    case 2: return launch_grouped_mode<MODE, RG, 2>(a, grid);
+    case 3: return launch_grouped_mode<MODE, RG, 3>(a, grid);
+    default: return launch_grouped_mode<MODE, RG, kMaxWaveQuads>(a, grid);
+  }
+}
+
+// Row groups per workgroup: enough that the grid holds about one workgroup per CU (a
+// long walk keeps the next group's weights in flight; measured best against 2 and 4
+// workgroups per CU).
+static void grouped_split(QmvArgs& a, int64_t slots) {
+  const int64_t want = 256;
+  int64_t per = (a.rg_n * slots + want - 1) / want;
+  if (per < 1) per = 1;
+  if (per > a.rg_n) per = a.rg_n;
+  a.rg_per_wg = (int)per;
+  a.rg_chunks = (a.rg_n + per - 1) / per;
+}
+
 int launch_qmv_grouped(int mode, QmvArgs a, int64_t n, int64_t k, int n_expert, int64_t n_pairs) {
   a.n_expert = n_expert;
   const int64_t slots = (n_pairs < n_expert) ? n_pairs : n_expert;  // routed experts at most
   if (mode == kQmvGateUp) {
     qmv_plan(a, n, k, kGateUpRG);
     if (a.S != 1) return set_error(-3, "grouped matvec: K above 4096 is not supported");
-    return launch_sized<kQmvGateUp, kGateUpRG>(a, slots * a.rg_n);
+    grouped_split(a, slots);
+    return launch_grouped_sized<kQmvGateUp, kGateUpRG>(a, slots * a.rg_chunks);
   }
   qmv_plan(a, n, k, kDownRG);
   if (a.S != 1) return set_error(-3, "grouped matvec: K above 4096 is not supported");
-  return launch_sized<kQmvDown, kDownRG>(a, slots * a.rg_n);
+  grouped_split(a, slots);
+  return launch_grouped_sized<kQmvDown, kDownRG>(a, slots * a.rg_chunks);
 }
 
 }  // namespace iq4

@@ -25,6 +25,8 @@ struct QmvArgs {
   // launch plan (qmv_plan)
   int64_t n, nt, rg_n, nibble_bytes;
   int kq_n, S, slice_quads, wave_quads, nwaves;
+  int rg_per_wg;            // grouped: row groups walked by one workgroup
+  int64_t rg_chunks;        // grouped: workgroups per expert slot
   hipStream_t stream;
 };
 
