@@ -41,10 +41,12 @@ N_BANKS = 8                 # expert banks the decode step rotates over
 # at the time: a kernel changed since then reports traffic null.  Commands and raw
 # figures: profiles/<name>.txt.
 MEASURED_TRAFFIC = {
-    "qmv_dense_4096x4096_T1-4": (9968189, "9148a83eabf59afb", ("qmv.hip", "qmv.hpp", "common.hpp")),
-    "qgemm_gateup_moe_prefill_3256tok": (418056742, "ad7f045771126915", ("gemm.hip", "gemm.hpp", "common.hpp")),
-    "qgemm_down_moe_prefill_3256tok": (391365660, "ad7f045771126915", ("gemm.hip", "gemm.hpp", "common.hpp")),
-    "qgemm_dense_13056x4096x14336_chunk512": (95007150, "ad7f045771126915", ("gemm.hip", "gemm.hpp", "common.hpp")),
+    "qmv_dense_4096x4096_T1-4": (9981504, "fc5aa085b65aa127", ("qmv.hip", "qmv.hpp", "common.hpp")),
+    "qmv_grouped_gateup_moe_decode_4tok": (55504894, "fc5aa085b65aa127", ("qmv.hip", "qmv.hpp", "common.hpp")),
+    "qmv_grouped_down_moe_decode_4tok": (28679031, "fc5aa085b65aa127", ("qmv.hip", "qmv.hpp", "common.hpp")),
+    "qgemm_gateup_moe_prefill_3256tok": (502365665, "0dbe9099b8be0229", ("gemm.hip", "gemm.hpp", "common.hpp")),
+    "qgemm_down_moe_prefill_3256tok": (457448583, "0dbe9099b8be0229", ("gemm.hip", "gemm.hpp", "common.hpp")),
+    "qgemm_dense_13056x4096x14336_chunk512": (95007159, "0dbe9099b8be0229", ("gemm.hip", "gemm.hpp", "common.hpp")),
 }
 
 
@@ -361,7 +363,9 @@ def main():
                                      traffic=sum_traffic(*["qgemm_dense_13056x4096x14336_chunk512"] * 26)),
             "moe_decode_step": roof("hbm", unique_bytes / (comp["moe_decode"] * 1e-3) / 1e9, HBM_PEAK_GBS,
                                     "GB/s", f"gather + qmv<gateup> + qmv<down> + combine, {n_unique} "
-                                    "unique experts' weights"),
+                                    "unique experts' weights; traffic = HBM bytes of the two matvec launches",
+                                    traffic=sum_traffic("qmv_grouped_gateup_moe_decode_4tok",
+                                                        "qmv_grouped_down_moe_decode_4tok")),
             "dequant": roof("hbm", deq_bytes / (comp["dequant"] * 1e-3) / 1e9, HBM_PEAK_GBS, "GB/s",
                             "dequant_kernel<f16>: 9.4 MB of blocks in, 33.5 MB of f16 out"),
         },
