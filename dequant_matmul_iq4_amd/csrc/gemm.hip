@@ -11,19 +11,23 @@
 //           scales by the pair's gate weight and writes the pair's row (or adds it
 //           atomically into the token's output).
 //
-// Tiling (workgroup = 4 waves, 128 x 256 outputs, K walked in 4-block quads):
-//   * a ring of 3 LDS stages, each holding one quad of the workgroup's operands and
-//     filled two quads ahead, straight from global memory with global_load_lds (no
+// Tiling (workgroup = 8 waves, two per SIMD; K walked in 4-block quads):
+//   * each wave owns 128 x 64 outputs (fp32 accumulators in AGPRs).  The MoE products
+//     use 128 x 512 tiles (8 column groups of 64 weight rows).  The long prompt uses
+//     128 x 256 tiles: 4 column groups, the two waves of a group multiply blocks 0-1
+//     and 2-3 of each quad and their sums are added once after the loop;
+//   * a ring of 2 LDS stages, each holding one quad of the workgroup's operands and
+//     filled one quad ahead, straight from global memory with global_load_lds (no
 //     operand passes through VGPRs on its way in):
 //       activations  32 KiB: every 16-row x 32-k fragment in matrix-core A order
 //                    (lane l = 16g + r holds row r, elements 8g..8g+7), one
-//                    dwordx4 copy per fragment; wave w copies block w of the quad;
-//       weights      4 x 4.5 KiB: each wave copies its own 4 packed row tiles
-//                    (1 KiB of indices + 128 B of scales each) as they are in HBM;
+//                    dwordx4 copy per fragment, the 32 fragments split over the waves;
+//       weights      4.5 KiB per column group: its 4 packed row tiles (1 KiB of
+//                    indices + 128 B of scales each) as they are in HBM;
 //   * each wave decodes its 64 weight rows into B fragments: a byte-indexed LDS table
-//     gives two binary16 levels per index byte, one packed binary16 multiply by the
-//     block scale gives the binary16 rounding of the exact decoded weight.  No decoded
-//     weight goes through LDS or HBM;
+//     (replicated, each lane reading its own copy) gives two binary16 levels per index
+//     byte, one packed binary16 multiply by the block scale gives the binary16
+//     rounding of the exact decoded weight.  No decoded weight goes through LDS or HBM;
 //   * per block a wave issues 8 x 4 MFMAs against 8 A-fragment reads; the next block's
 //     16 table reads are issued under the current block's MFMAs.
 // The copies are issued from inline assembly so that the compiler, which cannot tell
@@ -46,16 +50,25 @@ constexpr int kStages = 2;               // quads in the ring (filled one quad a
 constexpr int kABytes = kTileBlocks * kMT * 1024;                        // 32 KiB
 constexpr int kWaveBBytes = kWaveRT * (kTileNibbleBytes + kTileScaleBytes);  // 4.5 KiB
 
-// Shape of a workgroup of NW waves: NW x 64 weight rows, one A quad shared by all.
-template <int NW>
+// Shape of a workgroup of NW waves in NW / KS column groups of 64 weight rows; the KS
+// waves of a column group split each quad's blocks between them (KS = 2: blocks 0-1 and
+// 2-3), their partial sums added once after the loop.  One A quad is shared by all.
+template <int NW, int KS>
 struct Shape {
-  static constexpr int kBN = NW * kWaveRT * kTileRows;                 // weight rows per workgroup
-  static constexpr int kStageBytes = kABytes + NW * kWaveBBytes;       // one quad of operands
-  static constexpr int kAPerWave = kTileBlocks * kMT / NW;             // A fragments each wave copies
-  static constexpr int kCopiesPerQuad = kAPerWave + kWaveRT + 2;       // + index tiles + 2 scale copies
+  static constexpr int kNC = NW / KS;                                   // column groups
+  static constexpr int kBN = kNC * kWaveRT * kTileRows;                 // weight rows per workgroup
+  static constexpr int kStageBytes = kABytes + kNC * kWaveBBytes;       // one quad of operands
+  static constexpr int kAPerWave = kTileBlocks * kMT / NW;              // A fragments each wave copies
+  static constexpr int kNibPerWave = kWaveRT / KS;                      // index tiles each wave copies
+  static constexpr int kSclPerWave = 2 / KS;                            // scale copies each wave issues
+  static constexpr int kCopiesPerQuad = kAPerWave + kNibPerWave + kSclPerWave;
+  static constexpr int kBlocksPerWave = kTileBlocks / KS;              // blocks of a quad each wave multiplies
   // replicas of the level table (fewer bank conflicts), as many as the LDS left allows
-  static constexpr int kLutCopies = (NW == 4) ? 32 : 16;
+  static constexpr int kLutCopies = (kNC == 4) ? 32 : 16;
+  static_assert(KS == 1 || KS == 2, "K split");
   static_assert(kStages * kStageBytes + 256 * 4 * kLutCopies + 2048 <= 160 * 1024, "LDS budget");
+  static_assert(KS == 1 || (kMT / 2) * kWaveRT * kNC * 64 * 16 <= kStages * kStageBytes,
+                "the K-split reduction fits in the ring");
 };
 
 __device__ __forceinline__ uint32_t f16_of_level(int c) {
@@ -128,11 +141,12 @@ __device__ __forceinline__ int64_t xcd_swizzle_grouped(int64_t b, int64_t G1, in
 
 static inline int64_t round8(int64_t g) { return (g + 7) / 8 * 8; }
 
-template <int MODE, int NW>
+template <int MODE, int NW, int KS>
 __global__ void __launch_bounds__(NW * 64) qgemm_kernel(GemmArgs a) {
-  using S = Shape<NW>;
+  using S = Shape<NW, KS>;
   constexpr int kBN = S::kBN, kStageBytes = S::kStageBytes, kLutCopies = S::kLutCopies;
-  constexpr int kAPerWave = S::kAPerWave, kCopiesPerQuad = S::kCopiesPerQuad;
+  constexpr int kAPerWave = S::kAPerWave, kCopiesPerQuad = S::kCopiesPerQuad, kNC = S::kNC;
+  constexpr int kNibPerWave = S::kNibPerWave, kSclPerWave = S::kSclPerWave, kBPW = S::kBlocksPerWave;
   __shared__ __attribute__((aligned(1024))) uint8_t ring[kStages][kStageBytes];
   __shared__ uint32_t lut[256 * kLutCopies];  // entry e of copy c at e * kLutCopies + c
   __shared__ int32_t tile_pair[kBM];          // DOWN: pair id and gate weight of each row
@@ -141,6 +155,8 @@ __global__ void __launch_bounds__(NW * 64) qgemm_kernel(GemmArgs a) {
   const int tid = threadIdx.x;
   const int lane = tid & 63;
   const int wave = __builtin_amdgcn_readfirstlane(tid >> 6);
+  const int cg = (KS == 1) ? wave : wave % kNC;  // column group (its 64 weight rows)
+  const int kp = (KS == 1) ? 0 : wave / kNC;     // which blocks of each quad it multiplies
   const int g = lane >> 4, c = lane & 15;
   if (tid < 256) {
     const uint32_t v = f16_of_level(level_of(tid & 15)) | (f16_of_level(level_of(tid >> 4)) << 16);
@@ -205,9 +221,9 @@ __global__ void __launch_bounds__(NW * 64) qgemm_kernel(GemmArgs a) {
     a_off[i] = (uint32_t)(2 * (src_row * a.lda + 32 * ablk + 8 * g));
   }
 
-  // ---- weight row tiles of this wave -------------------------------------------------
-  // DENSE / DOWN: rows n0 + 64w + 16r, r = 0..3 of W0.
-  // GATEUP: r = 0,1 -> gate rows n0 + 32w + 16r;  r = 2,3 -> up rows n0 + 32w + 16(r-2).
+  // ---- weight row tiles of this wave's column group cg --------------------------------
+  // DENSE / DOWN: rows n0 + 64cg + 16r, r = 0..3 of W0.
+  // GATEUP: r = 0,1 -> gate rows n0 + 32cg + 16r;  r = 2,3 -> up rows n0 + 32cg + 16(r-2).
   // Row tiles past N are replaced by the last row tile (read in bounds, never stored),
   // so the two tiles of each scale copy are equal or ascending in memory.
   const uint8_t* wbase[kWaveRT];
@@ -217,10 +233,10 @@ __global__ void __launch_bounds__(NW * 64) qgemm_kernel(GemmArgs a) {
   for (int r = 0; r < kWaveRT; ++r) {
     int64_t row0;
     if (MODE == kGemmGateUp) {
-      row0 = n0 + 32 * wave + 16 * (r & 1);
+      row0 = n0 + 32 * cg + 16 * (r & 1);
       wbase[r] = (r < 2) ? W0 : W1;
     } else {
-      row0 = n0 + 64 * wave + 16 * r;
+      row0 = n0 + 64 * cg + 16 * r;
       wbase[r] = W0;
     }
     rt_ok[r] = row0 < a.N;
@@ -232,19 +248,18 @@ __global__ void __launch_bounds__(NW * 64) qgemm_kernel(GemmArgs a) {
   for (int i = 0; i < 2; ++i)
     s_off[i] = (uint32_t)(4 * (lane & 31) + (lane >> 5) * (wtile0[2 * i + 1] - wtile0[2 * i]) * kTileScaleBytes);
 
-  // copy quad q into its stage: A block `wave` (8 fragments), then this wave's tiles
   // copy number `idx` (0 .. kCopiesPerQuad-1) of quad q into its stage: this wave's A
-  // fragments, then its 4 index tiles, then its 2 scale copies
+  // fragments, then its share of its column group's index tiles and scale copies
   auto copy_piece = [&](int q, int idx) {
     const uint32_t st = ring0 + (uint32_t)((q % kStages) * kStageBytes);
-    const uint32_t sb = st + kABytes + wave * kWaveBBytes;
+    const uint32_t sb = st + kABytes + cg * kWaveBBytes;
     if (idx < kAPerWave) {
       copy16(a.A + (int64_t)q * kTileK, a_off[idx], st + (uint32_t)((f0 + idx) * 1024));
-    } else if (idx < kAPerWave + kWaveRT) {
-      const int r = idx - kAPerWave;
+    } else if (idx < kAPerWave + kNibPerWave) {
+      const int r = kp * kNibPerWave + (idx - kAPerWave);
       copy16(wbase[r] + (wtile0[r] + q) * kTileNibbleBytes, 16 * lane, sb + r * kTileNibbleBytes);
     } else {
-      const int i = idx - kAPerWave - kWaveRT;
+      const int i = kp * kSclPerWave + (idx - kAPerWave - kNibPerWave);
       copy4(wbase[2 * i] + nib_bytes + (wtile0[2 * i] + q) * kTileScaleBytes, s_off[i],
             sb + kWaveRT * kTileNibbleBytes + i * 2 * kTileScaleBytes);
     }
@@ -260,11 +275,16 @@ __global__ void __launch_bounds__(NW * 64) qgemm_kernel(GemmArgs a) {
 #pragma unroll
     for (int r = 0; r < kWaveRT; ++r) acc[i][r] = f32x4{0.f, 0.f, 0.f, 0.f};
 
+  // index word of this wave's block jj (block kp * kBPW + jj of the quad) in a row tile
+  auto nib_word = [&](const uint4& nb, int jj) -> uint32_t {
+    if (KS == 1) return (jj == 0) ? nb.x : (jj == 1) ? nb.y : (jj == 2) ? nb.z : nb.w;
+    return kp ? (jj ? nb.w : nb.z) : (jj ? nb.y : nb.x);
+  };
   // LUT values of one block: 16 independent LDS reads.
-  auto lut_reads = [&](const uint4 (&nib)[kWaveRT], int j, uint32_t (&lv)[kWaveRT][4]) {
+  auto lut_reads = [&](const uint4 (&nib)[kWaveRT], int jj, uint32_t (&lv)[kWaveRT][4]) {
 #pragma unroll
     for (int r = 0; r < kWaveRT; ++r) {
-      const uint32_t w = (j == 0) ? nib[r].x : (j == 1) ? nib[r].y : (j == 2) ? nib[r].z : nib[r].w;
+      const uint32_t w = nib_word(nib[r], jj);
       lv[r][0] = lutc[(w & 0xFF) * kLutCopies];
       lv[r][1] = lutc[((w >> 8) & 0xFF) * kLutCopies];
       lv[r][2] = lutc[((w >> 16) & 0xFF) * kLutCopies];
@@ -297,7 +317,7 @@ __global__ void __launch_bounds__(NW * 64) qgemm_kernel(GemmArgs a) {
       if (q + 1 < kq_n) copy_quad(q + 1);
 
       const uint8_t* st = &ring[q % kStages][0];
-      const uint8_t* sb = st + kABytes + (tid >> 6) * kWaveBBytes;
+      const uint8_t* sb = st + kABytes + cg * kWaveBBytes;
       uint4 nib[kWaveRT];
       uint2 scl[kWaveRT];
 #pragma unroll
@@ -308,16 +328,17 @@ __global__ void __launch_bounds__(NW * 64) qgemm_kernel(GemmArgs a) {
       uint32_t lv[kWaveRT][4];
       lut_reads(nib, 0, lv);
 #pragma unroll
-      for (int j = 0; j < kTileBlocks; ++j) {
+      for (int jj = 0; jj < kBPW; ++jj) {
+        const int j = kp * kBPW + jj;  // block of the quad
         u32x4 bf[kWaveRT];
 #pragma unroll
         for (int r = 0; r < kWaveRT; ++r) {
-          const uint32_t sw = (j < 2) ? scl[r].x : scl[r].y;
-          const uint32_t dd = __builtin_amdgcn_perm(sw, sw, (j & 1) ? 0x03020302u : 0x01000100u);
+          const uint32_t sw = (KS == 1) ? ((jj < 2) ? scl[r].x : scl[r].y) : (kp ? scl[r].y : scl[r].x);
+          const uint32_t dd = __builtin_amdgcn_perm(sw, sw, (jj & 1) ? 0x03020302u : 0x01000100u);
 #pragma unroll
           for (int i = 0; i < 4; ++i) bf[r][i] = pk_mul_f16(lv[r][i], dd);
         }
-        if (j + 1 < kTileBlocks) lut_reads(nib, j + 1, lv);  // next block's reads under these MFMAs
+        if (jj + 1 < kBPW) lut_reads(nib, jj + 1, lv);  // next block's reads under these MFMAs
 #pragma unroll
         for (int mt = 0; mt < kMT; ++mt) {
           if (PARTIAL && mt >= nfr) break;  // fragment rows wholly past the tile's rows
@@ -331,6 +352,36 @@ __global__ void __launch_bounds__(NW * 64) qgemm_kernel(GemmArgs a) {
   if (nfr == kMT) main_loop(std::false_type{});
   else main_loop(std::true_type{});
 
+  if constexpr (KS == 2) {
+    // the column group's two partial sums: the kp = 1 wave hands its accumulators to its
+    // kp = 0 partner through the (now free) ring, half the fragment rows at a time; the
+    // sum is (blocks 0-1) + (blocks 2-3) of every quad, a fixed order
+    f32x4* red = reinterpret_cast<f32x4*>(&ring[0][0]);
+#pragma unroll
+    for (int half = 0; half < 2; ++half) {
+      __syncthreads();  // the ring is free (first half) / the partners have read (second)
+      if (kp == 1) {
+#pragma unroll
+        for (int ml = 0; ml < kMT / 2; ++ml)
+#pragma unroll
+          for (int r = 0; r < kWaveRT; ++r) red[((ml * kWaveRT + r) * kNC + cg) * 64 + lane] = acc[half * (kMT / 2) + ml][r];
+      }
+      __syncthreads();
+      if (kp == 0) {
+#pragma unroll
+        for (int ml = 0; ml < kMT / 2; ++ml)
+#pragma unroll
+          for (int r = 0; r < kWaveRT; ++r) {
+            const f32x4 o = red[((ml * kWaveRT + r) * kNC + cg) * 64 + lane];
+            f32x4& v = acc[half * (kMT / 2) + ml][r];
+#pragma unroll
+            for (int i = 0; i < 4; ++i) v[i] = v[i] + o[i];
+          }
+      }
+    }
+    if (kp != 0) return;  // the kp = 0 waves store
+  }
+
   // ---- epilogue: lane holds D[4g + i][c] of each (mt, r) fragment -------------------
   if (MODE == kGemmDense) {
 #pragma unroll
@@ -339,7 +390,7 @@ __global__ void __launch_bounds__(NW * 64) qgemm_kernel(GemmArgs a) {
       for (int i = 0; i < 4; ++i) {
         const int rr = 16 * mt + 4 * g + i;
         if (rr >= rows) continue;
-        float* crow = a.C + (m0 + rr) * a.ldc + n0 + 64 * wave + c;
+        float* crow = a.C + (m0 + rr) * a.ldc + n0 + 64 * cg + c;
 #pragma unroll
         for (int r = 0; r < kWaveRT; ++r)
           if (rt_ok[r]) crow[16 * r] = acc[mt][r][i];
@@ -351,7 +402,7 @@ __global__ void __launch_bounds__(NW * 64) qgemm_kernel(GemmArgs a) {
       for (int i = 0; i < 4; ++i) {
         const int rr = 16 * mt + 4 * g + i;
         if (rr >= rows) continue;
-        uint16_t* hrow = a.H + (seg0 + m0 + rr) * a.ldh + n0 + 32 * wave + c;
+        uint16_t* hrow = a.H + (seg0 + m0 + rr) * a.ldh + n0 + 32 * cg + c;
 #pragma unroll
         for (int r = 0; r < 2; ++r) {
           if (!rt_ok[r]) continue;
@@ -370,12 +421,12 @@ __global__ void __launch_bounds__(NW * 64) qgemm_kernel(GemmArgs a) {
         const int p = tile_pair[rr];
         const float gw = tile_gw[rr];
         if (a.atomic) {
-          float* orow = a.out + (int64_t)(p / a.top_k) * a.ldo + n0 + 64 * wave + c;
+          float* orow = a.out + (int64_t)(p / a.top_k) * a.ldo + n0 + 64 * cg + c;
 #pragma unroll
           for (int r = 0; r < kWaveRT; ++r)
             if (rt_ok[r]) atomicAdd(orow + 16 * r, gw * acc[mt][r][i]);
         } else {
-          float* yrow = a.C + (int64_t)p * a.ldc + n0 + 64 * wave + c;
+          float* yrow = a.C + (int64_t)p * a.ldc + n0 + 64 * cg + c;
 #pragma unroll
           for (int r = 0; r < kWaveRT; ++r)
             if (rt_ok[r]) yrow[16 * r] = gw * acc[mt][r][i];
@@ -384,12 +435,16 @@ __global__ void __launch_bounds__(NW * 64) qgemm_kernel(GemmArgs a) {
   }
 }
 
-constexpr int kDenseWaves = 4;    // long prompt: 128 x 256 tiles keep a 512-token chunk on ~224 CUs
-constexpr int kGroupedWaves = 8;  // MoE: 128 x 512 tiles (two waves per SIMD)
+// 8 waves (two per SIMD) in both uses.  The long prompt: 128 x 256 tiles, each quad's
+// blocks split between the two waves of a column group, so a 512-token chunk stays on
+// ~224 CUs.  The MoE products: 128 x 512 tiles, no split (twice the workgroups of the
+// split shape measured slower: each pays the tile's fill and epilogue).
+constexpr int kDenseWaves = 8, kDenseKS = 2;
+constexpr int kGroupedWaves = 8, kGroupedKS = 1;
 
 int launch_qgemm_dense(const uint8_t* packed, int64_t n, int64_t k, const uint16_t* x, int64_t m,
                        int64_t ldx, float* y, int64_t ldy, int64_t chunk, hipStream_t s) {
-  constexpr int kBN = Shape<kDenseWaves>::kBN;
+  constexpr int kBN = Shape<kDenseWaves, kDenseKS>::kBN;
   if (chunk <= 0) chunk = m;
   for (int64_t c0 = 0; c0 < m; c0 += chunk) {
     GemmArgs a{};
@@ -402,25 +457,25 @@ int launch_qgemm_dense(const uint8_t* packed, int64_t n, int64_t k, const uint16
     a.C = y + c0 * ldy;
     a.ldc = ldy;
     const int64_t grid = round8(((a.M + kBM - 1) / kBM) * ((n + kBN - 1) / kBN));
-    hipLaunchKernelGGL((qgemm_kernel<kGemmDense, kDenseWaves>), dim3((unsigned)grid), dim3(64 * kDenseWaves), 0,
-                       s, a);
+    hipLaunchKernelGGL((qgemm_kernel<kGemmDense, kDenseWaves, kDenseKS>), dim3((unsigned)grid),
+                       dim3(64 * kDenseWaves), 0, s, a);
     if (int e = check_launch("qgemm_kernel<dense>")) return e;
   }
   return 0;
 }
 
 int launch_qgemm_grouped(int mode, GemmArgs a, int64_t max_tiles, hipStream_t s) {
-  constexpr int kBN = Shape<kGroupedWaves>::kBN;
+  constexpr int kBN = Shape<kGroupedWaves, kGroupedKS>::kBN;
   // GATEUP: a workgroup covers kBN/2 intermediate columns (gate and up rows side by side)
   a.n_tiles_n = (mode == kGemmGateUp) ? (a.N + kBN / 2 - 1) / (kBN / 2) : (a.N + kBN - 1) / kBN;
   const int64_t grid = round8(max_tiles * a.n_tiles_n) + 8;  // + the rounding of the full-tile range
   if (grid == 0) return 0;
   if (mode == kGemmGateUp)
-    hipLaunchKernelGGL((qgemm_kernel<kGemmGateUp, kGroupedWaves>), dim3((unsigned)grid), dim3(64 * kGroupedWaves),
-                       0, s, a);
+    hipLaunchKernelGGL((qgemm_kernel<kGemmGateUp, kGroupedWaves, kGroupedKS>), dim3((unsigned)grid),
+                       dim3(64 * kGroupedWaves), 0, s, a);
   else
-    hipLaunchKernelGGL((qgemm_kernel<kGemmDown, kGroupedWaves>), dim3((unsigned)grid), dim3(64 * kGroupedWaves), 0,
-                       s, a);
+    hipLaunchKernelGGL((qgemm_kernel<kGemmDown, kGroupedWaves, kGroupedKS>), dim3((unsigned)grid),
+                       dim3(64 * kGroupedWaves), 0, s, a);
   return check_launch(mode == kGemmGateUp ? "qgemm_kernel<gateup>" : "qgemm_kernel<down>");
 }
 
