@@ -11,14 +11,15 @@
 //           scales by the pair's gate weight and writes the pair's row (or adds it
 //           atomically into the token's output).
 //
-// Tiling (workgroup = 8 waves, two per SIMD; K walked in 4-block quads):
-//   * each wave owns 128 x 64 outputs (fp32 accumulators in AGPRs).  The MoE products
-//     use 128 x 512 tiles (8 column groups of 64 weight rows).  The long prompt uses
-//     128 x 256 tiles: 4 column groups, the two waves of a group multiply blocks 0-1
-//     and 2-3 of each quad and their sums are added once after the loop;
-//   * a ring of 2 LDS stages, each holding one quad of the workgroup's operands and
-//     filled one quad ahead, straight from global memory with global_load_lds (no
-//     operand passes through VGPRs on its way in):
+// Tiling (K walked in 4-block quads; each wave owns 128 x 64 outputs, fp32 accumulators):
+//   * the long prompt: 8 waves (two per SIMD), 128 x 256 tiles: 4 column groups of 64
+//     weight rows, the two waves of a group multiply blocks 0-1 and 2-3 of each quad and
+//     their sums are added once after the loop; a ring of 2 LDS stages filled one quad
+//     ahead;
+//   * the MoE products: 4 waves, 128 x 256 tiles, a ring of one stage refilled after
+//     each quad; two workgroups share a CU and cover each other's waits;
+//   * each stage holds one quad of the workgroup's operands, copied straight from
+//     global memory with global_load_lds (no operand passes through VGPRs on its way in):
 //       activations  32 KiB: every 16-row x 32-k fragment in matrix-core A order
 //                    (lane l = 16g + r holds row r, elements 8g..8g+7), one
 //                    dwordx4 copy per fragment, the 32 fragments split over the waves;
@@ -34,7 +35,8 @@
 // the ring stages apart, does not drain every copy in flight before each LDS read; the
 // kernel waits for them itself: per quad one s_waitcnt for this wave's copies of the
 // quad, then one workgroup barrier (the quad is complete for everyone, and the stage
-// filled next is no longer read by anyone).
+// filled next is no longer read by anyone; a one-stage ring takes a second barrier
+// after the quad's MFMAs before it is refilled).
 #include <type_traits>
 
 #include "common.hpp"
@@ -46,15 +48,16 @@ namespace iq4 {
 constexpr int kBM = 128;                 // rows of A per workgroup
 constexpr int kWaveRT = 4;               // packed row tiles (16 rows) per wave
 constexpr int kMT = kBM / 16;            // 8 fragment rows of A
-constexpr int kStages = 2;               // quads in the ring (filled one quad ahead)
 constexpr int kABytes = kTileBlocks * kMT * 1024;                        // 32 KiB
 constexpr int kWaveBBytes = kWaveRT * (kTileNibbleBytes + kTileScaleBytes);  // 4.5 KiB
 
 // Shape of a workgroup of NW waves in NW / KS column groups of 64 weight rows; the KS
 // waves of a column group split each quad's blocks between them (KS = 2: blocks 0-1 and
 // 2-3), their partial sums added once after the loop.  One A quad is shared by all.
-template <int NW, int KS>
+template <int NW, int KS, int ST>
 struct Shape {
+  static constexpr int kStages = ST;  // quads in the ring: 2 = filled one quad ahead; 1 = refilled
+                                      // after each quad (two workgroups per CU overlap instead)
   static constexpr int kNC = NW / KS;                                   // column groups
   static constexpr int kBN = kNC * kWaveRT * kTileRows;                 // weight rows per workgroup
   static constexpr int kStageBytes = kABytes + kNC * kWaveBBytes;       // one quad of operands
@@ -64,9 +67,12 @@ struct Shape {
   static constexpr int kCopiesPerQuad = kAPerWave + kNibPerWave + kSclPerWave;
   static constexpr int kBlocksPerWave = kTileBlocks / KS;              // blocks of a quad each wave multiplies
   // replicas of the level table (fewer bank conflicts), as many as the LDS left allows
-  static constexpr int kLutCopies = (kNC == 4) ? 32 : 16;
+  static constexpr int kLutCopies = (ST == 1) ? 16 : (kNC == 4) ? 32 : 16;
   static_assert(KS == 1 || KS == 2, "K split");
-  static_assert(kStages * kStageBytes + 256 * 4 * kLutCopies + 2048 <= 160 * 1024, "LDS budget");
+  static_assert(ST == 1 || ST == 2, "ring depth");
+  static constexpr bool kTwoPerCU = (ST == 1);  // two workgroups share a CU
+  static_assert(kStages * kStageBytes + 256 * 4 * kLutCopies + 2048 <= (kTwoPerCU ? 80 : 160) * 1024,
+                "LDS budget");
   static_assert(KS == 1 || (kMT / 2) * kWaveRT * kNC * 64 * 16 <= kStages * kStageBytes,
                 "the K-split reduction fits in the ring");
 };
@@ -141,9 +147,13 @@ __device__ __forceinline__ int64_t xcd_swizzle_grouped(int64_t b, int64_t G1, in
 
 static inline int64_t round8(int64_t g) { return (g + 7) / 8 * 8; }
 
-template <int MODE, int NW, int KS>
-__global__ void __launch_bounds__(NW * 64) qgemm_kernel(GemmArgs a) {
-  using S = Shape<NW, KS>;
+// waves per SIMD: NW / 4 per workgroup, times two where two workgroups share a CU
+template <int MODE, int NW, int KS, int ST>
+__global__ void __launch_bounds__(NW * 64)
+__attribute__((amdgpu_waves_per_eu((NW / 4) * (Shape<NW, KS, ST>::kTwoPerCU ? 2 : 1))))
+qgemm_kernel(GemmArgs a) {
+  using S = Shape<NW, KS, ST>;
+  constexpr int kStages = S::kStages;
   constexpr int kBN = S::kBN, kStageBytes = S::kStageBytes, kLutCopies = S::kLutCopies;
   constexpr int kAPerWave = S::kAPerWave, kCopiesPerQuad = S::kCopiesPerQuad, kNC = S::kNC;
   constexpr int kNibPerWave = S::kNibPerWave, kSclPerWave = S::kSclPerWave, kBPW = S::kBlocksPerWave;
@@ -276,12 +286,12 @@ __global__ void __launch_bounds__(NW * 64) qgemm_kernel(GemmArgs a) {
     for (int r = 0; r < kWaveRT; ++r) acc[i][r] = f32x4{0.f, 0.f, 0.f, 0.f};
 
   // index word of this wave's block jj (block kp * kBPW + jj of the quad) in a row tile
-  auto nib_word = [&](const uint4& nb, int jj) -> uint32_t {
+  auto nib_word = [&](const u32x4& nb, int jj) -> uint32_t {
     if (KS == 1) return (jj == 0) ? nb.x : (jj == 1) ? nb.y : (jj == 2) ? nb.z : nb.w;
     return kp ? (jj ? nb.w : nb.z) : (jj ? nb.y : nb.x);
   };
   // LUT values of one block: 16 independent LDS reads.
-  auto lut_reads = [&](const uint4 (&nib)[kWaveRT], int jj, uint32_t (&lv)[kWaveRT][4]) {
+  auto lut_reads = [&](const u32x4 (&nib)[kWaveRT], int jj, uint32_t (&lv)[kWaveRT][4]) {
 #pragma unroll
     for (int r = 0; r < kWaveRT; ++r) {
       const uint32_t w = nib_word(nib[r], jj);
@@ -292,8 +302,9 @@ __global__ void __launch_bounds__(NW * 64) qgemm_kernel(GemmArgs a) {
     }
   };
 
+  // the ring's first quads (a one-stage ring: quad 0, refilled after each quad)
 #pragma unroll
-  for (int i = 0; i < kStages - 1; ++i)
+  for (int i = 0; i < (kStages > 1 ? kStages - 1 : 1); ++i)
     if (i < kq_n) copy_quad(i);
   if (MODE == kGemmDown && tid < rows) {
     // the epilogue's per-row pair id and gate weight, fetched once per tile (after the
@@ -311,19 +322,18 @@ __global__ void __launch_bounds__(NW * 64) qgemm_kernel(GemmArgs a) {
     constexpr bool PARTIAL = decltype(partial_tag)::value;
     for (int q = 0; q < kq_n; ++q) {
       // this wave's copies of quad q are the last it issued: wait for all of them
-      static_assert(kStages == 2, "the wait count assumes a ring filled one quad ahead");
       wait_vmcnt<0>();
       lds_barrier();  // quad q is in LDS for everyone; quad q-1's stage is free
-      if (q + 1 < kq_n) copy_quad(q + 1);
+      if (kStages == 2 && q + 1 < kq_n) copy_quad(q + 1);
 
       const uint8_t* st = &ring[q % kStages][0];
       const uint8_t* sb = st + kABytes + cg * kWaveBBytes;
-      uint4 nib[kWaveRT];
-      uint2 scl[kWaveRT];
+      u32x4 nib[kWaveRT];
+      u32x2 scl[kWaveRT];
 #pragma unroll
       for (int r = 0; r < kWaveRT; ++r) {
-        nib[r] = *reinterpret_cast<const uint4*>(sb + r * kTileNibbleBytes + lane * 16);
-        scl[r] = *reinterpret_cast<const uint2*>(sb + kWaveRT * kTileNibbleBytes + r * kTileScaleBytes + c * 8);
+        nib[r] = *reinterpret_cast<const u32x4*>(sb + r * kTileNibbleBytes + lane * 16);
+        scl[r] = *reinterpret_cast<const u32x2*>(sb + kWaveRT * kTileNibbleBytes + r * kTileScaleBytes + c * 8);
       }
       uint32_t lv[kWaveRT][4];
       lut_reads(nib, 0, lv);
@@ -339,13 +349,31 @@ __global__ void __launch_bounds__(NW * 64) qgemm_kernel(GemmArgs a) {
           for (int i = 0; i < 4; ++i) bf[r][i] = pk_mul_f16(lv[r][i], dd);
         }
         if (jj + 1 < kBPW) lut_reads(nib, jj + 1, lv);  // next block's reads under these MFMAs
+        const uint8_t* ab = st + j * kMT * 1024 + lane * 16;  // the block's A fragments
+        if constexpr (!PARTIAL) {
+          // all 8 fragment reads issued before the first MFMA (the scheduler otherwise keeps
+          // two in flight and the matrix core waits on each pair)
+          u32x4 af[kMT];
 #pragma unroll
-        for (int mt = 0; mt < kMT; ++mt) {
-          if (PARTIAL && mt >= nfr) break;  // fragment rows wholly past the tile's rows
-          const u32x4 af = *reinterpret_cast<const u32x4*>(st + (j * kMT + mt) * 1024 + lane * 16);
+          for (int mt = 0; mt < kMT; ++mt) af[mt] = *reinterpret_cast<const u32x4*>(ab + mt * 1024);
+          __builtin_amdgcn_sched_barrier(0);
 #pragma unroll
-          for (int r = 0; r < kWaveRT; ++r) acc[mt][r] = mfma_f16(af, bf[r], acc[mt][r]);
+          for (int mt = 0; mt < kMT; ++mt)
+#pragma unroll
+            for (int r = 0; r < kWaveRT; ++r) acc[mt][r] = mfma_f16(af[mt], bf[r], acc[mt][r]);
+        } else {
+#pragma unroll
+          for (int mt = 0; mt < kMT; ++mt) {
+            if (mt >= nfr) break;  // fragment rows wholly past the tile's rows
+            const u32x4 af = *reinterpret_cast<const u32x4*>(ab + mt * 1024);
+#pragma unroll
+            for (int r = 0; r < kWaveRT; ++r) acc[mt][r] = mfma_f16(af, bf[r], acc[mt][r]);
+          }
         }
+      }
+      if (kStages == 1 && q + 1 < kq_n) {
+        lds_barrier();  // everyone is done reading the stage
+        copy_quad(q + 1);
       }
     }
   };
@@ -435,16 +463,18 @@ __global__ void __launch_bounds__(NW * 64) qgemm_kernel(GemmArgs a) {
   }
 }
 
-// 8 waves (two per SIMD) in both uses.  The long prompt: 128 x 256 tiles, each quad's
-// blocks split between the two waves of a column group, so a 512-token chunk stays on
-// ~224 CUs.  The MoE products: 128 x 512 tiles, no split (twice the workgroups of the
-// split shape measured slower: each pays the tile's fill and epilogue).
-constexpr int kDenseWaves = 8, kDenseKS = 2;
-constexpr int kGroupedWaves = 8, kGroupedKS = 1;
+// The long prompt: 8 waves (two per SIMD), 128 x 256 tiles, each quad's blocks split
+// between the two waves of a column group, a two-stage ring; a 512-token chunk stays on
+// ~224 CUs.  The MoE products (short K, many small tiles): 4 waves, 128 x 256 tiles, a
+// one-stage ring, so two workgroups share a CU and one's copies, fill and epilogue run
+// under the other's MFMAs.
+constexpr int kDenseWaves = 8, kDenseKS = 2, kDenseST = 2;
+constexpr int kGuWaves = 4, kGuKS = 1, kGuST = 1;
+constexpr int kDnWaves = 4, kDnKS = 1, kDnST = 1;
 
 int launch_qgemm_dense(const uint8_t* packed, int64_t n, int64_t k, const uint16_t* x, int64_t m,
                        int64_t ldx, float* y, int64_t ldy, int64_t chunk, hipStream_t s) {
-  constexpr int kBN = Shape<kDenseWaves, kDenseKS>::kBN;
+  constexpr int kBN = Shape<kDenseWaves, kDenseKS, kDenseST>::kBN;
   if (chunk <= 0) chunk = m;
   for (int64_t c0 = 0; c0 < m; c0 += chunk) {
     GemmArgs a{};
@@ -457,26 +487,27 @@ int launch_qgemm_dense(const uint8_t* packed, int64_t n, int64_t k, const uint16
     a.C = y + c0 * ldy;
     a.ldc = ldy;
     const int64_t grid = round8(((a.M + kBM - 1) / kBM) * ((n + kBN - 1) / kBN));
-    hipLaunchKernelGGL((qgemm_kernel<kGemmDense, kDenseWaves, kDenseKS>), dim3((unsigned)grid),
+    hipLaunchKernelGGL((qgemm_kernel<kGemmDense, kDenseWaves, kDenseKS, kDenseST>), dim3((unsigned)grid),
                        dim3(64 * kDenseWaves), 0, s, a);
     if (int e = check_launch("qgemm_kernel<dense>")) return e;
   }
   return 0;
 }
 
-int launch_qgemm_grouped(int mode, GemmArgs a, int64_t max_tiles, hipStream_t s) {
-  constexpr int kBN = Shape<kGroupedWaves, kGroupedKS>::kBN;
+template <int MODE, int NW, int KS, int ST>
+static int launch_grouped(GemmArgs a, int64_t max_tiles, hipStream_t s) {
+  constexpr int kBN = Shape<NW, KS, ST>::kBN;
   // GATEUP: a workgroup covers kBN/2 intermediate columns (gate and up rows side by side)
-  a.n_tiles_n = (mode == kGemmGateUp) ? (a.N + kBN / 2 - 1) / (kBN / 2) : (a.N + kBN - 1) / kBN;
+  a.n_tiles_n = (MODE == kGemmGateUp) ? (a.N + kBN / 2 - 1) / (kBN / 2) : (a.N + kBN - 1) / kBN;
   const int64_t grid = round8(max_tiles * a.n_tiles_n) + 8;  // + the rounding of the full-tile range
   if (grid == 0) return 0;
-  if (mode == kGemmGateUp)
-    hipLaunchKernelGGL((qgemm_kernel<kGemmGateUp, kGroupedWaves, kGroupedKS>), dim3((unsigned)grid),
-                       dim3(64 * kGroupedWaves), 0, s, a);
-  else
-    hipLaunchKernelGGL((qgemm_kernel<kGemmDown, kGroupedWaves, kGroupedKS>), dim3((unsigned)grid),
-                       dim3(64 * kGroupedWaves), 0, s, a);
-  return check_launch(mode == kGemmGateUp ? "qgemm_kernel<gateup>" : "qgemm_kernel<down>");
+  hipLaunchKernelGGL((qgemm_kernel<MODE, NW, KS, ST>), dim3((unsigned)grid), dim3(64 * NW), 0, s, a);
+  return check_launch(MODE == kGemmGateUp ? "qgemm_kernel<gateup>" : "qgemm_kernel<down>");
+}
+
+int launch_qgemm_grouped(int mode, GemmArgs a, int64_t max_tiles, hipStream_t s) {
+  if (mode == kGemmGateUp) return launch_grouped<kGemmGateUp, kGuWaves, kGuKS, kGuST>(a, max_tiles, s);
+  return launch_grouped<kGemmDown, kDnWaves, kDnKS, kDnST>(a, max_tiles, s);
 }
 
 }  // namespace iq4
