@@ -16,10 +16,12 @@
 //     weight rows, the two waves of a group multiply blocks 0-1 and 2-3 of each quad and
 //     their sums are added once after the loop; a ring of 2 LDS stages filled one quad
 //     ahead;
-//   * the MoE products: 4 waves, 128 x 256 tiles, a ring of one stage refilled after
-//     each quad; two workgroups share a CU and cover each other's waits;
-//   * each stage holds one quad of the workgroup's operands, copied straight from
-//     global memory with global_load_lds (no operand passes through VGPRs on its way in):
+//   * the MoE products: 4 waves, 128 x 256 tiles; the activations in one stage refilled
+//     after each quad, the weight tiles in two filled one quad ahead; two workgroups
+//     share a CU and cover each other's waits;
+//   * a stage holds one quad of the workgroup's activations or weight tiles, copied
+//     straight from global memory with global_load_lds (no operand passes through VGPRs
+//     on its way in):
 //       activations  32 KiB: every 16-row x 32-k fragment in matrix-core A order
 //                    (lane l = 16g + r holds row r, elements 8g..8g+7), one
 //                    dwordx4 copy per fragment, the 32 fragments split over the waves;
@@ -29,8 +31,8 @@
 //     (replicated, each lane reading its own copy) gives two binary16 levels per index
 //     byte, one packed binary16 multiply by the block scale gives the binary16
 //     rounding of the exact decoded weight.  No decoded weight goes through LDS or HBM;
-//   * per block a wave issues 8 x 4 MFMAs against 8 A-fragment reads; the next block's
-//     16 table reads are issued under the current block's MFMAs.
+//   * per block a wave issues its 16 table reads for the next block and its 8 A-fragment
+//     reads, then 8 x 4 MFMAs (the table reads complete under them).
 // The copies are issued from inline assembly so that the compiler, which cannot tell
 // the ring stages apart, does not drain every copy in flight before each LDS read; the
 // kernel waits for them itself: per quad one s_waitcnt for this wave's copies of the
@@ -54,27 +56,26 @@ constexpr int kWaveBBytes = kWaveRT * (kTileNibbleBytes + kTileScaleBytes);  // 
 // Shape of a workgroup of NW waves in NW / KS column groups of 64 weight rows; the KS
 // waves of a column group split each quad's blocks between them (KS = 2: blocks 0-1 and
 // 2-3), their partial sums added once after the loop.  One A quad is shared by all.
-template <int NW, int KS, int ST>
+// SA, SB: quads of activations and of weights held in LDS.  2 = filled one quad ahead;
+// 1 = refilled after each quad (two workgroups share a CU and cover each other's waits).
+template <int NW, int KS, int SA, int SB>
 struct Shape {
-  static constexpr int kStages = ST;  // quads in the ring: 2 = filled one quad ahead; 1 = refilled
-                                      // after each quad (two workgroups per CU overlap instead)
   static constexpr int kNC = NW / KS;                                   // column groups
   static constexpr int kBN = kNC * kWaveRT * kTileRows;                 // weight rows per workgroup
-  static constexpr int kStageBytes = kABytes + kNC * kWaveBBytes;       // one quad of operands
+  static constexpr int kBStageBytes = kNC * kWaveBBytes;                // one quad of weight tiles
   static constexpr int kAPerWave = kTileBlocks * kMT / NW;              // A fragments each wave copies
   static constexpr int kNibPerWave = kWaveRT / KS;                      // index tiles each wave copies
   static constexpr int kSclPerWave = 2 / KS;                            // scale copies each wave issues
-  static constexpr int kCopiesPerQuad = kAPerWave + kNibPerWave + kSclPerWave;
   static constexpr int kBlocksPerWave = kTileBlocks / KS;              // blocks of a quad each wave multiplies
   // replicas of the level table (fewer bank conflicts), as many as the LDS left allows
-  static constexpr int kLutCopies = (ST == 1) ? 16 : (kNC == 4) ? 32 : 16;
+  static constexpr bool kTwoPerCU = (SA == 1);  // two workgroups share a CU
+  static constexpr int kLutCopies = kTwoPerCU ? (SB == 1 ? 16 : 8) : (kNC == 4) ? 32 : 16;
   static_assert(KS == 1 || KS == 2, "K split");
-  static_assert(ST == 1 || ST == 2, "ring depth");
-  static constexpr bool kTwoPerCU = (ST == 1);  // two workgroups share a CU
-  static_assert(kStages * kStageBytes + 256 * 4 * kLutCopies + 2048 <= (kTwoPerCU ? 80 : 160) * 1024,
+  static_assert((SA == 1 || SA == 2) && (SB == 1 || SB == 2), "ring depth");
+  static_assert(SA * kABytes + SB * kBStageBytes + 256 * 4 * kLutCopies + 1024 <= (kTwoPerCU ? 80 : 160) * 1024,
                 "LDS budget");
-  static_assert(KS == 1 || (kMT / 2) * kWaveRT * kNC * 64 * 16 <= kStages * kStageBytes,
-                "the K-split reduction fits in the ring");
+  static_assert(KS == 1 || (kMT / 2) * kWaveRT * kNC * 64 * 16 <= SA * kABytes,
+                "the K-split reduction fits in the activation ring");
 };
 
 __device__ __forceinline__ uint32_t f16_of_level(int c) {
@@ -148,16 +149,16 @@ __device__ __forceinline__ int64_t xcd_swizzle_grouped(int64_t b, int64_t G1, in
 static inline int64_t round8(int64_t g) { return (g + 7) / 8 * 8; }
 
 // waves per SIMD: NW / 4 per workgroup, times two where two workgroups share a CU
-template <int MODE, int NW, int KS, int ST>
+template <int MODE, int NW, int KS, int SA, int SB>
 __global__ void __launch_bounds__(NW * 64)
-__attribute__((amdgpu_waves_per_eu((NW / 4) * (Shape<NW, KS, ST>::kTwoPerCU ? 2 : 1))))
+__attribute__((amdgpu_waves_per_eu((NW / 4) * (Shape<NW, KS, SA, SB>::kTwoPerCU ? 2 : 1))))
 qgemm_kernel(GemmArgs a) {
-  using S = Shape<NW, KS, ST>;
-  constexpr int kStages = S::kStages;
-  constexpr int kBN = S::kBN, kStageBytes = S::kStageBytes, kLutCopies = S::kLutCopies;
-  constexpr int kAPerWave = S::kAPerWave, kCopiesPerQuad = S::kCopiesPerQuad, kNC = S::kNC;
+  using S = Shape<NW, KS, SA, SB>;
+  constexpr int kBN = S::kBN, kBStageBytes = S::kBStageBytes, kLutCopies = S::kLutCopies;
+  constexpr int kAPerWave = S::kAPerWave, kNC = S::kNC;
   constexpr int kNibPerWave = S::kNibPerWave, kSclPerWave = S::kSclPerWave, kBPW = S::kBlocksPerWave;
-  __shared__ __attribute__((aligned(1024))) uint8_t ring[kStages][kStageBytes];
+  __shared__ __attribute__((aligned(1024))) uint8_t ring_a[SA][kABytes];
+  __shared__ __attribute__((aligned(1024))) uint8_t ring_b[SB][kBStageBytes];
   __shared__ uint32_t lut[256 * kLutCopies];  // entry e of copy c at e * kLutCopies + c
   __shared__ int32_t tile_pair[kBM];          // DOWN: pair id and gate weight of each row
   __shared__ float tile_gw[kBM];
@@ -211,24 +212,24 @@ qgemm_kernel(GemmArgs a) {
   // multiplies only these; the copies still bring all rows so the wait counts hold)
   const int nfr = __builtin_amdgcn_readfirstlane((int)((rows + 15) / 16));
   const int64_t nib_bytes = a.N * (a.K / kQK) * kNibbleBytes;
-  const uint32_t ring0 = lds_addr(&ring[0][0]);
+  const uint32_t ring_a0 = lds_addr(&ring_a[0][0]), ring_b0 = lds_addr(&ring_b[0][0]);
 
   // ---- activation rows this lane copies ---------------------------------------------
   // The quad's 32 fragments f = 8 j + mt (block j, fragment row mt) are split evenly over
   // the waves: wave w copies f = w * kAPerWave .. +kAPerWave-1 (one block), lane l = 16g + r
   // bringing row r of the fragment row, elements 8g .. 8g+7.
   // (rows past the tile's valid rows repeat its last row: read in bounds, never stored)
-  const int f0 = wave * kAPerWave, ablk = f0 / kMT;
+  const int f0 = wave * kAPerWave;
   uint32_t a_off[kAPerWave];  // byte offsets from A (the launcher checks they fit in 32 bits)
 #pragma unroll
   for (int i = 0; i < kAPerWave; ++i) {
-    const int mt = (f0 + i) % kMT;
+    const int f = f0 + i, mt = f % kMT, j = f / kMT;
     const int64_t r = min((int64_t)(16 * mt + c), rows - 1);
     int64_t src_row;
     if (MODE == kGemmDense) src_row = m0 + r;
     else if (MODE == kGemmGateUp) src_row = a.pairs[seg0 + m0 + r] / a.top_k;  // token of the pair
     else src_row = seg0 + m0 + r;                                             // h in sorted order
-    a_off[i] = (uint32_t)(2 * (src_row * a.lda + 32 * ablk + 8 * g));
+    a_off[i] = (uint32_t)(2 * (src_row * a.lda + 32 * j + 8 * g));
   }
 
   // ---- weight row tiles of this wave's column group cg --------------------------------
@@ -258,25 +259,27 @@ qgemm_kernel(GemmArgs a) {
   for (int i = 0; i < 2; ++i)
     s_off[i] = (uint32_t)(4 * (lane & 31) + (lane >> 5) * (wtile0[2 * i + 1] - wtile0[2 * i]) * kTileScaleBytes);
 
-  // copy number `idx` (0 .. kCopiesPerQuad-1) of quad q into its stage: this wave's A
-  // fragments, then its share of its column group's index tiles and scale copies
-  auto copy_piece = [&](int q, int idx) {
-    const uint32_t st = ring0 + (uint32_t)((q % kStages) * kStageBytes);
-    const uint32_t sb = st + kABytes + cg * kWaveBBytes;
-    if (idx < kAPerWave) {
-      copy16(a.A + (int64_t)q * kTileK, a_off[idx], st + (uint32_t)((f0 + idx) * 1024));
-    } else if (idx < kAPerWave + kNibPerWave) {
-      const int r = kp * kNibPerWave + (idx - kAPerWave);
+  // quad q's copies into its stages: this wave's A fragments; its share of its column
+  // group's index tiles and scale copies
+  auto copy_a = [&](int q) {
+    const uint32_t st = ring_a0 + (uint32_t)((q % SA) * kABytes);
+#pragma unroll
+    for (int i = 0; i < kAPerWave; ++i)
+      copy16(a.A + (int64_t)q * kTileK, a_off[i], st + (uint32_t)((f0 + i) * 1024));
+  };
+  auto copy_b = [&](int q) {
+    const uint32_t sb = ring_b0 + (uint32_t)((q % SB) * kBStageBytes + cg * kWaveBBytes);
+#pragma unroll
+    for (int n = 0; n < kNibPerWave; ++n) {
+      const int r = kp * kNibPerWave + n;
       copy16(wbase[r] + (wtile0[r] + q) * kTileNibbleBytes, 16 * lane, sb + r * kTileNibbleBytes);
-    } else {
-      const int i = kp * kSclPerWave + (idx - kAPerWave - kNibPerWave);
+    }
+#pragma unroll
+    for (int n = 0; n < kSclPerWave; ++n) {
+      const int i = kp * kSclPerWave + n;
       copy4(wbase[2 * i] + nib_bytes + (wtile0[2 * i] + q) * kTileScaleBytes, s_off[i],
             sb + kWaveRT * kTileNibbleBytes + i * 2 * kTileScaleBytes);
     }
-  };
-  auto copy_quad = [&](int q) {
-#pragma unroll
-    for (int idx = 0; idx < kCopiesPerQuad; ++idx) copy_piece(q, idx);
   };
 
   f32x4 acc[kMT][kWaveRT];
@@ -302,10 +305,11 @@ qgemm_kernel(GemmArgs a) {
     }
   };
 
-  // the ring's first quads (a one-stage ring: quad 0, refilled after each quad)
-#pragma unroll
-  for (int i = 0; i < (kStages > 1 ? kStages - 1 : 1); ++i)
-    if (i < kq_n) copy_quad(i);
+  // quad 0 (a two-stage ring is filled one quad ahead; a one-stage ring after each quad)
+  if (kq_n > 0) {
+    copy_b(0);
+    copy_a(0);
+  }
   if (MODE == kGemmDown && tid < rows) {
     // the epilogue's per-row pair id and gate weight, fetched once per tile (after the
     // first copies are in flight) instead of as two dependent loads per stored row
@@ -323,11 +327,14 @@ qgemm_kernel(GemmArgs a) {
     for (int q = 0; q < kq_n; ++q) {
       // this wave's copies of quad q are the last it issued: wait for all of them
       wait_vmcnt<0>();
-      lds_barrier();  // quad q is in LDS for everyone; quad q-1's stage is free
-      if (kStages == 2 && q + 1 < kq_n) copy_quad(q + 1);
+      lds_barrier();  // quad q is in LDS for everyone; quad q-1's stages are free
+      if (q + 1 < kq_n) {
+        if (SB == 2) copy_b(q + 1);
+        if (SA == 2) copy_a(q + 1);
+      }
 
-      const uint8_t* st = &ring[q % kStages][0];
-      const uint8_t* sb = st + kABytes + cg * kWaveBBytes;
+      const uint8_t* st = &ring_a[q % SA][0];
+      const uint8_t* sb = &ring_b[q % SB][0] + cg * kWaveBBytes;
       u32x4 nib[kWaveRT];
       u32x2 scl[kWaveRT];
 #pragma unroll
@@ -371,9 +378,10 @@ qgemm_kernel(GemmArgs a) {
           }
         }
       }
-      if (kStages == 1 && q + 1 < kq_n) {
-        lds_barrier();  // everyone is done reading the stage
-        copy_quad(q + 1);
+      if ((SA == 1 || SB == 1) && q + 1 < kq_n) {
+        lds_barrier();  // everyone is done reading the one-stage ring(s)
+        if (SB == 1) copy_b(q + 1);
+        if (SA == 1) copy_a(q + 1);
       }
     }
   };
@@ -384,7 +392,7 @@ qgemm_kernel(GemmArgs a) {
     // the column group's two partial sums: the kp = 1 wave hands its accumulators to its
     // kp = 0 partner through the (now free) ring, half the fragment rows at a time; the
     // sum is (blocks 0-1) + (blocks 2-3) of every quad, a fixed order
-    f32x4* red = reinterpret_cast<f32x4*>(&ring[0][0]);
+    f32x4* red = reinterpret_cast<f32x4*>(&ring_a[0][0]);
 #pragma unroll
     for (int half = 0; half < 2; ++half) {
       __syncthreads();  // the ring is free (first half) / the partners have read (second)
@@ -464,17 +472,17 @@ qgemm_kernel(GemmArgs a) {
 }
 
 // The long prompt: 8 waves (two per SIMD), 128 x 256 tiles, each quad's blocks split
-// between the two waves of a column group, a two-stage ring; a 512-token chunk stays on
-// ~224 CUs.  The MoE products (short K, many small tiles): 4 waves, 128 x 256 tiles, a
-// one-stage ring, so two workgroups share a CU and one's copies, fill and epilogue run
-// under the other's MFMAs.
-constexpr int kDenseWaves = 8, kDenseKS = 2, kDenseST = 2;
-constexpr int kGuWaves = 4, kGuKS = 1, kGuST = 1;
-constexpr int kDnWaves = 4, kDnKS = 1, kDnST = 1;
+// between the two waves of a column group, two-stage rings; a 512-token chunk stays on
+// ~224 CUs.  The MoE products (short K, many small tiles): 4 waves, 128 x 256 tiles,
+// one activation stage and two weight stages (73 KiB with an 8-copy table), so two
+// workgroups share a CU and one's copies, fill and epilogue run under the other's MFMAs.
+constexpr int kDenseWaves = 8, kDenseKS = 2, kDenseSA = 2, kDenseSB = 2;
+constexpr int kGuWaves = 4, kGuKS = 1, kGuSA = 1, kGuSB = 2;
+constexpr int kDnWaves = 4, kDnKS = 1, kDnSA = 1, kDnSB = 2;
 
 int launch_qgemm_dense(const uint8_t* packed, int64_t n, int64_t k, const uint16_t* x, int64_t m,
                        int64_t ldx, float* y, int64_t ldy, int64_t chunk, hipStream_t s) {
-  constexpr int kBN = Shape<kDenseWaves, kDenseKS, kDenseST>::kBN;
+  constexpr int kBN = Shape<kDenseWaves, kDenseKS, kDenseSA, kDenseSB>::kBN;
   if (chunk <= 0) chunk = m;
   for (int64_t c0 = 0; c0 < m; c0 += chunk) {
     GemmArgs a{};
@@ -487,27 +495,27 @@ int launch_qgemm_dense(const uint8_t* packed, int64_t n, int64_t k, const uint16
     a.C = y + c0 * ldy;
     a.ldc = ldy;
     const int64_t grid = round8(((a.M + kBM - 1) / kBM) * ((n + kBN - 1) / kBN));
-    hipLaunchKernelGGL((qgemm_kernel<kGemmDense, kDenseWaves, kDenseKS, kDenseST>), dim3((unsigned)grid),
+    hipLaunchKernelGGL((qgemm_kernel<kGemmDense, kDenseWaves, kDenseKS, kDenseSA, kDenseSB>), dim3((unsigned)grid),
                        dim3(64 * kDenseWaves), 0, s, a);
     if (int e = check_launch("qgemm_kernel<dense>")) return e;
   }
   return 0;
 }
 
-template <int MODE, int NW, int KS, int ST>
+template <int MODE, int NW, int KS, int SA, int SB>
 static int launch_grouped(GemmArgs a, int64_t max_tiles, hipStream_t s) {
-  constexpr int kBN = Shape<NW, KS, ST>::kBN;
+  constexpr int kBN = Shape<NW, KS, SA, SB>::kBN;
   // GATEUP: a workgroup covers kBN/2 intermediate columns (gate and up rows side by side)
   a.n_tiles_n = (MODE == kGemmGateUp) ? (a.N + kBN / 2 - 1) / (kBN / 2) : (a.N + kBN - 1) / kBN;
   const int64_t grid = round8(max_tiles * a.n_tiles_n) + 8;  // + the rounding of the full-tile range
   if (grid == 0) return 0;
-  hipLaunchKernelGGL((qgemm_kernel<MODE, NW, KS, ST>), dim3((unsigned)grid), dim3(64 * NW), 0, s, a);
+  hipLaunchKernelGGL((qgemm_kernel<MODE, NW, KS, SA, SB>), dim3((unsigned)grid), dim3(64 * NW), 0, s, a);
   return check_launch(MODE == kGemmGateUp ? "qgemm_kernel<gateup>" : "qgemm_kernel<down>");
 }
 
 int launch_qgemm_grouped(int mode, GemmArgs a, int64_t max_tiles, hipStream_t s) {
-  if (mode == kGemmGateUp) return launch_grouped<kGemmGateUp, kGuWaves, kGuKS, kGuST>(a, max_tiles, s);
-  return launch_grouped<kGemmDown, kDnWaves, kDnKS, kDnST>(a, max_tiles, s);
+  if (mode == kGemmGateUp) return launch_grouped<kGemmGateUp, kGuWaves, kGuKS, kGuSA, kGuSB>(a, max_tiles, s);
+  return launch_grouped<kGemmDown, kDnWaves, kDnKS, kDnSA, kDnSB>(a, max_tiles, s);
 }
 
 }  // namespace iq4
