@@ -17,8 +17,9 @@
 //     their sums are added once after the loop; a ring of 2 LDS stages filled one quad
 //     ahead;
 //   * the MoE products: 4 waves, 128 x 256 tiles; the activations in one stage refilled
-//     after each quad, the weight tiles in two filled one quad ahead; two workgroups
-//     share a CU and cover each other's waits;
+//     block by block (block j of the next quad once every wave has multiplied block j
+//     of this one), the weight tiles in two stages filled one quad ahead; two
+//     workgroups share a CU and cover each other's waits;
 //   * a stage holds one quad of the workgroup's activations or weight tiles, copied
 //     straight from global memory with global_load_lds (no operand passes through VGPRs
 //     on its way in):
@@ -37,8 +38,8 @@
 // the ring stages apart, does not drain every copy in flight before each LDS read; the
 // kernel waits for them itself: per quad one s_waitcnt for this wave's copies of the
 // quad, then one workgroup barrier (the quad is complete for everyone, and the stage
-// filled next is no longer read by anyone; a one-stage ring takes a second barrier
-// after the quad's MFMAs before it is refilled).
+// filled next is no longer read by anyone).  The block-by-block refill instead waits
+// and meets at a barrier after each block, with the wait counts worked out below.
 #include <type_traits>
 
 #include "common.hpp"
@@ -58,7 +59,9 @@ constexpr int kWaveBBytes = kWaveRT * (kTileNibbleBytes + kTileScaleBytes);  // 
 // 2-3), their partial sums added once after the loop.  One A quad is shared by all.
 // SA, SB: quads of activations and of weights held in LDS.  2 = filled one quad ahead;
 // 1 = refilled after each quad (two workgroups share a CU and cover each other's waits).
-template <int NW, int KS, int SA, int SB>
+// PB (one activation stage): the stage is refilled block by block, block j of the next
+// quad as soon as every wave has multiplied block j of this one.
+template <int NW, int KS, int SA, int SB, bool PB = false>
 struct Shape {
   static constexpr int kNC = NW / KS;                                   // column groups
   static constexpr int kBN = kNC * kWaveRT * kTileRows;                 // weight rows per workgroup
@@ -72,6 +75,7 @@ struct Shape {
   static constexpr int kLutCopies = kTwoPerCU ? (SB == 1 ? 16 : 8) : (kNC == 4) ? 32 : 16;
   static_assert(KS == 1 || KS == 2, "K split");
   static_assert((SA == 1 || SA == 2) && (SB == 1 || SB == 2), "ring depth");
+  static_assert(!PB || (NW == 4 && KS == 1 && SA == 1 && SB == 2), "block refills: 4 waves, one A stage");
   static_assert(SA * kABytes + SB * kBStageBytes + 256 * 4 * kLutCopies + 1024 <= (kTwoPerCU ? 80 : 160) * 1024,
                 "LDS budget");
   static_assert(KS == 1 || (kMT / 2) * kWaveRT * kNC * 64 * 16 <= SA * kABytes,
@@ -149,11 +153,11 @@ __device__ __forceinline__ int64_t xcd_swizzle_grouped(int64_t b, int64_t G1, in
 static inline int64_t round8(int64_t g) { return (g + 7) / 8 * 8; }
 
 // waves per SIMD: NW / 4 per workgroup, times two where two workgroups share a CU
-template <int MODE, int NW, int KS, int SA, int SB>
+template <int MODE, int NW, int KS, int SA, int SB, bool PB>
 __global__ void __launch_bounds__(NW * 64)
-__attribute__((amdgpu_waves_per_eu((NW / 4) * (Shape<NW, KS, SA, SB>::kTwoPerCU ? 2 : 1))))
+__attribute__((amdgpu_waves_per_eu((NW / 4) * (Shape<NW, KS, SA, SB, PB>::kTwoPerCU ? 2 : 1))))
 qgemm_kernel(GemmArgs a) {
-  using S = Shape<NW, KS, SA, SB>;
+  using S = Shape<NW, KS, SA, SB, PB>;
   constexpr int kBN = S::kBN, kBStageBytes = S::kBStageBytes, kLutCopies = S::kLutCopies;
   constexpr int kAPerWave = S::kAPerWave, kNC = S::kNC;
   constexpr int kNibPerWave = S::kNibPerWave, kSclPerWave = S::kSclPerWave, kBPW = S::kBlocksPerWave;
@@ -217,13 +221,15 @@ qgemm_kernel(GemmArgs a) {
   // ---- activation rows this lane copies ---------------------------------------------
   // The quad's 32 fragments f = 8 j + mt (block j, fragment row mt) are split evenly over
   // the waves: wave w copies f = w * kAPerWave .. +kAPerWave-1 (one block), lane l = 16g + r
-  // bringing row r of the fragment row, elements 8g .. 8g+7.
+  // bringing row r of the fragment row, elements 8g .. 8g+7.  PB: copies 2j and 2j+1 of
+  // wave w are fragment rows 2w and 2w+1 of block j (each block spread over all waves).
   // (rows past the tile's valid rows repeat its last row: read in bounds, never stored)
   const int f0 = wave * kAPerWave;
+  auto a_frag = [&](int i) -> int { return PB ? kMT * (i >> 1) + 2 * wave + (i & 1) : f0 + i; };
   uint32_t a_off[kAPerWave];  // byte offsets from A (the launcher checks they fit in 32 bits)
 #pragma unroll
   for (int i = 0; i < kAPerWave; ++i) {
-    const int f = f0 + i, mt = f % kMT, j = f / kMT;
+    const int f = a_frag(i), mt = f % kMT, j = f / kMT;
     const int64_t r = min((int64_t)(16 * mt + c), rows - 1);
     int64_t src_row;
     if (MODE == kGemmDense) src_row = m0 + r;
@@ -265,7 +271,12 @@ qgemm_kernel(GemmArgs a) {
     const uint32_t st = ring_a0 + (uint32_t)((q % SA) * kABytes);
 #pragma unroll
     for (int i = 0; i < kAPerWave; ++i)
-      copy16(a.A + (int64_t)q * kTileK, a_off[i], st + (uint32_t)((f0 + i) * 1024));
+      copy16(a.A + (int64_t)q * kTileK, a_off[i], st + (uint32_t)(a_frag(i) * 1024));
+  };
+  auto copy_a_block = [&](int q, int j) {  // PB: this wave's 2 fragments of block j
+#pragma unroll
+    for (int i = 2 * j; i < 2 * j + 2; ++i)
+      copy16(a.A + (int64_t)q * kTileK, a_off[i], ring_a0 + (uint32_t)(a_frag(i) * 1024));
   };
   auto copy_b = [&](int q) {
     const uint32_t sb = ring_b0 + (uint32_t)((q % SB) * kBStageBytes + cg * kWaveBBytes);
@@ -308,7 +319,8 @@ qgemm_kernel(GemmArgs a) {
   // quad 0 (a two-stage ring is filled one quad ahead; a one-stage ring after each quad)
   if (kq_n > 0) {
     copy_b(0);
-    copy_a(0);
+    copy_a(0);  // (PB: blocks 0, 1, 2, 3 in this order)
+    if (PB && kq_n > 1) copy_b(1);
   }
   if (MODE == kGemmDown && tid < rows) {
     // the epilogue's per-row pair id and gate weight, fetched once per tile (after the
@@ -322,15 +334,27 @@ qgemm_kernel(GemmArgs a) {
   // branch in the unrolled body; a partial tile (an expert's or a chunk's last) skips the
   // fragment rows wholly past its rows (the copies still bring them, so the wait counts
   // hold).
+  // PB wait counts: this wave issues 2 activation copies per block and kBC weight copies
+  // per quad, in the order  ... blocks 1-3 of quad q, weights of q+1, blocks 0-3 of q+1
+  // (each after that block of q is multiplied), weights of q+2 ...
+  constexpr int kBC = kNibPerWave + kSclPerWave;
+  if constexpr (PB) {
+    // weights and block 0 of quad 0: younger are blocks 1-3 and the weights of quad 1
+    if (kq_n > 1) wait_vmcnt<6 + kBC>();
+    else wait_vmcnt<6>();
+    lds_barrier();
+  }
   auto main_loop = [&](auto partial_tag) {
     constexpr bool PARTIAL = decltype(partial_tag)::value;
     for (int q = 0; q < kq_n; ++q) {
-      // this wave's copies of quad q are the last it issued: wait for all of them
-      wait_vmcnt<0>();
-      lds_barrier();  // quad q is in LDS for everyone; quad q-1's stages are free
-      if (q + 1 < kq_n) {
-        if (SB == 2) copy_b(q + 1);
-        if (SA == 2) copy_a(q + 1);
+      if constexpr (!PB) {
+        // this wave's copies of quad q are the last it issued: wait for all of them
+        wait_vmcnt<0>();
+        lds_barrier();  // quad q is in LDS for everyone; quad q-1's stages are free
+        if (q + 1 < kq_n) {
+          if (SB == 2) copy_b(q + 1);
+          if (SA == 2) copy_a(q + 1);
+        }
       }
 
       const uint8_t* st = &ring_a[q % SA][0];
@@ -377,8 +401,23 @@ qgemm_kernel(GemmArgs a) {
             for (int r = 0; r < kWaveRT; ++r) acc[mt][r] = mfma_f16(af, bf[r], acc[mt][r]);
           }
         }
+        if constexpr (PB) {
+          // block jj + 1 of this quad (jj < 3), or block 0 and the weights of the next,
+          // must have landed; once every wave is past block jj, its slot takes block jj
+          // of the next quad
+          const bool more = q + 1 < kq_n;
+          if (jj < 3) {
+            if (more) wait_vmcnt<4 + kBC>();  // younger: 2 blocks' copies and one quad's weights
+            else wait_vmcnt<0>();
+          } else if (more) {
+            wait_vmcnt<4>();  // younger: blocks 1-2 of the next quad
+          }
+          if (jj < 3 || more) lds_barrier();
+          if (more) copy_a_block(q + 1, jj);
+          if (jj == 3 && q + 2 < kq_n) copy_b(q + 2);
+        }
       }
-      if ((SA == 1 || SB == 1) && q + 1 < kq_n) {
+      if (!PB && (SA == 1 || SB == 1) && q + 1 < kq_n) {
         lds_barrier();  // everyone is done reading the one-stage ring(s)
         if (SB == 1) copy_b(q + 1);
         if (SA == 1) copy_a(q + 1);
@@ -474,15 +513,18 @@ qgemm_kernel(GemmArgs a) {
 // The long prompt: 8 waves (two per SIMD), 128 x 256 tiles, each quad's blocks split
 // between the two waves of a column group, two-stage rings; a 512-token chunk stays on
 // ~224 CUs.  The MoE products (short K, many small tiles): 4 waves, 128 x 256 tiles,
-// one activation stage and two weight stages (73 KiB with an 8-copy table), so two
-// workgroups share a CU and one's copies, fill and epilogue run under the other's MFMAs.
+// one activation stage refilled block by block and two weight stages (77 KiB with an
+// 8-copy table), so two workgroups share a CU and one's copy waits, fill and epilogue
+// run under the other's MFMAs.
 constexpr int kDenseWaves = 8, kDenseKS = 2, kDenseSA = 2, kDenseSB = 2;
 constexpr int kGuWaves = 4, kGuKS = 1, kGuSA = 1, kGuSB = 2;
+constexpr bool kGuPB = true;
 constexpr int kDnWaves = 4, kDnKS = 1, kDnSA = 1, kDnSB = 2;
+constexpr bool kDnPB = true;
 
 int launch_qgemm_dense(const uint8_t* packed, int64_t n, int64_t k, const uint16_t* x, int64_t m,
                        int64_t ldx, float* y, int64_t ldy, int64_t chunk, hipStream_t s) {
-  constexpr int kBN = Shape<kDenseWaves, kDenseKS, kDenseSA, kDenseSB>::kBN;
+  constexpr int kBN = Shape<kDenseWaves, kDenseKS, kDenseSA, kDenseSB, false>::kBN;
   if (chunk <= 0) chunk = m;
   for (int64_t c0 = 0; c0 < m; c0 += chunk) {
     GemmArgs a{};
@@ -495,27 +537,27 @@ int launch_qgemm_dense(const uint8_t* packed, int64_t n, int64_t k, const uint16
     a.C = y + c0 * ldy;
     a.ldc = ldy;
     const int64_t grid = round8(((a.M + kBM - 1) / kBM) * ((n + kBN - 1) / kBN));
-    hipLaunchKernelGGL((qgemm_kernel<kGemmDense, kDenseWaves, kDenseKS, kDenseSA, kDenseSB>), dim3((unsigned)grid),
+    hipLaunchKernelGGL((qgemm_kernel<kGemmDense, kDenseWaves, kDenseKS, kDenseSA, kDenseSB, false>), dim3((unsigned)grid),
                        dim3(64 * kDenseWaves), 0, s, a);
     if (int e = check_launch("qgemm_kernel<dense>")) return e;
   }
   return 0;
 }
 
-template <int MODE, int NW, int KS, int SA, int SB>
+template <int MODE, int NW, int KS, int SA, int SB, bool PB>
 static int launch_grouped(GemmArgs a, int64_t max_tiles, hipStream_t s) {
-  constexpr int kBN = Shape<NW, KS, SA, SB>::kBN;
+  constexpr int kBN = Shape<NW, KS, SA, SB, PB>::kBN;
   // GATEUP: a workgroup covers kBN/2 intermediate columns (gate and up rows side by side)
   a.n_tiles_n = (MODE == kGemmGateUp) ? (a.N + kBN / 2 - 1) / (kBN / 2) : (a.N + kBN - 1) / kBN;
   const int64_t grid = round8(max_tiles * a.n_tiles_n) + 8;  // + the rounding of the full-tile range
   if (grid == 0) return 0;
-  hipLaunchKernelGGL((qgemm_kernel<MODE, NW, KS, SA, SB>), dim3((unsigned)grid), dim3(64 * NW), 0, s, a);
+  hipLaunchKernelGGL((qgemm_kernel<MODE, NW, KS, SA, SB, PB>), dim3((unsigned)grid), dim3(64 * NW), 0, s, a);
   return check_launch(MODE == kGemmGateUp ? "qgemm_kernel<gateup>" : "qgemm_kernel<down>");
 }
 
 int launch_qgemm_grouped(int mode, GemmArgs a, int64_t max_tiles, hipStream_t s) {
-  if (mode == kGemmGateUp) return launch_grouped<kGemmGateUp, kGuWaves, kGuKS, kGuSA, kGuSB>(a, max_tiles, s);
-  return launch_grouped<kGemmDown, kDnWaves, kDnKS, kDnSA, kDnSB>(a, max_tiles, s);
+  if (mode == kGemmGateUp) return launch_grouped<kGemmGateUp, kGuWaves, kGuKS, kGuSA, kGuSB, kGuPB>(a, max_tiles, s);
+  return launch_grouped<kGemmDown, kDnWaves, kDnKS, kDnSA, kDnSB, kDnPB>(a, max_tiles, s);
 }
 
 }  // namespace iq4
