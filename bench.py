@@ -42,12 +42,12 @@ N_BANKS = 8                 # expert banks the decode step rotates over
 # at the time: a kernel changed since then reports traffic null.  Commands and raw
 # figures: profiles/<name>.txt.
 MEASURED_TRAFFIC = {
-    "qmv_dense_4096x4096_T1-4": (9981504, "fc5aa085b65aa127", ("qmv.hip", "qmv.hpp", "common.hpp")),
-    "qmv_grouped_gateup_moe_decode_4tok": (55505052, "fc5aa085b65aa127", ("qmv.hip", "qmv.hpp", "common.hpp")),
-    "qmv_grouped_down_moe_decode_4tok": (28679035, "fc5aa085b65aa127", ("qmv.hip", "qmv.hpp", "common.hpp")),
-    "qgemm_gateup_moe_prefill_3256tok": (571779853, "a2845a35ef6cab04", ("gemm.hip", "gemm.hpp", "common.hpp")),
-    "qgemm_down_moe_prefill_3256tok": (506691382, "a2845a35ef6cab04", ("gemm.hip", "gemm.hpp", "common.hpp")),
-    "qgemm_dense_13056x4096x14336_chunk512": (94965238, "a2845a35ef6cab04", ("gemm.hip", "gemm.hpp", "common.hpp")),
+    "qmv_dense_4096x4096_T1-4": (9981496, "fc5aa085b65aa127", ("qmv.hip", "qmv.hpp", "common.hpp")),
+    "qmv_grouped_gateup_moe_decode_4tok": (55495591, "fc5aa085b65aa127", ("qmv.hip", "qmv.hpp", "common.hpp")),
+    "qmv_grouped_down_moe_decode_4tok": (28675033, "fc5aa085b65aa127", ("qmv.hip", "qmv.hpp", "common.hpp")),
+    "qgemm_gateup_moe_prefill_3256tok": (589939749, "b714e2dbb4e2f59c", ("gemm.hip", "gemm.hpp", "common.hpp")),
+    "qgemm_down_moe_prefill_3256tok": (507588057, "b714e2dbb4e2f59c", ("gemm.hip", "gemm.hpp", "common.hpp")),
+    "qgemm_dense_13056x4096x14336_chunk512": (94965181, "b714e2dbb4e2f59c", ("gemm.hip", "gemm.hpp", "common.hpp")),
 }
 
 

@@ -71,11 +71,11 @@ struct Shape {
   static constexpr int kSclPerWave = 2 / KS;                            // scale copies each wave issues
   static constexpr int kBlocksPerWave = kTileBlocks / KS;              // blocks of a quad each wave multiplies
   // replicas of the level table (fewer bank conflicts), as many as the LDS left allows
-  static constexpr bool kTwoPerCU = (SA == 1);  // two workgroups share a CU
+  static constexpr bool kTwoPerCU = (SA == 1 && NW == 4);  // two workgroups share a CU
   static constexpr int kLutCopies = kTwoPerCU ? (SB == 1 ? 16 : 8) : (kNC == 4) ? 32 : 16;
   static_assert(KS == 1 || KS == 2, "K split");
   static_assert((SA == 1 || SA == 2) && (SB == 1 || SB == 2), "ring depth");
-  static_assert(!PB || (NW == 4 && KS == 1 && SA == 1 && SB == 2), "block refills: 4 waves, one A stage");
+  static_assert(!PB || (KS == 1 && SA == 1 && SB == 2), "block refills: one A stage, two weight stages");
   static_assert(SA * kABytes + SB * kBStageBytes + 256 * 4 * kLutCopies + 1024 <= (kTwoPerCU ? 80 : 160) * 1024,
                 "LDS budget");
   static_assert(KS == 1 || (kMT / 2) * kWaveRT * kNC * 64 * 16 <= SA * kABytes,
@@ -221,11 +221,13 @@ qgemm_kernel(GemmArgs a) {
   // ---- activation rows this lane copies ---------------------------------------------
   // The quad's 32 fragments f = 8 j + mt (block j, fragment row mt) are split evenly over
   // the waves: wave w copies f = w * kAPerWave .. +kAPerWave-1 (one block), lane l = 16g + r
-  // bringing row r of the fragment row, elements 8g .. 8g+7.  PB: copies 2j and 2j+1 of
-  // wave w are fragment rows 2w and 2w+1 of block j (each block spread over all waves).
+  // bringing row r of the fragment row, elements 8g .. 8g+7.  PB: copies kAB j .. kAB j +
+  // kAB-1 of wave w are fragment rows kAB w .. of block j (each block spread over all
+  // waves).
   // (rows past the tile's valid rows repeat its last row: read in bounds, never stored)
   const int f0 = wave * kAPerWave;
-  auto a_frag = [&](int i) -> int { return PB ? kMT * (i >> 1) + 2 * wave + (i & 1) : f0 + i; };
+  constexpr int kAB = kMT / NW;  // PB: this wave's copies per block
+  auto a_frag = [&](int i) -> int { return PB ? kMT * (i / kAB) + kAB * wave + i % kAB : f0 + i; };
   uint32_t a_off[kAPerWave];  // byte offsets from A (the launcher checks they fit in 32 bits)
 #pragma unroll
   for (int i = 0; i < kAPerWave; ++i) {
@@ -273,9 +275,9 @@ qgemm_kernel(GemmArgs a) {
     for (int i = 0; i < kAPerWave; ++i)
       copy16(a.A + (int64_t)q * kTileK, a_off[i], st + (uint32_t)(a_frag(i) * 1024));
   };
-  auto copy_a_block = [&](int q, int j) {  // PB: this wave's 2 fragments of block j
+  auto copy_a_block = [&](int q, int j) {  // PB: this wave's kAB fragments of block j
 #pragma unroll
-    for (int i = 2 * j; i < 2 * j + 2; ++i)
+    for (int i = kAB * j; i < kAB * j + kAB; ++i)
       copy16(a.A + (int64_t)q * kTileK, a_off[i], ring_a0 + (uint32_t)(a_frag(i) * 1024));
   };
   auto copy_b = [&](int q) {
@@ -334,14 +336,14 @@ qgemm_kernel(GemmArgs a) {
   // branch in the unrolled body; a partial tile (an expert's or a chunk's last) skips the
   // fragment rows wholly past its rows (the copies still bring them, so the wait counts
   // hold).
-  // PB wait counts: this wave issues 2 activation copies per block and kBC weight copies
-  // per quad, in the order  ... blocks 1-3 of quad q, weights of q+1, blocks 0-3 of q+1
-  // (each after that block of q is multiplied), weights of q+2 ...
+  // PB wait counts: this wave issues kAB activation copies per block and kBC weight
+  // copies per quad, in the order  ... blocks 1-3 of quad q, weights of q+1, blocks 0-3
+  // of q+1 (each after that block of q is multiplied), weights of q+2 ...
   constexpr int kBC = kNibPerWave + kSclPerWave;
   if constexpr (PB) {
     // weights and block 0 of quad 0: younger are blocks 1-3 and the weights of quad 1
-    if (kq_n > 1) wait_vmcnt<6 + kBC>();
-    else wait_vmcnt<6>();
+    if (kq_n > 1) wait_vmcnt<3 * kAB + kBC>();
+    else wait_vmcnt<3 * kAB>();
     lds_barrier();
   }
   auto main_loop = [&](auto partial_tag) {
@@ -407,10 +409,10 @@ qgemm_kernel(GemmArgs a) {
           // of the next quad
           const bool more = q + 1 < kq_n;
           if (jj < 3) {
-            if (more) wait_vmcnt<4 + kBC>();  // younger: 2 blocks' copies and one quad's weights
+            if (more) wait_vmcnt<2 * kAB + kBC>();  // younger: 2 blocks' copies, one quad's weights
             else wait_vmcnt<0>();
           } else if (more) {
-            wait_vmcnt<4>();  // younger: blocks 1-2 of the next quad
+            wait_vmcnt<2 * kAB>();  // younger: blocks 1-2 of the next quad
           }
           if (jj < 3 || more) lds_barrier();
           if (more) copy_a_block(q + 1, jj);
