@@ -72,6 +72,14 @@ __device__ __forceinline__ float h2f(uint16_t h) {
   return __half2float(__ushort_as_half(h));
 }
 
+// Workgroup barrier that orders LDS only: it waits for no global load in flight (the
+// kernels wait for their loads explicitly or through data dependences).
+__device__ __forceinline__ void lds_barrier() {
+  __builtin_amdgcn_fence(__ATOMIC_RELEASE, "workgroup", "local");
+  __builtin_amdgcn_s_barrier();
+  __builtin_amdgcn_fence(__ATOMIC_ACQUIRE, "workgroup", "local");
+}
+
 // ---------------------------------------------------------------------------------
 // Host-side status handling.
 int set_error(int code, const char* fmt, ...);

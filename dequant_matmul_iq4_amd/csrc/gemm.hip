@@ -114,14 +114,6 @@ __device__ __forceinline__ void copy4(const void* base, uint32_t voff, uint32_t 
                : "memory");
 }
 
-// Workgroup barrier ordering LDS only: the copies are waited for explicitly, so the
-// barrier must not wait for every global load in flight.
-__device__ __forceinline__ void lds_barrier() {
-  __builtin_amdgcn_fence(__ATOMIC_RELEASE, "workgroup", "local");
-  __builtin_amdgcn_s_barrier();
-  __builtin_amdgcn_fence(__ATOMIC_ACQUIRE, "workgroup", "local");
-}
-
 // XCD-aware order of the workgroups: hardware deals workgroup b to XCD b mod 8, so
 // logical tile L = (b mod 8) * ceil(G / 8) + b / 8 gives each XCD a run of consecutive
 // logical tiles (which share activation tiles and weight row tiles) in its own L2.

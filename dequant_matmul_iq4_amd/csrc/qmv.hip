@@ -92,17 +92,37 @@ __device__ __forceinline__ const float* column_ptr(const QmvArgs& a, int mode, i
 constexpr int kFragRows = 12;
 constexpr int kFragBytes = 4 * kFragRows * 16;  // 768 B per block
 
-// Dense verify-window matvec: one workgroup per RG row tiles and K slice; each wave owns
-// WQ quads of the slice (registers and LDS sized to K).
-template <int MODE, int RG, int WQ>
-__global__ void __launch_bounds__(512) qmv_kernel(QmvArgs a) {
-  static_assert(MODE == kQmvDense, "the grouped modes have their own kernel");
-  constexpr int NMAT = (MODE == kQmvGateUp) ? 2 : 1;
-  constexpr int ROWS = RG * kTileRows;
+// Exact three-way bf16 split of two values, packed per part: word s holds part s of v0
+// in its low and of v1 in its high half (parts as split_part gives them).
+__device__ __forceinline__ void split_pair(float v0, float v1, uint32_t out[3]) {
+  const uint32_t u0 = __float_as_uint(v0), u1 = __float_as_uint(v1);
+  const float r0 = v0 - __uint_as_float(u0 & 0xFFFF0000u);  // exact (Sterbenz)
+  const float r1 = v1 - __uint_as_float(u1 & 0xFFFF0000u);
+  const uint32_t m0 = __float_as_uint(r0), m1 = __float_as_uint(r1);
+  const float l0 = r0 - __uint_as_float(m0 & 0xFFFF0000u);  // exact, <= 8 significant bits
+  const float l1 = r1 - __uint_as_float(m1 & 0xFFFF0000u);
+  out[0] = __builtin_amdgcn_perm(u1, u0, 0x07060302u);  // upper halves of (u0, u1)
+  out[1] = __builtin_amdgcn_perm(m1, m0, 0x07060302u);
+  out[2] = __builtin_amdgcn_perm(__float_as_uint(l1), __float_as_uint(l0), 0x07060302u);
+}
+
+// Byte-indexed level table, replicated so that a wave's lookups never conflict: entry e
+// of copy j sits at word 32 e + j, i.e. always in LDS bank j, and lane l reads copy
+// l mod 32.
+constexpr int kLutCopies = 32;
+
+// Dense verify-window matvec: one workgroup per row tile and K slice; each wave owns WQ
+// quads of the slice (registers and LDS sized to K).  The code of a pass is straight
+// line, in the order the data arrive: the pass's activations are requested first (L2
+// hot), then every weight of the wave; the activations are split and staged while the
+// weights stream in, and quad u is decoded and multiplied as soon as its own weights
+// have landed, so the arithmetic runs under the weight stream instead of after it.
+template <int WQ>
+__global__ void __launch_bounds__(512) qmv_dense_kernel(QmvArgs a) {
   constexpr int XBYTES = kWaves * WQ * 4 * kFragBytes;
-  static_assert(kWaves * NMAT * RG * 64 * 16 <= XBYTES, "reduction scratch does not fit");  // every wave's slot
-  __shared__ uint32_t lut[256];
+  __shared__ uint32_t lut[256 * kLutCopies];
   __shared__ __attribute__((aligned(16))) uint8_t xs[XBYTES + 256];  // + room for padding-row reads
+  __shared__ f32x4 red[kWaves * 64];
   __shared__ int s_last;
 
   const int tid = threadIdx.x;
@@ -112,32 +132,24 @@ __global__ void __launch_bounds__(512) qmv_kernel(QmvArgs a) {
   // ---- tile of this workgroup ---------------------------------------------------------
   const int64_t rg = blockIdx.x / a.S;
   const int slice = (int)(blockIdx.x % a.S);
-  const int64_t seg0 = 0, ncols = a.T;
-  const uint8_t* W[2] = {a.W0, a.W1};
+  const int64_t ncols = a.T;
   const int kq_n = a.kq_n;
   const int kqa = slice * a.slice_quads;                 // first quad of the slice
   const int nq_slice = min(a.slice_quads, kq_n - kqa);   // quads in the slice
   const int wq0 = wave * a.wave_quads;                   // this wave's quads (slice-relative)
   const int wq1 = min(wq0 + a.wave_quads, nq_slice);
+  const int wblk = 4 * (wq1 - wq0);                      // blocks of this wave (0 if idle)
+  uint8_t* xw = xs + wave * (4 * WQ) * kFragBytes;       // the wave's own staging region
 
-  // This wave's activations: blocks [4 * wq0, 4 * wq1) of the slice, staged by the wave
-  // itself into its own LDS region (no workgroup barrier before the products).
-  const int wblk = 4 * (wq1 - wq0);  // blocks of this wave (0 for an idle wave)
-  uint8_t* xw = xs + wave * (4 * WQ) * kFragBytes;
-  float4 xr[WQ][2];  // staging tasks: at most T * 16 WQ blocks-groups = 64 WQ, i.e. WQ per lane
+  float4 xr[WQ][2];
   auto load_x = [&](int64_t t0, int T) {  // tasks (column t, block, k-group gg), 64 lanes
     const int ntask = T * wblk * 4;
-    // the pass's column rows first, one uniform load per column (not one per task)
-    const float* col[kCols];
-#pragma unroll
-    for (int t = 0; t < kCols; ++t) col[t] = column_ptr(a, MODE, seg0, t0 + min(t, T - 1));
 #pragma unroll
     for (int i = 0; i < WQ; ++i) {
       const int task = lane + 64 * i;
       if (task < ntask) {
         const int gg = task & 3, bl = (task >> 2) % wblk, t = (task >> 2) / wblk;
-        const float* cp = (t == 0) ? col[0] : (t == 1) ? col[1] : (t == 2) ? col[2] : col[3];
-        const float* p = cp + ((int64_t)(kqa + wq0) * 4 + bl) * kQK + 8 * gg;
+        const float* p = a.x + (t0 + t) * a.ldx + ((int64_t)(kqa + wq0) * 4 + bl) * kQK + 8 * gg;
         xr[i][0] = *reinterpret_cast<const float4*>(p);
         xr[i][1] = *reinterpret_cast<const float4*>(p + 4);
       }
@@ -151,186 +163,147 @@ __global__ void __launch_bounds__(512) qmv_kernel(QmvArgs a) {
       if (task < ntask) {
         const int gg = task & 3, bl = (task >> 2) % wblk, t = (task >> 2) / wblk;
         const float4 xa = xr[i][0], xb = xr[i][1];
+        uint32_t p0[3], p1[3], p2[3], p3[3];
+        split_pair(xa.x, xa.y, p0);
+        split_pair(xa.z, xa.w, p1);
+        split_pair(xb.x, xb.y, p2);
+        split_pair(xb.z, xb.w, p3);
         uint8_t* dst = xw + (bl * 4 + gg) * (kFragRows * 16) + t * 16;
 #pragma unroll
-        for (int sp = 0; sp < 3; ++sp) {
-          uint4 f;
-          f.x = split_part(xa.x, sp) | (split_part(xa.y, sp) << 16);
-          f.y = split_part(xa.z, sp) | (split_part(xa.w, sp) << 16);
-          f.z = split_part(xb.x, sp) | (split_part(xb.y, sp) << 16);
-          f.w = split_part(xb.z, sp) | (split_part(xb.w, sp) << 16);
-          *reinterpret_cast<uint4*>(dst + sp * 4 * 16) = f;
-        }
-      }
-    }
-    // LDS accesses of one wave execute in order: the wave's reads below see these
-    // writes; this only keeps the compiler from moving them.
-    __builtin_amdgcn_fence(__ATOMIC_RELEASE, "wavefront");
-    __builtin_amdgcn_wave_barrier();
-    __builtin_amdgcn_fence(__ATOMIC_ACQUIRE, "wavefront");
-  };
-
-  uint4 nib[WQ][NMAT][RG];
-  uint2 scl[WQ][NMAT][RG];
-  auto load_w = [&](int u0, int u1) {
-#pragma unroll
-    for (int u = 0; u < WQ; ++u) {
-      if (u < u0 || u >= u1) continue;
-#pragma unroll
-      for (int r = 0; r < RG; ++r) {
-        const int64_t rt = min(rg * RG + r, a.nt - 1);
-#pragma unroll
-        for (int m = 0; m < NMAT; ++m) {
-          const uint8_t* tp = W[m] + (rt * kq_n + kqa) * kTileNibbleBytes + lane * 16;
-          const uint8_t* sp = W[m] + a.nibble_bytes + (rt * kq_n + kqa) * kTileScaleBytes + c * 8;
-          const int q = min(wq0 + u, max(wq1 - 1, 0));
-          nib[u][m][r] = *reinterpret_cast<const uint4*>(tp + (int64_t)q * kTileNibbleBytes);
-          scl[u][m][r] = *reinterpret_cast<const uint2*>(sp + (int64_t)q * kTileScaleBytes);
-        }
+        for (int sp = 0; sp < 3; ++sp)
+          *reinterpret_cast<uint4*>(dst + sp * 4 * 16) = uint4{p0[sp], p1[sp], p2[sp], p3[sp]};
       }
     }
   };
-  // the first quad's weights, then the activations (L2-hot, staged while the rest
-  // streams in), then the other quads
-  load_w(0, 1);
-  load_x(0, (int)min((int64_t)kCols, ncols));
-  load_w(1, WQ);
-  for (int i = tid; i < 256; i += blockDim.x)
-    lut[i] = bf16_of_level(level_of(i & 15)) | (bf16_of_level(level_of(i >> 4)) << 16);
-  __syncthreads();  // the table (LDS only: no wait on the loads in flight)
 
-  for (int64_t t0 = 0; t0 < ncols; t0 += kCols) {  // passes of up to 4 columns
-    const int T = (int)min((int64_t)kCols, ncols - t0);
-    if (t0 > 0) load_x(t0, T);
-    store_x(T);
+  uint4 nib[WQ];
+  uint2 scl[WQ];
+  const uint8_t* tp = a.W0 + (rg * kq_n + kqa) * kTileNibbleBytes + lane * 16;
+  const uint8_t* sp = a.W0 + a.nibble_bytes + (rg * kq_n + kqa) * kTileScaleBytes + c * 8;
 
-    // ---- the wave's quads: per quad, every LDS read first, then 4 x NMAT x RG
-    // independent MFMAs, then the scale FMAs.  Lanes of padding rows (s = 3 or a
-    // column >= T) read whatever lies there: an MFMA output row depends on its own A row
-    // only, and those rows are never used.
-    f32x4 acc[NMAT][RG];
+  // ---- requests: the first pass's activations, then every weight of the wave --------
+  const int T0 = (int)min((int64_t)kCols, ncols);
+  load_x(0, T0);
 #pragma unroll
-    for (int m = 0; m < NMAT; ++m)
+  for (int u = 0; u < WQ; ++u) {
+    const int q = min(wq0 + u, max(wq1 - 1, 0));  // idle slots reload a valid quad
+    nib[u] = *reinterpret_cast<const uint4*>(tp + (int64_t)q * kTileNibbleBytes);
+    scl[u] = *reinterpret_cast<const uint2*>(sp + (int64_t)q * kTileScaleBytes);
+  }
+  // ---- level table (every copy of entry e written by two threads, 16 words each) ------
+  for (int i = tid; i < 512; i += blockDim.x) {
+    const int e = i >> 1;
+    const uint32_t v = bf16_of_level(level_of(e & 15)) | (bf16_of_level(level_of(e >> 4)) << 16);
+    uint4* dst = reinterpret_cast<uint4*>(lut + e * kLutCopies + (i & 1) * 16);
 #pragma unroll
-      for (int r = 0; r < RG; ++r) acc[m][r] = f32x4{0.f, 0.f, 0.f, 0.f};
+    for (int w4 = 0; w4 < 4; ++w4) dst[w4] = uint4{v, v, v, v};
+  }
+  const uint32_t* lutl = lut + (lane & (kLutCopies - 1));
+
+  auto multiply = [&](f32x4& acc) {
+    acc = f32x4{0.f, 0.f, 0.f, 0.f};
 #pragma unroll
     for (int u = 0; u < WQ; ++u) {
       if (wq0 + u >= wq1) break;
-      u32x4 xf[4];
-      u32x4 bf[4][NMAT][RG];
+      __builtin_amdgcn_sched_barrier(0);  // quad u's work waits for quad u's weights only
+      u32x4 xf[4], bf[4];
 #pragma unroll
       for (int j = 0; j < 4; ++j) {
         const int bl = 4 * u + j;  // block within this wave's run
         xf[j] = *reinterpret_cast<const u32x4*>(xw + (bl * 4 + g) * (kFragRows * 16) + c * 16);
-#pragma unroll
-        for (int m = 0; m < NMAT; ++m)
-#pragma unroll
-          for (int r = 0; r < RG; ++r) {
-            const uint4 nb = nib[u][m][r];
-            const uint32_t w = (j == 0) ? nb.x : (j == 1) ? nb.y : (j == 2) ? nb.z : nb.w;
-            bf[j][m][r][0] = lut[w & 0xFF];
-            bf[j][m][r][1] = lut[(w >> 8) & 0xFF];
-            bf[j][m][r][2] = lut[(w >> 16) & 0xFF];
-            bf[j][m][r][3] = lut[w >> 24];
-          }
+        const uint32_t w = (j == 0) ? nib[u].x : (j == 1) ? nib[u].y : (j == 2) ? nib[u].z : nib[u].w;
+        bf[j][0] = lutl[(w & 0xFF) * kLutCopies];
+        bf[j][1] = lutl[((w >> 8) & 0xFF) * kLutCopies];
+        bf[j][2] = lutl[((w >> 16) & 0xFF) * kLutCopies];
+        bf[j][3] = lutl[(w >> 24) * kLutCopies];
       }
-      f32x4 prod[4][NMAT][RG];
+      f32x4 prod[4];
 #pragma unroll
-      for (int j = 0; j < 4; ++j)
+      for (int j = 0; j < 4; ++j) prod[j] = mfma_bf16(xf[j], bf[j], f32x4{0.f, 0.f, 0.f, 0.f});
 #pragma unroll
-        for (int m = 0; m < NMAT; ++m)
+      for (int j = 0; j < 4; ++j) {
+        const uint32_t sw = (j < 2) ? scl[u].x : scl[u].y;
+        const float d = h2f((uint16_t)(sw >> (16 * (j & 1))));
 #pragma unroll
-          for (int r = 0; r < RG; ++r) prod[j][m][r] = mfma_bf16(xf[j], bf[j][m][r], f32x4{0.f, 0.f, 0.f, 0.f});
-#pragma unroll
-      for (int j = 0; j < 4; ++j)
-#pragma unroll
-        for (int m = 0; m < NMAT; ++m)
-#pragma unroll
-          for (int r = 0; r < RG; ++r) {
-            const uint2 sc = scl[u][m][r];
-            const uint32_t sw = (j < 2) ? sc.x : sc.y;
-            const float d = h2f((uint16_t)(sw >> (16 * (j & 1))));
-#pragma unroll
-            for (int i = 0; i < 4; ++i) acc[m][r][i] = __builtin_fmaf(d, prod[j][m][r][i], acc[m][r][i]);
-          }
+        for (int i = 0; i < 4; ++i) acc[i] = __builtin_fmaf(d, prod[j][i], acc[i]);
+      }
     }
-    __syncthreads();  // every wave is done reading the staged activations
+  };
 
-    // ---- reduction over the waves' K runs, then the three parts ---------------------
-    // Lane (g, c) holds D[4g + i][c]: part s = g, column i, weight row c.
-    f32x4* red = reinterpret_cast<f32x4*>(xs);
+  // Cross-wave reduction in wave order, then the three parts; stores (or split-K
+  // partials) for columns t0 .. t0 + T - 1.
+  auto reduce_store = [&](int64_t t0, int T, const f32x4& acc) {
+    red[wave * 64 + lane] = acc;
+    lds_barrier();
+    // Lane (g, c) held D[4g + i][c]: part s = g, column i, weight row c.
+    const int idx = tid;  // T * 16 <= 64 outputs: the first wave
+    const int t = idx >> 4, row = idx & 15;
+    float v = 0.f;
+    if (idx < T * kTileRows) {
+      const float* redf = reinterpret_cast<const float*>(red);
+      float pv[3][kWaves];
 #pragma unroll
-    for (int m = 0; m < NMAT; ++m)
+      for (int p = 0; p < 3; ++p)
 #pragma unroll
-      for (int r = 0; r < RG; ++r) red[((wave * NMAT + m) * RG + r) * 64 + lane] = acc[m][r];
-    __syncthreads();
-    const int nout = T * ROWS;
-    // one round unless a narrow workgroup holds more outputs than threads (grouped
-    // modes with two row tiles and a short K); the trip count is uniform
-    for (int idx0 = 0; idx0 < nout; idx0 += (int)blockDim.x) {
-      const int idx = idx0 + tid;
-      const int t = idx / ROWS, rr = idx % ROWS;
-      const int r = rr >> 4, row = rr & 15;
-      float v[NMAT];
-      if (idx < nout) {
+        for (int w2 = 0; w2 < kWaves; ++w2) pv[p][w2] = redf[(w2 * 64 + 16 * p + row) * 4 + t];
+      float part[3];
 #pragma unroll
-        for (int m = 0; m < NMAT; ++m) {
-          float part[3];
-          // every partial slot is read at once (slots of absent waves lie inside the
-          // staging buffer; their values are not used), then added in wave order
-          const float* redf = reinterpret_cast<const float*>(red);
-          float pv[3][kWaves];
+      for (int p = 0; p < 3; ++p) {
+        float sum = pv[p][0];
 #pragma unroll
-          for (int p = 0; p < 3; ++p)
-#pragma unroll
-            for (int w2 = 0; w2 < kWaves; ++w2)
-              pv[p][w2] = redf[(((w2 * NMAT + m) * RG + r) * 64 + 16 * p + row) * 4 + t];
-#pragma unroll
-          for (int p = 0; p < 3; ++p) {
-            float sum = pv[p][0];
-#pragma unroll
-            for (int w2 = 1; w2 < kWaves; ++w2) sum = (w2 < nwaves) ? sum + pv[p][w2] : sum;
-            part[p] = sum;
-          }
-          v[m] = (part[0] + part[1]) + part[2];
-        }
+        for (int w2 = 1; w2 < kWaves; ++w2) sum = (w2 < nwaves) ? sum + pv[p][w2] : sum;
+        part[p] = sum;
       }
-      const int64_t col = rg * ROWS + rr;  // output row index (weight row)
-      const bool col_ok = col < a.n;
-      if (MODE == kQmvDense) {
-        if (a.S == 1) {
-          if (idx < nout && col_ok) a.y[(t0 + t) * a.ldy + col] = v[0];
-        } else {
-          // split K: partial sums to the workspace; the last of the S workgroups of this
-          // row group adds them in slice order.  The partials are written and read with
-          // agent-scope atomic stores / loads, which go to the device coherence point
-          // one access at a time, so no cache-wide writeback or invalidate is needed;
-          // s_waitcnt(0) makes every store complete before this workgroup's arrival is
-          // counted, and the last arriver issues its loads only after seeing the count.
-          float* part = a.partials + (rg * a.S + slice) * (kCols * ROWS);
-          if (idx < nout)
-            __hip_atomic_store(part + t * ROWS + rr, v[0], __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
-          __builtin_amdgcn_s_waitcnt(0);
-          __syncthreads();
-          if (tid == 0)
-            s_last = __hip_atomic_fetch_add(a.counters + rg, 1, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT) ==
-                     a.S - 1;
-          __syncthreads();
-          if (s_last) {
-            if (idx < nout && col_ok) {
-              const float* p0 = a.partials + rg * a.S * (kCols * ROWS) + t * ROWS + rr;
-              float sum = __hip_atomic_load(p0, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
-              for (int sl = 1; sl < a.S; ++sl)
-                sum += __hip_atomic_load(p0 + sl * (kCols * ROWS), __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
-              a.y[(t0 + t) * a.ldy + col] = sum;
-            }
-            // leaves the workspace ready for the next call
-            if (tid == 0) __hip_atomic_store(a.counters + rg, 0, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
-          }
-        }
-      }
+      v = (part[0] + part[1]) + part[2];
     }
-    if (t0 + kCols < ncols) __syncthreads();  // LDS is reused by the next pass
+    const int64_t col = rg * kTileRows + row;  // output row index (weight row)
+    const bool ok = idx < T * kTileRows && col < a.n;
+    if (a.S == 1) {
+      if (ok) a.y[(t0 + t) * a.ldy + col] = v;
+      return;
+    }
+    // Split K: partial sums to the workspace; the last of the S workgroups of this row
+    // tile adds them in slice order.  The partials are written and read with agent-scope
+    // atomic stores / loads, which go to the device coherence point one access at a
+    // time, so no cache-wide writeback or invalidate is needed; s_waitcnt(0) makes every
+    // store complete before this workgroup's arrival is counted, and the last arriver
+    // issues its loads only after seeing the count.
+    float* part = a.partials + (rg * a.S + slice) * (kCols * kTileRows);
+    if (idx < T * kTileRows)
+      __hip_atomic_store(part + t * kTileRows + row, v, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
+    __builtin_amdgcn_s_waitcnt(0);
+    __syncthreads();
+    if (tid == 0)
+      s_last = __hip_atomic_fetch_add(a.counters + rg, 1, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT) == a.S - 1;
+    __syncthreads();
+    if (s_last) {
+      if (ok) {
+        const float* p0 = a.partials + rg * a.S * (kCols * kTileRows) + t * kTileRows + row;
+        float sum = __hip_atomic_load(p0, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
+        for (int sl = 1; sl < a.S; ++sl)
+          sum += __hip_atomic_load(p0 + sl * (kCols * kTileRows), __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
+        a.y[(t0 + t) * a.ldy + col] = sum;
+      }
+      // leaves the workspace ready for the next call
+      if (tid == 0) __hip_atomic_store(a.counters + rg, 0, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
+    }
+    __syncthreads();  // the counter and red are reused by a next pass
+  };
+
+  // ---- the first pass (up to 4 columns) -------------------------------------------
+  store_x(T0);   // waits for the activations only
+  lds_barrier();  // the table (LDS only: no wait on the weights in flight)
+  f32x4 acc;
+  multiply(acc);
+  reduce_store(0, T0, acc);
+  // ---- further passes of 4 columns (T > 4): same weights, next columns ---------------
+  for (int64_t t0 = kCols; t0 < ncols; t0 += kCols) {
+    const int T = (int)min((int64_t)kCols, ncols - t0);
+    lds_barrier();  // every wave is done with red
+    load_x(t0, T);
+    store_x(T);
+    multiply(acc);
+    reduce_store(t0, T, acc);
   }
 }
 
@@ -611,22 +584,11 @@ int64_t qmv_workspace_bytes(int64_t n, int64_t k) {
   return a.rg_n * a.S * kCols * kDenseRG * kTileRows * (int64_t)sizeof(float) + 256 + a.rg_n * 4;
 }
 
-template <int MODE, int RG, int XQ>
-static int launch_mode(const QmvArgs& a, int64_t grid) {
+template <int WQ>
+static int launch_dense(const QmvArgs& a, int64_t grid) {
   if (grid == 0) return 0;
-  hipLaunchKernelGGL((qmv_kernel<MODE, RG, XQ>), dim3((unsigned)grid), dim3(64 * a.nwaves), 0, a.stream, a);
-  return check_launch("qmv_kernel");
-}
-
-// Instantiation by quads per wave (the plan gives 1..4).
-template <int MODE, int RG>
-static int launch_sized(const QmvArgs& a, int64_t grid) {
-  switch (a.wave_quads) {
-    case 1: return launch_mode<MODE, RG, 1>(a, grid);
-    case 2: return launch_mode<MODE, RG, 2>(a, grid);
-    case 3: return launch_mode<MODE, RG, 3>(a, grid);
-    default: return launch_mode<MODE, RG, kMaxWaveQuads>(a, grid);
-  }
+  hipLaunchKernelGGL((qmv_dense_kernel<WQ>), dim3((unsigned)grid), dim3(64 * a.nwaves), 0, a.stream, a);
+  return check_launch("qmv_dense_kernel");
 }
 
 int launch_qmv(const uint8_t* packed, int64_t n, int64_t k, const float* x, int64_t ldx, int T,
@@ -645,7 +607,13 @@ int launch_qmv(const uint8_t* packed, int64_t n, int64_t k, const float* x, int6
     a.partials = static_cast<float*>(workspace);
     a.counters = reinterpret_cast<int*>(static_cast<uint8_t*>(workspace) + ((pbytes + 255) / 256) * 256);
   }
-  return launch_sized<kQmvDense, kDenseRG>(a, a.rg_n * a.S);
+  const int64_t grid = a.rg_n * a.S;
+  switch (a.wave_quads) {  // instantiation by quads per wave (the plan gives 1..4)
+    case 1: return launch_dense<1>(a, grid);
+    case 2: return launch_dense<2>(a, grid);
+    case 3: return launch_dense<3>(a, grid);
+    default: return launch_dense<kMaxWaveQuads>(a, grid);
+  }
 }
 
 template <int MODE, int RG, int WQ>
