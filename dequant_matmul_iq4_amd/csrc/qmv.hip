@@ -117,8 +117,9 @@ constexpr int kLutCopies = 32;
 // hot), then every weight of the wave; the activations are split and staged while the
 // weights stream in, and quad u is decoded and multiplied as soon as its own weights
 // have landed, so the arithmetic runs under the weight stream instead of after it.
-template <int WQ>
+template <int WQ, int TP>
 __global__ void __launch_bounds__(512) qmv_dense_kernel(QmvArgs a) {
+  static_assert(TP >= 1 && TP <= kCols, "first pass: 1..4 columns");
   constexpr int XBYTES = kWaves * WQ * 4 * kFragBytes;
   __shared__ uint32_t lut[256 * kLutCopies];
   __shared__ __attribute__((aligned(16))) uint8_t xs[XBYTES + 256];  // + room for padding-row reads
@@ -141,14 +142,17 @@ __global__ void __launch_bounds__(512) qmv_dense_kernel(QmvArgs a) {
   const int wblk = 4 * (wq1 - wq0);                      // blocks of this wave (0 if idle)
   uint8_t* xw = xs + wave * (4 * WQ) * kFragBytes;       // the wave's own staging region
 
+  // Staging tasks: (column t, block bl, k-group gg) = task (t SLOTS + 4 bl + gg), task =
+  // lane + 64 i; a full wave's mapping is fixed at compile time (for WQ = 4 lane l always
+  // stages slot l and i is the column), blocks past a short wave's run are skipped.
+  constexpr int SLOTS = 16 * WQ;
   float4 xr[WQ][2];
-  auto load_x = [&](int64_t t0, int T) {  // tasks (column t, block, k-group gg), 64 lanes
-    const int ntask = T * wblk * 4;
+  auto load_x = [&](int64_t t0, int T) {
 #pragma unroll
     for (int i = 0; i < WQ; ++i) {
       const int task = lane + 64 * i;
-      if (task < ntask) {
-        const int gg = task & 3, bl = (task >> 2) % wblk, t = (task >> 2) / wblk;
+      const int t = task / SLOTS, bl = (task % SLOTS) >> 2, gg = task & 3;
+      if (t < T && bl < wblk) {
         const float* p = a.x + (t0 + t) * a.ldx + ((int64_t)(kqa + wq0) * 4 + bl) * kQK + 8 * gg;
         xr[i][0] = *reinterpret_cast<const float4*>(p);
         xr[i][1] = *reinterpret_cast<const float4*>(p + 4);
@@ -156,12 +160,11 @@ __global__ void __launch_bounds__(512) qmv_dense_kernel(QmvArgs a) {
     }
   };
   auto store_x = [&](int T) {  // split and store in fragment order
-    const int ntask = T * wblk * 4;
 #pragma unroll
     for (int i = 0; i < WQ; ++i) {
       const int task = lane + 64 * i;
-      if (task < ntask) {
-        const int gg = task & 3, bl = (task >> 2) % wblk, t = (task >> 2) / wblk;
+      const int t = task / SLOTS, bl = (task % SLOTS) >> 2, gg = task & 3;
+      if (t < T && bl < wblk) {
         const float4 xa = xr[i][0], xb = xr[i][1];
         uint32_t p0[3], p1[3], p2[3], p3[3];
         split_pair(xa.x, xa.y, p0);
@@ -182,7 +185,7 @@ __global__ void __launch_bounds__(512) qmv_dense_kernel(QmvArgs a) {
   const uint8_t* sp = a.W0 + a.nibble_bytes + (rg * kq_n + kqa) * kTileScaleBytes + c * 8;
 
   // ---- requests: the first pass's activations, then every weight of the wave --------
-  const int T0 = (int)min((int64_t)kCols, ncols);
+  constexpr int T0 = TP;  // columns of the first pass, min(T, 4): fixed per instantiation
   load_x(0, T0);
 #pragma unroll
   for (int u = 0; u < WQ; ++u) {
@@ -584,11 +587,22 @@ int64_t qmv_workspace_bytes(int64_t n, int64_t k) {
   return a.rg_n * a.S * kCols * kDenseRG * kTileRows * (int64_t)sizeof(float) + 256 + a.rg_n * 4;
 }
 
+template <int WQ, int TP>
+static int launch_dense_t(const QmvArgs& a, int64_t grid) {
+  if (grid == 0) return 0;
+  hipLaunchKernelGGL((qmv_dense_kernel<WQ, TP>), dim3((unsigned)grid), dim3(64 * a.nwaves), 0, a.stream, a);
+  return check_launch("qmv_dense_kernel");
+}
+
+// Instantiation by the first pass's column count.
 template <int WQ>
 static int launch_dense(const QmvArgs& a, int64_t grid) {
-  if (grid == 0) return 0;
-  hipLaunchKernelGGL((qmv_dense_kernel<WQ>), dim3((unsigned)grid), dim3(64 * a.nwaves), 0, a.stream, a);
-  return check_launch("qmv_dense_kernel");
+  switch (a.T < kCols ? a.T : kCols) {
+    case 1: return launch_dense_t<WQ, 1>(a, grid);
+    case 2: return launch_dense_t<WQ, 2>(a, grid);
+    case 3: return launch_dense_t<WQ, 3>(a, grid);
+    default: return launch_dense_t<WQ, kCols>(a, grid);
+  }
 }
 
 int launch_qmv(const uint8_t* packed, int64_t n, int64_t k, const float* x, int64_t ldx, int T,
