@@ -147,7 +147,8 @@ int iq4_moe_gather(const int32_t* ids, int64_t n_pairs, int32_t n_expert, int32_
   if (!aligned(ids, 4) || !aligned(counts, 4) || !aligned(offsets, 4) || !aligned(pairs, 4) ||
       !aligned(slot_row, 4))
     return set_error(IQ4_E_ALIGN, "iq4_moe_gather: pointers must be 4-byte aligned");
-  return launch_gather(ids, n_pairs, n_expert, counts, offsets, pairs, slot_row, as_stream(stream));
+  return launch_gather(ids, n_pairs, n_expert, counts, offsets, pairs, slot_row, nullptr, nullptr,
+                       as_stream(stream));
 }
 
 static int check_moe_sizes(const char* fn, int64_t n_tok, int32_t top_k, int32_t n_expert,

@@ -14,7 +14,9 @@ int launch_qmv(const uint8_t* packed, int64_t n, int64_t k, const float* x, int6
 
 int launch_route_topk(const float* logits, int64_t n_tok, int n_expert, int top_k, int32_t* ids,
                       float* w, hipStream_t s);
+// tiles / num_tiles: the grouped GEMM's tile list, built in the same launch (or null)
 int launch_gather(const int32_t* ids, int64_t n_pairs, int n_expert, int32_t* counts,
-                  int32_t* offsets, int32_t* pairs, int32_t* slot_row, hipStream_t s);
+                  int32_t* offsets, int32_t* pairs, int32_t* slot_row, int32_t* tiles,
+                  int32_t* num_tiles, hipStream_t s);
 
 }  // namespace iq4

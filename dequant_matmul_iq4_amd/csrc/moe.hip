@@ -1,8 +1,8 @@
-// moe.hip -- the mixture-of-experts path around the products: the per-expert tile list,
-// the gate-weighted combine, and the orchestration of one MoE layer call.
+// moe.hip -- the mixture-of-experts path around the products: the gate-weighted
+// combine and the orchestration of one MoE layer call.
 //
 // Prefill (binary16 activations):
-//   gather -> tile list -> GEMM gate|up (+SwiGLU, h binary16) -> GEMM down (x gate
+//   gather (+ tile list) -> GEMM gate|up (+SwiGLU, h binary16) -> GEMM down (x gate
 //   weight) -> combine.
 // Decode (fp32 activations, few tokens):
 //   gather -> grouped matvec gate|up (+SwiGLU, h fp32) -> grouped matvec down (x gate
@@ -21,50 +21,6 @@ namespace iq4 {
 
 constexpr int kTileM = 128;  // rows per GEMM tile (gemm.hip kBM)
 constexpr int kMaxTopK = 16;  // the largest top_k the call accepts
-
-// One workgroup.  The tile list holds every expert's full 128-row tiles first
-// (expert-major, an expert's tiles adjacent), then the experts' partial last tiles by
-// descending row count (ties: lower expert first), so the products can run the lighter
-// tiles last.  num_tiles[0] = all tiles, num_tiles[1] = full tiles.
-__global__ void __launch_bounds__(1024) tiles_kernel(const int32_t* __restrict__ counts, int n_expert,
-                                                     int32_t* __restrict__ tiles,
-                                                     int32_t* __restrict__ num_tiles) {
-  __shared__ int scan[1024];
-  __shared__ int part_rows[1024];
-  const int e = threadIdx.x;
-  const int cnt = (e < n_expert) ? counts[e] : 0;
-  const int nf = cnt / kTileM;  // full tiles
-  const int pr = cnt % kTileM;  // rows of the partial tile (0: none)
-  scan[e] = nf;
-  part_rows[e] = pr;
-  __syncthreads();
-  for (int off = 1; off < 1024; off <<= 1) {  // inclusive Hillis-Steele scan
-    const int v = (e >= off) ? scan[e - off] : 0;
-    __syncthreads();
-    scan[e] += v;
-    __syncthreads();
-  }
-  const int full = scan[1023];
-  const int base = scan[e] - nf;
-  for (int i = 0; i < nf; ++i) {
-    tiles[2 * (base + i)] = e;
-    tiles[2 * (base + i) + 1] = i;
-  }
-  if (pr > 0) {
-    int rank = 0;
-    for (int e2 = 0; e2 < n_expert; ++e2) {
-      const int p2 = part_rows[e2];
-      rank += (p2 > pr) || (p2 == pr && e2 < e);
-    }
-    tiles[2 * (full + rank)] = e;
-    tiles[2 * (full + rank) + 1] = nf;
-  }
-  const int partial = __syncthreads_count(pr > 0);
-  if (e == 0) {
-    num_tiles[0] = full + partial;
-    num_tiles[1] = full;
-  }
-}
 
 // out[t][h] = sum_j rows[t * k + j][h], j ascending; one thread per 4 outputs.
 __global__ void __launch_bounds__(256) combine_kernel(const float* __restrict__ rows, int64_t ldr,
@@ -136,7 +92,10 @@ int launch_moe(const MoeCall& m, hipStream_t s) {
   const int64_t P = m.n_tok * m.top_k;
   if (m.n_tok == 0) return 0;
 
-  if (int e = launch_gather(m.ids, P, m.n_expert, counts, offsets, pairs, slot_row, s)) return e;
+  // prefill: the gather also writes the grouped GEMM's tile list
+  if (int e = launch_gather(m.ids, P, m.n_expert, counts, offsets, pairs, slot_row, m.f16 ? tiles : nullptr,
+                            m.f16 ? num_tiles : nullptr, s))
+    return e;
 
   const int64_t gate_stride = m.inter * (m.hidden / kQK) * kBlockBytes;
   const int64_t down_stride = m.hidden * (m.inter / kQK) * kBlockBytes;
@@ -149,8 +108,6 @@ int launch_moe(const MoeCall& m, hipStream_t s) {
   }
 
   if (m.f16) {
-    hipLaunchKernelGGL(tiles_kernel, dim3(1), dim3(1024), 0, s, counts, m.n_expert, tiles, num_tiles);
-    if (int e = check_launch("tiles_kernel")) return e;
     uint16_t* h = reinterpret_cast<uint16_t*>(ws + L.h);
     GemmArgs g{};
     g.A = static_cast<const uint16_t*>(m.x);
