@@ -60,17 +60,6 @@ __device__ __forceinline__ uint32_t bf16_of_level(int c) {
   return __float_as_uint((float)c) >> 16;  // exact: |c| <= 127
 }
 
-// Part s (0 = hi, 1 = mid, 2 = lo) of the exact three-way bf16 split of v.
-__device__ __forceinline__ uint32_t split_part(float v, int s) {
-  uint32_t u = __float_as_uint(v);
-  if (s == 0) return u >> 16;
-  float r1 = v - __uint_as_float(u & 0xFFFF0000u);  // exact (Sterbenz)
-  uint32_t u1 = __float_as_uint(r1);
-  if (s == 1) return u1 >> 16;
-  float r2 = r1 - __uint_as_float(u1 & 0xFFFF0000u);  // exact, <= 8 significant bits
-  return __float_as_uint(r2) >> 16;
-}
-
 // Column t of the call: where its activations live.  The pair list is read through the
 // constant address space (it is not written during the call), so a uniform lookup is a
 // scalar load, counted apart from the weight loads in flight.
@@ -93,7 +82,9 @@ constexpr int kFragRows = 12;
 constexpr int kFragBytes = 4 * kFragRows * 16;  // 768 B per block
 
 // Exact three-way bf16 split of two values, packed per part: word s holds part s of v0
-// in its low and of v1 in its high half (parts as split_part gives them).
+// in its low and of v1 in its high half.  Part 0 (hi) is the top 16 bits of v; part 1
+// (mid) the top 16 bits of r = v - hi; part 2 (lo) is r - mid, which has at most 8
+// significant bits: every subtraction is exact, so v = hi + mid + lo.
 __device__ __forceinline__ void split_pair(float v0, float v1, uint32_t out[3]) {
   const uint32_t u0 = __float_as_uint(v0), u1 = __float_as_uint(v1);
   const float r0 = v0 - __uint_as_float(u0 & 0xFFFF0000u);  // exact (Sterbenz)
@@ -106,10 +97,12 @@ __device__ __forceinline__ void split_pair(float v0, float v1, uint32_t out[3]) 
   out[2] = __builtin_amdgcn_perm(__float_as_uint(l1), __float_as_uint(l0), 0x07060302u);
 }
 
-// Byte-indexed level table, replicated so that a wave's lookups never conflict: entry e
-// of copy j sits at word 32 e + j, i.e. always in LDS bank j, and lane l reads copy
-// l mod 32.
+// Byte-indexed level table, replicated against bank conflicts: entry e of copy j sits at
+// word C e + j and lane l reads copy l mod C.  With C = 32 (dense kernel) a copy lies in
+// one LDS bank, so a wave's lookups never conflict; the grouped kernels keep C = 8 (8 KiB)
+// so that two of their workgroups still share a CU.
 constexpr int kLutCopies = 32;
+constexpr int kGroupedLutCopies = 8;
 
 // Dense verify-window matvec: one workgroup per row tile and K slice; each wave owns WQ
 // quads of the slice (registers and LDS sized to K).  The code of a pass is straight
@@ -322,7 +315,7 @@ __global__ void __launch_bounds__(512) qmv_grouped_kernel(QmvArgs a) {
   constexpr int ROWS = RG * kTileRows;
   constexpr int XBYTES = kWaves * WQ * 4 * kFragBytes;
   constexpr int REDN = kWaves * NMAT * RG * 64;  // one f32x4 partial per (wave, matrix, tile, lane)
-  __shared__ uint32_t lut[256];
+  __shared__ uint32_t lut[256 * kGroupedLutCopies];
   __shared__ __attribute__((aligned(16))) uint8_t xs[XBYTES + 256];  // + room for padding-row reads
   __shared__ f32x4 red[REDN];
 
@@ -363,17 +356,18 @@ __global__ void __launch_bounds__(512) qmv_grouped_kernel(QmvArgs a) {
   // ---- this wave's activations (blocks [4 wq0, 4 wq1)), staged by the wave itself ----
   const int wblk = 4 * (wq1 - wq0);
   uint8_t* xw = xs + wave * (4 * WQ) * kFragBytes;
+  constexpr int SLOTS = 16 * WQ;  // staging tasks: (t, bl, gg) = task (t SLOTS + 4 bl + gg)
+  const uint32_t* lutl = lut + (lane & (kGroupedLutCopies - 1));  // this lane's table copy
   float4 xr[WQ][2];
   auto load_x = [&](int64_t t0, int T) {  // tasks (column t, block, k-group gg), 64 lanes
-    const int ntask = T * wblk * 4;
     const float* col[kCols];
 #pragma unroll
     for (int t = 0; t < kCols; ++t) col[t] = column_ptr(a, MODE, seg0, t0 + min(t, T - 1));
 #pragma unroll
     for (int i = 0; i < WQ; ++i) {
       const int task = lane + 64 * i;
-      if (task < ntask) {
-        const int gg = task & 3, bl = (task >> 2) % wblk, t = (task >> 2) / wblk;
+      const int t = task / SLOTS, bl = (task % SLOTS) >> 2, gg = task & 3;
+      if (t < T && bl < wblk) {
         const float* cp = (t == 0) ? col[0] : (t == 1) ? col[1] : (t == 2) ? col[2] : col[3];
         const float* p = cp + ((int64_t)wq0 * 4 + bl) * kQK + 8 * gg;
         xr[i][0] = *reinterpret_cast<const float4*>(p);
@@ -382,23 +376,21 @@ __global__ void __launch_bounds__(512) qmv_grouped_kernel(QmvArgs a) {
     }
   };
   auto store_x = [&](int T) {  // split and store in fragment order
-    const int ntask = T * wblk * 4;
 #pragma unroll
     for (int i = 0; i < WQ; ++i) {
       const int task = lane + 64 * i;
-      if (task < ntask) {
-        const int gg = task & 3, bl = (task >> 2) % wblk, t = (task >> 2) / wblk;
+      const int t = task / SLOTS, bl = (task % SLOTS) >> 2, gg = task & 3;
+      if (t < T && bl < wblk) {
         const float4 xa = xr[i][0], xb = xr[i][1];
+        uint32_t p0[3], p1[3], p2[3], p3[3];
+        split_pair(xa.x, xa.y, p0);
+        split_pair(xa.z, xa.w, p1);
+        split_pair(xb.x, xb.y, p2);
+        split_pair(xb.z, xb.w, p3);
         uint8_t* dst = xw + (bl * 4 + gg) * (kFragRows * 16) + t * 16;
 #pragma unroll
-        for (int sp = 0; sp < 3; ++sp) {
-          uint4 f;
-          f.x = split_part(xa.x, sp) | (split_part(xa.y, sp) << 16);
-          f.y = split_part(xa.z, sp) | (split_part(xa.w, sp) << 16);
-          f.z = split_part(xb.x, sp) | (split_part(xb.y, sp) << 16);
-          f.w = split_part(xb.z, sp) | (split_part(xb.w, sp) << 16);
-          *reinterpret_cast<uint4*>(dst + sp * 4 * 16) = f;
-        }
+        for (int sp = 0; sp < 3; ++sp)
+          *reinterpret_cast<uint4*>(dst + sp * 4 * 16) = uint4{p0[sp], p1[sp], p2[sp], p3[sp]};
       }
     }
     // LDS accesses of one wave execute in order: the wave's reads below see these
@@ -454,6 +446,7 @@ __global__ void __launch_bounds__(512) qmv_grouped_kernel(QmvArgs a) {
 #pragma unroll
     for (int u = 0; u < WQ; ++u) {
       if (wq0 + u >= wq1) break;
+      __builtin_amdgcn_sched_barrier(0);  // quad u's work waits for quad u's weights only
 #pragma unroll
       for (int j = 0; j < 4; ++j) {
         const int bl = 4 * u + j;
@@ -465,10 +458,10 @@ __global__ void __launch_bounds__(512) qmv_grouped_kernel(QmvArgs a) {
           for (int r = 0; r < RG; ++r) {
             const uint4 nb = ws.nib[u][m][r];
             const uint32_t w = (j == 0) ? nb.x : (j == 1) ? nb.y : (j == 2) ? nb.z : nb.w;
-            bf[m][r][0] = lut[w & 0xFF];
-            bf[m][r][1] = lut[(w >> 8) & 0xFF];
-            bf[m][r][2] = lut[(w >> 16) & 0xFF];
-            bf[m][r][3] = lut[w >> 24];
+            bf[m][r][0] = lutl[(w & 0xFF) * kGroupedLutCopies];
+            bf[m][r][1] = lutl[((w >> 8) & 0xFF) * kGroupedLutCopies];
+            bf[m][r][2] = lutl[((w >> 16) & 0xFF) * kGroupedLutCopies];
+            bf[m][r][3] = lutl[(w >> 24) * kGroupedLutCopies];
           }
 #pragma unroll
         for (int m = 0; m < NMAT; ++m)
@@ -540,8 +533,12 @@ __global__ void __launch_bounds__(512) qmv_grouped_kernel(QmvArgs a) {
     load_x(0, (int)ncols);
     load_cols(0, (int)ncols);
   }
-  for (int i = tid; i < 256; i += blockDim.x)
-    lut[i] = bf16_of_level(level_of(i & 15)) | (bf16_of_level(level_of(i >> 4)) << 16);
+  for (int e = tid; e < 256; e += blockDim.x) {
+    const uint32_t v = bf16_of_level(level_of(e & 15)) | (bf16_of_level(level_of(e >> 4)) << 16);
+    uint4* dst = reinterpret_cast<uint4*>(lut + e * kGroupedLutCopies);
+#pragma unroll
+    for (int w4 = 0; w4 < kGroupedLutCopies / 4; ++w4) dst[w4] = uint4{v, v, v, v};
+  }
   __syncthreads();  // the table (LDS only: no wait on the loads in flight)
   if (one_pass) store_x((int)ncols);
 

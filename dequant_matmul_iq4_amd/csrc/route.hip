@@ -85,12 +85,14 @@ __global__ void __launch_bounds__(kGatherThreads) gather_kernel(const int32_t* _
   const int64_t p0 = wave * seg;
   const int64_t p1 = min(p0 + seg, n_pairs);
 
-  // ids are read 8 x 64 at a time (independent loads in flight; out of range -> never equal
-  // to, nor below, any expert)
-  constexpr int kBatch = 8;
+  // ids are read 32 x 64 at a time (independent loads in flight; out of range -> never
+  // equal to, nor below, any expert).  A wave whose segment fits in one batch (up to
+  // 32,768 pairs per call) keeps it in registers for pass 2 instead of reading it again.
+  constexpr int kBatch = 32;
+  const bool one_batch = p1 - p0 <= 64 * kBatch;
+  int v[kBatch];
   int eq = 0, lt = 0;
   for (int64_t pb = p0; pb < p1; pb += 64 * kBatch) {
-    int v[kBatch];
 #pragma unroll
     for (int u = 0; u < kBatch; ++u) {
       const int64_t p = pb + 64 * u + lane;
@@ -156,11 +158,12 @@ __global__ void __launch_bounds__(kGatherThreads) gather_kernel(const int32_t* _
   }
   const uint64_t below = (lane == 0) ? 0ull : (~0ull >> (64 - lane));
   for (int64_t pb = p0; pb < p1; pb += 64 * kBatch) {
-    int v[kBatch];
+    if (!one_batch) {
 #pragma unroll
-    for (int u = 0; u < kBatch; ++u) {
-      const int64_t p = pb + 64 * u + lane;
-      v[u] = (p < p1) ? ids[p] : INT_MAX;
+      for (int u = 0; u < kBatch; ++u) {
+        const int64_t p = pb + 64 * u + lane;
+        v[u] = (p < p1) ? ids[p] : INT_MAX;
+      }
     }
 #pragma unroll
     for (int u = 0; u < kBatch; ++u) {  // in pair order: u, then lane
