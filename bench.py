@@ -42,12 +42,12 @@ N_BANKS = 8                 # expert banks the decode step rotates over
 # at the time: a kernel changed since then reports traffic null.  Commands and raw
 # figures: profiles/<name>.txt.
 MEASURED_TRAFFIC = {
-    "qmv_dense_4096x4096_T1-4": (9981496, "fc5aa085b65aa127", ("qmv.hip", "qmv.hpp", "common.hpp")),
-    "qmv_grouped_gateup_moe_decode_4tok": (55495591, "fc5aa085b65aa127", ("qmv.hip", "qmv.hpp", "common.hpp")),
-    "qmv_grouped_down_moe_decode_4tok": (28675033, "fc5aa085b65aa127", ("qmv.hip", "qmv.hpp", "common.hpp")),
-    "qgemm_gateup_moe_prefill_3256tok": (589939749, "b714e2dbb4e2f59c", ("gemm.hip", "gemm.hpp", "common.hpp")),
-    "qgemm_down_moe_prefill_3256tok": (507588057, "b714e2dbb4e2f59c", ("gemm.hip", "gemm.hpp", "common.hpp")),
-    "qgemm_dense_13056x4096x14336_chunk512": (94965181, "b714e2dbb4e2f59c", ("gemm.hip", "gemm.hpp", "common.hpp")),
+    "qmv_dense_4096x4096_T1-4": (9926208, "585d2bb4783ac636", ("qmv.hip", "qmv.hpp", "common.hpp")),
+    "qmv_grouped_gateup_moe_decode_4tok": (55484735, "585d2bb4783ac636", ("qmv.hip", "qmv.hpp", "common.hpp")),
+    "qmv_grouped_down_moe_decode_4tok": (28657493, "585d2bb4783ac636", ("qmv.hip", "qmv.hpp", "common.hpp")),
+    "qgemm_gateup_moe_prefill_3256tok": (589236475, "fa0fd0a4be8a57c4", ("gemm.hip", "gemm.hpp", "common.hpp")),
+    "qgemm_down_moe_prefill_3256tok": (507852230, "fa0fd0a4be8a57c4", ("gemm.hip", "gemm.hpp", "common.hpp")),
+    "qgemm_dense_13056x4096x14336_chunk512": (94965194, "fa0fd0a4be8a57c4", ("gemm.hip", "gemm.hpp", "common.hpp")),
 }
 
 
@@ -363,7 +363,7 @@ def main():
             "component_ms_per_step": {kk: round(v, 4) for kk, v in comp.items()},
         },
         "roofline": roof("hbm", mm_achieved, HBM_PEAK_GBS, "GB/s",
-                         "qmv_kernel<dense>: verify-window matvec, bytes = W + X + Y per call, "
+                         "qmv_dense_kernel: verify-window matvec, bytes = W + X + Y per call, "
                          "mean over T=1..4; traffic = HBM bytes per launch",
                          traffic=measured_traffic("qmv_dense_4096x4096_T1-4")),
         "rooflines": {
