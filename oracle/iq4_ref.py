@@ -24,7 +24,16 @@ Readings where the pages are silent (each also listed in the design notes):
   k selected logits; routing takes the k largest logits, ties to the lower expert id
   (page 3: the module docstring of the TP-2 layout and the ``markov_local_argmax``
   docstring both break ties toward the smaller index);
-* every output is float32, computed here as the float64 result rounded once.
+* every output is float32, computed here as the float64 result rounded once;
+* 8-bit activations (page 1's ``verify.hpp`` holds the window's T activation columns
+  in the q8_1 format for the decode products; the pages name the format but never
+  print it): per column and per block
+  of 32 consecutive k, ``d = f32(absmax) / 127`` (binary32 division), ``r = 1 / d``
+  (binary32 division; 0 when f16(d) is 0), ``q_i = round_half_away(f32(x_i * r))`` clamped
+  to [-127, 127], and the stored scale is ``f16_rne(d)``; the product of a weight block
+  and an activation block is ``d_w * d_x * sum_i c[q_w,i] * q_i``.  This is the public
+  definition of that 8-bit block format; its sum field serves zero-offset formats only
+  and is not produced.
 
 Parity pins: the test-suite checks each function here against something other than
 itself (closed forms, brute force in exact rationals, invariants, hand-written golden
@@ -38,6 +47,7 @@ __all__ = [
     "CODEBOOK", "QK", "BLOCK_BYTES",
     "decode_blocks", "decode_blocks_f16", "encode_blocks",
     "qmv", "route_topk", "gather", "silu", "moe", "gemm",
+    "quantize_q8_1", "qmv_q8",
 ]
 
 #: The fixed 16-level int8 codebook of the block format (workload definition).
@@ -239,3 +249,58 @@ def gemm(blocks, n: int, k: int, x) -> np.ndarray:
     W = _matrix(blocks, n, k)
     X = np.asarray(x).astype(np.float64).reshape(-1, k)
     return (X @ W.T).astype(np.float32)
+
+
+def _round_half_away(v: np.ndarray) -> np.ndarray:
+    """Nearest integer of float32 values, halves away from zero (C ``roundf``), done
+    in exact steps: ``v - trunc(v)`` is exact in float32 for |v| < 2^23."""
+    v = np.asarray(v, dtype=np.float32)
+    t = np.trunc(v)
+    frac = np.abs(v - t)
+    return t + np.where(frac >= np.float32(0.5), np.sign(v), np.float32(0)).astype(np.float32)
+
+
+def quantize_q8_1(x):
+    """8-bit block quantisation of float32 activations ``x`` ([T, k], k % 32 == 0).
+
+    Per column t and block b of 32 consecutive k: ``d = f32(absmax) / 127`` and
+    ``r = 1 / d`` as IEEE binary32 divisions, ``q_i`` the
+    nearest integer of the binary32 product ``x_i * r`` (halves away from zero), clamped
+    to [-127, 127]; the stored scale is d rounded to binary16, and a block whose stored
+    scale is zero gets zero codes (r = 0).  Non-finite x are not defined.  Returns ``q``
+    (int8 ``[T, k]``) and ``d`` (float16 ``[T, k/32]``): the activation side of page 1's
+    decode products (``verify.hpp`` member declarations).
+    """
+    X = np.asarray(x, dtype=np.float32)
+    T, k = X.reshape(X.shape[0] if X.ndim > 1 else 1, -1).shape
+    if k % QK:
+        raise ValueError("K must be a multiple of 32")
+    B = X.reshape(T, k // QK, QK)
+    amax = np.max(np.abs(B), axis=2)
+    d = (amax / np.float32(127)).astype(np.float32)
+    d16 = d.astype(np.float16)
+    # a block whose stored scale is zero (absmax < 127 * 2^-25) contributes nothing:
+    # its codes are zero (this also keeps 1/d finite)
+    with np.errstate(divide="ignore"):
+        r = np.where(d16 != 0, np.float32(1) / d, np.float32(0)).astype(np.float32)
+    v = (B * r[:, :, None]).astype(np.float32)
+    q = np.clip(_round_half_away(v), -127, 127).astype(np.int8)
+    return q.reshape(T, k), d16
+
+
+def qmv_q8(blocks, n: int, k: int, q, d) -> np.ndarray:
+    """T-column product with 8-bit activations: ``Y[t][r] = sum_b dw[r][b] * dx[t][b] *
+    sum_i c[qw[r][32b+i]] * q[t][32b+i]`` (integer block dots, each scaled by the
+    product of the two binary16 scales), summed in float64 and rounded once to float32
+    (``[T, n]``).  ``q``, ``d`` as :func:`quantize_q8_1` returns them."""
+    b = _as_blocks(blocks)
+    if k % QK or b.shape[0] != n * (k // QK):
+        raise ValueError("block count does not match N x K")
+    nb = k // QK
+    cb = np.asarray(CODEBOOK, dtype=np.int64)
+    lev = cb[_indices(b)].reshape(n, nb, QK)              # integer levels
+    dw = _scales(b).reshape(n, nb)                         # float64 (exact)
+    Q = np.asarray(q, dtype=np.int64).reshape(-1, nb, QK)
+    dx = np.asarray(d, dtype=np.float16).astype(np.float64).reshape(-1, nb)
+    dots = np.einsum("rbi,tbi->trb", lev, Q)               # exact integers
+    return np.einsum("trb,rb,tb->tr", dots.astype(np.float64), dw, dx).astype(np.float32)

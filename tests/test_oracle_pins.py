@@ -405,12 +405,96 @@ def pin_moe_subset_rows():
     assert np.array_equal(sub, full[[4, 1]])
 
 
+# ----------------------------------------------------------------------------------
+# pins: 8-bit activations (quantize_q8_1, qmv_q8)
+
+
+def bf_quantize_q8_block(xs):
+    """Quantise 32 float32 values by hand: exact rationals, each IEEE step rounded
+    explicitly (binary32 division, reciprocal and product; binary16 scale)."""
+    xf = [Fraction(float(v)) for v in xs]
+    a = max(abs(v) for v in xf)
+    d32 = f32(a / 127)
+    d16 = f16(Fraction(d32))
+    if d16 == 0:
+        return [0] * 32, d16
+    r = f32(1 / Fraction(d32))
+    q = []
+    for v in xf:
+        p = Fraction(f32(v * Fraction(r)))
+        n = (abs(p) + Fraction(1, 2)).__floor__()  # halves away from zero
+        n = min(n, 127)
+        q.append(int(n if p >= 0 else -n))
+    return q, d16
+
+
+def q8_special_blocks():
+    blocks = [np.zeros(32, np.float32)]
+    # absmax 127: d = r = 1, so every value below is its own product; halves go away
+    # from zero
+    ties = [127.0, -127.0, 0.5, -0.5, 1.5, -1.5, 2.5, -2.5, 126.5, -126.5, 0.49999997, -0.49999997]
+    blocks.append(np.array(ties + [0.0] * (32 - len(ties)), np.float32))
+    blocks.append(np.full(32, 3.0e-6, np.float32))        # stored scale rounds to zero
+    blocks.append(np.linspace(-1e-3, 2e-3, 32, dtype=np.float32))
+    blocks.append(np.linspace(-6e4, 5e4, 32, dtype=np.float32))
+    return blocks
+
+
+def pin_q8_quantize_bruteforce():
+    rng = np.random.default_rng(7)
+    xs = [rng.standard_normal(32).astype(np.float32) * s for s in (1.0, 1e-3, 300.0)]
+    xs += [rng.standard_normal(32).astype(np.float32) for _ in range(20)]
+    xs += q8_special_blocks()
+    x = np.stack(xs).reshape(1, -1)
+    q, d = R.quantize_q8_1(x)
+    for b, xb in enumerate(xs):
+        wq, wd = bf_quantize_q8_block(xb)
+        assert list(q[0, 32 * b:32 * b + 32]) == wq, b
+        assert f16_bits(float(d[0, b])) == f16_bits(wd), b
+
+
+def pin_q8_quantize_ties():
+    x = q8_special_blocks()[1].reshape(1, 32)
+    q, d = R.quantize_q8_1(x)
+    assert float(d[0, 0]) == 1.0
+    want = [127, -127, 1, -1, 2, -2, 3, -3, 127, -127, 0, 0] + [0] * 20
+    assert list(q[0]) == want
+
+
+def pin_qmv_q8_fraction():
+    rng = np.random.default_rng(8)
+    n, k, T = 3, 64, 2
+    blocks = rand_blocks(rng, n * k // 32)
+    x = rng.standard_normal((T, k)).astype(np.float32)
+    q, d = R.quantize_q8_1(x)
+    y = R.qmv_q8(blocks, n, k, q, d)
+    W = bf_matrix(blocks, n, k)
+    for t in range(T):
+        xh = [Fraction(float(d[t, c // 32])) * int(q[t, c]) for c in range(k)]
+        for r in range(n):
+            assert_f32_close_to_exact(y[t, r], sum(W[r][c] * xh[c] for c in range(k)))
+
+
+def pin_qmv_q8_on_grid_equals_fp32():
+    # activations already on the 8-bit grid of their blocks (integers, each block's
+    # absmax 127, so d = r = 1): the 8-bit product equals the float product
+    rng = np.random.default_rng(9)
+    n, k, T = 8, 256, 3
+    blocks = rand_blocks(rng, n * k // 32)
+    x = rng.integers(-127, 128, (T, k)).astype(np.float32)
+    x[:, ::32] = 127.0
+    q, d = R.quantize_q8_1(x)
+    assert np.all(d == 1.0) and np.array_equal(q.astype(np.float32), x)
+    assert np.array_equal(R.qmv_q8(blocks, n, k, q, d), R.qmv(blocks, n, k, x))
+
+
 PINS = [
     pin_codebook, pin_block_size, pin_decode_golden, pin_decode_closed_form, pin_decode_f16,
     pin_encode_golden, pin_encode_bruteforce, pin_encode_idempotent, pin_encode_zero,
     pin_qmv_one_hot, pin_qmv_fraction, pin_qmv_integer_exact, pin_gemm_fraction,
     pin_gemm_integer_exact, pin_route_golden, pin_route_bruteforce, pin_gather_bruteforce,
     pin_silu, pin_moe_single_expert_is_dense_ffn, pin_moe_weight_summed_dense, pin_moe_subset_rows,
+    pin_q8_quantize_bruteforce, pin_q8_quantize_ties, pin_qmv_q8_fraction, pin_qmv_q8_on_grid_equals_fp32,
 ]
 
 
@@ -496,6 +580,35 @@ def _moe_drop_weight(x, ids, w, *a, **kw):
     return _orig_moe(x, ids, np.ones_like(np.asarray(w)), *a, **kw)
 
 
+_orig_quantize_q8 = R.quantize_q8_1
+_orig_qmv_q8 = R.qmv_q8
+
+
+def _q8_ties_to_even(x):
+    X = np.asarray(x, dtype=np.float32).reshape(np.asarray(x).shape[0], -1)
+    q, d = _orig_quantize_q8(X)
+    B = X.reshape(X.shape[0], -1, 32)
+    d32 = np.max(np.abs(B), axis=2) / np.float32(127)
+    with np.errstate(divide="ignore"):
+        r = np.where(d != 0, np.float32(1) / d32, np.float32(0)).astype(np.float32)
+    v = (B * r[:, :, None]).astype(np.float32)
+    return np.clip(np.rint(v), -127, 127).astype(np.int8).reshape(X.shape), d
+
+
+def _q8_reciprocal_of_stored_scale(x):
+    X = np.asarray(x, dtype=np.float32).reshape(np.asarray(x).shape[0], -1)
+    q, d = _orig_quantize_q8(X)
+    B = X.reshape(X.shape[0], -1, 32)
+    with np.errstate(divide="ignore"):
+        r = np.where(d != 0, np.float32(1) / d.astype(np.float32), np.float32(0)).astype(np.float32)
+    v = (B * r[:, :, None]).astype(np.float32)
+    return np.clip(R._round_half_away(v), -127, 127).astype(np.int8).reshape(X.shape), d
+
+
+def _qmv_q8_no_act_scale(blocks, n, k, q, d):
+    return _orig_qmv_q8(blocks, n, k, q, np.ones_like(np.asarray(d)))
+
+
 PLANTED = {
     "codebook sign": ("CODEBOOK", tuple(-c for c in R.CODEBOOK)),
     "codebook off by one": ("CODEBOOK", tuple(R.CODEBOOK[1:]) + (127,)),
@@ -507,6 +620,9 @@ PLANTED = {
     "silu sign": ("silu", _silu_wrong_sign),
     "encode ties upward": ("encode_blocks", _encode_round_half_up),
     "moe drops gate weight": ("moe", _moe_drop_weight),
+    "q8 ties to even": ("quantize_q8_1", _q8_ties_to_even),
+    "q8 reciprocal of the stored scale": ("quantize_q8_1", _q8_reciprocal_of_stored_scale),
+    "q8 product drops the activation scale": ("qmv_q8", _qmv_q8_no_act_scale),
 }
 
 
