@@ -38,6 +38,8 @@ SIGNATURES = {
     "iq4_qmv_workspace_size": (ctypes.c_int, [_c_i64, _c_i64, ctypes.POINTER(_c_sz)]),
     "iq4_qmv_multi": (ctypes.c_int, [_c_p, _c_i64, _c_i64, _c_p, _c_i64, _c_i32, _c_p, _c_i64, _c_p, _c_sz,
                                      _c_p]),
+    "iq4_quantize_q8_1": (ctypes.c_int, [_c_p, _c_i64, _c_i64, _c_i64, _c_p, _c_p, _c_p]),
+    "iq4_qmv_q8": (ctypes.c_int, [_c_p, _c_i64, _c_i64, _c_p, _c_p, _c_i32, _c_p, _c_i64, _c_p, _c_sz, _c_p]),
     "iq4_route_topk": (ctypes.c_int, [_c_p, _c_i64, _c_i32, _c_i32, _c_p, _c_p, _c_p]),
     "iq4_moe_gather": (ctypes.c_int, [_c_p, _c_i64, _c_i32, _c_p, _c_p, _c_p, _c_p, _c_p]),
     "iq4_moe_workspace_size": (ctypes.c_int, [_c_i64, _c_i32, _c_i32, _c_i64, _c_i64, _c_i32,
@@ -128,6 +130,15 @@ def iq4_qmv_workspace_size(n, k) -> int:
 
 def iq4_qmv_multi(packed, n, k, x, ldx, T, y, ldy, workspace=None, ws_bytes=0, stream=None):
     _call("iq4_qmv_multi", _ptr(packed), n, k, _ptr(x), ldx, T, _ptr(y), ldy, _ptr(workspace), ws_bytes,
+          _stream(stream))
+
+
+def iq4_quantize_q8_1(x, T, k, ldx, q, d, stream=None):
+    _call("iq4_quantize_q8_1", _ptr(x), T, k, ldx, _ptr(q), _ptr(d), _stream(stream))
+
+
+def iq4_qmv_q8(packed, n, k, q, d, T, y, ldy, workspace=None, ws_bytes=0, stream=None):
+    _call("iq4_qmv_q8", _ptr(packed), n, k, _ptr(q), _ptr(d), T, _ptr(y), ldy, _ptr(workspace), ws_bytes,
           _stream(stream))
 
 

@@ -125,6 +125,37 @@ int iq4_qmv_multi(const void* packed, int64_t n, int64_t k, const float* x, int6
                     as_stream(stream));
 }
 
+int iq4_quantize_q8_1(const float* x, int64_t T, int64_t k, int64_t ldx, int8_t* q, uint16_t* d,
+                      void* stream) {
+  clear_error();
+  if (T < 0 || k <= 0 || k % kQK || k > (int64_t)1 << 24)
+    return set_error(IQ4_E_ARG, "iq4_quantize_q8_1: need T >= 0 and 0 < k <= 2^24, k %% 32 == 0");
+  if (ldx < k || ldx % 4) return set_error(IQ4_E_ARG, "iq4_quantize_q8_1: ldx must be >= k and a multiple of 4");
+  if (T == 0) return IQ4_OK;
+  if (!x || !q || !d) return set_error(IQ4_E_ARG, "iq4_quantize_q8_1: null pointer");
+  if (!aligned(x, 16) || !aligned(q, 8) || !aligned(d, 2))
+    return set_error(IQ4_E_ALIGN, "iq4_quantize_q8_1: x must be 16-byte, q 8-byte, d 2-byte aligned");
+  return launch_quantize_q8(x, T, k, ldx, q, d, as_stream(stream));
+}
+
+int iq4_qmv_q8(const void* packed, int64_t n, int64_t k, const int8_t* q, const uint16_t* d, int32_t T,
+               float* y, int64_t ldy, void* workspace, size_t ws_bytes, void* stream) {
+  clear_error();
+  if (int e = check_matrix("iq4_qmv_q8", n, k)) return e;
+  if (T < 1 || T > 8) return set_error(IQ4_E_ARG, "iq4_qmv_q8: T must be in 1..8 (got %d)", T);
+  if (ldy < n) return set_error(IQ4_E_ARG, "iq4_qmv_q8: ldy must be >= n");
+  if (!packed || !q || !d || !y) return set_error(IQ4_E_ARG, "iq4_qmv_q8: null pointer");
+  if (!aligned(packed, 256) || !aligned(q, 8) || !aligned(d, 2) || !aligned(y, 4))
+    return set_error(IQ4_E_ALIGN, "iq4_qmv_q8: packed must be 256-byte, q 8-byte, d 2-byte, y 4-byte aligned");
+  const int64_t need = qmv_workspace_bytes(n, k);
+  if (need > 0) {
+    if (!workspace || ws_bytes < (size_t)need)
+      return set_error(IQ4_E_WORKSPACE, "iq4_qmv_q8: needs a workspace of %lld bytes", (long long)need);
+    if (!aligned(workspace, 256)) return set_error(IQ4_E_ALIGN, "iq4_qmv_q8: workspace must be 256-byte aligned");
+  }
+  return launch_qmv_q8(static_cast<const uint8_t*>(packed), n, k, q, d, T, y, ldy, workspace, as_stream(stream));
+}
+
 int iq4_route_topk(const float* logits, int64_t n_tok, int32_t n_expert, int32_t top_k,
                    int32_t* ids, float* w, void* stream) {
   clear_error();

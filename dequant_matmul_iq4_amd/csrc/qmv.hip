@@ -577,11 +577,20 @@ static void qmv_plan(QmvArgs& a, int64_t n, int64_t k, int rg_rows) {
   a.nwaves = (a.slice_quads + a.wave_quads - 1) / a.wave_quads;
 }
 
+// Split-K workspace (both the float and the 8-bit-activation matvec): the float
+// call's partials (4 columns per row group and slice), the arrival counters (one per
+// row group, shared by both calls and left at zero by each), then the 8-bit call's
+// partials (8 columns).
+static inline int64_t align256(int64_t b) { return (b + 255) / 256 * 256; }
+static int64_t ws_partials4(const QmvArgs& a) { return a.rg_n * a.S * kCols * kTileRows * (int64_t)sizeof(float); }
+static int64_t ws_counters_off(const QmvArgs& a) { return align256(ws_partials4(a)); }
+static int64_t ws_partials8_off(const QmvArgs& a) { return ws_counters_off(a) + align256(a.rg_n * 4); }
+
 int64_t qmv_workspace_bytes(int64_t n, int64_t k) {
   QmvArgs a{};
   qmv_plan(a, n, k, kDenseRG);
   if (a.S == 1) return 0;
-  return a.rg_n * a.S * kCols * kDenseRG * kTileRows * (int64_t)sizeof(float) + 256 + a.rg_n * 4;
+  return ws_partials8_off(a) + 2 * ws_partials4(a);
 }
 
 template <int WQ, int TP>
@@ -614,9 +623,8 @@ int launch_qmv(const uint8_t* packed, int64_t n, int64_t k, const float* x, int6
   a.stream = s;
   qmv_plan(a, n, k, kDenseRG);
   if (a.S > 1) {
-    const int64_t pbytes = a.rg_n * a.S * kCols * kDenseRG * kTileRows * (int64_t)sizeof(float);
     a.partials = static_cast<float*>(workspace);
-    a.counters = reinterpret_cast<int*>(static_cast<uint8_t*>(workspace) + ((pbytes + 255) / 256) * 256);
+    a.counters = reinterpret_cast<int*>(static_cast<uint8_t*>(workspace) + ws_counters_off(a));
   }
   const int64_t grid = a.rg_n * a.S;
   switch (a.wave_quads) {  // instantiation by quads per wave (the plan gives 1..4)
@@ -670,6 +678,279 @@ int launch_qmv_grouped(int mode, QmvArgs a, int64_t n, int64_t k, int n_expert, 
   if (a.S != 1) return set_error(-3, "grouped matvec: K above 4096 is not supported");
   grouped_split(a, slots);
   return launch_grouped_sized<kQmvDown, kDownRG>(a, slots * a.rg_chunks);
+}
+
+// ---------------------------------------------------------------------------------
+// 8-bit activations: page 1's decode products read the window's T activation columns
+// as q8_1 blocks (verify.hpp member declarations).  Per column and 32-k block:
+// d = f32(absmax) / 127, r = 1 / d (IEEE binary32 divisions; r = 0 when d rounds to a
+// zero binary16), q = nearest integer of f32(x * r), halves away from zero, clamped to
+// +-127; stored: the codes (int8 [T][K]) and d as binary16 ([T][K/32]).
+
+// One lane per 8 consecutive k of one column; the 4 lanes of a block exchange their
+// maxima with two xor shuffles (K % 32 == 0, so a block never straddles columns).
+__global__ void __launch_bounds__(256) quantize_q8_kernel(const float* __restrict__ x, int64_t T, int64_t K,
+                                                          int64_t ldx, int8_t* __restrict__ q,
+                                                          uint16_t* __restrict__ d) {
+  const int64_t i = (int64_t)blockIdx.x * blockDim.x + threadIdx.x;
+  const int64_t per = K / 8;
+  const bool ok = i < T * per;
+  const int64_t t = ok ? i / per : 0, k8 = ok ? (i % per) * 8 : 0;
+  float v[8];
+  if (ok) {
+    const float4 a = *reinterpret_cast<const float4*>(x + t * ldx + k8);
+    const float4 b = *reinterpret_cast<const float4*>(x + t * ldx + k8 + 4);
+    v[0] = a.x; v[1] = a.y; v[2] = a.z; v[3] = a.w;
+    v[4] = b.x; v[5] = b.y; v[6] = b.z; v[7] = b.w;
+  } else {
+#pragma unroll
+    for (int j = 0; j < 8; ++j) v[j] = 0.f;
+  }
+  float m = 0.f;
+#pragma unroll
+  for (int j = 0; j < 8; ++j) m = fmaxf(m, fabsf(v[j]));
+  m = fmaxf(m, __shfl_xor(m, 1));
+  m = fmaxf(m, __shfl_xor(m, 2));
+  const float dd = m / 127.0f;
+  const uint16_t h = __half_as_ushort(__float2half_rn(dd));
+  const float r = (h != 0) ? 1.0f / dd : 0.0f;
+  uint32_t w[2] = {0u, 0u};
+#pragma unroll
+  for (int j = 0; j < 8; ++j) {
+    const float p = v[j] * r;
+    const float tr = truncf(p);
+    float c = tr + ((fabsf(p - tr) >= 0.5f) ? copysignf(1.0f, p) : 0.0f);  // halves away from zero
+    c = fminf(fmaxf(c, -127.0f), 127.0f);
+    w[j >> 2] |= ((uint32_t)(int)c & 0xFFu) << (8 * (j & 3));
+  }
+  if (ok) {
+    *reinterpret_cast<uint2*>(q + t * K + k8) = uint2{w[0], w[1]};
+    if ((i & 3) == 0) d[t * (K / kQK) + k8 / kQK] = h;
+  }
+}
+
+// T-column matvec on 8-bit activations, T <= 8: the dense kernel's plan, weight stream
+// and level table, with A = the codes (one row per token; exact in bf16, |q| <= 127).
+// A block's MFMA result is then the exact integer dot sum_i c[q_w,i] * q_i (products of
+// at most 14 bits, sums below 2^24), scaled by the exact product of the two binary16
+// scales with one fp32 FMA per block.  A column's arithmetic never depends on T.
+constexpr int kQ8Rows = 8;                      // tokens per call (A rows 0..7)
+constexpr int kQ8FragBytes = 4 * kQ8Rows * 16;  // 512 B per block: [k-group g][token][16 B]
+
+template <int WQ, int TP>
+__global__ void __launch_bounds__(512) qmv_q8_kernel(QmvArgs a) {
+  static_assert(TP >= 1 && TP <= kQ8Rows, "1..8 columns");
+  constexpr int XBYTES = kWaves * WQ * 4 * kQ8FragBytes;
+  __shared__ uint32_t lut[256 * kLutCopies];
+  __shared__ __attribute__((aligned(16))) uint8_t xs[XBYTES];
+  __shared__ __attribute__((aligned(16))) uint16_t dxs[kWaves * WQ * 4 * kQ8Rows];  // [block][token]
+  __shared__ f32x4 red[kWaves * 64];
+  __shared__ int s_last;
+
+  const int tid = threadIdx.x;
+  const int lane = tid & 63, wave = tid >> 6, nwaves = (int)(blockDim.x >> 6);
+  const int c = lane & 15, g = lane >> 4;
+  const int T = a.T;  // <= TP
+
+  const int64_t rg = blockIdx.x / a.S;
+  const int slice = (int)(blockIdx.x % a.S);
+  const int kq_n = a.kq_n;
+  const int kqa = slice * a.slice_quads;
+  const int nq_slice = min(a.slice_quads, kq_n - kqa);
+  const int wq0 = wave * a.wave_quads;
+  const int wq1 = min(wq0 + a.wave_quads, nq_slice);
+  const int wblk = 4 * (wq1 - wq0);
+  uint8_t* xw = xs + wave * (4 * WQ) * kQ8FragBytes;
+  uint16_t* dxw = dxs + wave * (4 * WQ) * kQ8Rows;
+
+  // staging tasks (token t, block bl, k-group gg) = task (t SLOTS + 4 bl + gg), task =
+  // lane + 64 i: 8 codes each, the gg = 0 task also the block's scale
+  constexpr int SLOTS = 16 * WQ;
+  constexpr int NT = (TP * SLOTS + 63) / 64;
+  uint2 xr[NT];
+  uint16_t dr[NT];
+  const int64_t kb0 = (int64_t)(kqa + wq0) * 4;  // first block of the wave's run
+#pragma unroll
+  for (int i = 0; i < NT; ++i) {
+    const int task = lane + 64 * i;
+    const int t = task / SLOTS, bl = (task % SLOTS) >> 2, gg = task & 3;
+    if (t < T && bl < wblk) {
+      xr[i] = *reinterpret_cast<const uint2*>(a.xq + t * a.ldx + (kb0 + bl) * kQK + 8 * gg);
+      if (gg == 0) dr[i] = a.xd[t * (a.ldx / kQK) + kb0 + bl];
+    }
+  }
+  uint4 nib[WQ];
+  uint2 scl[WQ];
+  const uint8_t* tp = a.W0 + (rg * kq_n + kqa) * kTileNibbleBytes + lane * 16;
+  const uint8_t* sp = a.W0 + a.nibble_bytes + (rg * kq_n + kqa) * kTileScaleBytes + c * 8;
+#pragma unroll
+  for (int u = 0; u < WQ; ++u) {
+    const int q = min(wq0 + u, max(wq1 - 1, 0));
+    nib[u] = *reinterpret_cast<const uint4*>(tp + (int64_t)q * kTileNibbleBytes);
+    scl[u] = *reinterpret_cast<const uint2*>(sp + (int64_t)q * kTileScaleBytes);
+  }
+  for (int i = tid; i < 512; i += blockDim.x) {
+    const int e = i >> 1;
+    const uint32_t v = bf16_of_level(level_of(e & 15)) | (bf16_of_level(level_of(e >> 4)) << 16);
+    uint4* dst = reinterpret_cast<uint4*>(lut + e * kLutCopies + (i & 1) * 16);
+#pragma unroll
+    for (int w4 = 0; w4 < 4; ++w4) dst[w4] = uint4{v, v, v, v};
+  }
+  const uint32_t* lutl = lut + (lane & (kLutCopies - 1));
+
+  // codes -> bf16 A rows (exact), scales -> LDS
+#pragma unroll
+  for (int i = 0; i < NT; ++i) {
+    const int task = lane + 64 * i;
+    const int t = task / SLOTS, bl = (task % SLOTS) >> 2, gg = task & 3;
+    if (t < T && bl < wblk) {
+      uint32_t f[4];
+#pragma unroll
+      for (int j = 0; j < 4; ++j) {
+        const uint32_t word = (j < 2) ? xr[i].x : xr[i].y;
+        const int s0 = 16 * (j & 1);
+        const float lo = (float)(int8_t)((word >> s0) & 0xFFu);
+        const float hi = (float)(int8_t)((word >> (s0 + 8)) & 0xFFu);
+        f[j] = __builtin_amdgcn_perm(__float_as_uint(hi), __float_as_uint(lo), 0x07060302u);
+      }
+      *reinterpret_cast<uint4*>(xw + (bl * 4 + gg) * (kQ8Rows * 16) + t * 16) = uint4{f[0], f[1], f[2], f[3]};
+      if (gg == 0) dxw[bl * kQ8Rows + t] = dr[i];
+    }
+  }
+  lds_barrier();  // the table (LDS only: no wait on the weights in flight)
+
+  // lanes of rows >= 8 (and of tokens >= T) read some token's row: their outputs are
+  // never used, and an MFMA output row depends on its own A row only
+  f32x4 acc = f32x4{0.f, 0.f, 0.f, 0.f};
+#pragma unroll
+  for (int u = 0; u < WQ; ++u) {
+    if (wq0 + u >= wq1) break;
+    __builtin_amdgcn_sched_barrier(0);  // quad u's work waits for quad u's weights only
+    u32x4 xf[4], bf[4];
+#pragma unroll
+    for (int j = 0; j < 4; ++j) {
+      const int bl = 4 * u + j;
+      xf[j] = *reinterpret_cast<const u32x4*>(xw + (bl * 4 + g) * (kQ8Rows * 16) + (c & 7) * 16);
+      const uint32_t w = (j == 0) ? nib[u].x : (j == 1) ? nib[u].y : (j == 2) ? nib[u].z : nib[u].w;
+      bf[j][0] = lutl[(w & 0xFF) * kLutCopies];
+      bf[j][1] = lutl[((w >> 8) & 0xFF) * kLutCopies];
+      bf[j][2] = lutl[((w >> 16) & 0xFF) * kLutCopies];
+      bf[j][3] = lutl[(w >> 24) * kLutCopies];
+    }
+    f32x4 prod[4];
+#pragma unroll
+    for (int j = 0; j < 4; ++j) prod[j] = mfma_bf16(xf[j], bf[j], f32x4{0.f, 0.f, 0.f, 0.f});
+#pragma unroll
+    for (int j = 0; j < 4; ++j) {
+      const int bl = 4 * u + j;
+      const uint32_t sw = (j < 2) ? scl[u].x : scl[u].y;
+      const float dw = h2f((uint16_t)(sw >> (16 * (j & 1))));
+      const uint2 dx4 = *reinterpret_cast<const uint2*>(dxw + bl * kQ8Rows + 4 * (g & 1));
+#pragma unroll
+      for (int i = 0; i < 4; ++i) {
+        const uint32_t hw = (i < 2) ? dx4.x : dx4.y;
+        const float s = dw * h2f((uint16_t)(hw >> (16 * (i & 1))));  // exact: 11 x 11 bits
+        acc[i] = __builtin_fmaf(s, prod[j][i], acc[i]);
+      }
+    }
+  }
+
+  // cross-wave reduction in wave order: lane (g, c) held D[4g + i][c], token 4g + i.
+  // Up to 128 outputs: a narrow workgroup (small K) covers them in several rounds.
+  red[wave * 64 + lane] = acc;
+  lds_barrier();
+  const float* redf = reinterpret_cast<const float*>(red);
+  const int nout = T * kTileRows;
+  auto output = [&](int idx) -> float {
+    const int t = idx >> 4, row = idx & 15;
+    float pv[kWaves];
+#pragma unroll
+    for (int w2 = 0; w2 < kWaves; ++w2) pv[w2] = redf[(w2 * 64 + 16 * (t >> 2) + row) * 4 + (t & 3)];
+    float v = pv[0];
+#pragma unroll
+    for (int w2 = 1; w2 < kWaves; ++w2) v = (w2 < nwaves) ? v + pv[w2] : v;
+    return v;
+  };
+  if (a.S == 1) {
+    for (int idx = tid; idx < nout; idx += (int)blockDim.x) {
+      const int64_t col = rg * kTileRows + (idx & 15);
+      if (col < a.n) a.y[(idx >> 4) * a.ldy + col] = output(idx);
+    }
+    return;
+  }
+  // split K: as the float matvec (agent-scope stores, counter, last arriver adds the
+  // slices in order and resets the counter)
+  float* part = a.partials + (rg * a.S + slice) * (kQ8Rows * kTileRows);
+  for (int idx = tid; idx < nout; idx += (int)blockDim.x)
+    __hip_atomic_store(part + idx, output(idx), __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
+  __builtin_amdgcn_s_waitcnt(0);
+  __syncthreads();
+  if (tid == 0)
+    s_last = __hip_atomic_fetch_add(a.counters + rg, 1, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT) == a.S - 1;
+  __syncthreads();
+  if (s_last) {
+    for (int idx = tid; idx < nout; idx += (int)blockDim.x) {
+      const int64_t col = rg * kTileRows + (idx & 15);
+      if (col >= a.n) continue;
+      const float* p0 = a.partials + rg * a.S * (kQ8Rows * kTileRows) + idx;
+      float sum = __hip_atomic_load(p0, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
+      for (int sl = 1; sl < a.S; ++sl)
+        sum += __hip_atomic_load(p0 + sl * (kQ8Rows * kTileRows), __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
+      a.y[(idx >> 4) * a.ldy + col] = sum;
+    }
+    if (tid == 0) __hip_atomic_store(a.counters + rg, 0, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
+  }
+}
+
+int launch_quantize_q8(const float* x, int64_t T, int64_t k, int64_t ldx, int8_t* q, uint16_t* d,
+                       hipStream_t s) {
+  const int64_t n8 = T * (k / 8);
+  if (n8 == 0) return 0;
+  hipLaunchKernelGGL(quantize_q8_kernel, dim3((unsigned)((n8 + 255) / 256)), dim3(256), 0, s, x, T, k, ldx, q, d);
+  return check_launch("quantize_q8_kernel");
+}
+
+template <int WQ, int TP>
+static int launch_q8_t(const QmvArgs& a, int64_t grid) {
+  hipLaunchKernelGGL((qmv_q8_kernel<WQ, TP>), dim3((unsigned)grid), dim3(64 * a.nwaves), 0, a.stream, a);
+  return check_launch("qmv_q8_kernel");
+}
+
+template <int WQ>
+static int launch_q8(const QmvArgs& a, int64_t grid) {
+  switch (a.T) {
+    case 1: return launch_q8_t<WQ, 1>(a, grid);
+    case 2: return launch_q8_t<WQ, 2>(a, grid);
+    case 3: return launch_q8_t<WQ, 3>(a, grid);
+    case 4: return launch_q8_t<WQ, 4>(a, grid);
+    default: return launch_q8_t<WQ, kQ8Rows>(a, grid);
+  }
+}
+
+int launch_qmv_q8(const uint8_t* packed, int64_t n, int64_t k, const int8_t* q, const uint16_t* d, int T,
+                  float* y, int64_t ldy, void* workspace, hipStream_t s) {
+  QmvArgs a{};
+  a.W0 = packed;
+  a.xq = q;
+  a.xd = d;
+  a.ldx = k;
+  a.T = T;
+  a.y = y;
+  a.ldy = ldy;
+  a.stream = s;
+  qmv_plan(a, n, k, kDenseRG);
+  if (a.S > 1) {
+    a.counters = reinterpret_cast<int*>(static_cast<uint8_t*>(workspace) + ws_counters_off(a));
+    a.partials = reinterpret_cast<float*>(static_cast<uint8_t*>(workspace) + ws_partials8_off(a));
+  }
+  const int64_t grid = a.rg_n * a.S;
+  if (grid == 0) return 0;
+  switch (a.wave_quads) {
+    case 1: return launch_q8<1>(a, grid);
+    case 2: return launch_q8<2>(a, grid);
+    case 3: return launch_q8<3>(a, grid);
+    default: return launch_q8<kMaxWaveQuads>(a, grid);
+  }
 }
 
 }  // namespace iq4

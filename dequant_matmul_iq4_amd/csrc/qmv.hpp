@@ -11,6 +11,8 @@ struct QmvArgs {
   const uint8_t* W1;        // GATEUP: up bank
   int64_t w_expert_stride;  // bytes between experts' packed matrices
   const float* x;           // DENSE: X [T][ldx]; GATEUP: X [n_tok][ldx]; DOWN: h [pairs][ldx]
+  const int8_t* xq;         // 8-bit activations: codes [T][K] (ldx = K)
+  const uint16_t* xd;       // 8-bit activations: binary16 block scales [T][K/32]
   int64_t ldx;
   int T;                    // DENSE: columns
   float* y;                 // DENSE: Y [T][ldy]; GATEUP: h [pairs][ldy]; DOWN: rows [pairs][ldy]
@@ -31,6 +33,10 @@ struct QmvArgs {
 };
 
 int64_t qmv_workspace_bytes(int64_t n, int64_t k);
+int launch_quantize_q8(const float* x, int64_t T, int64_t k, int64_t ldx, int8_t* q, uint16_t* d,
+                       hipStream_t s);
+int launch_qmv_q8(const uint8_t* packed, int64_t n, int64_t k, const int8_t* q, const uint16_t* d, int T,
+                  float* y, int64_t ldy, void* workspace, hipStream_t s);
 int launch_qmv_grouped(int mode, QmvArgs a, int64_t n, int64_t k, int n_expert, int64_t n_pairs);
 
 }  // namespace iq4

@@ -113,8 +113,9 @@ int64_t iq4_packed_bytes(int64_t n, int64_t k);
 int iq4_pack_weights(const void* blocks, int64_t n, int64_t k, void* packed, void* stream);
 
 /*
- * Workspace bytes iq4_qmv_multi needs for an n x k matrix (written to *bytes; 0 when
- * the shape is covered without splitting K over workgroups).  Depends on n and k only.
+ * Workspace bytes iq4_qmv_multi and iq4_qmv_q8 need for an n x k matrix (written to
+ * *bytes; 0 when the shape is covered without splitting K over workgroups).  Depends on
+ * n and k only.
  */
 int iq4_qmv_workspace_size(int64_t n, int64_t k, size_t* bytes);
 
@@ -140,6 +141,44 @@ int iq4_qmv_workspace_size(int64_t n, int64_t k, size_t* bytes);
 int iq4_qmv_multi(const void* packed, int64_t n, int64_t k, const float* x, int64_t ldx,
                   int32_t T, float* y, int64_t ldy, void* workspace, size_t ws_bytes,
                   void* stream);
+
+/*
+ * 8-bit block quantisation of fp32 activations (the activation side of page 1's
+ * decode products: its verify.hpp keeps the window's T activation columns as q8_1
+ * blocks; the pages name that format without printing it).  Per column t and block of
+ * 32 consecutive k:
+ *   d = f32(absmax) / 127 and r = 1 / d (IEEE binary32 divisions; r = 0 when d rounds
+ *   to a zero binary16), q_i = nearest integer of f32(x_i * r), halves away from zero,
+ *   clamped to [-127, 127];  stored: q (int8) and d rounded to binary16.
+ * The format's sum field (needed only by zero-offset weight formats) is not produced.
+ *   x   [T][ldx] float32, 16-byte aligned, ldx >= k, ldx % 4 == 0, finite values.
+ *   q   [T][k] int8 (row stride k), 8-byte aligned.
+ *   d   [T][k/32] binary16 (row stride k/32), 2-byte aligned.
+ *   T >= 0 (0: no-op), k > 0, k % 32 == 0.
+ * Bit-exact: the codes and scales are a function of x alone.
+ * Errors: IQ4_E_ARG (sizes, ldx, null pointer), IQ4_E_ALIGN.
+ */
+int iq4_quantize_q8_1(const float* x, int64_t T, int64_t k, int64_t ldx, int8_t* q, uint16_t* d,
+                      void* stream);
+
+/*
+ * T-column quantised matrix-vector product on 8-bit activations (page 1's decode
+ * numerics; page 2's interleaved-matvec commit messages describe its integer block
+ * dots):
+ *   Y[t][r] = sum_b dw[r][b] * dx[t][b] * sum_i c[qw[r][32b+i]] * q[t][32b+i],
+ * each block's dot an exact integer, scaled by the exact product of the two binary16
+ * scales with one fp32 fused multiply-add, fp32 result.  Column t of a T-column call is
+ * bitwise equal to a 1-column call on column t; results are deterministic.
+ *   packed     W in the packed layout (iq4_pack_weights), 256-byte aligned.
+ *   q, d       as iq4_quantize_q8_1 writes them for T columns of this k.
+ *   y          [T][ldy] float32, ldy >= n, 4-byte aligned.   T: 1..8.
+ *   workspace  as for iq4_qmv_multi (iq4_qmv_workspace_size covers both calls; the
+ *              two may share one workspace on one stream).
+ * Errors: IQ4_E_ARG (T, ldy, null pointer), IQ4_E_UNSUPPORTED (n % 16, k % 128),
+ * IQ4_E_ALIGN, IQ4_E_WORKSPACE.
+ */
+int iq4_qmv_q8(const void* packed, int64_t n, int64_t k, const int8_t* q, const uint16_t* d, int32_t T,
+               float* y, int64_t ldy, void* workspace, size_t ws_bytes, void* stream);
 
 /*
  * Top-k routing from router logits: ids[t] = the top_k experts with the largest

@@ -115,3 +115,26 @@ def test_binding_raises_with_message():
     with pytest.raises(iq4.IQ4Error) as ei:
         iq4.iq4_qmv_multi(FAKE, 16, 128, FAKE, 128, 0, FAKE, 16, None, 0, stream=0)
     assert ei.value.code == iq4.IQ4_E_ARG and "T must be" in str(ei.value)
+
+
+def test_q8_validation_errors_never_launch():
+    # quantize: k % 32, ldx, alignment, null
+    assert _rc("iq4_quantize_q8_1", FAKE, 2, 48, 48, FAKE, FAKE, None) == iq4.IQ4_E_ARG
+    assert _rc("iq4_quantize_q8_1", FAKE, 2, 64, 60, FAKE, FAKE, None) == iq4.IQ4_E_ARG
+    assert _rc("iq4_quantize_q8_1", FAKE, -1, 64, 64, FAKE, FAKE, None) == iq4.IQ4_E_ARG
+    assert _rc("iq4_quantize_q8_1", FAKE + 4, 2, 64, 64, FAKE, FAKE, None) == iq4.IQ4_E_ALIGN
+    assert _rc("iq4_quantize_q8_1", FAKE, 2, 64, 64, FAKE + 4, FAKE, None) == iq4.IQ4_E_ALIGN
+    assert _rc("iq4_quantize_q8_1", FAKE, 2, 64, 64, None, FAKE, None) == iq4.IQ4_E_ARG
+    assert _rc("iq4_quantize_q8_1", None, 0, 64, 64, None, None, None) == iq4.IQ4_OK  # T = 0: no-op
+    # matvec: T range, shape, ldy, alignment, workspace
+    assert _rc("iq4_qmv_q8", FAKE, 16, 128, FAKE, FAKE, 0, FAKE, 16, None, 0, None) == iq4.IQ4_E_ARG
+    assert "T must be" in iq4.iq4_last_error()
+    assert _rc("iq4_qmv_q8", FAKE, 16, 128, FAKE, FAKE, 9, FAKE, 16, None, 0, None) == iq4.IQ4_E_ARG
+    assert _rc("iq4_qmv_q8", FAKE, 17, 128, FAKE, FAKE, 1, FAKE, 17, None, 0, None) == iq4.IQ4_E_UNSUPPORTED
+    assert _rc("iq4_qmv_q8", FAKE, 16, 96, FAKE, FAKE, 1, FAKE, 16, None, 0, None) == iq4.IQ4_E_UNSUPPORTED
+    assert _rc("iq4_qmv_q8", FAKE, 16, 128, FAKE, FAKE, 1, FAKE, 15, None, 0, None) == iq4.IQ4_E_ARG
+    assert _rc("iq4_qmv_q8", FAKE, 16, 128, FAKE + 4, FAKE, 1, FAKE, 16, None, 0, None) == iq4.IQ4_E_ALIGN
+    assert _rc("iq4_qmv_q8", FAKE, 16, 128, FAKE, FAKE + 1, 1, FAKE, 16, None, 0, None) == iq4.IQ4_E_ALIGN
+    assert _rc("iq4_qmv_q8", None, 16, 128, FAKE, FAKE, 1, FAKE, 16, None, 0, None) == iq4.IQ4_E_ARG
+    need = iq4.iq4_qmv_workspace_size(256, 14336)
+    assert _rc("iq4_qmv_q8", FAKE, 256, 14336, FAKE, FAKE, 1, FAKE, 256, FAKE, need - 1, None) == iq4.IQ4_E_WORKSPACE
