@@ -12,6 +12,8 @@ One step = one pass over every step of the hot path, on resident synthetic input
      comes from a graph of the eight steps replayed back to back;
   4. MoE prefill layer: 3,256 f16 tokens, Zipf(1.1)-skewed top-8 routing, same bank;
   5. long-prompt projection: 13,056 f16 tokens x W 14,336 x 4,096, 512-token chunks.
+Besides the step: the verify-window matvec on 8-bit activations (the q8_1 decode
+numerics) at T = 1..4 over the same weight copies, and the activation quantisation.
 
 Prints ONE JSON line.  ``value`` = effective weight GB/s of the verify-window matvec
 (total weight bytes of the T = 1..4 calls / their total time).  Launch times come from
@@ -186,6 +188,10 @@ def main():
     vwsb = iq4.iq4_qmv_workspace_size(n, k)
     vws = torch.zeros(max(vwsb, 256), dtype=torch.uint8, device="cuda")
     deq_out = torch.empty(n * k, dtype=torch.float16, device="cuda")
+    # 8-bit activations of the same four columns (the q8_1 decode numerics)
+    vq = torch.empty((4, k), dtype=torch.int8, device="cuda")
+    vd = torch.empty((4, k // 32), dtype=torch.int16, device="cuda")
+    iq4.iq4_quantize_q8_1(vx, 4, k, k, vq, vd)
 
     # The decode step reads ~80 MB of one bank; rotating over 8 banks (2.7 GB) puts 7
     # other steps' reads between two uses of a bank, well past the 256 MB Infinity Cache.
@@ -223,6 +229,12 @@ def main():
     # ---- the step's calls ----------------------------------------------------------------
     def mmvq(copy, T, s):
         iq4.iq4_qmv_multi(vcopies[copy % R], n, k, vx, k, T, vy, n, vws, vwsb, s)
+
+    def mmvq_q8(copy, T, s):
+        iq4.iq4_qmv_q8(vcopies[copy % R], n, k, vq, vd, T, vy, n, vws, vwsb, s)
+
+    def quantize_q8(s):
+        iq4.iq4_quantize_q8_1(vx, 4, k, k, vq, vd, s)
 
     def dequant(s):
         iq4.iq4_dequant_blocks(vblocks, n * k // 32, iq4.IQ4_F16, deq_out, s)
@@ -308,6 +320,24 @@ def main():
         b.record(stream)
         torch.cuda.synchronize()
         per_T[T] = a.elapsed_time(b) / (reps * R)  # ms per launch
+    # ---- the same for the 8-bit-activation matvec, and its activation quantisation -----
+    def per_launch_ms(fn, launches):
+        g = capture(fn)
+        g.replay()
+        torch.cuda.synchronize()
+        a, b = Ev(), Ev()
+        reps = 4
+        a.record(stream)
+        for _ in range(reps):
+            g.replay()
+        b.record(stream)
+        torch.cuda.synchronize()
+        return a.elapsed_time(b) / (reps * launches)
+
+    per_T_q8 = {T: per_launch_ms(lambda s, T=T: [mmvq_q8(c, T, s) for c in range(R)], R) for T in (1, 2, 3, 4)}
+    quant_ms = per_launch_ms(lambda s: [quantize_q8(s) for _ in range(R)], R)
+    q8_alg = sum(wb + T * k + T * (k // 32) * 2 + 4 * T * n for T in (1, 2, 3, 4))  # W + codes + scales + Y
+    q8_achieved = q8_alg / (sum(per_T_q8.values()) * 1e-3) / 1e9
     # ---- MoE decode step device time: one graph of N_BANKS steps back to back, so a
     # step's figure holds no graph-launch gap (the per-step events above include one) ---
     dec_all = capture(lambda s: [moe_decode(b, s) for b in banks])
@@ -356,6 +386,9 @@ def main():
             "moe_decode_us_per_step": round(dec_ms * 1e3, 2),
             "moe_decode_us_in_step": round(comp["moe_decode"] * 1e3, 2),
             "moe_decode_unique_experts": n_unique,
+            "mmvq_q8_us_per_call": {str(T): round(per_T_q8[T] * 1e3, 3) for T in per_T_q8},
+            "mmvq_q8_weight_gbs_per_T": {str(T): round(wb / (per_T_q8[T] * 1e-3) / 1e9, 1) for T in per_T_q8},
+            "quantize_q8_us_4x4096": round(quant_ms * 1e3, 3),
             "dense_ms_26_chunks": round(comp["dense"], 4),
             "dense_tflops": round(dense_flop / (comp["dense"] * 1e-3) / 1e12, 2),
             "dequant_us": round(comp["dequant"] * 1e3, 2),
@@ -381,6 +414,9 @@ def main():
                                     "unique experts' weights; traffic = HBM bytes of the two matvec launches",
                                     traffic=sum_traffic("qmv_grouped_gateup_moe_decode_4tok",
                                                         "qmv_grouped_down_moe_decode_4tok")),
+            "mmvq_q8": roof("hbm", q8_achieved, HBM_PEAK_GBS, "GB/s",
+                            "qmv_q8_kernel: verify-window matvec on 8-bit activations, bytes = W + codes + "
+                            "scales + Y per call, mean over T=1..4"),
             "dequant": roof("hbm", deq_bytes / (comp["dequant"] * 1e-3) / 1e9, HBM_PEAK_GBS, "GB/s",
                             "dequant_kernel<f16>: 9.4 MB of blocks in, 33.5 MB of f16 out"),
         },
