@@ -79,7 +79,12 @@ __device__ __forceinline__ const float* column_ptr(const QmvArgs& a, int mode, i
 // (s = 3) omitted, 16 bytes each: part s of elements 8g .. 8g+7 of the block (element
 // 8g+2i in the low, 8g+2i+1 in the high half of word i, the weights' index order).
 constexpr int kFragRows = 12;
-constexpr int kFragBytes = 4 * kFragRows * 16;  // 768 B per block
+// A (block, k-group) slot takes 13 rows of 16 B (12 used): the 16 lanes that stage
+// consecutive slots then write 16 distinct groups of 4 banks (a 12-row slot is 48
+// banks, which repeats every 4 lanes: 16-way conflicts on every staging store).
+constexpr int kFragStride = 13;
+static_assert(kFragStride > kFragRows, "a slot holds its rows");
+constexpr int kFragBytes = 4 * kFragStride * 16;  // 832 B per block
 
 // Exact three-way bf16 split of two values, packed per part: word s holds part s of v0
 // in its low and of v1 in its high half.  Part 0 (hi) is the top 16 bits of v; part 1
@@ -164,7 +169,7 @@ __global__ void __launch_bounds__(512) qmv_dense_kernel(QmvArgs a) {
         split_pair(xa.z, xa.w, p1);
         split_pair(xb.x, xb.y, p2);
         split_pair(xb.z, xb.w, p3);
-        uint8_t* dst = xw + (bl * 4 + gg) * (kFragRows * 16) + t * 16;
+        uint8_t* dst = xw + (bl * 4 + gg) * (kFragStride * 16) + t * 16;
 #pragma unroll
         for (int sp = 0; sp < 3; ++sp)
           *reinterpret_cast<uint4*>(dst + sp * 4 * 16) = uint4{p0[sp], p1[sp], p2[sp], p3[sp]};
@@ -206,7 +211,7 @@ __global__ void __launch_bounds__(512) qmv_dense_kernel(QmvArgs a) {
 #pragma unroll
       for (int j = 0; j < 4; ++j) {
         const int bl = 4 * u + j;  // block within this wave's run
-        xf[j] = *reinterpret_cast<const u32x4*>(xw + (bl * 4 + g) * (kFragRows * 16) + c * 16);
+        xf[j] = *reinterpret_cast<const u32x4*>(xw + (bl * 4 + g) * (kFragStride * 16) + c * 16);
         const uint32_t w = (j == 0) ? nib[u].x : (j == 1) ? nib[u].y : (j == 2) ? nib[u].z : nib[u].w;
         bf[j][0] = lutl[(w & 0xFF) * kLutCopies];
         bf[j][1] = lutl[((w >> 8) & 0xFF) * kLutCopies];
@@ -387,7 +392,7 @@ __global__ void __launch_bounds__(512) qmv_grouped_kernel(QmvArgs a) {
         split_pair(xa.z, xa.w, p1);
         split_pair(xb.x, xb.y, p2);
         split_pair(xb.z, xb.w, p3);
-        uint8_t* dst = xw + (bl * 4 + gg) * (kFragRows * 16) + t * 16;
+        uint8_t* dst = xw + (bl * 4 + gg) * (kFragStride * 16) + t * 16;
 #pragma unroll
         for (int sp = 0; sp < 3; ++sp)
           *reinterpret_cast<uint4*>(dst + sp * 4 * 16) = uint4{p0[sp], p1[sp], p2[sp], p3[sp]};
@@ -450,7 +455,7 @@ __global__ void __launch_bounds__(512) qmv_grouped_kernel(QmvArgs a) {
 #pragma unroll
       for (int j = 0; j < 4; ++j) {
         const int bl = 4 * u + j;
-        const u32x4 xf = *reinterpret_cast<const u32x4*>(xw + (bl * 4 + g) * (kFragRows * 16) + c * 16);
+        const u32x4 xf = *reinterpret_cast<const u32x4*>(xw + (bl * 4 + g) * (kFragStride * 16) + c * 16);
         u32x4 bf[NMAT][RG];
 #pragma unroll
         for (int m = 0; m < NMAT; ++m)
@@ -735,7 +740,8 @@ __global__ void __launch_bounds__(256) quantize_q8_kernel(const float* __restric
 // at most 14 bits, sums below 2^24), scaled by the exact product of the two binary16
 // scales with one fp32 FMA per block.  A column's arithmetic never depends on T.
 constexpr int kQ8Rows = 8;                      // tokens per call (A rows 0..7)
-constexpr int kQ8FragBytes = 4 * kQ8Rows * 16;  // 512 B per block: [k-group g][token][16 B]
+constexpr int kQ8Stride = 9;                      // rows per (block, k-group) slot (8 used; see kFragStride)
+constexpr int kQ8FragBytes = 4 * kQ8Stride * 16;  // 576 B per block: [k-group g][token][16 B]
 
 template <int WQ, int TP>
 __global__ void __launch_bounds__(512) qmv_q8_kernel(QmvArgs a) {
@@ -813,7 +819,7 @@ __global__ void __launch_bounds__(512) qmv_q8_kernel(QmvArgs a) {
         const float hi = (float)(int8_t)((word >> (s0 + 8)) & 0xFFu);
         f[j] = __builtin_amdgcn_perm(__float_as_uint(hi), __float_as_uint(lo), 0x07060302u);
       }
-      *reinterpret_cast<uint4*>(xw + (bl * 4 + gg) * (kQ8Rows * 16) + t * 16) = uint4{f[0], f[1], f[2], f[3]};
+      *reinterpret_cast<uint4*>(xw + (bl * 4 + gg) * (kQ8Stride * 16) + t * 16) = uint4{f[0], f[1], f[2], f[3]};
       if (gg == 0) dxw[bl * kQ8Rows + t] = dr[i];
     }
   }
@@ -830,7 +836,7 @@ __global__ void __launch_bounds__(512) qmv_q8_kernel(QmvArgs a) {
 #pragma unroll
     for (int j = 0; j < 4; ++j) {
       const int bl = 4 * u + j;
-      xf[j] = *reinterpret_cast<const u32x4*>(xw + (bl * 4 + g) * (kQ8Rows * 16) + (c & 7) * 16);
+      xf[j] = *reinterpret_cast<const u32x4*>(xw + (bl * 4 + g) * (kQ8Stride * 16) + (c & 7) * 16);
       const uint32_t w = (j == 0) ? nib[u].x : (j == 1) ? nib[u].y : (j == 2) ? nib[u].z : nib[u].w;
       bf[j][0] = lutl[(w & 0xFF) * kLutCopies];
       bf[j][1] = lutl[((w >> 8) & 0xFF) * kLutCopies];
