@@ -44,12 +44,13 @@ N_BANKS = 8                 # expert banks the decode step rotates over
 # at the time: a kernel changed since then reports traffic null.  Commands and raw
 # figures: profiles/<name>.txt.
 MEASURED_TRAFFIC = {
-    "qmv_dense_4096x4096_T1-4": (9926208, "585d2bb4783ac636", ("qmv.hip", "qmv.hpp", "common.hpp")),
-    "qmv_grouped_gateup_moe_decode_4tok": (55484735, "585d2bb4783ac636", ("qmv.hip", "qmv.hpp", "common.hpp")),
-    "qmv_grouped_down_moe_decode_4tok": (28657493, "585d2bb4783ac636", ("qmv.hip", "qmv.hpp", "common.hpp")),
-    "qgemm_gateup_moe_prefill_3256tok": (589236475, "fa0fd0a4be8a57c4", ("gemm.hip", "gemm.hpp", "common.hpp")),
-    "qgemm_down_moe_prefill_3256tok": (507852230, "fa0fd0a4be8a57c4", ("gemm.hip", "gemm.hpp", "common.hpp")),
-    "qgemm_dense_13056x4096x14336_chunk512": (94965194, "fa0fd0a4be8a57c4", ("gemm.hip", "gemm.hpp", "common.hpp")),
+    "qmv_dense_4096x4096_T1-4": (9929783, "dcca98bbc5adffe5", ("qmv.hip", "qmv.hpp", "common.hpp")),
+    "qmv_q8_4096x4096_T1-4": (9681450, "dcca98bbc5adffe5", ("qmv.hip", "qmv.hpp", "common.hpp")),
+    "qmv_grouped_gateup_moe_decode_4tok": (55478145, "dcca98bbc5adffe5", ("qmv.hip", "qmv.hpp", "common.hpp")),
+    "qmv_grouped_down_moe_decode_4tok": (28657563, "dcca98bbc5adffe5", ("qmv.hip", "qmv.hpp", "common.hpp")),
+    "qgemm_gateup_moe_prefill_3256tok": (589274979, "fa0fd0a4be8a57c4", ("gemm.hip", "gemm.hpp", "common.hpp")),
+    "qgemm_down_moe_prefill_3256tok": (507643848, "fa0fd0a4be8a57c4", ("gemm.hip", "gemm.hpp", "common.hpp")),
+    "qgemm_dense_13056x4096x14336_chunk512": (94965131, "fa0fd0a4be8a57c4", ("gemm.hip", "gemm.hpp", "common.hpp")),
 }
 
 
@@ -416,7 +417,8 @@ def main():
                                                         "qmv_grouped_down_moe_decode_4tok")),
             "mmvq_q8": roof("hbm", q8_achieved, HBM_PEAK_GBS, "GB/s",
                             "qmv_q8_kernel: verify-window matvec on 8-bit activations, bytes = W + codes + "
-                            "scales + Y per call, mean over T=1..4"),
+                            "scales + Y per call, mean over T=1..4; traffic = HBM bytes per launch",
+                            traffic=measured_traffic("qmv_q8_4096x4096_T1-4")),
             "dequant": roof("hbm", deq_bytes / (comp["dequant"] * 1e-3) / 1e9, HBM_PEAK_GBS, "GB/s",
                             "dequant_kernel<f16>: 9.4 MB of blocks in, 33.5 MB of f16 out"),
         },
