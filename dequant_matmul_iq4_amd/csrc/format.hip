@@ -52,23 +52,16 @@ __global__ void __launch_bounds__(256) quantize_kernel(const float* __restrict__
   }
 }
 
-// One thread per 8 consecutive outputs of a block: elements 8p .. 8p+7 are the low
-// (p < 2) or high (p >= 2) nibbles of index bytes 8(p % 2) .. 8(p % 2) + 7.
+// Elements 8p .. 8p+7 of one block are the low (p < 2) or high (p >= 2) nibbles of its
+// index bytes 8(p % 2) .. 8(p % 2) + 7 (the four 16-bit words v); they are stored as
+// output group i (8 consecutive outputs).
 template <bool F16>
-__global__ void __launch_bounds__(256) dequant_kernel(const uint16_t* __restrict__ blocks,
-                                                      int64_t nb, void* __restrict__ out) {
-  int64_t i = (int64_t)blockIdx.x * blockDim.x + threadIdx.x;
-  if (i >= nb * 4) return;
-  int64_t b = i >> 2;
-  int p = (int)(i & 3);
-  const uint16_t* blk = blocks + b * (kBlockBytes / 2);
-  const uint16_t dbits = blk[0];
+__device__ __forceinline__ void decode8(uint16_t dbits, const uint16_t (&v)[4], int p, void* out, int64_t i) {
   uint32_t bytes[8];
 #pragma unroll
   for (int j = 0; j < 4; ++j) {
-    uint16_t v = blk[1 + 4 * (p & 1) + j];
-    bytes[2 * j] = v & 0xFF;
-    bytes[2 * j + 1] = v >> 8;
+    bytes[2 * j] = v[j] & 0xFF;
+    bytes[2 * j + 1] = v[j] >> 8;
   }
   uint32_t q[8];
 #pragma unroll
@@ -95,6 +88,42 @@ __global__ void __launch_bounds__(256) dequant_kernel(const uint16_t* __restrict
     o[0] = make_float4(w[0], w[1], w[2], w[3]);
     o[1] = make_float4(w[4], w[5], w[6], w[7]);
   }
+}
+
+// Any alignment: one thread per 8 consecutive outputs, its block's bytes read directly.
+template <bool F16>
+__global__ void __launch_bounds__(256) dequant_kernel(const uint16_t* __restrict__ blocks,
+                                                      int64_t nb, void* __restrict__ out) {
+  int64_t i = (int64_t)blockIdx.x * blockDim.x + threadIdx.x;
+  if (i >= nb * 4) return;
+  const int64_t b = i >> 2;
+  const int p = (int)(i & 3);
+  const uint16_t* blk = blocks + b * (kBlockBytes / 2);
+  uint16_t v[4];
+#pragma unroll
+  for (int j = 0; j < 4; ++j) v[j] = blk[1 + 4 * (p & 1) + j];
+  decode8<F16>(blk[0], v, p, out, i);
+}
+
+// 16-byte-aligned blocks, 64 per workgroup: the workgroup's 1,152 bytes come in with
+// 72 coalesced 16-byte loads and each thread reads its block's bytes back from LDS
+// (the direct form issues five 2-byte loads per thread).
+constexpr int kStagedBlocks = 64;
+constexpr int kStagedChunks = kStagedBlocks * kBlockBytes / 16;  // 72
+
+template <bool F16>
+__global__ void __launch_bounds__(256) dequant_staged_kernel(const uint4* __restrict__ blocks,
+                                                             void* __restrict__ out) {
+  __shared__ uint4 st[kStagedChunks];
+  const int tid = threadIdx.x;
+  if (tid < kStagedChunks) st[tid] = blocks[(int64_t)blockIdx.x * kStagedChunks + tid];
+  __syncthreads();
+  const int b = tid >> 2, p = tid & 3;
+  const uint16_t* blk = reinterpret_cast<const uint16_t*>(st) + b * (kBlockBytes / 2);
+  uint16_t v[4];
+#pragma unroll
+  for (int j = 0; j < 4; ++j) v[j] = blk[1 + 4 * (p & 1) + j];
+  decode8<F16>(blk[0], v, p, out, (int64_t)blockIdx.x * 256 + tid);
 }
 
 // One thread per packed entry (64 per tile).  Entry l = 16g + j of tile (rt, kq) holds,
@@ -151,12 +180,27 @@ int launch_quantize(const float* src, int64_t nb, void* blocks, hipStream_t s) {
 
 int launch_dequant(const void* blocks, int64_t nb, bool f16, void* out, hipStream_t s) {
   if (nb == 0) return 0;
-  int64_t grid = (nb * 4 + 255) / 256;
   const uint16_t* b = static_cast<const uint16_t*>(blocks);
+  // whole groups of 64 blocks through the staged kernel when the blocks are 16-byte
+  // aligned; the rest (or everything, if unaligned) through the direct one
+  const int64_t groups = aligned(blocks, 16) ? nb / kStagedBlocks : 0;
+  if (groups > 0) {
+    const uint4* b16 = static_cast<const uint4*>(blocks);
+    if (f16)
+      hipLaunchKernelGGL(dequant_staged_kernel<true>, dim3((unsigned)groups), dim3(256), 0, s, b16, out);
+    else
+      hipLaunchKernelGGL(dequant_staged_kernel<false>, dim3((unsigned)groups), dim3(256), 0, s, b16, out);
+    if (int e = check_launch("dequant_staged_kernel")) return e;
+  }
+  const int64_t done = groups * kStagedBlocks, rest = nb - done;
+  if (rest == 0) return 0;
+  const uint16_t* bt = b + done * (kBlockBytes / 2);
+  void* ot = static_cast<uint8_t*>(out) + done * kQK * (f16 ? 2 : 4);
+  const int64_t grid = (rest * 4 + 255) / 256;
   if (f16)
-    hipLaunchKernelGGL(dequant_kernel<true>, dim3((unsigned)grid), dim3(256), 0, s, b, nb, out);
+    hipLaunchKernelGGL(dequant_kernel<true>, dim3((unsigned)grid), dim3(256), 0, s, bt, rest, ot);
   else
-    hipLaunchKernelGGL(dequant_kernel<false>, dim3((unsigned)grid), dim3(256), 0, s, b, nb, out);
+    hipLaunchKernelGGL(dequant_kernel<false>, dim3((unsigned)grid), dim3(256), 0, s, bt, rest, ot);
   return check_launch("dequant_kernel");
 }
 

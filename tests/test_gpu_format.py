@@ -80,3 +80,18 @@ def test_dequant_odd_count():
     rng = np.random.default_rng(3)
     b = oracle.encode_blocks(rng.standard_normal((7, 32)).astype(np.float32))
     assert bits_equal(gpu_dequant(b, False), oracle.decode_blocks(b))
+
+
+def test_dequant_staged_and_direct_paths():
+    """197 blocks: three staged groups of 64 plus a direct tail when 16-byte aligned,
+    and all direct when the same blocks start 2 bytes into an allocation."""
+    note("dequant: 197 blocks, aligned and at a 2-byte offset (f32 and f16)")
+    rng = np.random.default_rng(21)
+    b = oracle.encode_blocks((rng.standard_normal((197, 32)) * 0.02).astype(np.float32))
+    for f16, ref in ((False, oracle.decode_blocks(b)), (True, oracle.decode_blocks_f16(b))):
+        assert bits_equal(gpu_dequant(b, f16), ref)
+        raw = torch.zeros(b.size + 16, dtype=torch.uint8, device="cuda")
+        raw[2:2 + b.size] = dev(b.reshape(-1))
+        out = torch.empty(197 * 32, dtype=torch.float16 if f16 else torch.float32, device="cuda")
+        iq4.iq4_dequant_blocks(raw.data_ptr() + 2, 197, iq4.IQ4_F16 if f16 else iq4.IQ4_F32, out)
+        assert bits_equal(host(out).reshape(ref.shape), ref)
