@@ -44,10 +44,10 @@ N_BANKS = 8                 # expert banks the decode step rotates over
 # at the time: a kernel changed since then reports traffic null.  Commands and raw
 # figures: profiles/<name>.txt.
 MEASURED_TRAFFIC = {
-    "qmv_dense_4096x4096_T1-4": (9929783, "dcca98bbc5adffe5", ("qmv.hip", "qmv.hpp", "common.hpp")),
-    "qmv_q8_4096x4096_T1-4": (9681450, "dcca98bbc5adffe5", ("qmv.hip", "qmv.hpp", "common.hpp")),
-    "qmv_grouped_gateup_moe_decode_4tok": (55478145, "dcca98bbc5adffe5", ("qmv.hip", "qmv.hpp", "common.hpp")),
-    "qmv_grouped_down_moe_decode_4tok": (28657563, "dcca98bbc5adffe5", ("qmv.hip", "qmv.hpp", "common.hpp")),
+    "qmv_dense_4096x4096_T1-4": (9929783, "f1d00db3921a97c9", ("qmv.hip", "qmv.hpp", "common.hpp")),
+    "qmv_q8_4096x4096_T1-4": (9681450, "f1d00db3921a97c9", ("qmv.hip", "qmv.hpp", "common.hpp")),
+    "qmv_grouped_gateup_moe_decode_4tok": (55478145, "f1d00db3921a97c9", ("qmv.hip", "qmv.hpp", "common.hpp")),
+    "qmv_grouped_down_moe_decode_4tok": (28657563, "f1d00db3921a97c9", ("qmv.hip", "qmv.hpp", "common.hpp")),
     "qgemm_gateup_moe_prefill_3256tok": (589274979, "fa0fd0a4be8a57c4", ("gemm.hip", "gemm.hpp", "common.hpp")),
     "qgemm_down_moe_prefill_3256tok": (507643848, "fa0fd0a4be8a57c4", ("gemm.hip", "gemm.hpp", "common.hpp")),
     "qgemm_dense_13056x4096x14336_chunk512": (94965131, "fa0fd0a4be8a57c4", ("gemm.hip", "gemm.hpp", "common.hpp")),

@@ -21,9 +21,9 @@
 // Column invariance.  Token t's value never meets another token's: it sits in matrix
 // row 4s + (t mod 4) of the pass that holds it, the per-block scaling and the
 // reductions run the same instruction sequence for every t, and the wave / K-slice
-// split depends on K only.  Column t of a T-column call is therefore bitwise the 1-column call on token t
-// (the property page 1's verify window relies on: each window token reproduces plain
-// greedy decode bit for bit).
+// split depends on K only.  Column t of a T-column call is therefore bitwise the
+// 1-column call on token t (the property page 1's verify window relies on: each
+// window token reproduces plain greedy decode bit for bit).
 //
 // Work split.  A workgroup (up to 8 waves) owns RG row tiles (16 rows each) and a slice
 // of K of at most 128 blocks; each wave owns a contiguous run of at most 4 quads
@@ -41,7 +41,11 @@
 // issues one 128-bit load of indices (coalesced 1 KiB per wave) and one 64-bit load
 // of its row's four scales.  The index-to-level decode is a byte-indexed table in LDS
 // (one byte = two 4-bit indices of consecutive elements -> two bf16 levels), built from
-// register immediates.
+// register immediates and replicated so that lanes read their own copies.
+//
+// 8-bit activations.  The same plan, weight stream and table serve the product on
+// 8-bit activation codes (quantize_q8_kernel, qmv_q8_kernel at the end of this file):
+// a code is exact in bf16, so the matrix core returns each block's integer dot exactly.
 #include "common.hpp"
 #include "launch.hpp"
 #include "qmv.hpp"
