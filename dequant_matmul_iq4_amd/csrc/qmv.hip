@@ -571,6 +571,167 @@ __global__ void __launch_bounds__(512) qmv_grouped_kernel(QmvArgs a) {
   }
 }
 
+// Grouped down matvec for a short K (at most 7 quads, e.g. the MoE decode's intermediate
+// size): every wave owns whole 16-row tiles, all of K, so a tile's result needs no
+// cross-wave reduction and the loop has no barrier.  The workgroup stages its expert's
+// activation columns once (all of K, split into the three bf16 parts), every wave
+// requests the weights of its first two tiles at entry, and a tile's three parts are
+// added across lanes with two shuffles, in the order (hi + mid) + lo.  A column's
+// arithmetic never depends on the other columns.
+template <int KQ>
+__global__ void __launch_bounds__(512) qmv_down_tiles_kernel(QmvArgs a) {
+  constexpr int NB = 4 * KQ;  // blocks of K
+  __shared__ uint32_t lut[256 * kLutCopies];
+  __shared__ __attribute__((aligned(16))) uint8_t xs[NB * kFragBytes + 256];
+
+  const int tid = threadIdx.x;
+  const int lane = tid & 63, wave = tid >> 6, nwaves = (int)(blockDim.x >> 6);
+  const int c = lane & 15, g = lane >> 4;
+
+  // ---- expert slot (as the grouped kernel) and this workgroup's row tiles ------------
+  const int64_t slot = blockIdx.x / a.rg_chunks;
+  const int64_t t0 = (blockIdx.x % a.rg_chunks) * a.rg_per_wg;
+  const int64_t t1 = min(t0 + (int64_t)a.rg_per_wg, a.nt);
+  int64_t e = -1, before = 0, seg0 = 0, ncols = 0;
+  for (int e0 = 0; e0 < a.n_expert && e < 0; e0 += 64) {
+    const int ee = e0 + lane;
+    const int lo = (ee < a.n_expert) ? a.offsets[ee] : 0;
+    const int hi = (ee < a.n_expert) ? a.offsets[ee + 1] : 0;
+    const bool act = hi > lo;
+    const uint64_t m = __ballot(act);
+    const int64_t cnt = __popcll(m);
+    if (slot < before + cnt) {
+      const uint64_t below = (lane == 0) ? 0ull : (~0ull >> (64 - lane));
+      const uint64_t hit = __ballot(act && before + __popcll(m & below) == slot);
+      const int L = __ffsll((unsigned long long)hit) - 1;
+      e = e0 + L;
+      seg0 = __shfl(lo, L);
+      ncols = __shfl(hi, L) - seg0;
+    }
+    before += cnt;
+  }
+  if (e < 0 || t0 >= t1) return;  // uniform over the workgroup
+  const uint8_t* W = a.W0 + e * a.w_expert_stride;
+
+  struct WSet {
+    uint4 nib[KQ];
+    uint2 scl[KQ];
+  };
+  auto load_w = [&](WSet& w, int64_t rt) {
+#pragma unroll
+    for (int q = 0; q < KQ; ++q) {
+      w.nib[q] = *reinterpret_cast<const uint4*>(W + (rt * KQ + q) * kTileNibbleBytes + lane * 16);
+      w.scl[q] = *reinterpret_cast<const uint2*>(W + a.nibble_bytes + (rt * KQ + q) * kTileScaleBytes + c * 8);
+    }
+  };
+  WSet wa, wb;
+  const int64_t r0 = t0 + wave;
+  if (r0 < t1) load_w(wa, r0);
+  if (r0 + nwaves < t1) load_w(wb, r0 + nwaves);
+
+  for (int i = tid; i < 512; i += blockDim.x) {  // level table: entry i / 2, 16 copies each
+    const int le = i >> 1;
+    const uint32_t v = bf16_of_level(level_of(le & 15)) | (bf16_of_level(level_of(le >> 4)) << 16);
+    uint4* dst = reinterpret_cast<uint4*>(lut + le * kLutCopies + (i & 1) * 16);
+#pragma unroll
+    for (int w4 = 0; w4 < 4; ++w4) dst[w4] = uint4{v, v, v, v};
+  }
+  const uint32_t* lutl = lut + (lane & (kLutCopies - 1));
+
+  // the pass's columns: h rows seg0 + p0 + t (pair-sorted), their pair ids and gate
+  // weights (scalar loads: the lists are not written during the call)
+  const __attribute__((address_space(4))) int32_t* cpairs = (const __attribute__((address_space(4))) int32_t*)a.pairs;
+  const __attribute__((address_space(4))) float* cgate = (const __attribute__((address_space(4))) float*)a.gate_w;
+  constexpr int NTASK = kCols * NB * 4;  // (column, block, k-group) staging tasks of a pass
+
+  for (int64_t p0 = 0; p0 < ncols; p0 += kCols) {
+    const int T = (int)min((int64_t)kCols, ncols - p0);
+    int32_t pc[kCols];
+    float gw[kCols];
+#pragma unroll
+    for (int t = 0; t < kCols; ++t) {
+      const int idx = __builtin_amdgcn_readfirstlane((int)(seg0 + p0 + min(t, T - 1)));
+      pc[t] = cpairs[idx];
+      gw[t] = cgate[pc[t]];
+    }
+    if (p0 > 0) __syncthreads();  // every wave is done with the previous pass's columns
+    for (int task = tid; task < NTASK; task += (int)blockDim.x) {
+      const int t = task / (NB * 4), bl = (task >> 2) % NB, gg = task & 3;
+      if (t < T) {
+        const float* p = a.x + (seg0 + p0 + t) * a.ldx + bl * kQK + 8 * gg;
+        const float4 xa = *reinterpret_cast<const float4*>(p);
+        const float4 xb = *reinterpret_cast<const float4*>(p + 4);
+        uint32_t q0[3], q1[3], q2[3], q3[3];
+        split_pair(xa.x, xa.y, q0);
+        split_pair(xa.z, xa.w, q1);
+        split_pair(xb.x, xb.y, q2);
+        split_pair(xb.z, xb.w, q3);
+        uint8_t* dst = xs + (bl * 4 + gg) * (kFragStride * 16) + t * 16;
+#pragma unroll
+        for (int sp = 0; sp < 3; ++sp)
+          *reinterpret_cast<uint4*>(dst + sp * 4 * 16) = uint4{q0[sp], q1[sp], q2[sp], q3[sp]};
+      }
+    }
+    __syncthreads();  // the table and the staged columns
+
+    auto tile = [&](const WSet& w, int64_t rt) {
+      f32x4 acc = f32x4{0.f, 0.f, 0.f, 0.f};
+#pragma unroll
+      for (int q = 0; q < KQ; ++q) {
+        __builtin_amdgcn_sched_barrier(0);  // quad q's work waits for quad q's weights only
+        u32x4 xf[4], bf[4];
+#pragma unroll
+        for (int j = 0; j < 4; ++j) {
+          xf[j] = *reinterpret_cast<const u32x4*>(xs + ((4 * q + j) * 4 + g) * (kFragStride * 16) + c * 16);
+          const uint32_t wd = (j == 0) ? w.nib[q].x : (j == 1) ? w.nib[q].y : (j == 2) ? w.nib[q].z : w.nib[q].w;
+          bf[j][0] = lutl[(wd & 0xFF) * kLutCopies];
+          bf[j][1] = lutl[((wd >> 8) & 0xFF) * kLutCopies];
+          bf[j][2] = lutl[((wd >> 16) & 0xFF) * kLutCopies];
+          bf[j][3] = lutl[(wd >> 24) * kLutCopies];
+        }
+        f32x4 prod[4];
+#pragma unroll
+        for (int j = 0; j < 4; ++j) prod[j] = mfma_bf16(xf[j], bf[j], f32x4{0.f, 0.f, 0.f, 0.f});
+#pragma unroll
+        for (int j = 0; j < 4; ++j) {
+          const uint32_t sw = (j < 2) ? w.scl[q].x : w.scl[q].y;
+          const float d = h2f((uint16_t)(sw >> (16 * (j & 1))));
+#pragma unroll
+          for (int i = 0; i < 4; ++i) acc[i] = __builtin_fmaf(d, prod[j][i], acc[i]);
+        }
+      }
+      // lane (g, c) holds D[4g + i][c]: part g of column i, weight row c; lanes of
+      // k-group 0 add the parts of lanes c + 16 and c + 32
+      float v[kCols];
+#pragma unroll
+      for (int i = 0; i < kCols; ++i) {
+        const float mid = __shfl(acc[i], (lane + 16) & 63);
+        const float lo = __shfl(acc[i], (lane + 32) & 63);
+        v[i] = (acc[i] + mid) + lo;
+      }
+      const int64_t col = rt * kTileRows + c;
+      if (g == 0 && col < a.n) {
+#pragma unroll
+        for (int i = 0; i < kCols; ++i)
+          if (i < T) a.y[(int64_t)pc[i] * a.ldy + col] = gw[i] * v[i];
+      }
+    };
+    // tiles r0, r0 + nwaves, ...: sets wa / wb alternate, each refilled two tiles ahead
+    for (int64_t rt = r0; rt < t1; rt += 2 * nwaves) {
+      tile(wa, rt);
+      if (rt + 2 * nwaves < t1) load_w(wa, rt + 2 * nwaves);
+      if (rt + nwaves < t1) {
+        tile(wb, rt + nwaves);
+        if (rt + 3 * nwaves < t1) load_w(wb, rt + 3 * nwaves);
+      }
+    }
+    if (p0 + kCols < ncols) {  // a further pass walks the tiles again
+      if (r0 < t1) load_w(wa, r0);
+      if (r0 + nwaves < t1) load_w(wb, r0 + nwaves);
+    }
+  }
+}
+
 // Shape-only launch plan (never depends on T): K is cut into slices of at most
 // kSliceQuads quads (more than one slice only for K > 4096), each wave of a workgroup
 // owns a contiguous run of at most kMaxWaveQuads quads of the slice.
@@ -674,6 +835,15 @@ static void grouped_split(QmvArgs& a, int64_t slots) {
   a.rg_chunks = (a.rg_n + per - 1) / per;
 }
 
+constexpr int64_t kMaxDownTilesK = 7 * kTileK;  // 896: two weight sets of 7 quads still fit the registers
+
+template <int KQ>
+static int launch_down_tiles(const QmvArgs& a, int64_t grid) {
+  if (grid == 0) return 0;
+  hipLaunchKernelGGL((qmv_down_tiles_kernel<KQ>), dim3((unsigned)grid), dim3(512), 0, a.stream, a);
+  return check_launch("qmv_down_tiles_kernel");
+}
+
 int launch_qmv_grouped(int mode, QmvArgs a, int64_t n, int64_t k, int n_expert, int64_t n_pairs) {
   a.n_expert = n_expert;
   const int64_t slots = (n_pairs < n_expert) ? n_pairs : n_expert;  // routed experts at most
@@ -682,6 +852,24 @@ int launch_qmv_grouped(int mode, QmvArgs a, int64_t n, int64_t k, int n_expert, 
     if (a.S != 1) return set_error(-3, "grouped matvec: K above 4096 is not supported");
     grouped_split(a, slots);
     return launch_grouped_sized<kQmvGateUp, kGateUpRG>(a, slots * a.rg_chunks);
+  }
+  if (k <= kMaxDownTilesK) {  // whole row tiles per wave (short K)
+    qmv_plan(a, n, k, 1);
+    const int64_t want = 256;  // workgroups
+    int64_t per = (a.nt * slots + want - 1) / want;
+    if (per < 1) per = 1;
+    a.rg_per_wg = (int)per;
+    a.rg_chunks = (a.nt + per - 1) / per;
+    const int64_t grid = slots * a.rg_chunks;
+    switch (a.kq_n) {
+      case 1: return launch_down_tiles<1>(a, grid);
+      case 2: return launch_down_tiles<2>(a, grid);
+      case 3: return launch_down_tiles<3>(a, grid);
+      case 4: return launch_down_tiles<4>(a, grid);
+      case 5: return launch_down_tiles<5>(a, grid);
+      case 6: return launch_down_tiles<6>(a, grid);
+      default: return launch_down_tiles<7>(a, grid);
+    }
   }
   qmv_plan(a, n, k, kDownRG);
   if (a.S != 1) return set_error(-3, "grouped matvec: K above 4096 is not supported");
