@@ -44,13 +44,13 @@ N_BANKS = 8                 # expert banks the decode step rotates over
 # at the time: a kernel changed since then reports traffic null.  Commands and raw
 # figures: profiles/<name>.txt.
 MEASURED_TRAFFIC = {
-    "qmv_dense_4096x4096_T1-4": (9929783, "f1d00db3921a97c9", ("qmv.hip", "qmv.hpp", "common.hpp")),
-    "qmv_q8_4096x4096_T1-4": (9681450, "f1d00db3921a97c9", ("qmv.hip", "qmv.hpp", "common.hpp")),
-    "qmv_grouped_gateup_moe_decode_4tok": (55478145, "f1d00db3921a97c9", ("qmv.hip", "qmv.hpp", "common.hpp")),
-    "qmv_grouped_down_moe_decode_4tok": (28657563, "f1d00db3921a97c9", ("qmv.hip", "qmv.hpp", "common.hpp")),
-    "qgemm_gateup_moe_prefill_3256tok": (589274979, "fa0fd0a4be8a57c4", ("gemm.hip", "gemm.hpp", "common.hpp")),
-    "qgemm_down_moe_prefill_3256tok": (507643848, "fa0fd0a4be8a57c4", ("gemm.hip", "gemm.hpp", "common.hpp")),
-    "qgemm_dense_13056x4096x14336_chunk512": (94965131, "fa0fd0a4be8a57c4", ("gemm.hip", "gemm.hpp", "common.hpp")),
+    "qmv_dense_4096x4096_T1-4": (9933131, "6622aa6a06fe9024", ("qmv.hip", "qmv.hpp", "common.hpp")),
+    "qmv_q8_4096x4096_T1-4": (9675317, "6622aa6a06fe9024", ("qmv.hip", "qmv.hpp", "common.hpp")),
+    "qmv_grouped_gateup_moe_decode_4tok": (55484741, "6622aa6a06fe9024", ("qmv.hip", "qmv.hpp", "common.hpp")),
+    "qmv_down_moe_decode_4tok": (28722588, "6622aa6a06fe9024", ("qmv.hip", "qmv.hpp", "common.hpp")),
+    "qgemm_gateup_moe_prefill_3256tok": (589229220, "fa0fd0a4be8a57c4", ("gemm.hip", "gemm.hpp", "common.hpp")),
+    "qgemm_down_moe_prefill_3256tok": (507636567, "fa0fd0a4be8a57c4", ("gemm.hip", "gemm.hpp", "common.hpp")),
+    "qgemm_dense_13056x4096x14336_chunk512": (94965238, "fa0fd0a4be8a57c4", ("gemm.hip", "gemm.hpp", "common.hpp")),
 }
 
 
@@ -411,10 +411,10 @@ def main():
                                      "TFLOP/s", "qgemm<dense> x 26 chunks; traffic = HBM bytes of the 26 launches",
                                      traffic=sum_traffic(*["qgemm_dense_13056x4096x14336_chunk512"] * 26)),
             "moe_decode_step": roof("hbm", unique_bytes / (dec_ms * 1e-3) / 1e9, HBM_PEAK_GBS,
-                                    "GB/s", f"gather + qmv<gateup> + qmv<down> + combine, {n_unique} "
+                                    "GB/s", f"gather + qmv<gateup> + qmv_down_tiles + combine, {n_unique} "
                                     "unique experts' weights; traffic = HBM bytes of the two matvec launches",
                                     traffic=sum_traffic("qmv_grouped_gateup_moe_decode_4tok",
-                                                        "qmv_grouped_down_moe_decode_4tok")),
+                                                        "qmv_down_moe_decode_4tok")),
             "mmvq_q8": roof("hbm", q8_achieved, HBM_PEAK_GBS, "GB/s",
                             "qmv_q8_kernel: verify-window matvec on 8-bit activations, bytes = W + codes + "
                             "scales + Y per call, mean over T=1..4; traffic = HBM bytes per launch",
