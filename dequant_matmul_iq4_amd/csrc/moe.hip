@@ -6,7 +6,8 @@
 //   weight) -> combine.
 // Decode (fp32 activations, few tokens):
 //   gather -> grouped matvec gate|up (+SwiGLU, h fp32) -> grouped matvec down (x gate
-//   weight) -> combine.
+//   weight) -> combine; with at most 64 pairs there is no gather launch: each matvec
+//   workgroup finds its expert and that expert's pairs from the ids.
 // The combine adds each token's top_k weighted slot rows in slot order j = 0..k-1, so
 // the result does not depend on how pairs were scheduled (page 1's PoolMultiFn:
 // per-slot rows (n_tok * k, n_embd), then summed per token).  The atomic variant adds
@@ -92,10 +93,14 @@ int launch_moe(const MoeCall& m, hipStream_t s) {
   const int64_t P = m.n_tok * m.top_k;
   if (m.n_tok == 0) return 0;
 
-  // prefill: the gather also writes the grouped GEMM's tile list
-  if (int e = launch_gather(m.ids, P, m.n_expert, counts, offsets, pairs, slot_row, m.f16 ? tiles : nullptr,
-                            m.f16 ? num_tiles : nullptr, s))
-    return e;
+  // prefill: the gather also writes the grouped GEMM's tile list.  A decode step with
+  // few pairs skips it: its matvecs find each expert's pairs from the ids.
+  const bool direct = !m.f16 && P <= kDirectMaxPairs;
+  if (!direct) {
+    if (int e = launch_gather(m.ids, P, m.n_expert, counts, offsets, pairs, slot_row, m.f16 ? tiles : nullptr,
+                              m.f16 ? num_tiles : nullptr, s))
+      return e;
+  }
 
   const int64_t gate_stride = m.inter * (m.hidden / kQK) * kBlockBytes;
   const int64_t down_stride = m.hidden * (m.inter / kQK) * kBlockBytes;
@@ -156,6 +161,8 @@ int launch_moe(const MoeCall& m, hipStream_t s) {
     g.ldy = m.inter;
     g.offsets = offsets;
     g.pairs = pairs;
+    g.ids = direct ? m.ids : nullptr;
+    g.n_pairs = (int)P;
     g.top_k = m.top_k;
     g.stream = s;
     if (int e = launch_qmv_grouped(kQmvGateUp, g, m.inter, m.hidden, m.n_expert, P)) return e;
@@ -168,6 +175,8 @@ int launch_moe(const MoeCall& m, hipStream_t s) {
     d.ldy = m.hidden;
     d.offsets = offsets;
     d.pairs = pairs;
+    d.ids = direct ? m.ids : nullptr;
+    d.n_pairs = (int)P;
     d.gate_w = m.w;
     d.top_k = m.top_k;
     d.stream = s;

@@ -64,19 +64,100 @@ __device__ __forceinline__ uint32_t bf16_of_level(int c) {
   return __float_as_uint((float)c) >> 16;  // exact: |c| <= 127
 }
 
-// Column t of the call: where its activations live.  The pair list is read through the
-// constant address space (it is not written during the call), so a uniform lookup is a
-// scalar load, counted apart from the weight loads in flight.
-__device__ __forceinline__ const float* column_ptr(const QmvArgs& a, int mode, int64_t seg0,
+// The expert of a grouped workgroup's slot: slot i takes the i-th smallest expert id that
+// has routed pairs.  seg0 = its first position in the pair list sorted by (expert, pair
+// id), ncols = its pair count; with the ids given, cols = the mask of its pair ids (bit p
+// for pair p: the columns in ascending pair order).  e < 0: no such expert.
+struct SlotInfo {
+  int64_t e, seg0, ncols;
+  uint64_t cols;
+};
+
+// From the gather's offsets: a ballot over the experts, 64 at a time, in every wave.
+__device__ __forceinline__ SlotInfo slot_from_offsets(const QmvArgs& a, int64_t slot, int lane) {
+  SlotInfo s{-1, 0, 0, 0};
+  int64_t before = 0;
+  for (int e0 = 0; e0 < a.n_expert && s.e < 0; e0 += 64) {
+    const int ee = e0 + lane;
+    const int lo = (ee < a.n_expert) ? a.offsets[ee] : 0;
+    const int hi = (ee < a.n_expert) ? a.offsets[ee + 1] : 0;
+    const bool act = hi > lo;
+    const uint64_t m = __ballot(act);
+    const int64_t cnt = __popcll(m);
+    if (slot < before + cnt) {
+      const uint64_t below = (lane == 0) ? 0ull : (~0ull >> (64 - lane));
+      const uint64_t hit = __ballot(act && before + __popcll(m & below) == slot);
+      const int L = __ffsll((unsigned long long)hit) - 1;
+      s.e = e0 + L;
+      s.seg0 = __shfl(lo, L);
+      s.ncols = __shfl(hi, L) - s.seg0;
+    }
+    before += cnt;
+  }
+  return s;
+}
+
+// From the routed ids themselves (at most 64 pairs, one per lane), so that no gather has
+// to run first: the wave marks the experts present in a bitmap (bm: 32 words of LDS of
+// its own, 1024 experts), counts them per word with a prefix sum over lanes, and picks
+// the slot's word and bit.  An id outside [0, n_expert) marks nothing.
+__device__ __forceinline__ SlotInfo slot_from_ids(const QmvArgs& a, int64_t slot, uint32_t* bm,
+                                                  int lane) {
+  const int v = (lane < a.n_pairs) ? a.ids[lane] : -1;
+  const bool valid = (unsigned)v < (unsigned)a.n_expert;
+  if (lane < 32) bm[lane] = 0u;
+  // a wave's LDS accesses execute in order; the fences only keep the compiler from
+  // moving them
+  __builtin_amdgcn_fence(__ATOMIC_RELEASE, "wavefront");
+  __builtin_amdgcn_wave_barrier();
+  __builtin_amdgcn_fence(__ATOMIC_ACQUIRE, "wavefront");
+  if (valid) atomicOr(bm + (v >> 5), 1u << (v & 31));
+  __builtin_amdgcn_fence(__ATOMIC_RELEASE, "wavefront");
+  __builtin_amdgcn_wave_barrier();
+  __builtin_amdgcn_fence(__ATOMIC_ACQUIRE, "wavefront");
+  const uint32_t word = (lane < 32) ? bm[lane] : 0u;
+  const int cnt = __popc(word);
+  int incl = cnt;  // inclusive prefix sum of the per-word counts
+#pragma unroll
+  for (int d = 1; d < 32; d <<= 1) {
+    const int o = __shfl_up(incl, d);
+    if (lane >= d) incl += o;
+  }
+  const int excl = incl - cnt;
+  SlotInfo s{-1, 0, 0, 0};
+  const uint64_t hw = __ballot(lane < 32 && excl <= slot && slot < incl);
+  if (hw == 0) return s;  // uniform: past the experts present
+  const int W = __ffsll((unsigned long long)hw) - 1;
+  const uint32_t wd = __shfl(word, W);
+  const int r = (int)slot - __shfl(excl, W);
+  const bool hb = lane < 32 && ((wd >> lane) & 1u) && __popc(wd & ((1u << lane) - 1u)) == r;
+  s.e = W * 32 + (__ffsll((unsigned long long)__ballot(hb)) - 1);
+  s.seg0 = __popcll(__ballot(valid && v < s.e));
+  s.cols = __ballot(valid && v == s.e);
+  s.ncols = __popcll(s.cols);
+  return s;
+}
+
+// Pair id of column t of the slot (uniform).  The pair list is read through the constant
+// address space (it is not written during the call), so the lookup is a scalar load,
+// counted apart from the weight loads in flight.
+__device__ __forceinline__ int pair_of(const QmvArgs& a, const SlotInfo& s, int64_t t) {
+  if (a.ids) {
+    uint64_t m = s.cols;
+    for (int64_t i = 0; i < t; ++i) m &= m - 1;
+    return __builtin_amdgcn_readfirstlane(__ffsll((unsigned long long)m) - 1);
+  }
+  const __attribute__((address_space(4))) int32_t* pairs =
+      (const __attribute__((address_space(4))) int32_t*)a.pairs;
+  return pairs[__builtin_amdgcn_readfirstlane((int)(s.seg0 + t))];
+}
+
+// Column t of the call: where its activations live.
+__device__ __forceinline__ const float* column_ptr(const QmvArgs& a, int mode, const SlotInfo& s,
                                                    int64_t t) {
   if (mode == kQmvDense) return a.x + t * a.ldx;
-  if (mode == kQmvGateUp) {
-    const __attribute__((address_space(4))) int32_t* pairs =
-        (const __attribute__((address_space(4))) int32_t*)a.pairs;
-    const int idx = __builtin_amdgcn_readfirstlane((int)(seg0 + t));  // uniform by construction
-    return a.x + (int64_t)(pairs[idx] / a.top_k) * a.ldx;
-  }
-  return a.x + (seg0 + t) * a.ldx;  // kQmvDown: h rows in pair-sorted order
+  if (mode == kQmvGateUp) return a.x + (int64_t)(pair_of(a, s, t) / a.top_k) * a.ldx;
+  return a.x + (s.seg0 + t) * a.ldx;  // kQmvDown: h rows in pair-sorted order
 }
 
 // A-fragment store of the slice in LDS: [block][k-group g][row 4s+t], padding rows
@@ -327,6 +408,7 @@ __global__ void __launch_bounds__(512) qmv_grouped_kernel(QmvArgs a) {
   __shared__ uint32_t lut[256 * kGroupedLutCopies];
   __shared__ __attribute__((aligned(16))) uint8_t xs[XBYTES + 256];  // + room for padding-row reads
   __shared__ f32x4 red[REDN];
+  __shared__ uint32_t bm[kWaves * 32];  // slot lookup from the ids: a bitmap per wave
 
   const int tid = threadIdx.x;
   const int lane = tid & 63, wave = tid >> 6, nwaves = (int)(blockDim.x >> 6);
@@ -338,24 +420,8 @@ __global__ void __launch_bounds__(512) qmv_grouped_kernel(QmvArgs a) {
   const int64_t slot = blockIdx.x / a.rg_chunks;
   const int64_t rg0 = (blockIdx.x % a.rg_chunks) * a.rg_per_wg;
   const int64_t rg1 = min(rg0 + (int64_t)a.rg_per_wg, a.rg_n);
-  int64_t e = -1, before = 0, seg0 = 0, ncols = 0;
-  for (int e0 = 0; e0 < a.n_expert && e < 0; e0 += 64) {
-    const int ee = e0 + lane;
-    const int lo = (ee < a.n_expert) ? a.offsets[ee] : 0;
-    const int hi = (ee < a.n_expert) ? a.offsets[ee + 1] : 0;
-    const bool act = hi > lo;
-    const uint64_t m = __ballot(act);
-    const int64_t cnt = __popcll(m);
-    if (slot < before + cnt) {
-      const uint64_t below = (lane == 0) ? 0ull : (~0ull >> (64 - lane));
-      const uint64_t hit = __ballot(act && before + __popcll(m & below) == slot);
-      const int L = __ffsll((unsigned long long)hit) - 1;
-      e = e0 + L;
-      seg0 = __shfl(lo, L);
-      ncols = __shfl(hi, L) - seg0;
-    }
-    before += cnt;
-  }
+  const SlotInfo si = a.ids ? slot_from_ids(a, slot, bm + 32 * wave, lane) : slot_from_offsets(a, slot, lane);
+  const int64_t e = si.e, seg0 = si.seg0, ncols = si.ncols;
   if (e < 0 || rg0 >= rg1) return;
   const uint8_t* W[2] = {a.W0 + e * a.w_expert_stride, a.W1 + e * a.w_expert_stride};
   const int kq_n = a.kq_n;
@@ -371,7 +437,7 @@ __global__ void __launch_bounds__(512) qmv_grouped_kernel(QmvArgs a) {
   auto load_x = [&](int64_t t0, int T) {  // tasks (column t, block, k-group gg), 64 lanes
     const float* col[kCols];
 #pragma unroll
-    for (int t = 0; t < kCols; ++t) col[t] = column_ptr(a, MODE, seg0, t0 + min(t, T - 1));
+    for (int t = 0; t < kCols; ++t) col[t] = column_ptr(a, MODE, si, t0 + min(t, T - 1));
 #pragma unroll
     for (int i = 0; i < WQ; ++i) {
       const int task = lane + 64 * i;
@@ -410,7 +476,6 @@ __global__ void __launch_bounds__(512) qmv_grouped_kernel(QmvArgs a) {
   };
   // DOWN: each column's pair id and gate weight (scalar loads through the constant
   // address space: the lists are not written during the call)
-  const __attribute__((address_space(4))) int32_t* cpairs = (const __attribute__((address_space(4))) int32_t*)a.pairs;
   const __attribute__((address_space(4))) float* cgate = (const __attribute__((address_space(4))) float*)a.gate_w;
   int32_t pcol[kCols];
   float gwcol[kCols];
@@ -418,8 +483,7 @@ __global__ void __launch_bounds__(512) qmv_grouped_kernel(QmvArgs a) {
     if (MODE != kQmvDown) return;
 #pragma unroll
     for (int t = 0; t < kCols; ++t) {
-      const int idx = __builtin_amdgcn_readfirstlane((int)(seg0 + t0 + min(t, T - 1)));
-      pcol[t] = cpairs[idx];
+      pcol[t] = pair_of(a, si, t0 + min(t, T - 1));
       gwcol[t] = cgate[pcol[t]];
     }
   };
@@ -583,6 +647,7 @@ __global__ void __launch_bounds__(512) qmv_down_tiles_kernel(QmvArgs a) {
   constexpr int NB = 4 * KQ;  // blocks of K
   __shared__ uint32_t lut[256 * kLutCopies];
   __shared__ __attribute__((aligned(16))) uint8_t xs[NB * kFragBytes + 256];
+  __shared__ uint32_t bm[kWaves * 32];  // slot lookup from the ids: a bitmap per wave
 
   const int tid = threadIdx.x;
   const int lane = tid & 63, wave = tid >> 6, nwaves = (int)(blockDim.x >> 6);
@@ -592,24 +657,8 @@ __global__ void __launch_bounds__(512) qmv_down_tiles_kernel(QmvArgs a) {
   const int64_t slot = blockIdx.x / a.rg_chunks;
   const int64_t t0 = (blockIdx.x % a.rg_chunks) * a.rg_per_wg;
   const int64_t t1 = min(t0 + (int64_t)a.rg_per_wg, a.nt);
-  int64_t e = -1, before = 0, seg0 = 0, ncols = 0;
-  for (int e0 = 0; e0 < a.n_expert && e < 0; e0 += 64) {
-    const int ee = e0 + lane;
-    const int lo = (ee < a.n_expert) ? a.offsets[ee] : 0;
-    const int hi = (ee < a.n_expert) ? a.offsets[ee + 1] : 0;
-    const bool act = hi > lo;
-    const uint64_t m = __ballot(act);
-    const int64_t cnt = __popcll(m);
-    if (slot < before + cnt) {
-      const uint64_t below = (lane == 0) ? 0ull : (~0ull >> (64 - lane));
-      const uint64_t hit = __ballot(act && before + __popcll(m & below) == slot);
-      const int L = __ffsll((unsigned long long)hit) - 1;
-      e = e0 + L;
-      seg0 = __shfl(lo, L);
-      ncols = __shfl(hi, L) - seg0;
-    }
-    before += cnt;
-  }
+  const SlotInfo si = a.ids ? slot_from_ids(a, slot, bm + 32 * wave, lane) : slot_from_offsets(a, slot, lane);
+  const int64_t e = si.e, seg0 = si.seg0, ncols = si.ncols;
   if (e < 0 || t0 >= t1) return;  // uniform over the workgroup
   const uint8_t* W = a.W0 + e * a.w_expert_stride;
 
@@ -640,7 +689,6 @@ __global__ void __launch_bounds__(512) qmv_down_tiles_kernel(QmvArgs a) {
 
   // the pass's columns: h rows seg0 + p0 + t (pair-sorted), their pair ids and gate
   // weights (scalar loads: the lists are not written during the call)
-  const __attribute__((address_space(4))) int32_t* cpairs = (const __attribute__((address_space(4))) int32_t*)a.pairs;
   const __attribute__((address_space(4))) float* cgate = (const __attribute__((address_space(4))) float*)a.gate_w;
   constexpr int NTASK = kCols * NB * 4;  // (column, block, k-group) staging tasks of a pass
 
@@ -650,8 +698,7 @@ __global__ void __launch_bounds__(512) qmv_down_tiles_kernel(QmvArgs a) {
     float gw[kCols];
 #pragma unroll
     for (int t = 0; t < kCols; ++t) {
-      const int idx = __builtin_amdgcn_readfirstlane((int)(seg0 + p0 + min(t, T - 1)));
-      pc[t] = cpairs[idx];
+      pc[t] = pair_of(a, si, p0 + min(t, T - 1));
       gw[t] = cgate[pc[t]];
     }
     if (p0 > 0) __syncthreads();  // every wave is done with the previous pass's columns

@@ -19,6 +19,10 @@ struct QmvArgs {
   int64_t ldy;
   const int32_t* offsets;   // grouped: per-expert start in the sorted pair list [E+1]
   const int32_t* pairs;     // grouped: sorted pair ids
+  const int32_t* ids;       // grouped, at most 64 pairs: routed expert per pair id; when
+                            // set, each workgroup finds its expert's pairs from these
+                            // (offsets and pairs unused: no gather launch)
+  int n_pairs;              // grouped: routed pairs (with ids)
   const float* gate_w;      // DOWN: gate weight per pair id
   int top_k;
   int n_expert;             // grouped: experts in the bank
@@ -31,6 +35,10 @@ struct QmvArgs {
   int64_t rg_chunks;        // grouped: workgroups per expert slot
   hipStream_t stream;
 };
+
+// Grouped matvecs find their experts' pairs from the routed ids themselves (no gather
+// launch) for at most this many pairs: one id per lane of a wave.
+constexpr int kDirectMaxPairs = 64;
 
 int64_t qmv_workspace_bytes(int64_t n, int64_t k);
 int launch_quantize_q8(const float* x, int64_t T, int64_t k, int64_t ldx, int8_t* q, uint16_t* d,

@@ -228,8 +228,11 @@ int iq4_moe_workspace_size(int64_t n_tok, int32_t top_k, int32_t n_expert, int64
  *   w_down      n_expert packed hidden x inter matrices, expert e at
  *               e * iq4_packed_bytes(hidden, inter).
  *   out         [n_tok][ldo] float32, overwritten.
- *   workspace   >= iq4_moe_workspace_size(...) bytes, 256-byte aligned; the call
- *               leaves the gather (counts, offsets, pairs, slot_row) at its start.
+ *   workspace   >= iq4_moe_workspace_size(...) bytes, 256-byte aligned.  A prefill
+ *               call, or a decode call with more than 64 routed pairs, leaves the
+ *               gather (counts, offsets, pairs, slot_row) at its start; a decode call
+ *               with at most 64 pairs runs no gather (its matvecs find each expert's
+ *               pairs from ids) and leaves that region unspecified.
  *   flags       0 (deterministic) or IQ4_MOE_ATOMIC_COMBINE (prefill only).
  * Errors: IQ4_E_ARG, IQ4_E_ALIGN, IQ4_E_UNSUPPORTED (hidden or inter not multiples of
  * 256 / 128), IQ4_E_WORKSPACE.
