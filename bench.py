@@ -44,13 +44,13 @@ N_BANKS = 8                 # expert banks the decode step rotates over
 # at the time: a kernel changed since then reports traffic null.  Commands and raw
 # figures: profiles/<name>.txt.
 MEASURED_TRAFFIC = {
-    "qmv_dense_4096x4096_T1-4": (9933131, "6622aa6a06fe9024", ("qmv.hip", "qmv.hpp", "common.hpp")),
-    "qmv_q8_4096x4096_T1-4": (9675317, "6622aa6a06fe9024", ("qmv.hip", "qmv.hpp", "common.hpp")),
-    "qmv_grouped_gateup_moe_decode_4tok": (55484741, "6622aa6a06fe9024", ("qmv.hip", "qmv.hpp", "common.hpp")),
-    "qmv_down_moe_decode_4tok": (28722588, "6622aa6a06fe9024", ("qmv.hip", "qmv.hpp", "common.hpp")),
-    "qgemm_gateup_moe_prefill_3256tok": (589229220, "fa0fd0a4be8a57c4", ("gemm.hip", "gemm.hpp", "common.hpp")),
-    "qgemm_down_moe_prefill_3256tok": (507636567, "fa0fd0a4be8a57c4", ("gemm.hip", "gemm.hpp", "common.hpp")),
-    "qgemm_dense_13056x4096x14336_chunk512": (94965238, "fa0fd0a4be8a57c4", ("gemm.hip", "gemm.hpp", "common.hpp")),
+    "qmv_dense_4096x4096_T1-4": (9933120, "7fb8e538f99783c3", ("qmv.hip", "qmv.hpp", "common.hpp")),
+    "qmv_q8_4096x4096_T1-4": (9675314, "7fb8e538f99783c3", ("qmv.hip", "qmv.hpp", "common.hpp")),
+    "qmv_grouped_gateup_moe_decode_4tok": (55491660, "7fb8e538f99783c3", ("qmv.hip", "qmv.hpp", "common.hpp")),
+    "qmv_down_moe_decode_4tok": (28719533, "7fb8e538f99783c3", ("qmv.hip", "qmv.hpp", "common.hpp")),
+    "qgemm_gateup_moe_prefill_3256tok": (589349308, "fa0fd0a4be8a57c4", ("gemm.hip", "gemm.hpp", "common.hpp")),
+    "qgemm_down_moe_prefill_3256tok": (507657566, "fa0fd0a4be8a57c4", ("gemm.hip", "gemm.hpp", "common.hpp")),
+    "qgemm_dense_13056x4096x14336_chunk512": (94965181, "fa0fd0a4be8a57c4", ("gemm.hip", "gemm.hpp", "common.hpp")),
 }
 
 
