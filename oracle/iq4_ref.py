@@ -33,7 +33,9 @@ Readings where the pages are silent (each also listed in the design notes):
   to [-127, 127], and the stored scale is ``f16_rne(d)``; the product of a weight block
   and an activation block is ``d_w * d_x * sum_i c[q_w,i] * q_i``.  This is the public
   definition of that 8-bit block format; its sum field serves zero-offset formats only
-  and is not produced.
+  and is not produced;
+* a shared expert (page 3's cooperative decode adds it after the routed sum, weight 1)
+  has the routed experts' sizes and the same SwiGLU form.
 
 Parity pins: the test-suite checks each function here against something other than
 itself (closed forms, brute force in exact rationals, invariants, hand-written golden
@@ -47,7 +49,7 @@ __all__ = [
     "CODEBOOK", "QK", "BLOCK_BYTES",
     "decode_blocks", "decode_blocks_f16", "encode_blocks",
     "qmv", "route_topk", "gather", "silu", "moe", "gemm",
-    "quantize_q8_1", "qmv_q8",
+    "quantize_q8_1", "qmv_q8", "moe_shared",
 ]
 
 #: The fixed 16-level int8 codebook of the block format (workload definition).
@@ -215,6 +217,23 @@ def moe(x, ids, w, gate_blocks, up_blocks, down_blocks, hidden: int, inter: int,
     returned as float32 ``[len(tokens), hidden]``.  ``tokens`` restricts the
     computation to a subset of token rows (for sampled checks at full size).
     """
+    out, rows = _moe64(x, ids, w, gate_blocks, up_blocks, down_blocks, hidden, inter, tokens)
+    if return_pair_rows:
+        return out.astype(np.float32), rows
+    return out.astype(np.float32)
+
+
+def _expert_ffn(X, gate_b, up_b, down_b, hidden: int, inter: int) -> np.ndarray:
+    """One SwiGLU expert on float64 rows X: ``Wd (silu(Wg x) * (Wu x))``."""
+    Wg = _matrix(gate_b, inter, hidden)
+    Wu = _matrix(up_b, inter, hidden)
+    Wd = _matrix(down_b, hidden, inter)
+    h = silu(X @ Wg.T) * (X @ Wu.T)
+    return h @ Wd.T
+
+
+def _moe64(x, ids, w, gate_blocks, up_blocks, down_blocks, hidden, inter, tokens):
+    """``moe`` in float64: (out [len(tokens), hidden], pair rows [len(tokens), k, hidden])."""
     X = np.asarray(x).astype(np.float64)
     ids = np.asarray(ids)
     w = np.asarray(w, dtype=np.float32).astype(np.float64)
@@ -228,18 +247,26 @@ def moe(x, ids, w, gate_blocks, up_blocks, down_blocks, hidden: int, inter: int,
         if not sel:
             continue
         xi = X[[toks[i] for i, _ in sel]]
-        Wg = _matrix(gate_blocks[e], inter, hidden)
-        Wu = _matrix(up_blocks[e], inter, hidden)
-        Wd = _matrix(down_blocks[e], hidden, inter)
-        h = silu(xi @ Wg.T) * (xi @ Wu.T)
-        y = h @ Wd.T
+        y = _expert_ffn(xi, gate_blocks[e], up_blocks[e], down_blocks[e], hidden, inter)
         for r, (i, j) in enumerate(sel):
             rows[i, j] = y[r]
     for j in range(k):
         out += w[toks, j][:, None] * rows[:, j, :]
-    if return_pair_rows:
-        return out.astype(np.float32), rows
-    return out.astype(np.float32)
+    return out, rows
+
+
+def moe_shared(x, ids, w, gate_blocks, up_blocks, down_blocks, shared_gate, shared_up, shared_down,
+               hidden: int, inter: int, tokens=None):
+    """``moe`` plus a shared expert that every token passes through with weight 1:
+    ``out[t] = sum_j w[t][j] * y_tj + ys_t`` with ``ys_t`` the shared expert's SwiGLU FFN
+    of ``x_t`` (the same sizes as the routed experts).  Page 3 (the DSpark drafter
+    file, its cooperative decode with the shared expert): the shared expert's output is
+    added, with weight 1, to the routed sum.  float64, returned as float32."""
+    out, _ = _moe64(x, ids, w, gate_blocks, up_blocks, down_blocks, hidden, inter, tokens)
+    X = np.asarray(x).astype(np.float64)
+    toks = np.arange(X.shape[0]) if tokens is None else np.asarray(tokens)
+    ys = _expert_ffn(X[toks], shared_gate, shared_up, shared_down, hidden, inter)
+    return (out + ys).astype(np.float32)
 
 
 def gemm(blocks, n: int, k: int, x) -> np.ndarray:

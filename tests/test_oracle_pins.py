@@ -398,6 +398,50 @@ def pin_moe_weight_summed_dense():
         assert np.allclose(out[t], ref, rtol=1e-6, atol=1e-9 * np.abs(ref).max())
 
 
+def pin_moe_shared_bruteforce():
+    """moe_shared = the routed sum plus the shared expert's SwiGLU FFN with weight 1,
+    recomputed in exact rationals (except for the exponential) from the closed-form
+    decoded matrices."""
+    x, ids, w, gate, up, down, H, I = tiny_moe(seed=21, n=2, E=3, H=32, I=32)
+    rng = np.random.default_rng(22)
+    sg, su, sd = (rand_blocks(rng, I * H // 32, 0.1), rand_blocks(rng, I * H // 32, 0.1),
+                  rand_blocks(rng, H * I // 32, 0.1))
+    out = R.moe_shared(x, ids, w, gate, up, down, sg, su, sd, H, I)
+    mats = [(bf_matrix(gate[e], I, H), bf_matrix(up[e], I, H), bf_matrix(down[e], H, I)) for e in range(3)]
+    shared = (bf_matrix(sg, I, H), bf_matrix(su, I, H), bf_matrix(sd, H, I))
+
+    def ffn(m, xt):
+        Wg, Wu, Wd = m
+        g = [sum(Wg[i][c] * xt[c] for c in range(H)) for i in range(I)]
+        u = [sum(Wu[i][c] * xt[c] for c in range(H)) for i in range(I)]
+        h = [Fraction(float(gi) / (1 + math.exp(-float(gi)))) * ui for gi, ui in zip(g, u)]
+        return [sum(Wd[r][i] * h[i] for i in range(I)) for r in range(H)]
+
+    for t in range(x.shape[0]):
+        xt = [Fraction(float(v)) for v in x[t]]
+        acc = ffn(shared, xt)
+        for j in range(ids.shape[1]):
+            y = ffn(mats[ids[t, j]], xt)
+            acc = [a + Fraction(float(w[t, j])) * v for a, v in zip(acc, y)]
+        ref = np.array([float(v) for v in acc])
+        assert np.allclose(out[t], ref, rtol=1e-6, atol=1e-9 * np.abs(ref).max())
+
+
+def pin_moe_shared_is_an_always_on_expert():
+    """The shared expert is a routed expert that every token takes with weight 1: the
+    (separately pinned) routed oracle on the bank extended by it, with it appended to
+    every token's routing, gives the same result."""
+    x, ids, w, gate, up, down, H, I = tiny_moe(seed=23, n=4, k=2, E=4)
+    rng = np.random.default_rng(24)
+    sg, su, sd = (rand_blocks(rng, I * H // 32, 0.1), rand_blocks(rng, I * H // 32, 0.1),
+                  rand_blocks(rng, H * I // 32, 0.1))
+    out = R.moe_shared(x, ids, w, gate, up, down, sg, su, sd, H, I, tokens=[3, 0, 2])
+    ids2 = np.concatenate([ids, np.full((ids.shape[0], 1), 4, np.int32)], axis=1)
+    w2 = np.concatenate([w, np.ones((w.shape[0], 1), np.float32)], axis=1)
+    ref = R.moe(x, ids2, w2, gate + [sg], up + [su], down + [sd], H, I, tokens=[3, 0, 2])
+    assert np.allclose(out, ref, rtol=1e-12, atol=1e-12 * np.abs(ref).max())
+
+
 def pin_moe_subset_rows():
     x, ids, w, gate, up, down, H, I = tiny_moe(n=6)
     full = R.moe(x, ids, w, gate, up, down, H, I)
@@ -494,6 +538,7 @@ PINS = [
     pin_qmv_one_hot, pin_qmv_fraction, pin_qmv_integer_exact, pin_gemm_fraction,
     pin_gemm_integer_exact, pin_route_golden, pin_route_bruteforce, pin_gather_bruteforce,
     pin_silu, pin_moe_single_expert_is_dense_ffn, pin_moe_weight_summed_dense, pin_moe_subset_rows,
+    pin_moe_shared_bruteforce, pin_moe_shared_is_an_always_on_expert,
     pin_q8_quantize_bruteforce, pin_q8_quantize_ties, pin_qmv_q8_fraction, pin_qmv_q8_on_grid_equals_fp32,
 ]
 
@@ -609,6 +654,17 @@ def _qmv_q8_no_act_scale(blocks, n, k, q, d):
     return _orig_qmv_q8(blocks, n, k, q, np.ones_like(np.asarray(d)))
 
 
+_orig_moe_shared = R.moe_shared
+
+
+def _moe_shared_dropped(x, ids, w, gate, up, down, sg, su, sd, H, I, tokens=None):
+    return R.moe(x, ids, w, gate, up, down, H, I, tokens=tokens)
+
+
+def _moe_shared_gate_up_swapped(x, ids, w, gate, up, down, sg, su, sd, H, I, tokens=None):
+    return _orig_moe_shared(x, ids, w, gate, up, down, su, sg, sd, H, I, tokens=tokens)
+
+
 PLANTED = {
     "codebook sign": ("CODEBOOK", tuple(-c for c in R.CODEBOOK)),
     "codebook off by one": ("CODEBOOK", tuple(R.CODEBOOK[1:]) + (127,)),
@@ -623,6 +679,8 @@ PLANTED = {
     "q8 ties to even": ("quantize_q8_1", _q8_ties_to_even),
     "q8 reciprocal of the stored scale": ("quantize_q8_1", _q8_reciprocal_of_stored_scale),
     "q8 product drops the activation scale": ("qmv_q8", _qmv_q8_no_act_scale),
+    "shared expert dropped": ("moe_shared", _moe_shared_dropped),
+    "shared expert gate and up swapped": ("moe_shared", _moe_shared_gate_up_swapped),
 }
 
 
