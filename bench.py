@@ -44,13 +44,13 @@ N_BANKS = 8                 # expert banks the decode step rotates over
 # at the time: a kernel changed since then reports traffic null.  Commands and raw
 # figures: profiles/<name>.txt.
 MEASURED_TRAFFIC = {
-    "qmv_dense_4096x4096_T1-4": (9933120, "7fb8e538f99783c3", ("qmv.hip", "qmv.hpp", "common.hpp")),
-    "qmv_q8_4096x4096_T1-4": (9675314, "7fb8e538f99783c3", ("qmv.hip", "qmv.hpp", "common.hpp")),
-    "qmv_grouped_gateup_moe_decode_4tok": (55491660, "7fb8e538f99783c3", ("qmv.hip", "qmv.hpp", "common.hpp")),
-    "qmv_down_moe_decode_4tok": (28719533, "7fb8e538f99783c3", ("qmv.hip", "qmv.hpp", "common.hpp")),
-    "qgemm_gateup_moe_prefill_3256tok": (589349308, "fa0fd0a4be8a57c4", ("gemm.hip", "gemm.hpp", "common.hpp")),
-    "qgemm_down_moe_prefill_3256tok": (507657566, "fa0fd0a4be8a57c4", ("gemm.hip", "gemm.hpp", "common.hpp")),
-    "qgemm_dense_13056x4096x14336_chunk512": (94965181, "fa0fd0a4be8a57c4", ("gemm.hip", "gemm.hpp", "common.hpp")),
+    "qmv_dense_4096x4096_T1-4": (9931080, "e8ee9e4a5adb85bb", ("qmv.hip", "qmv.hpp", "common.hpp")),
+    "qmv_q8_4096x4096_T1-4": (9673266, "e8ee9e4a5adb85bb", ("qmv.hip", "qmv.hpp", "common.hpp")),
+    "qmv_grouped_gateup_moe_decode_4tok": (55481268, "e8ee9e4a5adb85bb", ("qmv.hip", "qmv.hpp", "common.hpp")),
+    "qmv_down_moe_decode_4tok": (28738222, "e8ee9e4a5adb85bb", ("qmv.hip", "qmv.hpp", "common.hpp")),
+    "qgemm_gateup_moe_prefill_3256tok": (589004852, "0f4774c413fa418b", ("gemm.hip", "gemm.hpp", "common.hpp")),
+    "qgemm_down_moe_prefill_3256tok": (507686493, "0f4774c413fa418b", ("gemm.hip", "gemm.hpp", "common.hpp")),
+    "qgemm_dense_13056x4096x14336_chunk512": (94965204, "0f4774c413fa418b", ("gemm.hip", "gemm.hpp", "common.hpp")),
 }
 
 
@@ -148,6 +148,9 @@ def main():
     ap.add_argument("--warmup", type=int, default=3)
     ap.add_argument("--copies", type=int, default=64)
     ap.add_argument("--no-cpu-baseline", action="store_true")
+    ap.add_argument("--no-shared", action="store_true",
+                    help="skip the shared-expert MoE timings beside the step (keeps per-kernel profiles "
+                         "to the step's own launches)")
     ap.add_argument("--copy-calibration", type=int, default=0, metavar="MIB",
                     help="only copy a float32 buffer of MIB MiB three times (the known-size "
                          "kernel that scales the FETCH_SIZE / WRITE_SIZE counters), then exit")
@@ -352,6 +355,32 @@ def main():
     b.record(stream)
     torch.cuda.synchronize()
     dec_ms = a.elapsed_time(b) / (reps * N_BANKS)
+    # ---- beside the step: the same layer with a shared expert (its weights: expert 0 of
+    # the bank four steps away, so they are as cold as the routed ones) ---------------
+    sgb, sdb = iq4.iq4_packed_bytes(INTER, HIDDEN), iq4.iq4_packed_bytes(HIDDEN, INTER)
+
+    def shared_of(i):
+        g, u, d = banks[(i + N_BANKS // 2) % N_BANKS]
+        return g[:sgb], u[:sgb], d[:sdb]
+    ds_wsb = iq4.iq4_moe_shared_workspace_size(4, TOP_K, N_EXPERT, HIDDEN, INTER, iq4.IQ4_F32)
+    ps_wsb = iq4.iq4_moe_shared_workspace_size(NP, TOP_K, N_EXPERT, HIDDEN, INTER, iq4.IQ4_F16)
+    ds_ws = torch.empty(0 if args.no_shared else ds_wsb, dtype=torch.uint8, device="cuda")
+    ps_ws = torch.empty(0 if args.no_shared else ps_wsb, dtype=torch.uint8, device="cuda")
+
+    def moe_decode_shared(i, s):
+        (g, u, d), (sg, su, sd) = banks[i], shared_of(i)
+        iq4.iq4_moe_expert_gemm_shared(dx, iq4.IQ4_F32, 4, HIDDEN, d_ids, d_w, TOP_K, N_EXPERT, HIDDEN, INTER,
+                                       g, u, d, sg, su, sd, d_out, HIDDEN, ds_ws, ds_wsb, 0, s)
+
+    def moe_prefill_shared(s):
+        (g, u, d), (sg, su, sd) = bank_a, shared_of(0)
+        iq4.iq4_moe_expert_gemm_shared(px, iq4.IQ4_F16, NP, HIDDEN, p_ids, p_w, TOP_K, N_EXPERT, HIDDEN, INTER,
+                                       g, u, d, sg, su, sd, p_out, HIDDEN, ps_ws, ps_wsb, 0, s)
+    dec_shared_ms = pre_shared_ms = float("nan")
+    if not args.no_shared:
+        dec_shared_ms = per_launch_ms(lambda s: [moe_decode_shared(i, s) for i in range(N_BANKS)], N_BANKS)
+        pre_shared_ms = per_launch_ms(lambda s: [moe_prefill_shared(s) for _ in range(2)], 2)
+    del ps_ws
     tot_ms = sum(per_T.values())
     value = 4 * wb / (tot_ms * 1e-3) / 1e9
     mm_alg = sum(wb + 2 * 4 * T * k for T in (1, 2, 3, 4))  # weights + X + Y per four calls
@@ -387,6 +416,10 @@ def main():
             "moe_decode_us_per_step": round(dec_ms * 1e3, 2),
             "moe_decode_us_in_step": round(comp["moe_decode"] * 1e3, 2),
             "moe_decode_unique_experts": n_unique,
+            "moe_decode_shared_us_per_step": None if args.no_shared else round(dec_shared_ms * 1e3, 2),
+            "moe_prefill_shared_ms_per_layer": None if args.no_shared else round(pre_shared_ms, 4),
+            "moe_prefill_shared_tflops": None if args.no_shared else
+            round(prefill_flop * (TOP_K + 1) / TOP_K / (pre_shared_ms * 1e-3) / 1e12, 2),
             "mmvq_q8_us_per_call": {str(T): round(per_T_q8[T] * 1e3, 3) for T in per_T_q8},
             "mmvq_q8_weight_gbs_per_T": {str(T): round(wb / (per_T_q8[T] * 1e-3) / 1e9, 1) for T in per_T_q8},
             "quantize_q8_us_4x4096": round(quant_ms * 1e3, 3),

@@ -47,6 +47,11 @@ SIGNATURES = {
     "iq4_moe_expert_gemm": (ctypes.c_int, [_c_p, _c_i32, _c_i64, _c_i64, _c_p, _c_p, _c_i32, _c_i32,
                                            _c_i64, _c_i64, _c_p, _c_p, _c_p, _c_p, _c_i64, _c_p,
                                            _c_sz, _c_u32, _c_p]),
+    "iq4_moe_shared_workspace_size": (ctypes.c_int, [_c_i64, _c_i32, _c_i32, _c_i64, _c_i64, _c_i32,
+                                                     ctypes.POINTER(_c_sz)]),
+    "iq4_moe_expert_gemm_shared": (ctypes.c_int, [_c_p, _c_i32, _c_i64, _c_i64, _c_p, _c_p, _c_i32, _c_i32,
+                                                  _c_i64, _c_i64, _c_p, _c_p, _c_p, _c_p, _c_p, _c_p, _c_p,
+                                                  _c_i64, _c_p, _c_sz, _c_u32, _c_p]),
     "iq4_qgemm": (ctypes.c_int, [_c_p, _c_i64, _c_i64, _c_p, _c_i64, _c_i64, _c_p, _c_i64, _c_i64, _c_p]),
 }
 
@@ -162,6 +167,20 @@ def iq4_moe_expert_gemm(x, act_dtype, n_tok, ldx, ids, w, top_k, n_expert, hidde
     _call("iq4_moe_expert_gemm", _ptr(x), act_dtype, n_tok, ldx, _ptr(ids), _ptr(w), top_k, n_expert,
           hidden, inter, _ptr(w_gate), _ptr(w_up), _ptr(w_down), _ptr(out), ldo, _ptr(workspace),
           ws_bytes, flags, _stream(stream))
+
+
+def iq4_moe_shared_workspace_size(n_tok, top_k, n_expert, hidden, inter, act_dtype) -> int:
+    out = _c_sz(0)
+    _call("iq4_moe_shared_workspace_size", n_tok, top_k, n_expert, hidden, inter, act_dtype, ctypes.byref(out))
+    return out.value
+
+
+def iq4_moe_expert_gemm_shared(x, act_dtype, n_tok, ldx, ids, w, top_k, n_expert, hidden, inter,
+                               w_gate, w_up, w_down, s_gate, s_up, s_down, out, ldo, workspace, ws_bytes,
+                               flags=0, stream=None):
+    _call("iq4_moe_expert_gemm_shared", _ptr(x), act_dtype, n_tok, ldx, _ptr(ids), _ptr(w), top_k, n_expert,
+          hidden, inter, _ptr(w_gate), _ptr(w_up), _ptr(w_down), _ptr(s_gate), _ptr(s_up), _ptr(s_down),
+          _ptr(out), ldo, _ptr(workspace), ws_bytes, flags, _stream(stream))
 
 
 def iq4_qgemm(packed, n, k, x, m, ldx, y, ldy, chunk, stream=None):

@@ -210,27 +210,42 @@ int iq4_moe_workspace_size(int64_t n_tok, int32_t top_k, int32_t n_expert, int64
   return IQ4_OK;
 }
 
-int iq4_moe_expert_gemm(const void* x, int32_t act_dtype, int64_t n_tok, int64_t ldx,
-                        const int32_t* ids, const float* w, int32_t top_k, int32_t n_expert,
-                        int64_t hidden, int64_t inter, const void* w_gate, const void* w_up,
-                        const void* w_down, float* out, int64_t ldo, void* workspace,
-                        size_t ws_bytes, uint32_t flags, void* stream) {
+// The shared-expert call is validated as the routed call with one more expert and slot.
+int iq4_moe_shared_workspace_size(int64_t n_tok, int32_t top_k, int32_t n_expert, int64_t hidden,
+                                  int64_t inter, int32_t act_dtype, size_t* bytes) {
   clear_error();
-  const char* fn = "iq4_moe_expert_gemm";
-  if (int e = check_moe_sizes(fn, n_tok, top_k, n_expert, hidden, inter, act_dtype)) return e;
+  if (!bytes) return set_error(IQ4_E_ARG, "iq4_moe_shared_workspace_size: null bytes");
+  *bytes = 0;
+  if (top_k < 1 || n_expert < 1) return set_error(IQ4_E_ARG, "iq4_moe_shared_workspace_size: need top_k, n_expert >= 1");
+  if (int e = check_moe_sizes("iq4_moe_shared_workspace_size", n_tok, top_k + 1, n_expert + 1, hidden, inter, act_dtype))
+    return e;
+  *bytes = (size_t)moe_layout(n_tok, top_k, n_expert, hidden, inter, act_dtype == IQ4_F16, true).total;
+  return IQ4_OK;
+}
+
+static int moe_call(const char* fn, const void* x, int32_t act_dtype, int64_t n_tok, int64_t ldx,
+                    const int32_t* ids, const float* w, int32_t top_k, int32_t n_expert, int64_t hidden,
+                    int64_t inter, const void* w_gate, const void* w_up, const void* w_down,
+                    const void* s_gate, const void* s_up, const void* s_down, float* out, int64_t ldo,
+                    void* workspace, size_t ws_bytes, uint32_t flags, void* stream) {
+  const bool shared = s_gate || s_up || s_down;
+  if (shared && (top_k < 1 || n_expert < 1)) return set_error(IQ4_E_ARG, "%s: need top_k, n_expert >= 1", fn);
+  const int sk = shared ? 1 : 0;  // the shared expert counts as one more expert and slot
+  if (int e = check_moe_sizes(fn, n_tok, top_k + sk, n_expert + sk, hidden, inter, act_dtype)) return e;
   if (flags & ~IQ4_MOE_ATOMIC_COMBINE) return set_error(IQ4_E_ARG, "%s: unknown flags", fn);
   if (ldx < hidden || ldo < hidden) return set_error(IQ4_E_ARG, "%s: ldx and ldo must be >= hidden", fn);
   if (n_tok == 0) return IQ4_OK;
-  if (!x || !ids || !w || !w_gate || !w_up || !w_down || !out)
+  if (!x || !ids || !w || !w_gate || !w_up || !w_down || !out || (shared && !(s_gate && s_up && s_down)))
     return set_error(IQ4_E_ARG, "%s: null pointer", fn);
   const bool f16 = act_dtype == IQ4_F16;
   if (!aligned(x, 16) || ldx % (f16 ? 8 : 4) || !aligned(out, 16) || ldo % 4 || !aligned(ids, 4) ||
-      !aligned(w, 4) || !aligned(w_gate, 256) || !aligned(w_up, 256) || !aligned(w_down, 256))
+      !aligned(w, 4) || !aligned(w_gate, 256) || !aligned(w_up, 256) || !aligned(w_down, 256) ||
+      (shared && (!aligned(s_gate, 256) || !aligned(s_up, 256) || !aligned(s_down, 256))))
     return set_error(IQ4_E_ALIGN, "%s: x/out 16-byte aligned with ldx %% %d == 0 and ldo %% 4 == 0, "
                      "weights 256-byte aligned", fn, f16 ? 8 : 4);
-  if (n_tok * ldx >= ((int64_t)1 << 31) || n_tok * top_k * inter >= ((int64_t)1 << 31))
+  if (n_tok * ldx >= ((int64_t)1 << 31) || n_tok * (top_k + sk) * inter >= ((int64_t)1 << 31))
     return set_error(IQ4_E_UNSUPPORTED, "%s: x and the intermediate rows must span fewer than 2^31 elements", fn);
-  const MoeLayout L = moe_layout(n_tok, top_k, n_expert, hidden, inter, f16);
+  const MoeLayout L = moe_layout(n_tok, top_k, n_expert, hidden, inter, f16, shared);
   if (!workspace || ws_bytes < (size_t)L.total)
     return set_error(IQ4_E_WORKSPACE, "%s: needs a workspace of %lld bytes", fn, (long long)L.total);
   if (!aligned(workspace, 256)) return set_error(IQ4_E_ALIGN, "%s: workspace must be 256-byte aligned", fn);
@@ -248,11 +263,37 @@ int iq4_moe_expert_gemm(const void* x, int32_t act_dtype, int64_t n_tok, int64_t
   m.w_gate = w_gate;
   m.w_up = w_up;
   m.w_down = w_down;
+  m.s_gate = shared ? s_gate : nullptr;
+  m.s_up = shared ? s_up : nullptr;
+  m.s_down = shared ? s_down : nullptr;
   m.out = out;
   m.ldo = ldo;
   m.workspace = workspace;
   m.atomic = (flags & IQ4_MOE_ATOMIC_COMBINE) != 0;
   return launch_moe(m, as_stream(stream));
+}
+
+int iq4_moe_expert_gemm(const void* x, int32_t act_dtype, int64_t n_tok, int64_t ldx,
+                        const int32_t* ids, const float* w, int32_t top_k, int32_t n_expert,
+                        int64_t hidden, int64_t inter, const void* w_gate, const void* w_up,
+                        const void* w_down, float* out, int64_t ldo, void* workspace,
+                        size_t ws_bytes, uint32_t flags, void* stream) {
+  clear_error();
+  return moe_call("iq4_moe_expert_gemm", x, act_dtype, n_tok, ldx, ids, w, top_k, n_expert, hidden, inter,
+                  w_gate, w_up, w_down, nullptr, nullptr, nullptr, out, ldo, workspace, ws_bytes, flags, stream);
+}
+
+int iq4_moe_expert_gemm_shared(const void* x, int32_t act_dtype, int64_t n_tok, int64_t ldx,
+                               const int32_t* ids, const float* w, int32_t top_k, int32_t n_expert,
+                               int64_t hidden, int64_t inter, const void* w_gate, const void* w_up,
+                               const void* w_down, const void* s_gate, const void* s_up,
+                               const void* s_down, float* out, int64_t ldo, void* workspace,
+                               size_t ws_bytes, uint32_t flags, void* stream) {
+  clear_error();
+  if (!s_gate || !s_up || !s_down) return set_error(IQ4_E_ARG, "iq4_moe_expert_gemm_shared: null shared expert");
+  return moe_call("iq4_moe_expert_gemm_shared", x, act_dtype, n_tok, ldx, ids, w, top_k, n_expert, hidden,
+                  inter, w_gate, w_up, w_down, s_gate, s_up, s_down, out, ldo, workspace, ws_bytes, flags,
+                  stream);
 }
 
 int iq4_qgemm(const void* packed, int64_t n, int64_t k, const void* x, int64_t m, int64_t ldx,

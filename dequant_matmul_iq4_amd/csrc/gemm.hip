@@ -200,8 +200,13 @@ qgemm_kernel(GemmArgs a) {
     // GATEUP: a workgroup covers 128 intermediate columns (each wave 32 gate rows and
     // the same 32 up rows); DOWN: 256 output rows.
     n0 = (MODE == kGemmGateUp) ? nt * (kBN / 2) : nt * kBN;
-    W0 += (int64_t)e * a.w_expert_stride;
-    if (MODE == kGemmGateUp) W1 += (int64_t)e * a.w_expert_stride;
+    if (a.S0 != nullptr && e == a.shared_e) {  // the shared expert, routed to every token by the caller
+      W0 = a.S0;
+      W1 = a.S1;
+    } else {
+      W0 += (int64_t)e * a.w_expert_stride;
+      if (MODE == kGemmGateUp) W1 += (int64_t)e * a.w_expert_stride;
+    }
   }
   const int kq_n = (int)(a.K / kTileK);
   // fragment rows holding valid rows (a partial last tile of an expert, or of a chunk,

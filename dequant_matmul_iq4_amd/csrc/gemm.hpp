@@ -12,6 +12,9 @@ struct GemmArgs {
   const uint8_t* W0;        // packed weights (DENSE: W; GATEUP: gate bank; DOWN: down bank)
   const uint8_t* W1;        // GATEUP: up bank
   int64_t w_expert_stride;  // bytes between experts' packed matrices
+  int shared_e;             // grouped, with S0 set: this expert index takes S0 / S1
+  const uint8_t* S0;        // the shared expert's packed matrices (as W0 / W1), or null
+  const uint8_t* S1;
   int64_t N, K;             // weight rows and reduction length of one matrix
   int64_t M;                // DENSE: rows of A in this launch
   float* C;                 // DENSE: output [M][ldc]; DOWN: per-pair rows [pairs][ldc]

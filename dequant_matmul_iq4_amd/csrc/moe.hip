@@ -62,9 +62,30 @@ __global__ void __launch_bounds__(256) zero_rows_kernel(float* __restrict__ out,
 
 static inline int64_t align256(int64_t b) { return (b + 255) / 256 * 256; }
 
+// Routing with the shared expert behind: slots 0..k-1 of every token are the routed ones,
+// slot k is expert n_expert with gate weight 1, so the combine adds the routed rows in
+// slot order and then the shared expert's row (routed sum + shared).
+__global__ void __launch_bounds__(256) append_shared_kernel(const int32_t* __restrict__ ids,
+                                                             const float* __restrict__ w, int64_t n_tok,
+                                                             int top_k, int n_expert,
+                                                             int32_t* __restrict__ ids2,
+                                                             float* __restrict__ w2) {
+  const int64_t i = (int64_t)blockIdx.x * blockDim.x + threadIdx.x;
+  const int k2 = top_k + 1;
+  if (i >= n_tok * k2) return;
+  const int64_t t = i / k2;
+  const int j = (int)(i % k2);
+  ids2[i] = (j == top_k) ? n_expert : ids[t * top_k + j];
+  w2[i] = (j == top_k) ? 1.0f : w[t * top_k + j];
+}
+
 MoeLayout moe_layout(int64_t n_tok, int top_k, int n_expert, int64_t hidden, int64_t inter,
-                     bool f16) {
+                     bool f16, bool shared) {
   MoeLayout L{};
+  if (shared) {  // the routed call's sizes with the shared expert as one more expert and slot
+    ++top_k;
+    ++n_expert;
+  }
   const int64_t P = n_tok * top_k;
   int64_t off = 0;
   L.counts = off;    off += align256(4 * (int64_t)n_expert);
@@ -76,12 +97,15 @@ MoeLayout moe_layout(int64_t n_tok, int top_k, int n_expert, int64_t hidden, int
   L.tiles = off;     off += align256(8 * L.max_tiles);
   L.h = off;         off += align256(P * inter * (f16 ? 2 : 4));
   L.rows = off;      off += align256(P * hidden * 4);
+  L.ids2 = off;      off += shared ? align256(4 * P) : 0;
+  L.w2 = off;        off += shared ? align256(4 * P) : 0;
   L.total = off;
   return L;
 }
 
 int launch_moe(const MoeCall& m, hipStream_t s) {
-  const MoeLayout L = moe_layout(m.n_tok, m.top_k, m.n_expert, m.hidden, m.inter, m.f16);
+  const bool shared = m.s_gate != nullptr;
+  const MoeLayout L = moe_layout(m.n_tok, m.top_k, m.n_expert, m.hidden, m.inter, m.f16, shared);
   uint8_t* ws = static_cast<uint8_t*>(m.workspace);
   int32_t* counts = reinterpret_cast<int32_t*>(ws + L.counts);
   int32_t* offsets = reinterpret_cast<int32_t*>(ws + L.offsets);
@@ -90,14 +114,28 @@ int launch_moe(const MoeCall& m, hipStream_t s) {
   int32_t* num_tiles = reinterpret_cast<int32_t*>(ws + L.num_tiles);
   int32_t* tiles = reinterpret_cast<int32_t*>(ws + L.tiles);
   float* rows = reinterpret_cast<float*>(ws + L.rows);
-  const int64_t P = m.n_tok * m.top_k;
   if (m.n_tok == 0) return 0;
+  // the routing the products see: with a shared expert, one more expert and slot
+  const int32_t* ids = m.ids;
+  const float* w = m.w;
+  const int top_k = m.top_k + (shared ? 1 : 0);
+  const int n_expert = m.n_expert + (shared ? 1 : 0);
+  const int64_t P = m.n_tok * top_k;
+  if (shared) {
+    int32_t* ids2 = reinterpret_cast<int32_t*>(ws + L.ids2);
+    float* w2 = reinterpret_cast<float*>(ws + L.w2);
+    hipLaunchKernelGGL(append_shared_kernel, dim3((unsigned)((P + 255) / 256)), dim3(256), 0, s, m.ids, m.w,
+                       m.n_tok, m.top_k, m.n_expert, ids2, w2);
+    if (int e = check_launch("append_shared_kernel")) return e;
+    ids = ids2;
+    w = w2;
+  }
 
   // prefill: the gather also writes the grouped GEMM's tile list.  A decode step with
   // few pairs skips it: its matvecs find each expert's pairs from the ids.
   const bool direct = !m.f16 && P <= kDirectMaxPairs;
   if (!direct) {
-    if (int e = launch_gather(m.ids, P, m.n_expert, counts, offsets, pairs, slot_row, m.f16 ? tiles : nullptr,
+    if (int e = launch_gather(ids, P, n_expert, counts, offsets, pairs, slot_row, m.f16 ? tiles : nullptr,
                               m.f16 ? num_tiles : nullptr, s))
       return e;
   }
@@ -120,6 +158,9 @@ int launch_moe(const MoeCall& m, hipStream_t s) {
     g.W0 = static_cast<const uint8_t*>(m.w_gate);
     g.W1 = static_cast<const uint8_t*>(m.w_up);
     g.w_expert_stride = gate_stride;
+    g.shared_e = m.n_expert;
+    g.S0 = static_cast<const uint8_t*>(m.s_gate);
+    g.S1 = static_cast<const uint8_t*>(m.s_up);
     g.N = m.inter;
     g.K = m.hidden;
     g.H = h;
@@ -128,13 +169,15 @@ int launch_moe(const MoeCall& m, hipStream_t s) {
     g.num_tiles = num_tiles;
     g.offsets = offsets;
     g.pairs = pairs;
-    g.top_k = m.top_k;
+    g.top_k = top_k;
     if (int e = launch_qgemm_grouped(kGemmGateUp, g, L.max_tiles, s)) return e;
     GemmArgs d{};
     d.A = h;
     d.lda = m.inter;
     d.W0 = static_cast<const uint8_t*>(m.w_down);
     d.w_expert_stride = down_stride;
+    d.shared_e = m.n_expert;
+    d.S0 = static_cast<const uint8_t*>(m.s_down);
     d.N = m.hidden;
     d.K = m.inter;
     d.C = rows;
@@ -143,8 +186,8 @@ int launch_moe(const MoeCall& m, hipStream_t s) {
     d.num_tiles = num_tiles;
     d.offsets = offsets;
     d.pairs = pairs;
-    d.gate_w = m.w;
-    d.top_k = m.top_k;
+    d.gate_w = w;
+    d.top_k = top_k;
     d.out = m.out;
     d.ldo = m.ldo;
     d.atomic = atomic ? 1 : 0;
@@ -155,38 +198,43 @@ int launch_moe(const MoeCall& m, hipStream_t s) {
     g.W0 = static_cast<const uint8_t*>(m.w_gate);
     g.W1 = static_cast<const uint8_t*>(m.w_up);
     g.w_expert_stride = gate_stride;
+    g.shared_e = m.n_expert;
+    g.S0 = static_cast<const uint8_t*>(m.s_gate);
+    g.S1 = static_cast<const uint8_t*>(m.s_up);
     g.x = static_cast<const float*>(m.x);
     g.ldx = m.ldx;
     g.y = h;
     g.ldy = m.inter;
     g.offsets = offsets;
     g.pairs = pairs;
-    g.ids = direct ? m.ids : nullptr;
+    g.ids = direct ? ids : nullptr;
     g.n_pairs = (int)P;
-    g.top_k = m.top_k;
+    g.top_k = top_k;
     g.stream = s;
-    if (int e = launch_qmv_grouped(kQmvGateUp, g, m.inter, m.hidden, m.n_expert, P)) return e;
+    if (int e = launch_qmv_grouped(kQmvGateUp, g, m.inter, m.hidden, n_expert, P)) return e;
     QmvArgs d{};
     d.W0 = static_cast<const uint8_t*>(m.w_down);
     d.w_expert_stride = down_stride;
+    d.shared_e = m.n_expert;
+    d.S0 = static_cast<const uint8_t*>(m.s_down);
     d.x = h;
     d.ldx = m.inter;
     d.y = rows;
     d.ldy = m.hidden;
     d.offsets = offsets;
     d.pairs = pairs;
-    d.ids = direct ? m.ids : nullptr;
+    d.ids = direct ? ids : nullptr;
     d.n_pairs = (int)P;
-    d.gate_w = m.w;
-    d.top_k = m.top_k;
+    d.gate_w = w;
+    d.top_k = top_k;
     d.stream = s;
-    if (int e = launch_qmv_grouped(kQmvDown, d, m.hidden, m.inter, m.n_expert, P)) return e;
+    if (int e = launch_qmv_grouped(kQmvDown, d, m.hidden, m.inter, n_expert, P)) return e;
   }
 
   if (!atomic) {
     const int64_t n4 = m.n_tok * (m.hidden / 4);
     hipLaunchKernelGGL(combine_kernel, dim3((unsigned)((n4 + 255) / 256)), dim3(256), 0, s, rows,
-                       m.hidden, m.n_tok, m.top_k, m.hidden, m.out, m.ldo);
+                       m.hidden, m.n_tok, top_k, m.hidden, m.out, m.ldo);
     if (int e = check_launch("combine_kernel")) return e;
   }
   return 0;

@@ -5,7 +5,7 @@
 namespace iq4 {
 
 struct MoeLayout {  // byte offsets into the caller's workspace
-  int64_t counts, offsets, pairs, slot_row, num_tiles, tiles, h, rows, total;
+  int64_t counts, offsets, pairs, slot_row, num_tiles, tiles, h, rows, ids2, w2, total;
   int64_t max_tiles;
 };
 
@@ -18,13 +18,17 @@ struct MoeCall {
   int top_k, n_expert;
   int64_t hidden, inter;
   const void *w_gate, *w_up, *w_down;
+  const void *s_gate, *s_up, *s_down;  // shared expert (gate/up inter x hidden, down
+                                       // hidden x inter), or null
   float* out;
   int64_t ldo;
   void* workspace;
   bool atomic;
 };
 
-MoeLayout moe_layout(int64_t n_tok, int top_k, int n_expert, int64_t hidden, int64_t inter, bool f16);
+// shared: the call adds a shared expert (routed as expert n_expert, slot top_k, weight 1)
+MoeLayout moe_layout(int64_t n_tok, int top_k, int n_expert, int64_t hidden, int64_t inter, bool f16,
+                     bool shared = false);
 int launch_moe(const MoeCall& m, hipStream_t s);
 
 }  // namespace iq4

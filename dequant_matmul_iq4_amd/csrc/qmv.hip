@@ -423,7 +423,8 @@ __global__ void __launch_bounds__(512) qmv_grouped_kernel(QmvArgs a) {
   const SlotInfo si = a.ids ? slot_from_ids(a, slot, bm + 32 * wave, lane) : slot_from_offsets(a, slot, lane);
   const int64_t e = si.e, seg0 = si.seg0, ncols = si.ncols;
   if (e < 0 || rg0 >= rg1) return;
-  const uint8_t* W[2] = {a.W0 + e * a.w_expert_stride, a.W1 + e * a.w_expert_stride};
+  const bool sh = a.S0 != nullptr && e == a.shared_e;  // the shared expert, routed to every token by the caller
+  const uint8_t* W[2] = {sh ? a.S0 : a.W0 + e * a.w_expert_stride, sh ? a.S1 : a.W1 + e * a.w_expert_stride};
   const int kq_n = a.kq_n;
   const int wq0 = wave * a.wave_quads;  // this wave's quads (a single slice: K <= 4096)
   const int wq1 = min(wq0 + a.wave_quads, kq_n);
@@ -660,7 +661,7 @@ __global__ void __launch_bounds__(512) qmv_down_tiles_kernel(QmvArgs a) {
   const SlotInfo si = a.ids ? slot_from_ids(a, slot, bm + 32 * wave, lane) : slot_from_offsets(a, slot, lane);
   const int64_t e = si.e, seg0 = si.seg0, ncols = si.ncols;
   if (e < 0 || t0 >= t1) return;  // uniform over the workgroup
-  const uint8_t* W = a.W0 + e * a.w_expert_stride;
+  const uint8_t* W = (a.S0 != nullptr && e == a.shared_e) ? a.S0 : a.W0 + e * a.w_expert_stride;  // shared expert
 
   struct WSet {
     uint4 nib[KQ];

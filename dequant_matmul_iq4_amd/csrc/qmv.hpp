@@ -10,6 +10,9 @@ struct QmvArgs {
   const uint8_t* W0;        // packed weights (DENSE: W; GATEUP: gate bank; DOWN: down bank)
   const uint8_t* W1;        // GATEUP: up bank
   int64_t w_expert_stride;  // bytes between experts' packed matrices
+  int shared_e;             // grouped, with S0 set: this expert index takes S0 / S1
+  const uint8_t* S0;        // the shared expert's packed matrices (as W0 / W1), or null
+  const uint8_t* S1;
   const float* x;           // DENSE: X [T][ldx]; GATEUP: X [n_tok][ldx]; DOWN: h [pairs][ldx]
   const int8_t* xq;         // 8-bit activations: codes [T][K] (ldx = K)
   const uint16_t* xd;       // 8-bit activations: binary16 block scales [T][K/32]

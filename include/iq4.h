@@ -244,6 +244,36 @@ int iq4_moe_expert_gemm(const void* x, int32_t act_dtype, int64_t n_tok, int64_t
                         size_t ws_bytes, uint32_t flags, void* stream);
 
 /*
+ * Workspace bytes needed by iq4_moe_expert_gemm_shared for these sizes (written to *bytes).
+ */
+int iq4_moe_shared_workspace_size(int64_t n_tok, int32_t top_k, int32_t n_expert, int64_t hidden,
+                                  int64_t inter, int32_t act_dtype, size_t* bytes);
+
+/*
+ * iq4_moe_expert_gemm plus a shared expert that every token passes through:
+ *   out[t] = (sum_j w[t][j] * y_tj) + ys_t,  ys_t = Ws_down (silu(Ws_gate x_t) * Ws_up x_t):
+ * the routed rows in slot order, then the shared expert's row.  Page 3 (the DSpark
+ * drafter file, its cooperative decode with the shared expert) adds the shared
+ * expert's output with weight 1 after the routed sum, in the same pass.  Here it is
+ * routed as one more expert (index n_expert, slot top_k of every token, gate weight 1)
+ * through the same products and the same ordered combine, so each token's row is
+ * bitwise the routed call's result on a bank extended by the shared expert with that
+ * routing.
+ *   s_gate, s_up  packed inter x hidden matrices;  s_down  packed hidden x inter
+ *               (256-byte aligned, the routed experts' sizes).
+ *   workspace   >= iq4_moe_shared_workspace_size(...) bytes, 256-byte aligned.  Its
+ *               gather (when one runs) is that of the extended routing.
+ *   Other arguments, flags and errors as iq4_moe_expert_gemm, with top_k <=
+ *   min(n_expert, 15) and n_expert <= 1023 (the extended routing within the limits).
+ */
+int iq4_moe_expert_gemm_shared(const void* x, int32_t act_dtype, int64_t n_tok, int64_t ldx,
+                               const int32_t* ids, const float* w, int32_t top_k, int32_t n_expert,
+                               int64_t hidden, int64_t inter, const void* w_gate, const void* w_up,
+                               const void* w_down, const void* s_gate, const void* s_up,
+                               const void* s_down, float* out, int64_t ldo, void* workspace,
+                               size_t ws_bytes, uint32_t flags, void* stream);
+
+/*
  * Dense dequant-fused GEMM over a prompt in chunks of `chunk` rows:
  *   Y[m][r] = sum_k X[m][k] * W[r][k]  (X f16, W decoded to f16, fp32 accumulation),
  * one launch per chunk of `chunk` consecutive rows of X (the last chunk may be short),

@@ -105,6 +105,31 @@ def test_moe_and_gemm_validation():
     assert _rc("iq4_qgemm", FAKE, 256, 256, FAKE, 0, 256, FAKE, 256, 512, None) == iq4.IQ4_OK
 
 
+def test_moe_shared_validation():
+    """The shared-expert call is validated as the routed call with one more expert and
+    slot; none of these launches."""
+    plain = iq4.iq4_moe_workspace_size(3256, 8, 128, 2048, 768, iq4.IQ4_F16)
+    ws = iq4.iq4_moe_shared_workspace_size(3256, 8, 128, 2048, 768, iq4.IQ4_F16)
+    assert ws >= iq4.iq4_moe_workspace_size(3256, 9, 129, 2048, 768, iq4.IQ4_F16) > plain
+    nb = ctypes.c_size_t(0)
+    L = iq4.lib()
+    assert L.iq4_moe_shared_workspace_size(16, 16, 128, 2048, 768, iq4.IQ4_F16, ctypes.byref(nb)) == iq4.IQ4_E_ARG
+    assert L.iq4_moe_shared_workspace_size(16, 8, 1024, 2048, 768, iq4.IQ4_F16, ctypes.byref(nb)) == iq4.IQ4_E_ARG
+    assert L.iq4_moe_shared_workspace_size(16, 15, 1023, 2048, 768, iq4.IQ4_F32, ctypes.byref(nb)) == iq4.IQ4_OK
+
+    def call(top_k=8, n_expert=128, shared=(FAKE, FAKE, FAKE), ws_bytes=1 << 30, flags=0):
+        return _rc("iq4_moe_expert_gemm_shared", FAKE, iq4.IQ4_F16, 16, 2048, FAKE, FAKE, top_k, n_expert, 2048,
+                   768, FAKE, FAKE, FAKE, *shared, FAKE, 2048, FAKE, ws_bytes, flags, None)
+    assert call(top_k=16) == iq4.IQ4_E_ARG  # the shared expert takes a 17th slot
+    assert call(n_expert=1024) == iq4.IQ4_E_ARG  # and a 1025th expert
+    assert call(shared=(FAKE, None, FAKE)) == iq4.IQ4_E_ARG
+    assert call(shared=(FAKE, FAKE, FAKE + 16)) == iq4.IQ4_E_ALIGN
+    need = iq4.iq4_moe_shared_workspace_size(16, 8, 128, 2048, 768, iq4.IQ4_F16)
+    assert need > iq4.iq4_moe_workspace_size(16, 8, 128, 2048, 768, iq4.IQ4_F16)
+    assert call(ws_bytes=need - 1) == iq4.IQ4_E_WORKSPACE
+    assert call(flags=4) == iq4.IQ4_E_ARG
+
+
 def test_zero_sized_calls_are_no_ops():
     assert _rc("iq4_quantize_blocks", None, 0, None, None) == iq4.IQ4_OK
     assert _rc("iq4_dequant_blocks", None, 0, 0, None, None) == iq4.IQ4_OK

@@ -156,6 +156,44 @@ def test_decode_direct_and_gathered_paths_agree():
     assert normwise(got, oracle.moe(x64, ids64, w64, gate, up, down, H, I)) <= 1e-3
 
 
+def run_moe_shared(x, ids, w, banks, shared, H, I, E, dtype="f16"):
+    n_tok, top_k = ids.shape
+    f16 = dtype == "f16"
+    xd = dev(x.astype(np.float16 if f16 else np.float32))
+    out = torch.full((n_tok, H), float("nan"), dtype=torch.float32, device="cuda")
+    act = iq4.IQ4_F16 if f16 else iq4.IQ4_F32
+    wsb = iq4.iq4_moe_shared_workspace_size(n_tok, top_k, E, H, I, act)
+    ws = torch.empty(max(wsb, 256), dtype=torch.uint8, device="cuda")
+    g, u, d = banks
+    sg, su, sd = shared
+    iq4.iq4_moe_expert_gemm_shared(xd, act, n_tok, H, dev(ids.astype(np.int32)), dev(w.astype(np.float32)), top_k,
+                                   E, H, I, g, u, d, sg, su, sd, out, H, ws, wsb, 0)
+    return host(out)
+
+
+@pytest.mark.parametrize("dtype,n_tok,k", [("f32", 4, 3), ("f32", 8, 8), ("f16", 300, 2), ("f16", 5, 8)])
+def test_shared_expert(small_bank, dtype, n_tok, k):
+    """A shared expert added after the routed sum: against the oracle, and bitwise equal
+    to the routed call on the bank extended by the shared expert, with it appended to
+    every token's routing at weight 1 (decode: 16 pairs direct, 72 pairs gathered)."""
+    note(f"moe shared expert: {dtype} n_tok={n_tok} k={k}")
+    B = small_bank
+    E, H, I = B["E"], B["H"], B["I"]
+    rng = np.random.default_rng(900 + n_tok * 10 + k)
+    sgate, sup, sdown = make_bank(rng, 1, H, I)
+    shared = (pack(sgate[0], I, H), pack(sup[0], I, H), pack(sdown[0], H, I))
+    ids, w = routing(rng, n_tok, E, k)
+    x = rng.standard_normal((n_tok, H)).astype(np.float16 if dtype == "f16" else np.float32)
+    got = run_moe_shared(x, ids, w, B["banks"], shared, H, I, E, dtype=dtype)
+    ref = oracle.moe_shared(x, ids, w, B["gate"], B["up"], B["down"], sgate[0], sup[0], sdown[0], H, I)
+    assert normwise(got, ref) <= (5e-3 if dtype == "f16" else 1e-3)
+    ext = (pack_bank(B["gate"] + sgate, I, H), pack_bank(B["up"] + sup, I, H), pack_bank(B["down"] + sdown, H, I))
+    ids2 = np.concatenate([ids, np.full((n_tok, 1), E, np.int32)], axis=1)
+    w2 = np.concatenate([w, np.ones((n_tok, 1), np.float32)], axis=1)
+    same, _ = run_moe(x, ids2, w2, ext, H, I, E + 1, dtype=dtype)
+    assert bits_equal(got, same)
+
+
 def test_prefill_batch_invariance(small_bank):
     note("moe prefill: batch invariance")
     B = small_bank
