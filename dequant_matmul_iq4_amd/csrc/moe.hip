@@ -233,7 +233,9 @@ int launch_moe(const MoeCall& m, hipStream_t s) {
 
   if (!atomic) {
     const int64_t n4 = m.n_tok * (m.hidden / 4);
-    hipLaunchKernelGGL(combine_kernel, dim3((unsigned)((n4 + 255) / 256)), dim3(256), 0, s, rows,
+    // a decode step's few outputs spread over more CUs (64-thread workgroups)
+    const int64_t cb = n4 < 65536 ? 64 : 256;
+    hipLaunchKernelGGL(combine_kernel, dim3((unsigned)((n4 + cb - 1) / cb)), dim3((unsigned)cb), 0, s, rows,
                        m.hidden, m.n_tok, top_k, m.hidden, m.out, m.ldo);
     if (int e = check_launch("combine_kernel")) return e;
   }

@@ -156,7 +156,7 @@ def test_decode_direct_and_gathered_paths_agree():
     assert normwise(got, oracle.moe(x64, ids64, w64, gate, up, down, H, I)) <= 1e-3
 
 
-def run_moe_shared(x, ids, w, banks, shared, H, I, E, dtype="f16"):
+def run_moe_shared(x, ids, w, banks, shared, H, I, E, dtype="f16", flags=0):
     n_tok, top_k = ids.shape
     f16 = dtype == "f16"
     xd = dev(x.astype(np.float16 if f16 else np.float32))
@@ -167,7 +167,7 @@ def run_moe_shared(x, ids, w, banks, shared, H, I, E, dtype="f16"):
     g, u, d = banks
     sg, su, sd = shared
     iq4.iq4_moe_expert_gemm_shared(xd, act, n_tok, H, dev(ids.astype(np.int32)), dev(w.astype(np.float32)), top_k,
-                                   E, H, I, g, u, d, sg, su, sd, out, H, ws, wsb, 0)
+                                   E, H, I, g, u, d, sg, su, sd, out, H, ws, wsb, flags)
     return host(out)
 
 
@@ -192,6 +192,21 @@ def test_shared_expert(small_bank, dtype, n_tok, k):
     w2 = np.concatenate([w, np.ones((n_tok, 1), np.float32)], axis=1)
     same, _ = run_moe(x, ids2, w2, ext, H, I, E + 1, dtype=dtype)
     assert bits_equal(got, same)
+
+
+def test_shared_expert_atomic_combine(small_bank):
+    """The shared expert with the atomic combine (prefill): within the f16 tolerance."""
+    note("moe shared expert: atomic combine")
+    B = small_bank
+    E, H, I = B["E"], B["H"], B["I"]
+    rng = np.random.default_rng(31)
+    sgate, sup, sdown = make_bank(rng, 1, H, I)
+    shared = (pack(sgate[0], I, H), pack(sup[0], I, H), pack(sdown[0], H, I))
+    ids, w = routing(rng, 200, E, 3)
+    x = rng.standard_normal((200, H)).astype(np.float16)
+    got = run_moe_shared(x, ids, w, B["banks"], shared, H, I, E, flags=iq4.IQ4_MOE_ATOMIC_COMBINE)
+    ref = oracle.moe_shared(x, ids, w, B["gate"], B["up"], B["down"], sgate[0], sup[0], sdown[0], H, I)
+    assert normwise(got, ref) <= 5e-3
 
 
 def test_prefill_batch_invariance(small_bank):
