@@ -407,7 +407,9 @@ __global__ void __launch_bounds__(512) qmv_grouped_kernel(QmvArgs a) {
   constexpr int REDN = kWaves * NMAT * RG * 64;  // one f32x4 partial per (wave, matrix, tile, lane)
   __shared__ uint32_t lut[256 * kLutCopies];
   __shared__ __attribute__((aligned(16))) uint8_t xs[XBYTES + 256];  // + room for padding-row reads
-  __shared__ f32x4 red[REDN];
+  // two reduction buffers where they fit (a buffer is then reused two calls later)
+  constexpr int NRED = (XBYTES + 256 + 256 * kLutCopies * 4 + 2 * REDN * 16 + kWaves * 32 * 4 <= 160 * 1024) ? 2 : 1;
+  __shared__ f32x4 red[NRED * REDN];
   __shared__ uint32_t bm[kWaves * 32];  // slot lookup from the ids: a bitmap per wave
 
   const int tid = threadIdx.x;
@@ -553,13 +555,15 @@ __global__ void __launch_bounds__(512) qmv_grouped_kernel(QmvArgs a) {
   };
   // reduction over the waves' K runs, then the three parts, then the mode's epilogue.
   // Lane (g, c) holds D[4g + i][c]: part s = g, column i, weight row c.
+  int rbuf = 0;  // the reduction buffer of the next call
   auto reduce_store = [&](int64_t rg, int64_t t0, int T, const f32x4 (&acc)[NMAT][RG]) {
 #pragma unroll
     for (int m = 0; m < NMAT; ++m)
 #pragma unroll
-      for (int r = 0; r < RG; ++r) red[((wave * NMAT + m) * RG + r) * 64 + lane] = acc[m][r];
+      for (int r = 0; r < RG; ++r) red[rbuf * REDN + ((wave * NMAT + m) * RG + r) * 64 + lane] = acc[m][r];
     __syncthreads();
-    const float* redf = reinterpret_cast<const float*>(red);
+    const float* redf = reinterpret_cast<const float*>(red + rbuf * REDN);
+    if (NRED == 2) rbuf ^= 1;
     const int nout = T * ROWS;
     for (int idx0 = 0; idx0 < nout; idx0 += (int)blockDim.x) {  // uniform trip count
       const int idx = idx0 + tid;
@@ -596,7 +600,9 @@ __global__ void __launch_bounds__(512) qmv_grouped_kernel(QmvArgs a) {
         }
       }
     }
-    __syncthreads();  // the partials are read; the slots can be reused
+    // with two buffers the next call writes the other one, and this one is written again
+    // only after the next call's barrier, which every wave passes after its reads
+    if (NRED == 1) __syncthreads();  // the partials are read; the slots can be reused
   };
 
   // ---- prologue: first row group's weights, then the columns, the table -------------

@@ -114,6 +114,24 @@ def test_decode_small(small_bank, n_tok, k):
     assert normwise(got, ref) <= 1e-3
 
 
+@pytest.mark.parametrize("H,I,E,n_tok,k", [(512, 1024, 4, 3, 2), (4096, 128, 3, 2, 2), (1280, 1152, 5, 8, 3),
+                                           (512, 1024, 16, 8, 12)])
+def test_decode_other_shapes(H, I, E, n_tok, k):
+    """Decode shapes off the workload's: a down product with K above 7 quads (the grouped
+    form, 8 and 9 quads, direct and gathered), a 4,096-wide gate|up (4 quads per wave)
+    and a 10-quad gate|up over 5 waves."""
+    note(f"moe decode: H={H} I={I} E={E} n_tok={n_tok} k={k}")
+    rng = np.random.default_rng(H + I + E + k)
+    gate, up, down = make_bank(rng, E, H, I)
+    banks = (pack_bank(gate, I, H), pack_bank(up, I, H), pack_bank(down, H, I))
+    ids, w = routing(rng, n_tok, E, k)
+    x = rng.standard_normal((n_tok, H)).astype(np.float32)
+    got, _ = run_moe(x, ids, w, banks, H, I, E, dtype="f32")
+    assert normwise(got, oracle.moe(x, ids, w, gate, up, down, H, I)) <= 1e-3
+    one, _ = run_moe(x[:1], ids[:1], w[:1], banks, H, I, E, dtype="f32")
+    assert bits_equal(got[0], one[0])
+
+
 def test_decode_batch_invariance(small_bank):
     """Each token of a 4-token decode step equals that token run alone, bitwise (the
     verify window's per-token property, for the expert path)."""
