@@ -44,10 +44,10 @@ N_BANKS = 8                 # expert banks the decode step rotates over
 # at the time: a kernel changed since then reports traffic null.  Commands and raw
 # figures: profiles/<name>.txt.
 MEASURED_TRAFFIC = {
-    "qmv_dense_4096x4096_T1-4": (9931077, "5e1d98c5a6cfc4f2", ("qmv.hip", "qmv.hpp", "common.hpp")),
-    "qmv_q8_4096x4096_T1-4": (9680944, "5e1d98c5a6cfc4f2", ("qmv.hip", "qmv.hpp", "common.hpp")),
-    "qmv_grouped_gateup_moe_decode_4tok": (55479934, "5e1d98c5a6cfc4f2", ("qmv.hip", "qmv.hpp", "common.hpp")),
-    "qmv_down_moe_decode_4tok": (28738220, "5e1d98c5a6cfc4f2", ("qmv.hip", "qmv.hpp", "common.hpp")),
+    "qmv_dense_4096x4096_T1-4": (9931077, "2bcc82aa376912f5", ("qmv.hip", "qmv.hpp", "common.hpp")),
+    "qmv_q8_4096x4096_T1-4": (9680944, "2bcc82aa376912f5", ("qmv.hip", "qmv.hpp", "common.hpp")),
+    "qmv_grouped_gateup_moe_decode_4tok": (55479934, "2bcc82aa376912f5", ("qmv.hip", "qmv.hpp", "common.hpp")),
+    "qmv_down_moe_decode_4tok": (28738220, "2bcc82aa376912f5", ("qmv.hip", "qmv.hpp", "common.hpp")),
     "qgemm_gateup_moe_prefill_3256tok": (589094655, "0f4774c413fa418b", ("gemm.hip", "gemm.hpp", "common.hpp")),
     "qgemm_down_moe_prefill_3256tok": (507598496, "0f4774c413fa418b", ("gemm.hip", "gemm.hpp", "common.hpp")),
     "qgemm_dense_13056x4096x14336_chunk512": (94965186, "0f4774c413fa418b", ("gemm.hip", "gemm.hpp", "common.hpp")),

@@ -417,8 +417,9 @@ __global__ void __launch_bounds__(512) qmv_grouped_kernel(QmvArgs a) {
   const int c = lane & 15, g = lane >> 4;
 
   // ---- expert slot and row groups of this workgroup ---------------------------------
-  // Slot i takes the i-th expert (ascending id) that has pairs, found by a ballot over
-  // the offsets in every wave; slots past the routed experts exit.
+  // Slot i takes the i-th expert (ascending id) that has pairs, found in every wave from
+  // the routed ids (at most 64 pairs) or the gather's offsets; slots past the routed
+  // experts exit.
   const int64_t slot = blockIdx.x / a.rg_chunks;
   const int64_t rg0 = (blockIdx.x % a.rg_chunks) * a.rg_per_wg;
   const int64_t rg1 = min(rg0 + (int64_t)a.rg_per_wg, a.rg_n);
