@@ -44,13 +44,14 @@ N_BANKS = 8                 # expert banks the decode step rotates over
 # at the time: a kernel changed since then reports traffic null.  Commands and raw
 # figures: profiles/<name>.txt.
 MEASURED_TRAFFIC = {
-    "qmv_dense_4096x4096_T1-4": (9931077, "2bcc82aa376912f5", ("qmv.hip", "qmv.hpp", "common.hpp")),
-    "qmv_q8_4096x4096_T1-4": (9680944, "2bcc82aa376912f5", ("qmv.hip", "qmv.hpp", "common.hpp")),
-    "qmv_grouped_gateup_moe_decode_4tok": (55479934, "2bcc82aa376912f5", ("qmv.hip", "qmv.hpp", "common.hpp")),
-    "qmv_down_moe_decode_4tok": (28738220, "2bcc82aa376912f5", ("qmv.hip", "qmv.hpp", "common.hpp")),
-    "qgemm_gateup_moe_prefill_3256tok": (589094655, "0f4774c413fa418b", ("gemm.hip", "gemm.hpp", "common.hpp")),
-    "qgemm_down_moe_prefill_3256tok": (507598496, "0f4774c413fa418b", ("gemm.hip", "gemm.hpp", "common.hpp")),
-    "qgemm_dense_13056x4096x14336_chunk512": (94965186, "0f4774c413fa418b", ("gemm.hip", "gemm.hpp", "common.hpp")),
+    "dequant_staged_4096x4096_f16": (43014186, "25db0a7fe6d27844", ("format.hip", "common.hpp")),
+    "qmv_dense_4096x4096_T1-4": (9931082, "2bcc82aa376912f5", ("qmv.hip", "qmv.hpp", "common.hpp")),
+    "qmv_q8_4096x4096_T1-4": (9680949, "2bcc82aa376912f5", ("qmv.hip", "qmv.hpp", "common.hpp")),
+    "qmv_grouped_gateup_moe_decode_4tok": (55479983, "2bcc82aa376912f5", ("qmv.hip", "qmv.hpp", "common.hpp")),
+    "qmv_down_moe_decode_4tok": (28736433, "2bcc82aa376912f5", ("qmv.hip", "qmv.hpp", "common.hpp")),
+    "qgemm_gateup_moe_prefill_3256tok": (590047812, "0f4774c413fa418b", ("gemm.hip", "gemm.hpp", "common.hpp")),
+    "qgemm_down_moe_prefill_3256tok": (507604182, "0f4774c413fa418b", ("gemm.hip", "gemm.hpp", "common.hpp")),
+    "qgemm_dense_13056x4096x14336_chunk512": (94965198, "0f4774c413fa418b", ("gemm.hip", "gemm.hpp", "common.hpp")),
 }
 
 
@@ -461,7 +462,8 @@ def main():
                             traffic=measured_traffic("qmv_q8_4096x4096_T1-4")),
             "dequant": roof("hbm", deq_bytes / (deq_ms * 1e-3) / 1e9, HBM_PEAK_GBS, "GB/s",
                             "dequant_staged_kernel<f16>: 9.4 MB of blocks in, 33.5 MB of f16 out, per launch "
-                            "(graph of 32 launches over cold copies)"),
+                            "(graph of 32 launches over cold copies); traffic = HBM bytes per launch",
+                            traffic=measured_traffic("dequant_staged_4096x4096_f16")),
         },
     }
     if not args.no_cpu_baseline:
