@@ -217,8 +217,10 @@ int iq4_moe_workspace_size(int64_t n_tok, int32_t top_k, int32_t n_expert, int64
  *   h = silu(g) * u,  y_tj = Wd_e h,  out[t] = sum_j w[t][j] * y_tj (added in j order).
  * Page 1 (verify.hpp, PoolMultiFn): x (n_tok, n_embd) and ids (n_tok, k) give
  * per-slot rows (n_tok*k, n_embd) that are then summed per token.
- *   x           [n_tok][ldx] activations: IQ4_F32 (decode path, n_tok <= 8: every
- *               product in fp32 through the T-column matvec) or IQ4_F16 (prefill path:
+ *   x           [n_tok][ldx] activations: IQ4_F32 (decode path, meant for a few
+ *               tokens, any n_tok accepted: every product in fp32 through the grouped
+ *               T-column matvec, an expert's columns 4 at a time; hidden and inter
+ *               <= 4096) or IQ4_F16 (prefill path:
  *               grouped GEMM on the matrix cores, weights decoded to f16, fp32
  *               accumulation, h rounded to f16 for the down product).
  *   ids, w      [n_tok][top_k] int32 / float32 (ids in [0, n_expert), not checked);
