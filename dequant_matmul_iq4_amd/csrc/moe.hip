@@ -23,31 +23,64 @@ namespace iq4 {
 constexpr int kTileM = 128;  // rows per GEMM tile (gemm.hip kBM)
 constexpr int kMaxTopK = 16;  // the largest top_k the call accepts
 
-// out[t][h] = sum_j rows[t * k + j][h], j ascending; one thread per 4 outputs.
+// out[t][h] = sum_j rows[t * K + j][h], j ascending; one thread per 4 outputs, K = top_k
+// fixed at compile time.  Every slot row is requested at once, with non-temporal loads
+// (each is read once), then added in slot order.
+template <int K>
 __global__ void __launch_bounds__(256) combine_kernel(const float* __restrict__ rows, int64_t ldr,
-                                                      int64_t n_tok, int top_k, int64_t hidden,
+                                                      int64_t n_tok, int64_t hidden,
                                                       float* __restrict__ out, int64_t ldo) {
   const int64_t per_tok = hidden / 4;
   const int64_t i = (int64_t)blockIdx.x * blockDim.x + threadIdx.x;
   if (i >= n_tok * per_tok) return;
   const int64_t t = i / per_tok, h = (i % per_tok) * 4;
-  const float* r = rows + t * top_k * ldr + h;
-  // every slot row is read at once (indices past top_k repeat the last one: in bounds,
-  // not added), then added in slot order
-  float4 v[kMaxTopK];
+  const float* r = rows + t * K * ldr + h;
+  f32x4 v[K];
 #pragma unroll
-  for (int j = 0; j < kMaxTopK; ++j) v[j] = *reinterpret_cast<const float4*>(r + min(j, top_k - 1) * ldr);
-  float4 acc = v[0];
+  for (int j = 0; j < K; ++j) v[j] = __builtin_nontemporal_load(reinterpret_cast<const f32x4*>(r + j * ldr));
+  f32x4 acc = v[0];
 #pragma unroll
-  for (int j = 1; j < kMaxTopK; ++j) {
-    if (j < top_k) {
-      acc.x += v[j].x;
-      acc.y += v[j].y;
-      acc.z += v[j].z;
-      acc.w += v[j].w;
-    }
+  for (int j = 1; j < K; ++j) {
+    acc.x += v[j].x;
+    acc.y += v[j].y;
+    acc.z += v[j].z;
+    acc.w += v[j].w;
   }
-  *reinterpret_cast<float4*>(out + t * ldo + h) = acc;
+  *reinterpret_cast<f32x4*>(out + t * ldo + h) = acc;
+}
+
+template <int K>
+static int launch_combine_k(const float* rows, int64_t n_tok, int64_t hidden, float* out, int64_t ldo,
+                            hipStream_t s) {
+  const int64_t n4 = n_tok * (hidden / 4);
+  // a decode step's few outputs spread over more CUs (64-thread workgroups)
+  const int64_t cb = n4 < 65536 ? 64 : 256;
+  hipLaunchKernelGGL(combine_kernel<K>, dim3((unsigned)((n4 + cb - 1) / cb)), dim3((unsigned)cb), 0, s, rows,
+                     hidden, n_tok, hidden, out, ldo);
+  return check_launch("combine_kernel");
+}
+
+static int launch_combine(const float* rows, int64_t n_tok, int top_k, int64_t hidden, float* out,
+                          int64_t ldo, hipStream_t s) {
+  switch (top_k) {
+    case 1: return launch_combine_k<1>(rows, n_tok, hidden, out, ldo, s);
+    case 2: return launch_combine_k<2>(rows, n_tok, hidden, out, ldo, s);
+    case 3: return launch_combine_k<3>(rows, n_tok, hidden, out, ldo, s);
+    case 4: return launch_combine_k<4>(rows, n_tok, hidden, out, ldo, s);
+    case 5: return launch_combine_k<5>(rows, n_tok, hidden, out, ldo, s);
+    case 6: return launch_combine_k<6>(rows, n_tok, hidden, out, ldo, s);
+    case 7: return launch_combine_k<7>(rows, n_tok, hidden, out, ldo, s);
+    case 8: return launch_combine_k<8>(rows, n_tok, hidden, out, ldo, s);
+    case 9: return launch_combine_k<9>(rows, n_tok, hidden, out, ldo, s);
+    case 10: return launch_combine_k<10>(rows, n_tok, hidden, out, ldo, s);
+    case 11: return launch_combine_k<11>(rows, n_tok, hidden, out, ldo, s);
+    case 12: return launch_combine_k<12>(rows, n_tok, hidden, out, ldo, s);
+    case 13: return launch_combine_k<13>(rows, n_tok, hidden, out, ldo, s);
+    case 14: return launch_combine_k<14>(rows, n_tok, hidden, out, ldo, s);
+    case 15: return launch_combine_k<15>(rows, n_tok, hidden, out, ldo, s);
+    case 16: return launch_combine_k<16>(rows, n_tok, hidden, out, ldo, s);
+    default: return set_error(-1, "combine: top_k must be 1..%d", kMaxTopK);
+  }
 }
 
 // Zero-fill (a kernel rather than a memset node, so the call stays graph-safe).
@@ -232,12 +265,7 @@ int launch_moe(const MoeCall& m, hipStream_t s) {
   }
 
   if (!atomic) {
-    const int64_t n4 = m.n_tok * (m.hidden / 4);
-    // a decode step's few outputs spread over more CUs (64-thread workgroups)
-    const int64_t cb = n4 < 65536 ? 64 : 256;
-    hipLaunchKernelGGL(combine_kernel, dim3((unsigned)((n4 + cb - 1) / cb)), dim3((unsigned)cb), 0, s, rows,
-                       m.hidden, m.n_tok, top_k, m.hidden, m.out, m.ldo);
-    if (int e = check_launch("combine_kernel")) return e;
+    if (int e = launch_combine(rows, m.n_tok, top_k, m.hidden, m.out, m.ldo, s)) return e;
   }
   return 0;
 }
