@@ -194,6 +194,11 @@ __device__ __forceinline__ void split_pair(float v0, float v1, uint32_t out[3]) 
 // copies measured 5 % slower on the MoE decode step.
 constexpr int kLutCopies = 32;
 
+template <int N>
+struct ColsC {  // a column count as a type (compile-time pass width)
+  static constexpr int value = N;
+};
+
 // Dense verify-window matvec: one workgroup per row tile and K slice; each wave owns WQ
 // quads of the slice (registers and LDS sized to K).  The code of a pass is straight
 // line, in the order the data arrive: the pass's activations are requested first (L2
@@ -286,7 +291,10 @@ __global__ void __launch_bounds__(512) qmv_dense_kernel(QmvArgs a) {
   }
   const uint32_t* lutl = lut + (lane & (kLutCopies - 1));
 
-  auto multiply = [&](f32x4& acc) {
+  // NC (compile time): the pass's columns; accumulator lane i holds column i, so the
+  // scale FMAs of columns past NC are skipped (their rows are never read)
+  auto multiply = [&](f32x4& acc, auto nc) {
+    constexpr int NC = decltype(nc)::value;
     acc = f32x4{0.f, 0.f, 0.f, 0.f};
 #pragma unroll
     for (int u = 0; u < WQ; ++u) {
@@ -311,7 +319,7 @@ __global__ void __launch_bounds__(512) qmv_dense_kernel(QmvArgs a) {
         const uint32_t sw = (j < 2) ? scl[u].x : scl[u].y;
         const float d = h2f((uint16_t)(sw >> (16 * (j & 1))));
 #pragma unroll
-        for (int i = 0; i < 4; ++i) acc[i] = __builtin_fmaf(d, prod[j][i], acc[i]);
+        for (int i = 0; i < NC; ++i) acc[i] = __builtin_fmaf(d, prod[j][i], acc[i]);
       }
     }
   };
@@ -380,7 +388,7 @@ __global__ void __launch_bounds__(512) qmv_dense_kernel(QmvArgs a) {
   store_x(T0);   // waits for the activations only
   lds_barrier();  // the table (LDS only: no wait on the weights in flight)
   f32x4 acc;
-  multiply(acc);
+  multiply(acc, ColsC<T0>{});
   reduce_store(0, T0, acc);
   // ---- further passes of 4 columns (T > 4): same weights, next columns ---------------
   for (int64_t t0 = kCols; t0 < ncols; t0 += kCols) {
@@ -388,7 +396,7 @@ __global__ void __launch_bounds__(512) qmv_dense_kernel(QmvArgs a) {
     lds_barrier();  // every wave is done with red
     load_x(t0, T);
     store_x(T);
-    multiply(acc);
+    multiply(acc, ColsC<kCols>{});
     reduce_store(t0, T, acc);
   }
 }
@@ -1099,8 +1107,9 @@ __global__ void __launch_bounds__(512) qmv_q8_kernel(QmvArgs a) {
       const uint32_t sw = (j < 2) ? scl[u].x : scl[u].y;
       const float dw = h2f((uint16_t)(sw >> (16 * (j & 1))));
       const uint2 dx4 = *reinterpret_cast<const uint2*>(dxw + bl * kQ8Rows + 4 * (g & 1));
+      // below 4 tokens only lanes i < TP of k-group 0 feed an output
 #pragma unroll
-      for (int i = 0; i < 4; ++i) {
+      for (int i = 0; i < (TP < 4 ? TP : 4); ++i) {
         const uint32_t hw = (i < 2) ? dx4.x : dx4.y;
         const float s = dw * h2f((uint16_t)(hw >> (16 * (i & 1))));  // exact: 11 x 11 bits
         acc[i] = __builtin_fmaf(s, prod[j][i], acc[i]);
