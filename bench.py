@@ -44,14 +44,14 @@ N_BANKS = 8                 # expert banks the decode step rotates over
 # at the time: a kernel changed since then reports traffic null.  Commands and raw
 # figures: profiles/<name>.txt.
 MEASURED_TRAFFIC = {
-    "dequant_staged_4096x4096_f16": (43014196, "25db0a7fe6d27844", ("format.hip", "common.hpp")),
-    "qmv_dense_4096x4096_T1-4": (9931082, "2bcc82aa376912f5", ("qmv.hip", "qmv.hpp", "common.hpp")),
-    "qmv_q8_4096x4096_T1-4": (9680955, "2bcc82aa376912f5", ("qmv.hip", "qmv.hpp", "common.hpp")),
-    "qmv_grouped_gateup_moe_decode_4tok": (55479962, "2bcc82aa376912f5", ("qmv.hip", "qmv.hpp", "common.hpp")),
-    "qmv_down_moe_decode_4tok": (28740324, "2bcc82aa376912f5", ("qmv.hip", "qmv.hpp", "common.hpp")),
-    "qgemm_gateup_moe_prefill_3256tok": (589186691, "0f4774c413fa418b", ("gemm.hip", "gemm.hpp", "common.hpp")),
-    "qgemm_down_moe_prefill_3256tok": (507664781, "0f4774c413fa418b", ("gemm.hip", "gemm.hpp", "common.hpp")),
-    "qgemm_dense_13056x4096x14336_chunk512": (94965266, "0f4774c413fa418b", ("gemm.hip", "gemm.hpp", "common.hpp")),
+    "dequant_staged_4096x4096_f16": (43014149, "25db0a7fe6d27844", ("format.hip", "common.hpp")),
+    "qmv_dense_4096x4096_T1-4": (9928256, "a3e206cf1de95580", ("qmv.hip", "qmv.hpp", "common.hpp")),
+    "qmv_q8_4096x4096_T1-4": (9670700, "a3e206cf1de95580", ("qmv.hip", "qmv.hpp", "common.hpp")),
+    "qmv_grouped_gateup_moe_decode_4tok": (55501318, "a3e206cf1de95580", ("qmv.hip", "qmv.hpp", "common.hpp")),
+    "qmv_down_moe_decode_4tok": (28740859, "a3e206cf1de95580", ("qmv.hip", "qmv.hpp", "common.hpp")),
+    "qgemm_gateup_moe_prefill_3256tok": (589100195, "0f4774c413fa418b", ("gemm.hip", "gemm.hpp", "common.hpp")),
+    "qgemm_down_moe_prefill_3256tok": (507634000, "0f4774c413fa418b", ("gemm.hip", "gemm.hpp", "common.hpp")),
+    "qgemm_dense_13056x4096x14336_chunk512": (94965153, "0f4774c413fa418b", ("gemm.hip", "gemm.hpp", "common.hpp")),
 }
 
 
