@@ -56,6 +56,7 @@ constexpr int kWaves = 8;              // waves per workgroup (at most)
 constexpr int kMaxWaveQuads = 4;       // quads per wave: all of a wave's weights in registers
 constexpr int kSliceQuads = kWaves * kMaxWaveQuads;  // 32 quads = 128 blocks = K 4096
 constexpr int kCols = 4;               // columns per pass (rows 4s + t of the A operand)
+constexpr int kSplitCols = 8;          // columns of the split-K partials (T <= 8)
 constexpr int kDenseRG = 1;            // row tiles per workgroup (dense)
 constexpr int kGateUpRG = 1;           // row tiles per matrix (gate + up)
 constexpr int kDownRG = 2;             // row tiles per workgroup (down)
@@ -362,24 +363,28 @@ __global__ void __launch_bounds__(512) qmv_dense_kernel(QmvArgs a) {
     // time, so no cache-wide writeback or invalidate is needed; s_waitcnt(0) makes every
     // store complete before this workgroup's arrival is counted, and the last arriver
     // issues its loads only after seeing the count.
-    float* part = a.partials + (rg * a.S + slice) * (kCols * kTileRows);
-    if (idx < T * kTileRows)
-      __hip_atomic_store(part + t * kTileRows + row, v, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
+    // Each pass (columns t0 .. t0 + 3) has partial slots and an arrival counter of its
+    // own: nothing orders the passes of different workgroups, so a slice that reaches
+    // the second pass early must not touch what the first pass's last arriver reads.
+    const int pass = (int)(t0 / kCols);
+    int* counter = a.counters + pass * a.rg_n + rg;
+    float* part = a.partials + (rg * a.S + slice) * (kSplitCols * kTileRows) + (t0 + t) * kTileRows + row;
+    if (idx < T * kTileRows) __hip_atomic_store(part, v, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
     __builtin_amdgcn_s_waitcnt(0);
     __syncthreads();
     if (tid == 0)
-      s_last = __hip_atomic_fetch_add(a.counters + rg, 1, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT) == a.S - 1;
+      s_last = __hip_atomic_fetch_add(counter, 1, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT) == a.S - 1;
     __syncthreads();
     if (s_last) {
       if (ok) {
-        const float* p0 = a.partials + rg * a.S * (kCols * kTileRows) + t * kTileRows + row;
+        const float* p0 = a.partials + rg * a.S * (kSplitCols * kTileRows) + (t0 + t) * kTileRows + row;
         float sum = __hip_atomic_load(p0, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
         for (int sl = 1; sl < a.S; ++sl)
-          sum += __hip_atomic_load(p0 + sl * (kCols * kTileRows), __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
+          sum += __hip_atomic_load(p0 + sl * (kSplitCols * kTileRows), __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
         a.y[(t0 + t) * a.ldy + col] = sum;
       }
       // leaves the workspace ready for the next call
-      if (tid == 0) __hip_atomic_store(a.counters + rg, 0, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
+      if (tid == 0) __hip_atomic_store(counter, 0, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
     }
     __syncthreads();  // the counter and red are reused by a next pass
   };
@@ -810,20 +815,19 @@ static void qmv_plan(QmvArgs& a, int64_t n, int64_t k, int rg_rows) {
   a.nwaves = (a.slice_quads + a.wave_quads - 1) / a.wave_quads;
 }
 
-// Split-K workspace (both the float and the 8-bit-activation matvec): the float
-// call's partials (4 columns per row group and slice), the arrival counters (one per
-// row group, shared by both calls and left at zero by each), then the 8-bit call's
-// partials (8 columns).
+// Split-K workspace (both the float and the 8-bit-activation matvec): the arrival
+// counters, one per (pass, row group) -- the float call runs up to two passes of 4
+// columns, the 8-bit call one pass of 8 and uses the first set -- left at zero by
+// each call; then the partial sums [row group][slice][8 columns][16 rows], where pass
+// p of the float call owns columns 4p .. 4p + 3.
 static inline int64_t align256(int64_t b) { return (b + 255) / 256 * 256; }
-static int64_t ws_partials4(const QmvArgs& a) { return a.rg_n * a.S * kCols * kTileRows * (int64_t)sizeof(float); }
-static int64_t ws_counters_off(const QmvArgs& a) { return align256(ws_partials4(a)); }
-static int64_t ws_partials8_off(const QmvArgs& a) { return ws_counters_off(a) + align256(a.rg_n * 4); }
+static int64_t ws_partials_off(const QmvArgs& a) { return align256(2 * a.rg_n * (int64_t)sizeof(int)); }
 
 int64_t qmv_workspace_bytes(int64_t n, int64_t k) {
   QmvArgs a{};
   qmv_plan(a, n, k, kDenseRG);
   if (a.S == 1) return 0;
-  return ws_partials8_off(a) + 2 * ws_partials4(a);
+  return ws_partials_off(a) + a.rg_n * a.S * kSplitCols * kTileRows * (int64_t)sizeof(float);
 }
 
 template <int WQ, int TP>
@@ -856,8 +860,8 @@ int launch_qmv(const uint8_t* packed, int64_t n, int64_t k, const float* x, int6
   a.stream = s;
   qmv_plan(a, n, k, kDenseRG);
   if (a.S > 1) {
-    a.partials = static_cast<float*>(workspace);
-    a.counters = reinterpret_cast<int*>(static_cast<uint8_t*>(workspace) + ws_counters_off(a));
+    a.counters = static_cast<int*>(workspace);
+    a.partials = reinterpret_cast<float*>(static_cast<uint8_t*>(workspace) + ws_partials_off(a));
   }
   const int64_t grid = a.rg_n * a.S;
   switch (a.wave_quads) {  // instantiation by quads per wave (the plan gives 1..4)
@@ -1202,8 +1206,8 @@ int launch_qmv_q8(const uint8_t* packed, int64_t n, int64_t k, const int8_t* q, 
   a.stream = s;
   qmv_plan(a, n, k, kDenseRG);
   if (a.S > 1) {
-    a.counters = reinterpret_cast<int*>(static_cast<uint8_t*>(workspace) + ws_counters_off(a));
-    a.partials = reinterpret_cast<float*>(static_cast<uint8_t*>(workspace) + ws_partials8_off(a));
+    a.counters = static_cast<int*>(workspace);
+    a.partials = reinterpret_cast<float*>(static_cast<uint8_t*>(workspace) + ws_partials_off(a));
   }
   const int64_t grid = a.rg_n * a.S;
   if (grid == 0) return 0;

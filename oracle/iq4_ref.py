@@ -274,8 +274,11 @@ def gemm(blocks, n: int, k: int, x) -> np.ndarray:
     (X token-major ``[M, k]``, any float dtype taken exactly), float64 sums,
     float32 ``[M, n]`` result."""
     W = _matrix(blocks, n, k)
-    X = np.asarray(x).astype(np.float64).reshape(-1, k)
-    return (X @ W.T).astype(np.float32)
+    X = np.asarray(x).reshape(-1, k)
+    Y = np.empty((X.shape[0], n), dtype=np.float32)
+    for i in range(0, X.shape[0], 512):  # rows are independent: bounds the float64 temporaries
+        Y[i:i + 512] = (X[i:i + 512].astype(np.float64) @ W.T).astype(np.float32)
+    return Y
 
 
 def _round_half_away(v: np.ndarray) -> np.ndarray:

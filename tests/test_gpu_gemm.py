@@ -66,20 +66,26 @@ def test_chunk_invariance_bitwise():
         assert bits_equal(run_qgemm(packed, n, k, x, chunk=chunk), ref), chunk
 
 
-def test_long_prompt_projection_sampled():
+def test_long_prompt_projection_full():
     """The full long-prompt workload: W 14,336 x 4,096 (seed 105), 13,056 f16 tokens in
-    512-token chunks; every output column checked on a sample of rows (first and last
-    chunk, the 256-token tail, and rows spread over the prompt)."""
-    note("qgemm: long prompt 13056 x 4096 x 14336, chunk 512")
+    512-token chunks (25 full chunks and a 256-token tail), exactly as the benchmark
+    launches it.  The output starts as NaN and every one of the 13,056 x 14,336 outputs
+    is compared with the oracle (5e-3)."""
+    import time
+    note("qgemm: long prompt 13056 x 4096 x 14336, chunk 512, every output")
     n, k, m = 14336, 4096, 13056
     _, b = workloads.dense_weights(synth.SEED_LONG, n, k)
     x = workloads.acts16(synth.SEED_LONG, m, k)
     packed = pack(b, n, k)
     xd = dev(x)
-    y = torch.empty((m, n), dtype=torch.float32, device="cuda")
+    y = torch.full((m, n), float("nan"), dtype=torch.float32, device="cuda")
     iq4.iq4_qgemm(packed, n, k, xd, m, k, y, n, 512)
-    rows = np.unique(np.concatenate([np.arange(0, 8), np.arange(12800, 12808), np.arange(13048, 13056),
-                                     np.linspace(0, m - 1, 40).astype(int)]))
-    got = host(y[torch.from_numpy(rows).cuda()])
-    ref = oracle.gemm(b, n, k, x[rows])
-    assert normwise(got, ref) <= TOL
+    got = host(y)
+    del y
+    t0 = time.perf_counter()
+    ref = oracle.gemm(b, n, k, x)
+    note(f"  oracle {time.perf_counter() - t0:.1f} s")
+    assert np.isfinite(got).all()
+    err = normwise(got, ref)
+    note(f"  normwise {err:.2e}")
+    assert err <= TOL

@@ -24,13 +24,16 @@ def pack_bank(blocks, n, k):
 
 
 def run_moe(x, ids, w, banks, H, I, E, flags=0, dtype="f16"):
+    """One call of the MoE layer.  The output and the whole workspace start as NaN bytes
+    (0xFF: a NaN in every float field, -1 in every integer one), so a row that no kernel
+    writes, or a stale workspace row that a kernel reads, shows up in the comparison."""
     n_tok, top_k = ids.shape
     f16 = dtype == "f16"
     xd = dev(x.astype(np.float16 if f16 else np.float32))
     out = torch.full((n_tok, H), float("nan"), dtype=torch.float32, device="cuda")
     act = iq4.IQ4_F16 if f16 else iq4.IQ4_F32
     wsb = iq4.iq4_moe_workspace_size(n_tok, top_k, E, H, I, act)
-    ws = torch.empty(max(wsb, 256), dtype=torch.uint8, device="cuda")
+    ws = torch.full((max(wsb, 256),), 0xFF, dtype=torch.uint8, device="cuda")
     g, u, d = banks
     iq4.iq4_moe_expert_gemm(xd, act, n_tok, H, dev(ids.astype(np.int32)), dev(w.astype(np.float32)), top_k, E,
                             H, I, g, u, d, out, H, ws, wsb, flags)
@@ -301,24 +304,40 @@ def test_decode_step_full_size(full_bank):
     assert err <= 1e-3
 
 
-def test_prefill_layer_full_size_sampled(full_bank):
+def test_prefill_layer_full_size(full_bank):
     """The prefill layer at its real shape and launch configuration: 3,256 f16 tokens with
-    Zipf(1.1)-skewed top-8 routing; sampled tokens against the oracle (5e-3)."""
+    Zipf(1.1)-skewed top-8 routing (experts of 27 to about 2,950 rows, so the grouped
+    GEMM's tile list, its partial tiles and its XCD order are all at their real sizes).
+    Every one of the 3,256 x 2,048 outputs against the oracle (5e-3), with the output and
+    the workspace NaN-filled before the call."""
+    import time
     n_tok = 3256
-    note("moe prefill full size: 3256 tokens, Zipf 1.1, top-8 of 128")
+    note("moe prefill full size: 3256 tokens, Zipf 1.1, top-8 of 128, every output")
     logits = synth.logits_zipf_gumbel(synth.SEED_PREFILL, synth.TAG_GUMBEL, n_tok, E_FULL)
     ids, w = oracle.route_topk(logits, K_FULL)
     x = synth.acts_f16(synth.SEED_PREFILL, synth.TAG_X, n_tok, H_FULL)
     B = full_bank
     got, _ = run_moe(x, ids, w, B["banks"], H_FULL, I_FULL, E_FULL, dtype="f16")
+    t0 = time.perf_counter()
+    ref = oracle.moe(x, ids, w, B["gate"], B["up"], B["down"], H_FULL, I_FULL)
+    note(f"  oracle {time.perf_counter() - t0:.1f} s")
     assert np.isfinite(got).all()
-    rng = np.random.default_rng(7)
-    # first, last, and tokens routed to the least and the most popular experts
-    counts = np.bincount(ids.reshape(-1), minlength=E_FULL)
-    rare = np.argmin(counts)
-    toks = sorted({0, n_tok - 1, int(np.nonzero((ids == rare).any(1))[0][0]),
-                   *rng.choice(n_tok, 29, replace=False).tolist()})
-    ref = oracle.moe(x, ids, w, B["gate"], B["up"], B["down"], H_FULL, I_FULL, tokens=toks)
-    err = normwise(got[toks], ref)
-    note(f"  {len(toks)} sampled tokens, normwise {err:.2e}")
+    err = normwise(got, ref)
+    worst = np.max(np.abs(got.astype(np.float64) - ref), axis=1) / np.max(np.abs(ref))
+    note(f"  normwise {err:.2e}; worst token {int(np.argmax(worst))}")
     assert err <= 5e-3
+
+
+def test_prefill_three_quad_shapes():
+    """A prefill bank whose products span several K quads at shapes off the workload's:
+    hidden 1,280 (10 quads in gate|up, not a multiple of 256 rows in down's output tile
+    walk) and inter 1,152 (9 quads in down); every output against the oracle."""
+    note("moe prefill: H=1280 I=1152 E=6 n_tok=260 k=3, every output")
+    rng = np.random.default_rng(1280)
+    E, H, I = 6, 1280, 1152
+    gate, up, down = make_bank(rng, E, H, I)
+    banks = (pack_bank(gate, I, H), pack_bank(up, I, H), pack_bank(down, H, I))
+    ids, w = routing(rng, 260, E, 3)
+    x = rng.standard_normal((260, H)).astype(np.float16)
+    got, _ = run_moe(x, ids, w, banks, H, I, E)
+    assert normwise(got, oracle.moe(x, ids, w, gate, up, down, H, I)) <= 5e-3
