@@ -24,6 +24,7 @@ IQ4_E_WORKSPACE = -5
 IQ4_F32 = 0
 IQ4_F16 = 1
 IQ4_MOE_ATOMIC_COMBINE = 1
+IQ4_QMV_NOALLOC_SCRATCH_BYTES = 4 << 20
 
 _c_i64, _c_i32, _c_u32, _c_p, _c_sz = ctypes.c_int64, ctypes.c_int32, ctypes.c_uint32, ctypes.c_void_p, ctypes.c_size_t
 
@@ -38,6 +39,7 @@ SIGNATURES = {
     "iq4_qmv_workspace_size": (ctypes.c_int, [_c_i64, _c_i64, ctypes.POINTER(_c_sz)]),
     "iq4_qmv_multi": (ctypes.c_int, [_c_p, _c_i64, _c_i64, _c_p, _c_i64, _c_i32, _c_p, _c_i64, _c_p, _c_sz,
                                      _c_p]),
+    "iq4_qmv_multi_noalloc": (ctypes.c_int, [_c_p, _c_i64, _c_i64, _c_p, _c_i64, _c_i32, _c_p, _c_i64, _c_p]),
     "iq4_quantize_q8_1": (ctypes.c_int, [_c_p, _c_i64, _c_i64, _c_i64, _c_p, _c_p, _c_p]),
     "iq4_qmv_q8": (ctypes.c_int, [_c_p, _c_i64, _c_i64, _c_p, _c_p, _c_i32, _c_p, _c_i64, _c_p, _c_sz, _c_p]),
     "iq4_route_topk": (ctypes.c_int, [_c_p, _c_i64, _c_i32, _c_i32, _c_p, _c_p, _c_p]),
@@ -136,6 +138,10 @@ def iq4_qmv_workspace_size(n, k) -> int:
 def iq4_qmv_multi(packed, n, k, x, ldx, T, y, ldy, workspace=None, ws_bytes=0, stream=None):
     _call("iq4_qmv_multi", _ptr(packed), n, k, _ptr(x), ldx, T, _ptr(y), ldy, _ptr(workspace), ws_bytes,
           _stream(stream))
+
+
+def iq4_qmv_multi_noalloc(packed, n, k, x, ldx, T, y, ldy, stream=None):
+    _call("iq4_qmv_multi_noalloc", _ptr(packed), n, k, _ptr(x), ldx, T, _ptr(y), ldy, _stream(stream))
 
 
 def iq4_quantize_q8_1(x, T, k, ldx, q, d, stream=None):

@@ -104,17 +104,23 @@ int iq4_qmv_workspace_size(int64_t n, int64_t k, size_t* bytes) {
   return IQ4_OK;
 }
 
+static int check_qmv(const char* fn, const void* packed, int64_t n, int64_t k, const float* x, int64_t ldx,
+                     int32_t T, const float* y, int64_t ldy) {
+  if (int e = check_matrix(fn, n, k)) return e;
+  if (T < 1 || T > 8) return set_error(IQ4_E_ARG, "%s: T must be in 1..8 (got %d)", fn, T);
+  if (ldx < k || ldx % 4) return set_error(IQ4_E_ARG, "%s: ldx must be >= k and a multiple of 4", fn);
+  if (ldy < n) return set_error(IQ4_E_ARG, "%s: ldy must be >= n", fn);
+  if (!packed || !x || !y) return set_error(IQ4_E_ARG, "%s: null pointer", fn);
+  if (!aligned(packed, 256) || !aligned(x, 16) || !aligned(y, 4))
+    return set_error(IQ4_E_ALIGN, "%s: packed must be 256-byte, x 16-byte, y 4-byte aligned", fn);
+  return IQ4_OK;
+}
+
 int iq4_qmv_multi(const void* packed, int64_t n, int64_t k, const float* x, int64_t ldx,
                   int32_t T, float* y, int64_t ldy, void* workspace, size_t ws_bytes,
                   void* stream) {
   clear_error();
-  if (int e = check_matrix("iq4_qmv_multi", n, k)) return e;
-  if (T < 1 || T > 8) return set_error(IQ4_E_ARG, "iq4_qmv_multi: T must be in 1..8 (got %d)", T);
-  if (ldx < k || ldx % 4) return set_error(IQ4_E_ARG, "iq4_qmv_multi: ldx must be >= k and a multiple of 4");
-  if (ldy < n) return set_error(IQ4_E_ARG, "iq4_qmv_multi: ldy must be >= n");
-  if (!packed || !x || !y) return set_error(IQ4_E_ARG, "iq4_qmv_multi: null pointer");
-  if (!aligned(packed, 256) || !aligned(x, 16) || !aligned(y, 4))
-    return set_error(IQ4_E_ALIGN, "iq4_qmv_multi: packed must be 256-byte, x 16-byte, y 4-byte aligned");
+  if (int e = check_qmv("iq4_qmv_multi", packed, n, k, x, ldx, T, y, ldy)) return e;
   const int64_t need = qmv_workspace_bytes(n, k);
   if (need > 0) {
     if (!workspace || ws_bytes < (size_t)need)
@@ -123,6 +129,13 @@ int iq4_qmv_multi(const void* packed, int64_t n, int64_t k, const float* x, int6
   }
   return launch_qmv(static_cast<const uint8_t*>(packed), n, k, x, ldx, T, y, ldy, workspace,
                     as_stream(stream));
+}
+
+int iq4_qmv_multi_noalloc(const void* packed, int64_t n, int64_t k, const float* x, int64_t ldx,
+                          int32_t T, float* y, int64_t ldy, void* stream) {
+  clear_error();
+  if (int e = check_qmv("iq4_qmv_multi_noalloc", packed, n, k, x, ldx, T, y, ldy)) return e;
+  return launch_qmv_noalloc(static_cast<const uint8_t*>(packed), n, k, x, ldx, T, y, ldy, as_stream(stream));
 }
 
 int iq4_quantize_q8_1(const float* x, int64_t T, int64_t k, int64_t ldx, int8_t* q, uint16_t* d,

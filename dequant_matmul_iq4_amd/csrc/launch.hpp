@@ -11,6 +11,9 @@ int launch_pack(const void* blocks, int64_t n, int64_t k, void* packed, hipStrea
 
 int launch_qmv(const uint8_t* packed, int64_t n, int64_t k, const float* x, int64_t ldx, int T,
                float* y, int64_t ldy, void* workspace, hipStream_t s);
+// as launch_qmv, the split-K scratch from the library's own device array (no workspace)
+int launch_qmv_noalloc(const uint8_t* packed, int64_t n, int64_t k, const float* x, int64_t ldx, int T,
+                       float* y, int64_t ldy, hipStream_t s);
 
 int launch_route_topk(const float* logits, int64_t n_tok, int n_expert, int top_k, int32_t* ids,
                       float* w, hipStream_t s);

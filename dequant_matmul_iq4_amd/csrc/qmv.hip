@@ -46,6 +46,9 @@
 // 8-bit activations.  The same plan, weight stream and table serve the product on
 // 8-bit activation codes (quantize_q8_kernel, qmv_q8_kernel at the end of this file):
 // a code is exact in bf16, so the matrix core returns each block's integer dot exactly.
+#include <mutex>
+
+#include "iq4.h"
 #include "common.hpp"
 #include "launch.hpp"
 #include "qmv.hpp"
@@ -870,6 +873,63 @@ int launch_qmv(const uint8_t* packed, int64_t n, int64_t k, const float* x, int6
     case 3: return launch_dense<3>(a, grid);
     default: return launch_dense<kMaxWaveQuads>(a, grid);
   }
+}
+
+// ---------------------------------------------------------------------------------
+// The matvec without a caller workspace (iq4_qmv_multi_noalloc), for callers that cannot
+// allocate: the split-K arrival counters and partial sums of a call live in this
+// file-scope device array.  Each GPU holds its own copy until the process ends.  In
+// host code the name `scratch` is only a host-side stand-in for the array: kernels get
+// the device address that hipGetSymbolAddress returns, looked up once per device (with
+// that device current) and kept in g_scratch.  Every call on one GPU shares that GPU's
+// copy: calls that overlap in time on one GPU race; calls in one stream order do not
+// (each leaves the counters at zero, as a caller workspace is left).
+constexpr int64_t kQmvScratchBytes = int64_t(4) << 20;
+static __device__ __align__(256) uint8_t scratch[kQmvScratchBytes];
+
+__global__ void __launch_bounds__(256) zero_scratch_kernel(uint4* p, int64_t n16) {
+  for (int64_t i = (int64_t)blockIdx.x * 256 + threadIdx.x; i < n16; i += (int64_t)gridDim.x * 256)
+    p[i] = uint4{0u, 0u, 0u, 0u};
+}
+
+constexpr int kMaxDevices = 64;
+static std::mutex g_scratch_mu;
+static void* g_scratch[kMaxDevices];
+
+// The device address of this GPU's scratch; the first call on a device looks it up and
+// clears the array with a fill kernel on `s` (a kernel, not a memset, so that a caller
+// capturing the call records no memset node).
+static int scratch_address(hipStream_t s, void** out) {
+  int dev = -1;
+  hipError_t e = hipGetDevice(&dev);
+  if (e != hipSuccess) return set_error(IQ4_E_HIP, "iq4_qmv_multi_noalloc: hipGetDevice: %s", hipGetErrorString(e));
+  if (dev < 0 || dev >= kMaxDevices) return set_error(IQ4_E_HIP, "iq4_qmv_multi_noalloc: device %d out of range", dev);
+  std::lock_guard<std::mutex> lock(g_scratch_mu);
+  if (!g_scratch[dev]) {
+    void* ptr = nullptr;
+    e = hipGetSymbolAddress(&ptr, HIP_SYMBOL(scratch));
+    if (e != hipSuccess || ptr == nullptr)
+      return set_error(IQ4_E_HIP, "iq4_qmv_multi_noalloc: hipGetSymbolAddress: %s", hipGetErrorString(e));
+    hipLaunchKernelGGL(zero_scratch_kernel, dim3(256), dim3(256), 0, s, static_cast<uint4*>(ptr),
+                       kQmvScratchBytes / 16);
+    if (int rc = check_launch("zero_scratch_kernel")) return rc;
+    g_scratch[dev] = ptr;
+  }
+  *out = g_scratch[dev];
+  return IQ4_OK;
+}
+
+int launch_qmv_noalloc(const uint8_t* packed, int64_t n, int64_t k, const float* x, int64_t ldx, int T,
+                       float* y, int64_t ldy, hipStream_t s) {
+  const int64_t need = qmv_workspace_bytes(n, k);
+  if (need > kQmvScratchBytes)
+    return set_error(IQ4_E_WORKSPACE,
+                     "iq4_qmv_multi_noalloc: n=%lld k=%lld needs %lld bytes of split-K scratch, above the "
+                     "%lld-byte array (use iq4_qmv_multi with a workspace)",
+                     (long long)n, (long long)k, (long long)need, (long long)kQmvScratchBytes);
+  void* ws = nullptr;
+  if (int rc = scratch_address(s, &ws)) return rc;
+  return launch_qmv(packed, n, k, x, ldx, T, y, ldy, need > 0 ? ws : nullptr, s);
 }
 
 template <int MODE, int RG, int WQ>

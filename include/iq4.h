@@ -143,6 +143,29 @@ int iq4_qmv_multi(const void* packed, int64_t n, int64_t k, const float* x, int6
                   void* stream);
 
 /*
+ * iq4_qmv_multi for callers that cannot allocate device memory (code under HIP graph
+ * capture, tight serving loops, harnesses that forbid hipMalloc): the same arguments
+ * without the workspace, the same results (bitwise: each column equals iq4_qmv_multi's
+ * and the 1-column call's), the same errors.  The split-K scratch that iq4_qmv_multi
+ * takes from a workspace (needed only when k > 4096) comes instead from a device array
+ * inside the library, IQ4_QMV_NOALLOC_SCRATCH_BYTES per GPU, held until the process ends.
+ *   - Nothing is allocated or freed in any call.
+ *   - A shape whose iq4_qmv_workspace_size exceeds IQ4_QMV_NOALLOC_SCRATCH_BYTES is
+ *     rejected with IQ4_E_WORKSPACE before anything is enqueued.
+ *   - `stream` must belong to the current device.  The first call on a device looks up
+ *     the array's address there and clears the array with a fill kernel on `stream`
+ *     (make that first call outside graph capture; later calls may be captured).
+ *   - All calls on one GPU share that GPU's array: calls that overlap in time on one GPU
+ *     (different streams, or graphs replayed concurrently) race and give wrong results.
+ *     Calls in one stream order are safe; each leaves the array ready for the next.
+ * Errors: as iq4_qmv_multi; IQ4_E_WORKSPACE for a shape above the array's size;
+ * IQ4_E_HIP if the array's address cannot be found.
+ */
+#define IQ4_QMV_NOALLOC_SCRATCH_BYTES (4u << 20)
+int iq4_qmv_multi_noalloc(const void* packed, int64_t n, int64_t k, const float* x, int64_t ldx,
+                          int32_t T, float* y, int64_t ldy, void* stream);
+
+/*
  * 8-bit block quantisation of fp32 activations (the activation side of page 1's
  * decode products: its verify.hpp keeps the window's T activation columns as q8_1
  * blocks; the pages name that format without printing it).  Per column t and block of

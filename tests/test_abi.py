@@ -163,3 +163,16 @@ def test_q8_validation_errors_never_launch():
     assert _rc("iq4_qmv_q8", None, 16, 128, FAKE, FAKE, 1, FAKE, 16, None, 0, None) == iq4.IQ4_E_ARG
     need = iq4.iq4_qmv_workspace_size(256, 14336)
     assert _rc("iq4_qmv_q8", FAKE, 256, 14336, FAKE, FAKE, 1, FAKE, 256, FAKE, need - 1, None) == iq4.IQ4_E_WORKSPACE
+
+
+def test_noalloc_matvec_validation_never_launches():
+    """The no-allocation matvec validates as iq4_qmv_multi and rejects shapes whose
+    split-K scratch would exceed its fixed device array, before any set-up or launch."""
+    assert _rc("iq4_qmv_multi_noalloc", FAKE, 16, 128, FAKE, 128, 0, FAKE, 16, None) == iq4.IQ4_E_ARG
+    assert "T must be" in iq4.iq4_last_error()
+    assert _rc("iq4_qmv_multi_noalloc", FAKE, 17, 128, FAKE, 128, 1, FAKE, 17, None) == iq4.IQ4_E_UNSUPPORTED
+    assert _rc("iq4_qmv_multi_noalloc", FAKE, 16, 128, FAKE + 4, 128, 1, FAKE, 16, None) == iq4.IQ4_E_ALIGN
+    n, k = 1 << 15, 1 << 17
+    assert iq4.iq4_qmv_workspace_size(n, k) > iq4.IQ4_QMV_NOALLOC_SCRATCH_BYTES
+    assert _rc("iq4_qmv_multi_noalloc", FAKE, n, k, FAKE, k, 1, FAKE, n, None) == iq4.IQ4_E_WORKSPACE
+    assert "scratch" in iq4.iq4_last_error()
