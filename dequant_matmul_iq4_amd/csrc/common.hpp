@@ -45,6 +45,7 @@ constexpr int kTileScaleBytes = 128;
 // ---------------------------------------------------------------------------------
 // Matrix-core operand types (v_mfma_f32_16x16x32_{bf16,f16}).
 typedef __bf16 bf16x8 __attribute__((ext_vector_type(8)));
+typedef __bf16 bf16x2 __attribute__((ext_vector_type(2)));
 typedef _Float16 f16x8 __attribute__((ext_vector_type(8)));
 typedef float f32x4 __attribute__((ext_vector_type(4)));
 typedef uint32_t u32x4 __attribute__((ext_vector_type(4)));

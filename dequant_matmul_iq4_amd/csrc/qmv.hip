@@ -5,18 +5,18 @@
 // FMA per weight per column plus the index decode: at T = 4 that is more than 4 VALU
 // operations per 4.5-bit weight, while streaming the weights at the HBM rate leaves a
 // budget of under 3 (256 CUs x 64 lanes x 2.4 GHz against 8 TB/s of 18-byte blocks).
-// So the K-reduction runs on the matrix cores instead, exactly:
+// So the K-reduction runs on the matrix cores instead:
 //
-//  * each fp32 activation x is split into three bf16 parts x = hi + mid + lo by
-//    truncation (hi keeps the top 8 significand bits, mid the next 8, lo the last 8);
-//    the split is exact for |x| >= 2^-100;
-//  * codebook levels are integers of at most 7 significant bits, exact in bf16, so
+//  * codebook levels are integers of at most 7 significant bits, exact in bf16;
+//  * each fp32 activation x goes in as bf16 parts: the verify-window kernel below uses
+//    two (hi = bf16(x), lo = bf16(x - hi): x to within 2^-18 |x|), the grouped MoE
+//    decode kernels three (hi, mid, lo by truncation: x exactly, for |x| >= 2^-100);
 //    every product level * part is exact in fp32;
 //  * one v_mfma_f32_16x16x32_bf16 covers one block of 32 weights for 16 weight rows
 //    (B operand) against 16 "rows" of A = (part s, token t) pairs, 4s + t;
 //  * the block scale d is applied to the 16x16 result with an fp32 FMA per block, the
 //    K-slices of the workgroup's waves are summed in a fixed order, and finally the
-//    three parts are added (hi + mid) + lo.
+//    parts are added.
 //
 // Column invariance.  Token t's value never meets another token's: it sits in matrix
 // row 4s + (t mod 4) of the pass that holds it, the per-block scaling and the
@@ -203,40 +203,98 @@ struct ColsC {  // a column count as a type (compile-time pass width)
   static constexpr int value = N;
 };
 
-// Dense verify-window matvec: one workgroup per row tile and K slice; each wave owns WQ
-// quads of the slice (registers and LDS sized to K).  The code of a pass is straight
-// line, in the order the data arrive: the pass's activations are requested first (L2
-// hot), then every weight of the wave; the activations are split and staged while the
+// ---------------------------------------------------------------------------------
+// Dense verify-window matvec.
+//
+// Activations.  Each fp32 activation x goes to the matrix core as two bf16 parts,
+// hi = bf16_rne(x) and lo = bf16_rne(x - hi), where x - hi is exact in fp32; so
+// hi + lo equals x to within 2^-18 |x|, far inside the fp32 paths' tolerance, and
+// hi * level and lo * level are exact products.  The parts sit in rows 4s + t of the
+// A operand (s = 0 hi, 1 lo; t = the column within a pass of 4), the weight levels
+// (exact in bf16) are the B operand; rows 8..15 are never read.
+//
+// Work split.  One workgroup per row tile (16 rows) and K slice; each wave owns a run
+// of WQ quads of the slice.  The code is straight line in the order the data arrive:
+// the pass's activations are requested first (L2 hot), then every weight of the wave;
+// the level table is built and the activations are split and staged in LDS while the
 // weights stream in, and quad u is decoded and multiplied as soon as its own weights
-// have landed, so the arithmetic runs under the weight stream instead of after it.
+// have landed.
+//
+// LDS.  The byte-indexed level table (one index byte = two 4-bit indices -> two bf16
+// levels) has kDenseLutCopies copies, entry e of copy j at word kDenseLutCopies e + j;
+// lane l reads copy l mod kDenseLutCopies, so a wave's 64 lookups are served at the
+// full LDS rate.  It sits at LDS offset 0 and is addressed with one byte permute: the
+// index byte lands in bits 8..15 of the address, the lane's copy in bits 0..7.  The
+// staged activations follow: per wave and block, 4 k-group slots of 8 rows (16 B
+// each) plus one row of padding, so the 16 lanes that stage consecutive slots write
+// distinct banks.
+constexpr int kDenseWaves = 8;  // waves per workgroup (at most)
+constexpr int kDenseLutCopies = 64;
+constexpr int kDenseLutBytes = 256 * kDenseLutCopies * 4;  // 64 KiB
+constexpr int kDenseSlot = 9 * 16;                         // 8 rows + 1 row of padding
+constexpr int kDenseBlockStage = 4 * kDenseSlot;           // 576 B per block
+
+// hi and lo parts of two values, packed per part: hi = (bf16(v0), bf16(v1)), lo likewise
+// for the residuals.  The residual v - hi is formed by a bf16 dot product whose only
+// non-zero term is -1 * hi (fused with v, rounded once): exact, since v - hi is
+// representable.
+// The two constants (-1, 0) and (0, -1) are passed in scalar registers: as an inline
+// constant, a packed bf16 operand's halves are not placed unambiguously.
+__device__ __forceinline__ void split_hi_lo(float v0, float v1, uint32_t& hi, uint32_t& lo) {
+  const bf16x2 h = {(__bf16)v0, (__bf16)v1};
+  uint32_t k_lo = 0x0000BF80u, k_hi = 0xBF800000u;  // (-1, 0) and (0, -1) as bf16 pairs
+  asm("" : "+s"(k_lo), "+s"(k_hi));                  // opaque: kept in registers
+  const float r0 = __builtin_amdgcn_fdot2_f32_bf16(h, __builtin_bit_cast(bf16x2, k_lo), v0, false);
+  const float r1 = __builtin_amdgcn_fdot2_f32_bf16(h, __builtin_bit_cast(bf16x2, k_hi), v1, false);
+  const bf16x2 l = {(__bf16)r0, (__bf16)r1};
+  hi = __builtin_bit_cast(uint32_t, h);
+  lo = __builtin_bit_cast(uint32_t, l);
+}
+
+// bf16 bit pattern of codebook level q (exact: |level| <= 127)
+__device__ __forceinline__ uint32_t bf16_level(uint32_t q) { return bf16_of_level(level_of(q)); }
+
 template <int WQ, int TP>
-__global__ void __launch_bounds__(512) qmv_dense_kernel(QmvArgs a) {
+__global__ void __launch_bounds__(64 * kDenseWaves) qmv_dense_kernel(QmvArgs a) {
   static_assert(TP >= 1 && TP <= kCols, "first pass: 1..4 columns");
-  constexpr int XBYTES = kWaves * WQ * 4 * kFragBytes;
-  __shared__ uint32_t lut[256 * kLutCopies];
-  __shared__ __attribute__((aligned(16))) uint8_t xs[XBYTES + 256];  // + room for padding-row reads
-  __shared__ f32x4 red[kWaves * 64];
+  constexpr int XBYTES = kDenseWaves * WQ * 4 * kDenseBlockStage;
+  __shared__ __attribute__((aligned(256))) uint8_t smem[kDenseLutBytes + XBYTES + kDenseWaves * 64 * 16];
   __shared__ int s_last;
+  // Every kernel argument, loaded at entry.  Left to itself the compiler loads some of
+  // them where they are first used, deep in the kernel; while such a scalar load is
+  // outstanding each wait for an LDS read must wait for it too.
+  const uint8_t* const W0 = a.W0;
+  const float* const X = a.x;
+  float* const Y = a.y;
+  float* const partials = a.partials;
+  int* const counters = a.counters;
+  const int64_t ldx = a.ldx, ldy = a.ldy, n_rows = a.n, rg_n = a.rg_n, nibble_bytes = a.nibble_bytes;
+  const int T_all = a.T, kq_n = a.kq_n, S = a.S, slice_quads = a.slice_quads, wave_quads = a.wave_quads;
+  asm volatile("" ::"s"(W0), "s"(X), "s"(Y), "s"(partials), "s"(counters), "s"(ldx), "s"(ldy), "s"(n_rows),
+               "s"(rg_n), "s"(nibble_bytes), "s"(T_all), "s"(kq_n), "s"(S), "s"(slice_quads), "s"(wave_quads));
+
+  uint8_t* const xs = smem + kDenseLutBytes;
+  f32x4* const red = reinterpret_cast<f32x4*>(smem + kDenseLutBytes + XBYTES);
+  typedef __attribute__((address_space(3))) const uint8_t lds_u8;
+  lds_u8* const lds = (lds_u8*)(__attribute__((address_space(3))) uint8_t*)smem;
 
   const int tid = threadIdx.x;
   const int lane = tid & 63, wave = tid >> 6, nwaves = (int)(blockDim.x >> 6);
   const int c = lane & 15, g = lane >> 4;
 
   // ---- tile of this workgroup ---------------------------------------------------------
-  const int64_t rg = blockIdx.x / a.S;
-  const int slice = (int)(blockIdx.x % a.S);
-  const int64_t ncols = a.T;
-  const int kq_n = a.kq_n;
-  const int kqa = slice * a.slice_quads;                 // first quad of the slice
-  const int nq_slice = min(a.slice_quads, kq_n - kqa);   // quads in the slice
-  const int wq0 = wave * a.wave_quads;                   // this wave's quads (slice-relative)
-  const int wq1 = min(wq0 + a.wave_quads, nq_slice);
+  const int64_t rg = blockIdx.x / S;
+  const int slice = (int)(blockIdx.x % S);
+  const int64_t ncols = T_all;
+  const int kqa = slice * slice_quads;                 // first quad of the slice
+  const int nq_slice = min(slice_quads, kq_n - kqa);   // quads in the slice
+  const int wq0 = wave * wave_quads;                   // this wave's quads (slice-relative)
+  const int wq1 = min(wq0 + wave_quads, nq_slice);
   const int wblk = 4 * (wq1 - wq0);                      // blocks of this wave (0 if idle)
-  uint8_t* xw = xs + wave * (4 * WQ) * kFragBytes;       // the wave's own staging region
+  uint8_t* xw = xs + wave * (4 * WQ) * kDenseBlockStage;  // the wave's own staging region
 
   // Staging tasks: (column t, block bl, k-group gg) = task (t SLOTS + 4 bl + gg), task =
-  // lane + 64 i; a full wave's mapping is fixed at compile time (for WQ = 4 lane l always
-  // stages slot l and i is the column), blocks past a short wave's run are skipped.
+  // lane + 64 i, fixed at compile time for a full wave; blocks past a short run skipped.
   constexpr int SLOTS = 16 * WQ;
   float4 xr[WQ][2];
   auto load_x = [&](int64_t t0, int T) {
@@ -245,36 +303,40 @@ __global__ void __launch_bounds__(512) qmv_dense_kernel(QmvArgs a) {
       const int task = lane + 64 * i;
       const int t = task / SLOTS, bl = (task % SLOTS) >> 2, gg = task & 3;
       if (t < T && bl < wblk) {
-        const float* p = a.x + (t0 + t) * a.ldx + ((int64_t)(kqa + wq0) * 4 + bl) * kQK + 8 * gg;
+        const float* p = X + (t0 + t) * ldx + ((int64_t)(kqa + wq0) * 4 + bl) * kQK + 8 * gg;
         xr[i][0] = *reinterpret_cast<const float4*>(p);
         xr[i][1] = *reinterpret_cast<const float4*>(p + 4);
       }
     }
   };
-  auto store_x = [&](int T) {  // split and store in fragment order
+  // split and store: part s of column t in row 4s + t.  LDS accesses of one wave execute
+  // in order, so the wave's fragment reads see these writes (the fences only keep the
+  // compiler from moving them) and a next pass's writes follow this pass's reads.
+  auto store_x = [&](int T) {
 #pragma unroll
     for (int i = 0; i < WQ; ++i) {
       const int task = lane + 64 * i;
       const int t = task / SLOTS, bl = (task % SLOTS) >> 2, gg = task & 3;
       if (t < T && bl < wblk) {
-        const float4 xa = xr[i][0], xb = xr[i][1];
-        uint32_t p0[3], p1[3], p2[3], p3[3];
-        split_pair(xa.x, xa.y, p0);
-        split_pair(xa.z, xa.w, p1);
-        split_pair(xb.x, xb.y, p2);
-        split_pair(xb.z, xb.w, p3);
-        uint8_t* dst = xw + (bl * 4 + gg) * (kFragStride * 16) + t * 16;
-#pragma unroll
-        for (int sp = 0; sp < 3; ++sp)
-          *reinterpret_cast<uint4*>(dst + sp * 4 * 16) = uint4{p0[sp], p1[sp], p2[sp], p3[sp]};
+        uint32_t h[4], l[4];
+        split_hi_lo(xr[i][0].x, xr[i][0].y, h[0], l[0]);
+        split_hi_lo(xr[i][0].z, xr[i][0].w, h[1], l[1]);
+        split_hi_lo(xr[i][1].x, xr[i][1].y, h[2], l[2]);
+        split_hi_lo(xr[i][1].z, xr[i][1].w, h[3], l[3]);
+        uint8_t* dst = xw + (bl * 4 + gg) * kDenseSlot + t * 16;
+        *reinterpret_cast<uint4*>(dst) = uint4{h[0], h[1], h[2], h[3]};
+        *reinterpret_cast<uint4*>(dst + 4 * 16) = uint4{l[0], l[1], l[2], l[3]};
       }
     }
+    __builtin_amdgcn_fence(__ATOMIC_RELEASE, "wavefront", "local");
+    __builtin_amdgcn_wave_barrier();
+    __builtin_amdgcn_fence(__ATOMIC_ACQUIRE, "wavefront", "local");
   };
 
   uint4 nib[WQ];
   uint2 scl[WQ];
-  const uint8_t* tp = a.W0 + (rg * kq_n + kqa) * kTileNibbleBytes + lane * 16;
-  const uint8_t* sp = a.W0 + a.nibble_bytes + (rg * kq_n + kqa) * kTileScaleBytes + c * 8;
+  const uint8_t* tp = W0 + (rg * kq_n + kqa) * kTileNibbleBytes + lane * 16;
+  const uint8_t* sp = W0 + nibble_bytes + (rg * kq_n + kqa) * kTileScaleBytes + c * 8;
 
   // ---- requests: the first pass's activations, then every weight of the wave --------
   constexpr int T0 = TP;  // columns of the first pass, min(T, 4): fixed per instantiation
@@ -285,20 +347,36 @@ __global__ void __launch_bounds__(512) qmv_dense_kernel(QmvArgs a) {
     nib[u] = *reinterpret_cast<const uint4*>(tp + (int64_t)q * kTileNibbleBytes);
     scl[u] = *reinterpret_cast<const uint2*>(sp + (int64_t)q * kTileScaleBytes);
   }
-  // ---- level table (every copy of entry e written by two threads, 16 words each) ------
-  for (int i = tid; i < 512; i += blockDim.x) {
-    const int e = i >> 1;
-    const uint32_t v = bf16_of_level(level_of(e & 15)) | (bf16_of_level(level_of(e >> 4)) << 16);
-    uint4* dst = reinterpret_cast<uint4*>(lut + e * kLutCopies + (i & 1) * 16);
+  // ---- level table: with NT = 64 kDenseWaves threads, 16-byte chunk q = tid + NT j
+  // holds copies 4(q mod 16) .. +3 of entry q / 16, whose low index is (tid / 16) mod 16
+  // for every j and whose high index (tid / 256) + (NT / 256) j is the same for the whole
+  // wave; consecutive lanes write consecutive chunks (no bank conflicts).
+  {
+    constexpr int NT = 64 * kDenseWaves;
+    const uint32_t lo = bf16_level((uint32_t)(tid >> 4) & 15u);
+    const uint32_t hsel = (uint32_t)__builtin_amdgcn_readfirstlane(tid >> 8);
+    uint4* dst = reinterpret_cast<uint4*>(smem) + tid;
 #pragma unroll
-    for (int w4 = 0; w4 < 4; ++w4) dst[w4] = uint4{v, v, v, v};
+    for (int j = 0; j < 4096 / NT; ++j) {
+      const uint32_t v = lo | (bf16_level(hsel + (uint32_t)(NT / 256) * j) << 16);
+      dst[NT * j] = uint4{v, v, v, v};
+    }
   }
-  const uint32_t* lutl = lut + (lane & (kLutCopies - 1));
+  // A lookup: byte b of index word w -> the lane's copy of entry w.byte[b]
+  const uint32_t lane_copy = (uint32_t)lane * 4u;
+  auto lookup = [&](uint32_t w, int b) -> uint32_t {
+    const uint32_t addr = __builtin_amdgcn_perm(lane_copy, w, 0x0c0c0004u | ((uint32_t)b << 8));
+    return *reinterpret_cast<__attribute__((address_space(3))) const uint32_t*>(lds + addr);
+  };
+  // this lane's A-fragment row in the wave's staging region (block bl at + bl * 4 slots)
+  lds_u8* const arow_p = lds + kDenseLutBytes + (wave * (4 * WQ) * kDenseBlockStage + g * kDenseSlot + c * 16);
 
-  // NC (compile time): the pass's columns; accumulator lane i holds column i, so the
-  // scale FMAs of columns past NC are skipped (their rows are never read)
+  // NC (compile time): the pass's columns; accumulator entry i of a lane in k-group g
+  // holds row 4g + i (g = 0: hi parts, g = 1: lo parts, column i), so the scale FMAs of
+  // columns past NC are skipped.  A-fragment reads are masked to the rows that exist.
   auto multiply = [&](f32x4& acc, auto nc) {
     constexpr int NC = decltype(nc)::value;
+    const bool arow = c < 8 && (c & 3) < NC;
     acc = f32x4{0.f, 0.f, 0.f, 0.f};
 #pragma unroll
     for (int u = 0; u < WQ; ++u) {
@@ -308,12 +386,11 @@ __global__ void __launch_bounds__(512) qmv_dense_kernel(QmvArgs a) {
 #pragma unroll
       for (int j = 0; j < 4; ++j) {
         const int bl = 4 * u + j;  // block within this wave's run
-        xf[j] = *reinterpret_cast<const u32x4*>(xw + (bl * 4 + g) * (kFragStride * 16) + c * 16);
+        if (arow)
+          xf[j] = *reinterpret_cast<__attribute__((address_space(3))) const u32x4*>(arow_p + bl * kDenseBlockStage);
         const uint32_t w = (j == 0) ? nib[u].x : (j == 1) ? nib[u].y : (j == 2) ? nib[u].z : nib[u].w;
-        bf[j][0] = lutl[(w & 0xFF) * kLutCopies];
-        bf[j][1] = lutl[((w >> 8) & 0xFF) * kLutCopies];
-        bf[j][2] = lutl[((w >> 16) & 0xFF) * kLutCopies];
-        bf[j][3] = lutl[(w >> 24) * kLutCopies];
+#pragma unroll
+        for (int b = 0; b < 4; ++b) bf[j][b] = lookup(w, b);
       }
       f32x4 prod[4];
 #pragma unroll
@@ -328,36 +405,36 @@ __global__ void __launch_bounds__(512) qmv_dense_kernel(QmvArgs a) {
     }
   };
 
-  // Cross-wave reduction in wave order, then the three parts; stores (or split-K
-  // partials) for columns t0 .. t0 + T - 1.
+  // Cross-wave reduction in wave order, hi parts and lo parts apart, then hi + lo;
+  // stores (or split-K partials) for columns t0 .. t0 + T - 1.
   auto reduce_store = [&](int64_t t0, int T, const f32x4& acc) {
     red[wave * 64 + lane] = acc;
     lds_barrier();
-    // Lane (g, c) held D[4g + i][c]: part s = g, column i, weight row c.
+    // lane (g, c) held D[4g + i][c]: part g, column i, weight row c
     const int idx = tid;  // T * 16 <= 64 outputs: the first wave
     const int t = idx >> 4, row = idx & 15;
     float v = 0.f;
     if (idx < T * kTileRows) {
       const float* redf = reinterpret_cast<const float*>(red);
-      float pv[3][kWaves];
+      float pv[2][kDenseWaves];
 #pragma unroll
-      for (int p = 0; p < 3; ++p)
+      for (int p = 0; p < 2; ++p)
 #pragma unroll
-        for (int w2 = 0; w2 < kWaves; ++w2) pv[p][w2] = redf[(w2 * 64 + 16 * p + row) * 4 + t];
-      float part[3];
+        for (int w2 = 0; w2 < kDenseWaves; ++w2) pv[p][w2] = redf[(w2 * 64 + 16 * p + row) * 4 + t];
+      float part[2];
 #pragma unroll
-      for (int p = 0; p < 3; ++p) {
+      for (int p = 0; p < 2; ++p) {
         float sum = pv[p][0];
 #pragma unroll
-        for (int w2 = 1; w2 < kWaves; ++w2) sum = (w2 < nwaves) ? sum + pv[p][w2] : sum;
+        for (int w2 = 1; w2 < kDenseWaves; ++w2) sum = (w2 < nwaves) ? sum + pv[p][w2] : sum;
         part[p] = sum;
       }
-      v = (part[0] + part[1]) + part[2];
+      v = part[0] + part[1];
     }
     const int64_t col = rg * kTileRows + row;  // output row index (weight row)
-    const bool ok = idx < T * kTileRows && col < a.n;
-    if (a.S == 1) {
-      if (ok) a.y[(t0 + t) * a.ldy + col] = v;
+    const bool ok = idx < T * kTileRows && col < n_rows;
+    if (S == 1) {
+      if (ok) Y[(t0 + t) * ldy + col] = v;
       return;
     }
     // Split K: partial sums to the workspace; the last of the S workgroups of this row
@@ -370,21 +447,21 @@ __global__ void __launch_bounds__(512) qmv_dense_kernel(QmvArgs a) {
     // own: nothing orders the passes of different workgroups, so a slice that reaches
     // the second pass early must not touch what the first pass's last arriver reads.
     const int pass = (int)(t0 / kCols);
-    int* counter = a.counters + pass * a.rg_n + rg;
-    float* part = a.partials + (rg * a.S + slice) * (kSplitCols * kTileRows) + (t0 + t) * kTileRows + row;
+    int* counter = counters + pass * rg_n + rg;
+    float* part = partials + (rg * S + slice) * (kSplitCols * kTileRows) + (t0 + t) * kTileRows + row;
     if (idx < T * kTileRows) __hip_atomic_store(part, v, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
     __builtin_amdgcn_s_waitcnt(0);
     __syncthreads();
     if (tid == 0)
-      s_last = __hip_atomic_fetch_add(counter, 1, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT) == a.S - 1;
+      s_last = __hip_atomic_fetch_add(counter, 1, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT) == S - 1;
     __syncthreads();
     if (s_last) {
       if (ok) {
-        const float* p0 = a.partials + rg * a.S * (kSplitCols * kTileRows) + (t0 + t) * kTileRows + row;
+        const float* p0 = partials + rg * S * (kSplitCols * kTileRows) + (t0 + t) * kTileRows + row;
         float sum = __hip_atomic_load(p0, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
-        for (int sl = 1; sl < a.S; ++sl)
+        for (int sl = 1; sl < S; ++sl)
           sum += __hip_atomic_load(p0 + sl * (kSplitCols * kTileRows), __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
-        a.y[(t0 + t) * a.ldy + col] = sum;
+        Y[(t0 + t) * ldy + col] = sum;
       }
       // leaves the workspace ready for the next call
       if (tid == 0) __hip_atomic_store(counter, 0, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
@@ -393,7 +470,7 @@ __global__ void __launch_bounds__(512) qmv_dense_kernel(QmvArgs a) {
   };
 
   // ---- the first pass (up to 4 columns) -------------------------------------------
-  store_x(T0);   // waits for the activations only
+  store_x(T0);    // waits for the activations only
   lds_barrier();  // the table (LDS only: no wait on the weights in flight)
   f32x4 acc;
   multiply(acc, ColsC<T0>{});
@@ -862,6 +939,8 @@ int launch_qmv(const uint8_t* packed, int64_t n, int64_t k, const float* x, int6
   a.ldy = ldy;
   a.stream = s;
   qmv_plan(a, n, k, kDenseRG);
+  a.wave_quads = (a.slice_quads + kDenseWaves - 1) / kDenseWaves;  // this kernel's own wave split
+  a.nwaves = (a.slice_quads + a.wave_quads - 1) / a.wave_quads;
   if (a.S > 1) {
     a.counters = static_cast<int*>(workspace);
     a.partials = reinterpret_cast<float*>(static_cast<uint8_t*>(workspace) + ws_partials_off(a));

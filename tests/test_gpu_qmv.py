@@ -120,7 +120,8 @@ def test_ragged_shapes(n, k, T):
 
 
 def test_wide_dynamic_range_activations():
-    """Activations spanning many binades (exercises the exact three-part split)."""
+    """Activations spanning many binades: the two bf16 parts of each activation carry it
+    to within 2^-18 of its magnitude, so the result is well inside 1e-5 normwise."""
     note("qmv: wide dynamic range")
     rng = np.random.default_rng(5)
     n, k = 64, 1024
