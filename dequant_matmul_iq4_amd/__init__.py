@@ -24,6 +24,9 @@ IQ4_E_WORKSPACE = -5
 IQ4_F32 = 0
 IQ4_F16 = 1
 IQ4_MOE_ATOMIC_COMBINE = 1
+IQ4_MOE_KEEP_INTERMEDIATE = 2
+# iq4_moe_intermediate_layout indices
+MOE_LAYOUT = {"total": 0, "counts": 1, "offsets": 2, "pairs": 3, "slot_row": 4, "h": 5, "rows": 6, "g": 7, "u": 8}
 IQ4_QMV_NOALLOC_SCRATCH_BYTES = 4 << 20
 
 _c_i64, _c_i32, _c_u32, _c_p, _c_sz = ctypes.c_int64, ctypes.c_int32, ctypes.c_uint32, ctypes.c_void_p, ctypes.c_size_t
@@ -46,6 +49,8 @@ SIGNATURES = {
     "iq4_moe_gather": (ctypes.c_int, [_c_p, _c_i64, _c_i32, _c_p, _c_p, _c_p, _c_p, _c_p]),
     "iq4_moe_workspace_size": (ctypes.c_int, [_c_i64, _c_i32, _c_i32, _c_i64, _c_i64, _c_i32,
                                               ctypes.POINTER(_c_sz)]),
+    "iq4_moe_intermediate_layout": (ctypes.c_int, [_c_i64, _c_i32, _c_i32, _c_i64, _c_i64, _c_i32, _c_i32,
+                                                   ctypes.POINTER(_c_i64)]),
     "iq4_moe_expert_gemm": (ctypes.c_int, [_c_p, _c_i32, _c_i64, _c_i64, _c_p, _c_p, _c_i32, _c_i32,
                                            _c_i64, _c_i64, _c_p, _c_p, _c_p, _c_p, _c_i64, _c_p,
                                            _c_sz, _c_u32, _c_p]),
@@ -166,6 +171,13 @@ def iq4_moe_workspace_size(n_tok, top_k, n_expert, hidden, inter, act_dtype) -> 
     out = _c_sz(0)
     _call("iq4_moe_workspace_size", n_tok, top_k, n_expert, hidden, inter, act_dtype, ctypes.byref(out))
     return out.value
+
+
+def iq4_moe_intermediate_layout(n_tok, top_k, n_expert, hidden, inter, act_dtype, shared=0) -> dict:
+    """Byte offsets of the kept intermediates (and the workspace size a keeping call needs)."""
+    out = (_c_i64 * 9)()
+    _call("iq4_moe_intermediate_layout", n_tok, top_k, n_expert, hidden, inter, act_dtype, shared, out)
+    return {name: int(out[i]) for name, i in MOE_LAYOUT.items()}
 
 
 def iq4_moe_expert_gemm(x, act_dtype, n_tok, ldx, ids, w, top_k, n_expert, hidden, inter,

@@ -245,7 +245,9 @@ static int moe_call(const char* fn, const void* x, int32_t act_dtype, int64_t n_
   if (shared && (top_k < 1 || n_expert < 1)) return set_error(IQ4_E_ARG, "%s: need top_k, n_expert >= 1", fn);
   const int sk = shared ? 1 : 0;  // the shared expert counts as one more expert and slot
   if (int e = check_moe_sizes(fn, n_tok, top_k + sk, n_expert + sk, hidden, inter, act_dtype)) return e;
-  if (flags & ~IQ4_MOE_ATOMIC_COMBINE) return set_error(IQ4_E_ARG, "%s: unknown flags", fn);
+  if (flags & ~(IQ4_MOE_ATOMIC_COMBINE | IQ4_MOE_KEEP_INTERMEDIATE))
+    return set_error(IQ4_E_ARG, "%s: unknown flags", fn);
+  const bool keep = (flags & IQ4_MOE_KEEP_INTERMEDIATE) != 0;
   if (ldx < hidden || ldo < hidden) return set_error(IQ4_E_ARG, "%s: ldx and ldo must be >= hidden", fn);
   if (n_tok == 0) return IQ4_OK;
   if (!x || !ids || !w || !w_gate || !w_up || !w_down || !out || (shared && !(s_gate && s_up && s_down)))
@@ -258,7 +260,7 @@ static int moe_call(const char* fn, const void* x, int32_t act_dtype, int64_t n_
                      "weights 256-byte aligned", fn, f16 ? 8 : 4);
   if (n_tok * ldx >= ((int64_t)1 << 31) || n_tok * (top_k + sk) * inter >= ((int64_t)1 << 31))
     return set_error(IQ4_E_UNSUPPORTED, "%s: x and the intermediate rows must span fewer than 2^31 elements", fn);
-  const MoeLayout L = moe_layout(n_tok, top_k, n_expert, hidden, inter, f16, shared);
+  const MoeLayout L = moe_layout(n_tok, top_k, n_expert, hidden, inter, f16, shared, keep);
   if (!workspace || ws_bytes < (size_t)L.total)
     return set_error(IQ4_E_WORKSPACE, "%s: needs a workspace of %lld bytes", fn, (long long)L.total);
   if (!aligned(workspace, 256)) return set_error(IQ4_E_ALIGN, "%s: workspace must be 256-byte aligned", fn);
@@ -283,7 +285,29 @@ static int moe_call(const char* fn, const void* x, int32_t act_dtype, int64_t n_
   m.ldo = ldo;
   m.workspace = workspace;
   m.atomic = (flags & IQ4_MOE_ATOMIC_COMBINE) != 0;
+  m.keep = keep;
   return launch_moe(m, as_stream(stream));
+}
+
+int iq4_moe_intermediate_layout(int64_t n_tok, int32_t top_k, int32_t n_expert, int64_t hidden,
+                                int64_t inter, int32_t act_dtype, int32_t shared, int64_t* layout) {
+  clear_error();
+  if (!layout) return set_error(IQ4_E_ARG, "iq4_moe_intermediate_layout: null layout");
+  const int sk = shared ? 1 : 0;
+  if (int e = check_moe_sizes("iq4_moe_intermediate_layout", n_tok, top_k + sk, n_expert + sk, hidden, inter,
+                              act_dtype))
+    return e;
+  const MoeLayout L = moe_layout(n_tok, top_k, n_expert, hidden, inter, act_dtype == IQ4_F16, shared != 0, true);
+  layout[IQ4_MOE_LAYOUT_TOTAL] = L.total;
+  layout[IQ4_MOE_LAYOUT_COUNTS] = L.counts;
+  layout[IQ4_MOE_LAYOUT_OFFSETS] = L.offsets;
+  layout[IQ4_MOE_LAYOUT_PAIRS] = L.pairs;
+  layout[IQ4_MOE_LAYOUT_SLOT_ROW] = L.slot_row;
+  layout[IQ4_MOE_LAYOUT_H] = L.h;
+  layout[IQ4_MOE_LAYOUT_ROWS] = L.rows;
+  layout[IQ4_MOE_LAYOUT_G] = L.g;
+  layout[IQ4_MOE_LAYOUT_U] = L.u;
+  return IQ4_OK;
 }
 
 int iq4_moe_expert_gemm(const void* x, int32_t act_dtype, int64_t n_tok, int64_t ldx,

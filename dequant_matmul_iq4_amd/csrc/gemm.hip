@@ -483,6 +483,11 @@ qgemm_kernel(GemmArgs a) {
           const float gv = acc[mt][r][i], uv = acc[mt][r + 2][i];
           const float h = gv / (1.0f + __expf(-gv)) * uv;
           hrow[16 * r] = __half_as_ushort(__float2half_rn(h));
+          if (a.G) {  // the intermediates kept (tests): g and u in the same place as h
+            const int64_t o = (seg0 + m0 + rr) * a.ldh + n0 + 32 * cg + c + 16 * r;
+            a.G[o] = gv;
+            a.U[o] = uv;
+          }
         }
       }
   } else {  // DOWN

@@ -21,6 +21,8 @@ struct GemmArgs {
   int64_t ldc;
   uint16_t* H;              // GATEUP: h = silu(g) * u as binary16 [pairs][ldh] (sorted order)
   int64_t ldh;
+  float* G;                 // GATEUP, or null: g and u themselves, fp32 [pairs][ldh] (sorted order)
+  float* U;
   const int32_t* tiles;     // grouped: (expert, m tile) pairs
   const int32_t* num_tiles; // grouped: [0] valid entries in `tiles`, [1] of them full tiles (listed first)
   int64_t n_tiles_n;        // grouped: workgroups per m tile along N (set by the launcher)

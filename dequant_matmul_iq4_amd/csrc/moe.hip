@@ -113,7 +113,7 @@ __global__ void __launch_bounds__(256) append_shared_kernel(const int32_t* __res
 }
 
 MoeLayout moe_layout(int64_t n_tok, int top_k, int n_expert, int64_t hidden, int64_t inter,
-                     bool f16, bool shared) {
+                     bool f16, bool shared, bool keep) {
   MoeLayout L{};
   if (shared) {  // the routed call's sizes with the shared expert as one more expert and slot
     ++top_k;
@@ -132,13 +132,17 @@ MoeLayout moe_layout(int64_t n_tok, int top_k, int n_expert, int64_t hidden, int
   L.rows = off;      off += align256(P * hidden * 4);
   L.ids2 = off;      off += shared ? align256(4 * P) : 0;
   L.w2 = off;        off += shared ? align256(4 * P) : 0;
+  L.g = keep ? off : -1; off += keep ? align256(P * inter * 4) : 0;
+  L.u = keep ? off : -1; off += keep ? align256(P * inter * 4) : 0;
   L.total = off;
   return L;
 }
 
 int launch_moe(const MoeCall& m, hipStream_t s) {
   const bool shared = m.s_gate != nullptr;
-  const MoeLayout L = moe_layout(m.n_tok, m.top_k, m.n_expert, m.hidden, m.inter, m.f16, shared);
+  const MoeLayout L = moe_layout(m.n_tok, m.top_k, m.n_expert, m.hidden, m.inter, m.f16, shared, m.keep);
+  float* keep_g = m.keep ? reinterpret_cast<float*>(static_cast<uint8_t*>(m.workspace) + L.g) : nullptr;
+  float* keep_u = m.keep ? reinterpret_cast<float*>(static_cast<uint8_t*>(m.workspace) + L.u) : nullptr;
   uint8_t* ws = static_cast<uint8_t*>(m.workspace);
   int32_t* counts = reinterpret_cast<int32_t*>(ws + L.counts);
   int32_t* offsets = reinterpret_cast<int32_t*>(ws + L.offsets);
@@ -165,8 +169,9 @@ int launch_moe(const MoeCall& m, hipStream_t s) {
   }
 
   // prefill: the gather also writes the grouped GEMM's tile list.  A decode step with
-  // few pairs skips it: its matvecs find each expert's pairs from the ids.
-  const bool direct = !m.f16 && P <= kDirectMaxPairs;
+  // few pairs skips it: its matvecs find each expert's pairs from the ids (unless the
+  // intermediates are kept: then the gather that indexes them always runs).
+  const bool direct = !m.f16 && P <= kDirectMaxPairs && !m.keep;
   if (!direct) {
     if (int e = launch_gather(ids, P, n_expert, counts, offsets, pairs, slot_row, m.f16 ? tiles : nullptr,
                               m.f16 ? num_tiles : nullptr, s))
@@ -203,6 +208,8 @@ int launch_moe(const MoeCall& m, hipStream_t s) {
     g.offsets = offsets;
     g.pairs = pairs;
     g.top_k = top_k;
+    g.G = keep_g;
+    g.U = keep_u;
     if (int e = launch_qgemm_grouped(kGemmGateUp, g, L.max_tiles, s)) return e;
     GemmArgs d{};
     d.A = h;
@@ -243,6 +250,8 @@ int launch_moe(const MoeCall& m, hipStream_t s) {
     g.ids = direct ? ids : nullptr;
     g.n_pairs = (int)P;
     g.top_k = top_k;
+    g.G = keep_g;
+    g.U = keep_u;
     g.stream = s;
     if (int e = launch_qmv_grouped(kQmvGateUp, g, m.inter, m.hidden, n_expert, P)) return e;
     QmvArgs d{};

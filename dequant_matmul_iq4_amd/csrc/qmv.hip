@@ -687,6 +687,10 @@ __global__ void __launch_bounds__(512) qmv_grouped_kernel(QmvArgs a) {
         if (MODE == kQmvGateUp) {
           const float gv = v[0], uv = v[NMAT - 1];
           a.y[(seg0 + t0 + t) * a.ldy + col] = gv / (1.0f + expf(-gv)) * uv;  // SwiGLU
+          if (a.G) {  // the intermediates kept (tests)
+            a.G[(seg0 + t0 + t) * a.ldy + col] = gv;
+            a.U[(seg0 + t0 + t) * a.ldy + col] = uv;
+          }
         } else {
           const int pc = (t == 0) ? pcol[0] : (t == 1) ? pcol[1] : (t == 2) ? pcol[2] : pcol[3];
           const float gw = (t == 0) ? gwcol[0] : (t == 1) ? gwcol[1] : (t == 2) ? gwcol[2] : gwcol[3];

@@ -27,6 +27,8 @@ struct QmvArgs {
                             // (offsets and pairs unused: no gather launch)
   int n_pairs;              // grouped: routed pairs (with ids)
   const float* gate_w;      // DOWN: gate weight per pair id
+  float* G;                 // GATEUP, or null: g and u themselves, [pairs][ldy] (sorted order)
+  float* U;
   int top_k;
   int n_expert;             // grouped: experts in the bank
   float* partials;          // DENSE split K: per-slice partial sums (workspace)

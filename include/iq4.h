@@ -51,8 +51,11 @@ extern "C" {
 #define IQ4_F16 1
 
 /* iq4_moe_expert_gemm flags */
-#define IQ4_MOE_ATOMIC_COMBINE 1u /* prefill: add slot rows into `out` with atomics
-                                     (faster, not bit-reproducible run to run)      */
+#define IQ4_MOE_ATOMIC_COMBINE 1u    /* prefill: add slot rows into `out` with atomics
+                                        (not bit-reproducible run to run)             */
+#define IQ4_MOE_KEEP_INTERMEDIATE 2u /* also keep the gate and up products g, u (fp32)
+                                        in the workspace, and always run the gather;
+                                        offsets: iq4_moe_intermediate_layout          */
 
 /* Text of the last error on the calling thread ("" if none).  Valid until the
  * thread's next iq4_* call. */
@@ -235,6 +238,37 @@ int iq4_moe_workspace_size(int64_t n_tok, int32_t top_k, int32_t n_expert, int64
                            int64_t inter, int32_t act_dtype, size_t* bytes);
 
 /*
+ * Where a call with IQ4_MOE_KEEP_INTERMEDIATE leaves its intermediate results in the
+ * workspace (byte offsets, written to layout[0 .. IQ4_MOE_LAYOUT_N - 1]), and how large
+ * that workspace must be (layout[IQ4_MOE_LAYOUT_TOTAL]; it exceeds
+ * iq4_moe_workspace_size by the g and u regions).  Page 1 (verify.hpp, PoolMultiFn)
+ * defines the layer's per-slot rows (n_tok * k, n_embd) and the expert plan (per-expert
+ * count, start and token list); they are kept here as:
+ *   COUNTS, OFFSETS, PAIRS, SLOT_ROW  the gather (int32), as iq4_moe_gather writes it;
+ *   G, U      g = Wg_e x_t and u = Wu_e x_t, float32 [P][inter], P = n_tok * top_k,
+ *             in pair-sorted order: row i belongs to pair PAIRS[i] (p = t * top_k + j);
+ *   H         h = silu(g) * u in the same order: binary16 (IQ4_F16) or float32 (IQ4_F32);
+ *   ROWS      the per-slot rows w[t][j] * (Wd_e h), float32 [P][hidden], row p = pair p
+ *             (token-major: the (n_tok * top_k, hidden) layout); not written by a call
+ *             with IQ4_MOE_ATOMIC_COMBINE.
+ * shared != 0: the layout of iq4_moe_expert_gemm_shared, whose pairs include the shared
+ * expert as slot top_k of every token (P = n_tok * (top_k + 1)).
+ * Errors: IQ4_E_ARG (sizes as for the calls).
+ */
+#define IQ4_MOE_LAYOUT_TOTAL 0
+#define IQ4_MOE_LAYOUT_COUNTS 1
+#define IQ4_MOE_LAYOUT_OFFSETS 2
+#define IQ4_MOE_LAYOUT_PAIRS 3
+#define IQ4_MOE_LAYOUT_SLOT_ROW 4
+#define IQ4_MOE_LAYOUT_H 5
+#define IQ4_MOE_LAYOUT_ROWS 6
+#define IQ4_MOE_LAYOUT_G 7
+#define IQ4_MOE_LAYOUT_U 8
+#define IQ4_MOE_LAYOUT_N 9
+int iq4_moe_intermediate_layout(int64_t n_tok, int32_t top_k, int32_t n_expert, int64_t hidden,
+                                int64_t inter, int32_t act_dtype, int32_t shared, int64_t* layout);
+
+/*
  * Mixture-of-experts FFN over routed tokens (SwiGLU experts, gate-weighted sum):
  *   for token t, slot j, e = ids[t][j]:  g = Wg_e x_t, u = Wu_e x_t,
  *   h = silu(g) * u,  y_tj = Wd_e h,  out[t] = sum_j w[t][j] * y_tj (added in j order).
@@ -258,7 +292,9 @@ int iq4_moe_workspace_size(int64_t n_tok, int32_t top_k, int32_t n_expert, int64
  *               gather (counts, offsets, pairs, slot_row) at its start; a decode call
  *               with at most 64 pairs runs no gather (its matvecs find each expert's
  *               pairs from ids) and leaves that region unspecified.
- *   flags       0 (deterministic) or IQ4_MOE_ATOMIC_COMBINE (prefill only).
+ *   flags       0 (deterministic), IQ4_MOE_ATOMIC_COMBINE (prefill only), and/or
+ *               IQ4_MOE_KEEP_INTERMEDIATE (the workspace must then hold
+ *               iq4_moe_intermediate_layout's total; the result is unchanged).
  * Errors: IQ4_E_ARG, IQ4_E_ALIGN, IQ4_E_UNSUPPORTED (hidden or inter not multiples of
  * 256 / 128), IQ4_E_WORKSPACE.
  */

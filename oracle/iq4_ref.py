@@ -49,7 +49,7 @@ __all__ = [
     "CODEBOOK", "QK", "BLOCK_BYTES",
     "decode_blocks", "decode_blocks_f16", "encode_blocks",
     "qmv", "route_topk", "gather", "silu", "moe", "gemm",
-    "quantize_q8_1", "qmv_q8", "moe_shared",
+    "quantize_q8_1", "qmv_q8", "moe_shared", "moe_gate_up",
 ]
 
 #: The fixed 16-level int8 codebook of the block format (workload definition).
@@ -221,6 +221,25 @@ def moe(x, ids, w, gate_blocks, up_blocks, down_blocks, hidden: int, inter: int,
     if return_pair_rows:
         return out.astype(np.float32), rows
     return out.astype(np.float32)
+
+
+def moe_gate_up(x, ids, gate_blocks, up_blocks, hidden: int, inter: int):
+    """The first products of every routed pair: ``g[p] = Wg_e x_t`` and ``u[p] = Wu_e x_t``
+    for pair ``p = t * k + j`` with ``e = ids[t][j]``, summed in float64, returned as
+    float64 ``[n_tok * k, inter]`` arrays in pair-id order -- the per-slot layout of page
+    1's ``PoolMultiFn`` (x (n_tok, n_embd), ids (n_tok, k) -> (n_tok * k, ...) rows)."""
+    X = np.asarray(x).astype(np.float64)
+    ids = np.asarray(ids)
+    n_tok, k = ids.shape
+    flat = ids.reshape(-1)
+    g = np.zeros((n_tok * k, inter), dtype=np.float64)
+    u = np.zeros((n_tok * k, inter), dtype=np.float64)
+    for e in np.unique(flat):
+        ps = np.nonzero(flat == e)[0]
+        xi = X[ps // k]
+        g[ps] = xi @ _matrix(gate_blocks[e], inter, hidden).T
+        u[ps] = xi @ _matrix(up_blocks[e], inter, hidden).T
+    return g, u
 
 
 def _expert_ffn(X, gate_b, up_b, down_b, hidden: int, inter: int) -> np.ndarray:

@@ -176,3 +176,24 @@ def test_noalloc_matvec_validation_never_launches():
     assert iq4.iq4_qmv_workspace_size(n, k) > iq4.IQ4_QMV_NOALLOC_SCRATCH_BYTES
     assert _rc("iq4_qmv_multi_noalloc", FAKE, n, k, FAKE, k, 1, FAKE, n, None) == iq4.IQ4_E_WORKSPACE
     assert "scratch" in iq4.iq4_last_error()
+
+
+def test_moe_keep_intermediate_layout():
+    """The kept-intermediates layout: regions in order, each inside the total, g and u
+    after everything a plain call uses; a keeping call with only the plain workspace is
+    rejected before any launch."""
+    for act in (iq4.IQ4_F16, iq4.IQ4_F32):
+        L = iq4.iq4_moe_intermediate_layout(3256, 8, 128, 2048, 768, act)
+        plain = iq4.iq4_moe_workspace_size(3256, 8, 128, 2048, 768, act)
+        P = 3256 * 8
+        assert L["g"] >= plain and L["u"] >= L["g"] + P * 768 * 4 and L["total"] >= L["u"] + P * 768 * 4
+        assert L["counts"] < L["offsets"] < L["pairs"] < L["slot_row"] < L["h"] < L["rows"] < L["g"]
+        assert all(v % 256 == 0 for v in L.values())
+    Ls = iq4.iq4_moe_intermediate_layout(16, 8, 128, 2048, 768, iq4.IQ4_F16, 1)
+    assert Ls["total"] > iq4.iq4_moe_intermediate_layout(16, 8, 128, 2048, 768, iq4.IQ4_F16)["total"]
+    plain = iq4.iq4_moe_workspace_size(16, 8, 128, 2048, 768, iq4.IQ4_F16)
+    rc = _rc("iq4_moe_expert_gemm", FAKE, iq4.IQ4_F16, 16, 2048, FAKE, FAKE, 8, 128, 2048, 768,
+             FAKE, FAKE, FAKE, FAKE, 2048, FAKE, plain, iq4.IQ4_MOE_KEEP_INTERMEDIATE, None)
+    assert rc == iq4.IQ4_E_WORKSPACE
+    with pytest.raises(iq4.IQ4Error):
+        iq4.iq4_moe_intermediate_layout(16, 17, 128, 2048, 768, iq4.IQ4_F16)

@@ -8,6 +8,7 @@ import dequant_matmul_iq4_amd as iq4
 import oracle
 import synth
 from gpu_util import bits_equal, dev, host, normwise, note, pack
+from test_oracle_pins import integer_exact_blocks
 
 pytestmark = pytest.mark.gpu
 
@@ -341,3 +342,93 @@ def test_prefill_three_quad_shapes():
     x = rng.standard_normal((260, H)).astype(np.float16)
     got, _ = run_moe(x, ids, w, banks, H, I, E)
     assert normwise(got, oracle.moe(x, ids, w, gate, up, down, H, I)) <= 5e-3
+
+
+# ---- the kept intermediates (IQ4_MOE_KEEP_INTERMEDIATE) ------------------------------------
+
+def run_moe_keep(x, ids, w, banks, H, I, E, dtype="f16"):
+    """A call with the intermediates kept: (out, {g, u, h, rows, pairs, counts, offsets}),
+    read back from the offsets iq4_moe_intermediate_layout gives; the workspace starts as
+    0xFF bytes."""
+    n_tok, top_k = ids.shape
+    f16 = dtype == "f16"
+    act = iq4.IQ4_F16 if f16 else iq4.IQ4_F32
+    L = iq4.iq4_moe_intermediate_layout(n_tok, top_k, E, H, I, act)
+    assert L["total"] > iq4.iq4_moe_workspace_size(n_tok, top_k, E, H, I, act)
+    ws = torch.full((L["total"],), 0xFF, dtype=torch.uint8, device="cuda")
+    out = torch.full((n_tok, H), float("nan"), dtype=torch.float32, device="cuda")
+    g_, u_, d_ = banks
+    iq4.iq4_moe_expert_gemm(dev(x.astype(np.float16 if f16 else np.float32)), act, n_tok, H,
+                            dev(ids.astype(np.int32)), dev(w.astype(np.float32)), top_k, E, H, I, g_, u_, d_, out,
+                            H, ws, L["total"], iq4.IQ4_MOE_KEEP_INTERMEDIATE)
+    P = n_tok * top_k
+    # a view of each region on the device, copied back one at a time
+    def region(name, count, dtype, shape):
+        nbytes = count * np.dtype(dtype).itemsize
+        return host(ws[L[name]:L[name] + nbytes]).view(dtype).reshape(shape)
+    r = {"pairs": region("pairs", P, np.int32, (P,)), "counts": region("counts", E, np.int32, (E,)),
+         "offsets": region("offsets", E + 1, np.int32, (E + 1,)),
+         "g": region("g", P * I, np.float32, (P, I)), "u": region("u", P * I, np.float32, (P, I)),
+         "h": region("h", P * I, np.float16 if f16 else np.float32, (P, I)),
+         "rows": region("rows", P * H, np.float32, (P, H))}
+    return host(out), r
+
+
+def integer_exact_bank(rng, E, H, I, s):
+    return ([integer_exact_blocks(rng, I * H // 32, s) for _ in range(E)],
+            [integer_exact_blocks(rng, I * H // 32, s) for _ in range(E)],
+            [integer_exact_blocks(rng, H * I // 32, s) for _ in range(E)])
+
+
+def check_kept(x, ids, w, blocks, H, I, E, out, r, dtype):
+    gate, up, down = blocks
+    P = ids.size
+    rc, ro, rp, _ = oracle.gather(ids, E)
+    assert bits_equal(r["pairs"], rp) and bits_equal(r["counts"], rc) and bits_equal(r["offsets"], ro)
+    # power-of-two scales and small-integer activations: g and u are exact, so bitwise
+    g, u = oracle.moe_gate_up(x, ids, gate, up, H, I)
+    assert bits_equal(r["g"], g[rp].astype(np.float32)), "g"
+    assert bits_equal(r["u"], u[rp].astype(np.float32)), "u"
+    h = oracle.silu(g) * u
+    assert normwise(r["h"].astype(np.float64), h[rp]) <= (5e-3 if dtype == "f16" else 1e-3)
+    ref_out, y = oracle.moe(x, ids, w, gate, up, down, H, I, return_pair_rows=True)
+    rows_ref = (np.asarray(w, dtype=np.float64)[:, :, None] * y).reshape(P, H)
+    assert normwise(r["rows"], rows_ref) <= (5e-3 if dtype == "f16" else 1e-3)
+    assert normwise(out, ref_out) <= (5e-3 if dtype == "f16" else 1e-3)
+
+
+def test_keep_intermediate_prefill_full_size_integer_exact():
+    """The prefill layer at its real shape (3,256 tokens, Zipf(1.1) top-8 of 128 experts,
+    hidden 2048, inter 768) on power-of-two-scale weights and small-integer f16
+    activations: the kept gate and up products equal the oracle's bitwise (every partial
+    sum is exact whatever the order), h, the per-slot rows and the output match within
+    the f16 tolerance, and keeping the intermediates leaves the output bitwise unchanged."""
+    n_tok, E, H, I, k = 3256, E_FULL, H_FULL, I_FULL, K_FULL
+    note("moe keep intermediates: prefill full size, integer-exact")
+    rng = np.random.default_rng(104)
+    blocks = integer_exact_bank(rng, E, H, I, 10)
+    banks = (pack_bank(blocks[0], I, H), pack_bank(blocks[1], I, H), pack_bank(blocks[2], H, I))
+    logits = synth.logits_zipf_gumbel(synth.SEED_PREFILL, synth.TAG_GUMBEL, n_tok, E)
+    ids, w = oracle.route_topk(logits, k)
+    x = rng.integers(-8, 9, (n_tok, H)).astype(np.float16)
+    out, r = run_moe_keep(x, ids, w, banks, H, I, E)
+    plain, _ = run_moe(x, ids, w, banks, H, I, E)
+    assert bits_equal(out, plain)
+    check_kept(x, ids, w, blocks, H, I, E, out, r, "f16")
+
+
+def test_keep_intermediate_decode_integer_exact():
+    """The fp32 decode path with the intermediates kept (the gather then always runs):
+    g and u bitwise, the rest within the fp32 tolerance, the output bitwise the plain
+    (gather-free) call's."""
+    note("moe keep intermediates: decode, integer-exact")
+    rng = np.random.default_rng(31)
+    E, H, I, n_tok, k = 8, 256, 128, 4, 3
+    blocks = integer_exact_bank(rng, E, H, I, 8)
+    banks = (pack_bank(blocks[0], I, H), pack_bank(blocks[1], I, H), pack_bank(blocks[2], H, I))
+    ids, w = routing(rng, n_tok, E, k)
+    x = rng.integers(-8, 9, (n_tok, H)).astype(np.float32)
+    out, r = run_moe_keep(x, ids, w, banks, H, I, E, dtype="f32")
+    plain, _ = run_moe(x, ids, w, banks, H, I, E, dtype="f32")
+    assert bits_equal(out, plain)
+    check_kept(x, ids, w, blocks, H, I, E, out, r, "f32")

@@ -398,6 +398,44 @@ def pin_moe_weight_summed_dense():
         assert np.allclose(out[t], ref, rtol=1e-6, atol=1e-9 * np.abs(ref).max())
 
 
+def pin_moe_gate_up_bruteforce():
+    """The kept first products: with power-of-two scales and small-integer activations
+    every product and sum is exact, so each g and u must equal the exact rational
+    product of the routed expert's closed-form decoded matrix with the token's row."""
+    rng = np.random.default_rng(23)
+    n, k, E, H, I = 4, 2, 3, 64, 32
+    gate = [integer_exact_blocks(rng, I * H // 32, 5) for _ in range(E)]
+    up = [integer_exact_blocks(rng, I * H // 32, 4) for _ in range(E)]
+    x = rng.integers(-8, 9, (n, H)).astype(np.float16)
+    ids = np.stack([rng.permutation(E)[:k] for _ in range(n)]).astype(np.int32)
+    g, u = R.moe_gate_up(x, ids, gate, up, H, I)
+    assert g.shape == u.shape == (n * k, I)
+    Wg = [bf_matrix(gate[e], I, H) for e in range(E)]
+    Wu = [bf_matrix(up[e], I, H) for e in range(E)]
+    for t in range(n):
+        for j in range(k):
+            e, p = ids[t, j], t * k + j
+            for i in range(I):
+                assert Fraction(float(g[p, i])) == sum(Wg[e][i][c] * int(x[t, c]) for c in range(H))
+                assert Fraction(float(u[p, i])) == sum(Wu[e][i][c] * int(x[t, c]) for c in range(H))
+
+
+def pin_moe_gate_up_composes_to_moe():
+    """silu(g) * u through each pair's down matrix, weighted and summed over the slots,
+    is the (separately pinned) MoE output."""
+    x, ids, w, gate, up, down, H, I = tiny_moe(seed=24)
+    g, u = R.moe_gate_up(x, ids, gate, up, H, I)
+    h = R.silu(g) * u
+    n, k = ids.shape
+    out = np.zeros((n, H))
+    for t in range(n):
+        for j in range(k):
+            e, p = ids[t, j], t * k + j
+            out[t] += float(w[t, j]) * (R._matrix(down[e], H, I) @ h[p])
+    ref = R.moe(x, ids, w, gate, up, down, H, I)
+    assert np.allclose(out, ref, rtol=1e-6, atol=1e-7 * np.abs(ref).max())
+
+
 def pin_moe_shared_bruteforce():
     """moe_shared = the routed sum plus the shared expert's SwiGLU FFN with weight 1,
     recomputed in exact rationals (except for the exponential) from the closed-form
@@ -539,6 +577,7 @@ PINS = [
     pin_gemm_integer_exact, pin_route_golden, pin_route_bruteforce, pin_gather_bruteforce,
     pin_silu, pin_moe_single_expert_is_dense_ffn, pin_moe_weight_summed_dense, pin_moe_subset_rows,
     pin_moe_shared_bruteforce, pin_moe_shared_is_an_always_on_expert,
+    pin_moe_gate_up_bruteforce, pin_moe_gate_up_composes_to_moe,
     pin_q8_quantize_bruteforce, pin_q8_quantize_ties, pin_qmv_q8_fraction, pin_qmv_q8_on_grid_equals_fp32,
 ]
 
@@ -665,6 +704,20 @@ def _moe_shared_gate_up_swapped(x, ids, w, gate, up, down, sg, su, sd, H, I, tok
     return _orig_moe_shared(x, ids, w, gate, up, down, su, sg, sd, H, I, tokens=tokens)
 
 
+_orig_moe_gate_up = R.moe_gate_up
+
+
+def _moe_gate_up_swapped(x, ids, gate, up, H, I):
+    g, u = _orig_moe_gate_up(x, ids, gate, up, H, I)
+    return u, g
+
+
+def _moe_gate_up_sorted_rows(x, ids, gate, up, H, I):
+    g, u = _orig_moe_gate_up(x, ids, gate, up, H, I)
+    order = np.argsort(np.asarray(ids).reshape(-1), kind="stable")  # pair-sorted, not pair-id order
+    return g[order], u[order]
+
+
 PLANTED = {
     "codebook sign": ("CODEBOOK", tuple(-c for c in R.CODEBOOK)),
     "codebook off by one": ("CODEBOOK", tuple(R.CODEBOOK[1:]) + (127,)),
@@ -681,6 +734,8 @@ PLANTED = {
     "q8 product drops the activation scale": ("qmv_q8", _qmv_q8_no_act_scale),
     "shared expert dropped": ("moe_shared", _moe_shared_dropped),
     "shared expert gate and up swapped": ("moe_shared", _moe_shared_gate_up_swapped),
+    "kept products gate and up swapped": ("moe_gate_up", _moe_gate_up_swapped),
+    "kept products in sorted order": ("moe_gate_up", _moe_gate_up_sorted_rows),
 }
 
 
