@@ -18,8 +18,11 @@ numerics) at T = 1..4 over the same weight copies, and the activation quantisati
 Prints ONE JSON line.  ``value`` = effective weight GB/s of the verify-window matvec
 (total weight bytes of the T = 1..4 calls / their total time).  Launch times come from
 HIP events around graph replays on the launch stream (many launches per replay, so
-per-launch CPU overhead does not enter).  ``cpu_baseline`` times the CPU oracle on a
-bounded sample of the matvec workload.
+per-launch CPU overhead does not enter), medians of 5 interleaved rounds after >= 200 ms
+of clock warm-up.  Beside the published peaks, each roofline states its rate against a
+ceiling measured in the same run (a plain streaming read of the same bytes, a pure
+matrix-core loop).  ``cpu_baseline`` times the CPU oracle on the matvec workload;
+``cpu_baselines`` on every config (threads = the cores this process may use).
 """
 from __future__ import annotations
 
@@ -28,6 +31,10 @@ import json
 import os
 import sys
 import time
+
+import numpy as np
+import ctypes
+import statistics
 
 ROOT = os.path.dirname(os.path.abspath(__file__))
 if ROOT not in sys.path:
@@ -44,14 +51,14 @@ N_BANKS = 8                 # expert banks the decode step rotates over
 # at the time: a kernel changed since then reports traffic null.  Commands and raw
 # figures: profiles/<name>.txt.
 MEASURED_TRAFFIC = {
-    "dequant_staged_4096x4096_f16": (43014149, "25db0a7fe6d27844", ("format.hip", "common.hpp")),
-    "qmv_dense_4096x4096_T1-4": (9928256, "a3e206cf1de95580", ("qmv.hip", "qmv.hpp", "common.hpp")),
-    "qmv_q8_4096x4096_T1-4": (9670700, "a3e206cf1de95580", ("qmv.hip", "qmv.hpp", "common.hpp")),
-    "qmv_grouped_gateup_moe_decode_4tok": (55501318, "a3e206cf1de95580", ("qmv.hip", "qmv.hpp", "common.hpp")),
-    "qmv_down_moe_decode_4tok": (28740859, "a3e206cf1de95580", ("qmv.hip", "qmv.hpp", "common.hpp")),
-    "qgemm_gateup_moe_prefill_3256tok": (589100195, "0f4774c413fa418b", ("gemm.hip", "gemm.hpp", "common.hpp")),
-    "qgemm_down_moe_prefill_3256tok": (507634000, "0f4774c413fa418b", ("gemm.hip", "gemm.hpp", "common.hpp")),
-    "qgemm_dense_13056x4096x14336_chunk512": (94965153, "0f4774c413fa418b", ("gemm.hip", "gemm.hpp", "common.hpp")),
+    "dequant_staged_4096x4096_f16": (43014176, "b7a9db4683211408", ("format.hip", "common.hpp")),
+    "qmv_dense_4096x4096_T1-4": (9929739, "f14631106fc06a90", ("qmv.hip", "qmv.hpp", "common.hpp")),
+    "qmv_q8_4096x4096_T1-4": (9672483, "f14631106fc06a90", ("qmv.hip", "qmv.hpp", "common.hpp")),
+    "qmv_grouped_gateup_moe_decode_4tok": (55509919, "f14631106fc06a90", ("qmv.hip", "qmv.hpp", "common.hpp")),
+    "qmv_down_moe_decode_4tok": (28738823, "f14631106fc06a90", ("qmv.hip", "qmv.hpp", "common.hpp")),
+    "qgemm_gateup_moe_prefill_3256tok": (588766084, "a2bf14d3011a2459", ("gemm.hip", "gemm.hpp", "common.hpp")),
+    "qgemm_down_moe_prefill_3256tok": (507669300, "a2bf14d3011a2459", ("gemm.hip", "gemm.hpp", "common.hpp")),
+    "qgemm_dense_13056x4096x14336_chunk512": (94965099, "a2bf14d3011a2459", ("gemm.hip", "gemm.hpp", "common.hpp")),
 }
 
 
@@ -107,39 +114,124 @@ def route(torch, iq4, logits):
     return ids, w
 
 
-def cpu_baseline(min_seconds: float = 10.0):
-    """The CPU oracle on the verify-window matvec, T = 1..4 per pass, repeated until
-    `min_seconds` of work; GB/s of weight bytes like the GPU value."""
+def cpu_model() -> str:
+    try:
+        with open("/proc/cpuinfo") as f:
+            for line in f:
+                if line.startswith("model name"):
+                    return line.split(":", 1)[1].strip()
+    except OSError:
+        pass
+    import platform
+    return platform.processor() or "unknown"
+
+
+def cpu_baselines(min_seconds: float = 8.0):
+    """The CPU oracle (as it stands: numpy float64) timed on this host's cores, every
+    config.  Threads = the cores this
+    process may run on (len(os.sched_getaffinity(0))), the BLAS pool limited to that.
+    Returns (headline entry for the verify-window matvec, per-config entries)."""
+    import statistics
     import oracle
     import synth
-    try:
-        from threadpoolctl import threadpool_info
-        cores = max([i.get("num_threads", 1) for i in threadpool_info()] + [1])
-    except Exception:
-        cores = 1
-    n = k = 4096
-    w = synth.weights_f32(synth.SEED_VERIFY, synth.TAG_WEIGHT, n, k)
-    blocks = oracle.encode_blocks(w.reshape(-1, 32))
-    x = synth.acts_f32(synth.SEED_VERIFY, synth.TAG_X, 4, k)
-    wbytes = blocks.size
-    done_bytes, passes = 0, 0
-    t0 = time.perf_counter()
-    while True:
-        for T in (1, 2, 3, 4):
-            oracle.qmv(blocks, n, k, x[:T])
-            done_bytes += wbytes
-        passes += 1
-        el = time.perf_counter() - t0
-        if el >= min_seconds or passes >= 50:
-            break
-    return {"value": round(done_bytes / el / 1e9, 4), "unit": "GB/s", "cores": int(cores), "kind": "oracle",
-            "sample": f"{passes} passes of the verify-window matvec (W 4096x4096, T=1..4): oracle decode + "
-                      f"float64 product, {el:.1f} s"}
+    from threadpoolctl import threadpool_limits
+
+    cores = len(os.sched_getaffinity(0))
+    model = cpu_model()
+    enc = lambda w: oracle.encode_blocks(w.reshape(-1, 32))  # noqa: E731
+    per = {}
+    with threadpool_limits(limits=cores):
+        # verify-window matvec (the headline), T = 1..4 per pass, at least min_seconds
+        n = k = 4096
+        b2 = enc(synth.weights_f32(synth.SEED_VERIFY, synth.TAG_WEIGHT, n, k))
+        x2 = synth.acts_f32(synth.SEED_VERIFY, synth.TAG_X, 4, k)
+        done_bytes, passes, t0 = 0, 0, time.perf_counter()
+        while True:
+            for T in (1, 2, 3, 4):
+                oracle.qmv(b2, n, k, x2[:T])
+                done_bytes += b2.size
+            passes += 1
+            el = time.perf_counter() - t0
+            if el >= min_seconds or passes >= 50:
+                break
+        head = {"value": round(done_bytes / el / 1e9, 4), "unit": "GB/s", "cores": cores, "kind": "oracle",
+                "cpu": model,
+                "sample": f"{passes} passes of the verify-window matvec (W 4096x4096, T=1..4): oracle decode + "
+                          f"float64 product, {el:.1f} s"}
+
+        def median_of(fn, runs=5):
+            ts = []
+            for _ in range(runs):
+                a = time.perf_counter()
+                fn()
+                ts.append(time.perf_counter() - a)
+            return statistics.median(ts)
+
+        # plumbing matvec 512 x 2048, T = 1: median of 5
+        b1 = enc(synth.weights_f32(synth.SEED_PLUMBING, synth.TAG_WEIGHT, 512, 2048))
+        x1 = synth.acts_f32(synth.SEED_PLUMBING, synth.TAG_X, 1, 2048)
+        t1 = median_of(lambda: oracle.qmv(b1, 512, 2048, x1))
+        per["plumbing_matvec_512x2048"] = {"ms": round(t1 * 1e3, 3), "weight_gbs": round(b1.size / t1 / 1e9, 4),
+                                           "runs": "median of 5"}
+        per["verify_window_matvec_4096x4096_T1-4"] = {"weight_gbs": head["value"], "runs": head["sample"]}
+
+        # The expert bank and the long-prompt weights are random valid blocks (a seeded
+        # binary16 scale of the synthetic weights' magnitude and uniform 4-bit indices):
+        # the oracle's time does not depend on the values, and encoding 600 M weights
+        # would take minutes of its own.
+        rng = np.random.default_rng(synth.SEED_EXPERTS)
+
+        def random_blocks(nn, kk):
+            nb = nn * kk // 32
+            out = np.empty((nb, 18), dtype=np.uint8)
+            d = (0.06 / 127 * (0.5 + rng.random(nb))).astype(np.float16)
+            out[:, 0:2] = d.astype("<f2").view(np.uint8).reshape(nb, 2)
+            out[:, 2:18] = rng.integers(0, 256, (nb, 16), dtype=np.uint8)
+            return out
+        gate = [random_blocks(INTER, HIDDEN) for _ in range(N_EXPERT)]
+        up = [random_blocks(INTER, HIDDEN) for _ in range(N_EXPERT)]
+        down = [random_blocks(HIDDEN, INTER) for _ in range(N_EXPERT)]
+        # MoE decode step: 4 fp32 tokens: median of 3
+        dl = synth.logits_normal(synth.SEED_DECODE, synth.TAG_LOGITS, 4, N_EXPERT)
+        dids, dw = oracle.route_topk(dl, TOP_K)
+        dx = synth.acts_f32(synth.SEED_DECODE, synth.TAG_X, 4, HIDDEN)
+        t3 = median_of(lambda: oracle.moe(dx, dids, dw, gate, up, down, HIDDEN, INTER), runs=3)
+        ubytes = len(np.unique(dids)) * 3 * (INTER * HIDDEN // 32 * 18)
+        per["moe_decode_step_4tok"] = {"us": round(t3 * 1e6, 1), "weight_gbs": round(ubytes / t3 / 1e9, 4),
+                                       "runs": "median of 3"}
+        # MoE prefill layer: one full run
+        pl = synth.logits_zipf_gumbel(synth.SEED_PREFILL, synth.TAG_GUMBEL, 3256, N_EXPERT)
+        pids, pw = oracle.route_topk(pl, TOP_K)
+        px = synth.acts_f16(synth.SEED_PREFILL, synth.TAG_X, 3256, HIDDEN)
+        a = time.perf_counter()
+        oracle.moe(px, pids, pw, gate, up, down, HIDDEN, INTER)
+        t4 = time.perf_counter() - a
+        flop4 = 3256 * TOP_K * 3 * 2 * HIDDEN * INTER
+        per["moe_prefill_layer_3256tok"] = {"ms": round(t4 * 1e3, 1), "gflops": round(flop4 / t4 / 1e9, 2),
+                                            "runs": "one full run"}
+        del gate, up, down
+        # long-prompt projection: one 512-token chunk, scaled by 25.5 (13,056 = 25.5 x 512)
+        b5 = random_blocks(14336, 4096)
+        x5 = synth.acts_f16(synth.SEED_LONG, synth.TAG_X, 512, 4096)
+        a = time.perf_counter()
+        oracle.gemm(b5, 14336, 4096, x5)
+        t5 = time.perf_counter() - a
+        flop5 = 2 * 512 * 14336 * 4096
+        per["long_prompt_projection_13056x4096x14336"] = {
+            "ms_estimated": round(t5 * 25.5 * 1e3, 1), "gflops": round(flop5 / t5 / 1e9, 2),
+            "runs": "one 512-token chunk timed, scaled by 25.5 (the full run is 25.5 chunks)"}
+    return head, {"cores": cores, "cpu": model, "kind": "oracle", "configs": per}
 
 
-def roof(bound, achieved, peak, unit, kernel, traffic=None):
-    return {"bound": bound, "achieved": round(achieved, 2), "peak": peak, "unit": unit,
-            "frac": round(achieved / peak, 4), "traffic": traffic, "kernel": kernel}
+def roof(bound, achieved, peak, unit, kernel, traffic=None, ceiling=None):
+    """achieved against the published peak, and against the measured ceiling of the same
+    bound on this GPU (a plain streaming read, or a pure matrix-core loop)."""
+    r = {"bound": bound, "achieved": round(achieved, 2), "peak": peak, "unit": unit,
+         "frac": round(achieved / peak, 4), "traffic": traffic, "kernel": kernel}
+    if ceiling:
+        r["measured_ceiling"] = round(ceiling, 1)
+        r["frac_of_measured_ceiling"] = round(achieved / ceiling, 4)
+    return r
 
 
 def main():
@@ -311,20 +403,62 @@ def main():
     comp = {name: sum(evs[i][j].elapsed_time(evs[i][j + 1]) for i in range(args.steps)) / args.steps
             for j, name in enumerate(("mmvq_4_calls", "dequant", "moe_decode", "moe_prefill", "dense"))}
 
-    # ---- per-launch matvec durations: graphs of R launches per T ------------------------
-    per_T = {}
-    for T in (1, 2, 3, 4):
-        g = capture(lambda s, T=T: [mmvq(c, T, s) for c in range(R)])
-        g.replay()
+    # ---- per-launch matvec durations: graphs of R launches per T, cold weights ----------
+    # Clocks ramp over ~100 ms, so the graphs are first replayed for >= 200 ms; then 5
+    # rounds, each replaying every T's graph in turn (interleaved), and the median per T.
+    mm_T = {T: capture(lambda s, T=T: [mmvq(c, T, s) for c in range(R)]) for T in (1, 2, 3, 4)}
+    hot_T = {T: capture(lambda s, T=T: [mmvq(0, T, s) for _ in range(R)]) for T in (1, 2, 3, 4)}
+    t_end = time.perf_counter() + 0.2
+    while time.perf_counter() < t_end:
+        for g in mm_T.values():
+            g.replay()
         torch.cuda.synchronize()
+
+    def replay_ms(g, launches, reps=2):
         a, b = Ev(), Ev()
-        reps = 4
         a.record(stream)
         for _ in range(reps):
             g.replay()
         b.record(stream)
         torch.cuda.synchronize()
-        per_T[T] = a.elapsed_time(b) / (reps * R)  # ms per launch
+        return a.elapsed_time(b) / (reps * launches)
+
+    ROUNDS = 5
+    rounds_T = {T: [] for T in mm_T}
+    rounds_hot = {T: [] for T in hot_T}
+    for _ in range(ROUNDS):
+        for T in (1, 2, 3, 4):
+            rounds_T[T].append(replay_ms(mm_T[T], R))
+            rounds_hot[T].append(replay_ms(hot_T[T], R))
+    per_T = {T: statistics.median(v) for T, v in rounds_T.items()}  # ms per launch
+    per_T_hot = {T: statistics.median(v) for T, v in rounds_hot.items()}
+    spread_T = {T: [round(min(v) * 1e3, 3), round(max(v) * 1e3, 3)] for T, v in rounds_T.items()}
+    del mm_T, hot_T
+
+    # ---- measured ceilings: a plain streaming read of the matvec's weight bytes (graphs
+    # of R launches over the same cold copies, the fastest of a few launch shapes), and a
+    # pure matrix-core loop (f16 16 x 16 x 32, two waves per SIMD, every CU) ---------------
+    ceil = ctypes.CDLL(os.path.join(ROOT, "dequant_matmul_iq4_amd", "libiq4_ceilings.so"))
+    ceil.iq4c_stream_read.argtypes = [ctypes.c_void_p, ctypes.c_int64, ctypes.c_int, ctypes.c_int, ctypes.c_void_p,
+                                      ctypes.c_void_p]
+    ceil.iq4c_mfma_loop.argtypes = [ctypes.c_int, ctypes.c_int, ctypes.c_void_p, ctypes.c_void_p]
+    sink = torch.zeros(4096, dtype=torch.int32, device="cuda")
+    stream_best = None
+    for nv in (1, 2, 4):
+        grid = (wb // 16 + 256 * nv - 1) // (256 * nv)
+        g = capture(lambda s, nv=nv, grid=grid: [ceil.iq4c_stream_read(vcopies[c].data_ptr(), wb // 16 * 16, nv, grid,
+                                                                        sink.data_ptr(), s) for c in range(R)])
+        g.replay()
+        ms = statistics.median([replay_ms(g, R) for _ in range(ROUNDS)])
+        stream_best = ms if stream_best is None else min(stream_best, ms)
+    mfma_iters, mfma_grid = 4096, 512
+    g = capture(lambda s: [ceil.iq4c_mfma_loop(mfma_iters, mfma_grid, sink.data_ptr(), s) for _ in range(4)])
+    g.replay()
+    mfma_ms = statistics.median([replay_ms(g, 4) for _ in range(ROUNDS)])
+    mfma_ceiling_tfs = mfma_grid * 4 * mfma_iters * 8 * 16384 / (mfma_ms * 1e-3) / 1e12
+    stream_ceiling_gbs = (wb // 16 * 16) / (stream_best * 1e-3) / 1e9
+    del g
+
     # ---- the same for the 8-bit-activation matvec, and its activation quantisation -----
     def per_launch_ms(fn, launches):
         g = capture(fn)
@@ -417,7 +551,20 @@ def main():
                         "(3256 tokens, Zipf 1.1, top-8 of 128, hidden 2048, inter 768) + long-prompt "
                         "projection (13056 x 4096 x 14336, 512-token chunks)",
             "mmvq_us_per_call": {str(T): round(per_T[T] * 1e3, 3) for T in per_T},
+            "mmvq_us_per_call_min_max_of_5_rounds": {str(T): spread_T[T] for T in spread_T},
             "mmvq_weight_gbs_per_T": {str(T): round(wb / (per_T[T] * 1e-3) / 1e9, 1) for T in per_T},
+            "mmvq_hot_us_per_call": {str(T): round(per_T_hot[T] * 1e3, 3) for T in per_T_hot},
+            "timing": "HIP events around graph replays of 64 launches on the launch stream; >= 200 ms of "
+                      "replays first (clock ramp); medians of 5 interleaved rounds; cold = 64 rotating weight "
+                      "copies (604 MB, past the 256 MB Infinity Cache), hot = one copy",
+            "measured_ceilings": {
+                "stream_read_us_9.4MB": round(stream_best * 1e3, 3),
+                "stream_read_gbs": round(stream_ceiling_gbs, 1),
+                "mfma_f16_tflops": round(mfma_ceiling_tfs, 1),
+                "how": "plain 16-byte grid-stride read of the matvec's weight bytes over the same cold copies "
+                       "(best of 3 launch shapes); v_mfma_f32_16x16x32_f16 loop, 8 independent accumulators "
+                       "per wave, 512 workgroups of 4 waves",
+            },
             "moe_prefill_ms_per_layer": round(comp["moe_prefill"], 4),
             "moe_prefill_tflops": round(prefill_flop / (comp["moe_prefill"] * 1e-3) / 1e12, 2),
             "moe_decode_us_per_step": round(dec_ms * 1e3, 2),
@@ -440,17 +587,20 @@ def main():
         "roofline": roof("hbm", mm_achieved, HBM_PEAK_GBS, "GB/s",
                          "qmv_dense_kernel: verify-window matvec, bytes = W + X + Y per call, "
                          "mean over T=1..4; traffic = HBM bytes per launch",
-                         traffic=measured_traffic("qmv_dense_4096x4096_T1-4")),
+                         traffic=measured_traffic("qmv_dense_4096x4096_T1-4"),
+                         ceiling=stream_ceiling_gbs),
         "rooflines": {
             "moe_prefill_layer": roof("mfma", prefill_flop / (comp["moe_prefill"] * 1e-3) / 1e12,
                                       F16_MFMA_PEAK_TFS, "TFLOP/s",
                                       "gather + qgemm<gateup> + qgemm<down> + combine, f16 MFMA; "
                                       "traffic = HBM bytes of the two GEMM launches",
                                       traffic=sum_traffic("qgemm_gateup_moe_prefill_3256tok",
-                                                          "qgemm_down_moe_prefill_3256tok")),
+                                                          "qgemm_down_moe_prefill_3256tok"),
+                                      ceiling=mfma_ceiling_tfs),
             "dense_projection": roof("mfma", dense_flop / (comp["dense"] * 1e-3) / 1e12, F16_MFMA_PEAK_TFS,
                                      "TFLOP/s", "qgemm<dense> x 26 chunks; traffic = HBM bytes of the 26 launches",
-                                     traffic=sum_traffic(*["qgemm_dense_13056x4096x14336_chunk512"] * 26)),
+                                     traffic=sum_traffic(*["qgemm_dense_13056x4096x14336_chunk512"] * 26),
+                                     ceiling=mfma_ceiling_tfs),
             "moe_decode_step": roof("hbm", unique_bytes / (dec_ms * 1e-3) / 1e9, HBM_PEAK_GBS,
                                     "GB/s", f"gather + qmv<gateup> + qmv_down_tiles + combine, {n_unique} "
                                     "unique experts' weights; traffic = HBM bytes of the two matvec launches",
@@ -467,8 +617,8 @@ def main():
         },
     }
     if not args.no_cpu_baseline:
-        log("cpu baseline (oracle)")
-        res["cpu_baseline"] = cpu_baseline()
+        log("cpu baselines (oracle, every config)")
+        res["cpu_baseline"], res["cpu_baselines"] = cpu_baselines()
     print(json.dumps(res))
 
 
