@@ -6,4 +6,8 @@ package: only the test suite, the smoke check of ``__graft_entry__`` and the
 the HIP library; the only module both sides use is ``synth`` (seeded random numbers).
 """
 from .iq4_ref import *  # noqa: F401,F403
-from .iq4_ref import __all__  # noqa: F401
+from .iq4_ref import __all__ as _nl_all
+from .iq4xs_ref import *  # noqa: F401,F403
+from .iq4xs_ref import __all__ as _xs_all
+
+__all__ = list(_nl_all) + list(_xs_all)
