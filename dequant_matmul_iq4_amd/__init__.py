@@ -43,6 +43,9 @@ SIGNATURES = {
     "iq4_qmv_multi": (ctypes.c_int, [_c_p, _c_i64, _c_i64, _c_p, _c_i64, _c_i32, _c_p, _c_i64, _c_p, _c_sz,
                                      _c_p]),
     "iq4_qmv_multi_noalloc": (ctypes.c_int, [_c_p, _c_i64, _c_i64, _c_p, _c_i64, _c_i32, _c_p, _c_i64, _c_p]),
+    "iq4_xs_bytes": (_c_i64, [_c_i64, _c_i64]),
+    "iq4_xs_dequant": (ctypes.c_int, [_c_p, _c_i64, _c_i32, _c_p, _c_p]),
+    "iq4_xs_qmv_multi": (ctypes.c_int, [_c_p, _c_i64, _c_i64, _c_p, _c_i64, _c_i32, _c_p, _c_i64, _c_p]),
     "iq4_quantize_q8_1": (ctypes.c_int, [_c_p, _c_i64, _c_i64, _c_i64, _c_p, _c_p, _c_p]),
     "iq4_qmv_q8": (ctypes.c_int, [_c_p, _c_i64, _c_i64, _c_p, _c_p, _c_i32, _c_p, _c_i64, _c_p, _c_sz, _c_p]),
     "iq4_route_topk": (ctypes.c_int, [_c_p, _c_i64, _c_i32, _c_i32, _c_p, _c_p, _c_p]),
@@ -147,6 +150,18 @@ def iq4_qmv_multi(packed, n, k, x, ldx, T, y, ldy, workspace=None, ws_bytes=0, s
 
 def iq4_qmv_multi_noalloc(packed, n, k, x, ldx, T, y, ldy, stream=None):
     _call("iq4_qmv_multi_noalloc", _ptr(packed), n, k, _ptr(x), ldx, T, _ptr(y), ldy, _stream(stream))
+
+
+def iq4_xs_bytes(n, k) -> int:
+    return lib().iq4_xs_bytes(n, k)
+
+
+def iq4_xs_dequant(sb, n_superblocks, out_dtype, out, stream=None):
+    _call("iq4_xs_dequant", _ptr(sb), n_superblocks, out_dtype, _ptr(out), _stream(stream))
+
+
+def iq4_xs_qmv_multi(w, n, k, x, ldx, T, y, ldy, stream=None):
+    _call("iq4_xs_qmv_multi", _ptr(w), n, k, _ptr(x), ldx, T, _ptr(y), ldy, _stream(stream))
 
 
 def iq4_quantize_q8_1(x, T, k, ldx, q, d, stream=None):

@@ -16,7 +16,7 @@ CSRC = os.path.join(PKG, "csrc")
 OUT = os.path.join(PKG, "libiq4.so")
 OBJ = os.path.join(ROOT, "_build")
 
-SOURCES = ["api.hip", "format.hip", "qmv.hip", "route.hip", "gemm.hip", "moe.hip"]
+SOURCES = ["api.hip", "format.hip", "qmv.hip", "route.hip", "gemm.hip", "moe.hip", "xs.hip"]
 
 HIPCC = os.environ.get("HIPCC", "/opt/rocm/bin/hipcc")
 ARCH = "gfx950"

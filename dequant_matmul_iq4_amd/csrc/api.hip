@@ -349,4 +349,41 @@ int iq4_qgemm(const void* packed, int64_t n, int64_t k, const void* x, int64_t m
                             ldx, y, ldy, chunk, as_stream(stream));
 }
 
+// ---- IQ4_XS super-blocks ----------------------------------------------------------
+
+int64_t iq4_xs_bytes(int64_t n, int64_t k) {
+  if (n < 1 || k < 1 || k % 256) return -1;
+  return n * (k / 256) * 136;
+}
+
+int iq4_xs_dequant(const void* sb, int64_t n_superblocks, int32_t out_dtype, void* out, void* stream) {
+  clear_error();
+  if (n_superblocks < 0) return set_error(IQ4_E_ARG, "iq4_xs_dequant: n_superblocks < 0");
+  if (out_dtype != IQ4_F32 && out_dtype != IQ4_F16)
+    return set_error(IQ4_E_ARG, "iq4_xs_dequant: out_dtype must be IQ4_F32 or IQ4_F16");
+  if (n_superblocks == 0) return IQ4_OK;
+  if (!sb || !out) return set_error(IQ4_E_ARG, "iq4_xs_dequant: null pointer");
+  if (n_superblocks > ((int64_t)1 << 40))
+    return set_error(IQ4_E_UNSUPPORTED, "iq4_xs_dequant: n_superblocks too large");
+  if (!aligned(sb, 8) || !aligned(out, 16))
+    return set_error(IQ4_E_ALIGN, "iq4_xs_dequant: sb must be 8-byte and out 16-byte aligned");
+  return launch_xs_dequant(sb, n_superblocks, out_dtype == IQ4_F16, out, as_stream(stream));
+}
+
+int iq4_xs_qmv_multi(const void* w, int64_t n, int64_t k, const float* x, int64_t ldx, int32_t T,
+                     float* y, int64_t ldy, void* stream) {
+  clear_error();
+  if (n < 1 || k < 1) return set_error(IQ4_E_ARG, "iq4_xs_qmv_multi: n and k must be positive");
+  if (k % 256 || k > ((int64_t)1 << 20) || n > ((int64_t)1 << 31))
+    return set_error(IQ4_E_UNSUPPORTED, "iq4_xs_qmv_multi: k must be a multiple of 256, k <= 2^20, n <= 2^31 "
+                     "(n=%lld k=%lld)", (long long)n, (long long)k);
+  if (T < 1 || T > 8) return set_error(IQ4_E_ARG, "iq4_xs_qmv_multi: T must be 1..8 (T=%d)", T);
+  if (!w || !x || !y) return set_error(IQ4_E_ARG, "iq4_xs_qmv_multi: null pointer");
+  if (ldx < k || ldy < n) return set_error(IQ4_E_ARG, "iq4_xs_qmv_multi: ldx < k or ldy < n");
+  if (!aligned(w, 8) || !aligned(x, 16) || ldx % 4 || !aligned(y, 4))
+    return set_error(IQ4_E_ALIGN, "iq4_xs_qmv_multi: w must be 8-byte, x 16-byte (ldx % 4 == 0) and y 4-byte "
+                     "aligned");
+  return launch_xs_qmv(w, n, k, x, ldx, T, y, ldy, as_stream(stream));
+}
+
 }  // extern "C"

@@ -22,4 +22,9 @@ int launch_gather(const int32_t* ids, int64_t n_pairs, int n_expert, int32_t* co
                   int32_t* offsets, int32_t* pairs, int32_t* slot_row, int32_t* tiles,
                   int32_t* num_tiles, hipStream_t s);
 
+// IQ4_XS super-blocks (xs.hip)
+int launch_xs_dequant(const void* sb, int64_t nsb, bool f16, void* out, hipStream_t s);
+int launch_xs_qmv(const void* w, int64_t n, int64_t k, const float* x, int64_t ldx, int T, float* y,
+                  int64_t ldy, hipStream_t s);
+
 }  // namespace iq4

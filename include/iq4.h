@@ -349,6 +349,52 @@ int iq4_moe_expert_gemm_shared(const void* x, int32_t act_dtype, int64_t n_tok, 
 int iq4_qgemm(const void* packed, int64_t n, int64_t k, const void* x, int64_t m, int64_t ldx,
               float* y, int64_t ldy, int64_t chunk, void* stream);
 
+/* ---------------------------------------------------------------------------------
+ * IQ4_XS super-blocks.  Page 2 (pull request "sm_80 (GA100) tuning") names this dense
+ * weight format in its wide-dequant commit message (decoded every prompt chunk), times
+ * its matvec in the MMVQ-IL harness commit message, and gives its block dot in the
+ * MMVQ-IL_PF commit message: the integer sum times the float of (ls - 32).  The bytes
+ * follow the format's public definition (the pages never print them):
+ *   256 weights in 136 bytes: d (binary16, bytes 0-1); a 16-bit word (bytes 2-3) whose
+ *   bits 2i, 2i+1 are the high two bits of sub-block i's 6-bit code ls_i; the low four
+ *   bits of ls_i in bytes 4 + i/2 (low nibble for even i); bytes 8 + 16i + m (m < 16)
+ *   hold the indices of elements 32i + m (low nibble) and 32i + 16 + m (high nibble);
+ *   w = d * (ls_i - 32) * codebook[q], exact in binary32.
+ * A matrix is stored row-major as n rows of k/256 super-blocks, as given (no repack).
+ */
+
+/* Bytes of an n x k super-block matrix (n * k/256 * 136), or -1 if n < 1, k < 1 or
+ * k % 256 != 0. */
+int64_t iq4_xs_bytes(int64_t n, int64_t k);
+
+/*
+ * Decode super-blocks: out[s][j] = d_s * (ls_{s, j/32} - 32) * codebook[q_{s,j}], in
+ * super-block order.
+ *   sb    [n_superblocks][136] bytes, 8-byte aligned.
+ *   out   [n_superblocks][256] of out_dtype: IQ4_F32 (exact) or IQ4_F16 (the exact
+ *         value rounded to nearest even, subnormals kept, overflow to inf); 16-byte
+ *         aligned.
+ * Bitwise equal to the host decode (the same rule as iq4_dequant_blocks).
+ * Errors: IQ4_E_ARG (n_superblocks < 0, bad dtype, null pointer), IQ4_E_ALIGN.
+ */
+int iq4_xs_dequant(const void* sb, int64_t n_superblocks, int32_t out_dtype, void* out, void* stream);
+
+/*
+ * T-column matvec on super-block weights: Y[t][r] = sum_k W[r][k] * X[t][k], t < T --
+ * the verify-window product of page 1 (commit "wire multi-token kernels into Verifier
+ * and MtpDrafter CUDA graphs", verify.hpp: the dense weights read once for T tokens)
+ * on the format above.  fp32 activations, exact decoded weights, fp32 accumulation.
+ * Column t of a call equals the T = 1 call on column t bit for bit.
+ *   w     n x k super-block matrix (iq4_xs_bytes(n, k) bytes), 8-byte aligned.
+ *   x     [T][ldx] float32, 16-byte aligned, ldx >= k, ldx % 4 == 0.
+ *   y     [T][ldy] float32 (written, never read), ldy >= n.
+ *   1 <= T <= 8; n >= 1; k >= 256, k % 256 == 0, k <= 2^20.  No workspace.
+ * Errors: IQ4_E_ARG (T range, null pointer, ldx/ldy), IQ4_E_ALIGN, IQ4_E_UNSUPPORTED
+ * (k % 256, sizes).
+ */
+int iq4_xs_qmv_multi(const void* w, int64_t n, int64_t k, const float* x, int64_t ldx, int32_t T,
+                     float* y, int64_t ldy, void* stream);
+
 #ifdef __cplusplus
 }
 #endif

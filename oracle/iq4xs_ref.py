@@ -103,12 +103,17 @@ def decode_xs_f16(sb) -> np.ndarray:
     return decode_xs(sb).astype(np.float16)
 
 
+_ENCODE_CHUNK = 4096
+
+
 def encode_xs(w) -> np.ndarray:
     """Test-input encoder: float32 weights ``[nsb, 256]`` -> super-blocks ``[nsb, 136]``
     (uint8), by the rule in the module docstring.  Inputs must be finite with
     ``max|w| / (127 * 31) <= 65504``."""
     w32 = np.ascontiguousarray(np.asarray(w, dtype=np.float32)).reshape(-1, 8, XS_SUB)
     nsb = w32.shape[0]
+    if nsb > _ENCODE_CHUNK:  # bound the [sb, 8, 32, 16] distance array; same result
+        return np.concatenate([encode_xs(w32[i:i + _ENCODE_CHUNK]) for i in range(0, nsb, _ENCODE_CHUNK)])
     s = (np.max(np.abs(w32), axis=2) / np.float32(127.0)).astype(np.float32)   # [nsb, 8]
     d16 = (np.max(s, axis=1) / np.float32(31.0)).astype(np.float32).astype(np.float16)
     d = d16.astype(np.float64)

@@ -30,7 +30,7 @@ Workload recipes (sizes from the five workloads these kernels are measured on):
 
 Seeds: plumbing matvec 101, verify-window matvec 102, expert bank 103 (shared by the
 decode step and the prefill layer), decode step 103, prefill layer 104, long-prompt
-projection 105.  Tensor tags: dense weight 0; expert e gate/up/down 3e, 3e+1, 3e+2;
+projection 105, IQ4_XS matvec shapes 106 and 107.  Tensor tags: dense weight 0; expert e gate/up/down 3e, 3e+1, 3e+2;
 activations 1000; decode logits 1001; Gumbel noise 1002.
 """
 from __future__ import annotations
@@ -51,6 +51,10 @@ SEED_EXPERTS = 103
 SEED_DECODE = 103
 SEED_PREFILL = 104
 SEED_LONG = 105
+# the IQ4_XS super-block matvec on the two shapes of page 2's cold/hot table
+# (2560 x 6144 and 6144 x 2560, read as N x K)
+SEED_XS_Z = 106
+SEED_XS_OUT = 107
 
 TAG_WEIGHT = 0
 TAG_X = 1000

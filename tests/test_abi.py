@@ -197,3 +197,28 @@ def test_moe_keep_intermediate_layout():
     assert rc == iq4.IQ4_E_WORKSPACE
     with pytest.raises(iq4.IQ4Error):
         iq4.iq4_moe_intermediate_layout(16, 17, 128, 2048, 768, iq4.IQ4_F16)
+
+
+def test_xs_validation_errors_never_launch():
+    """The IQ4_XS calls: sizes, T range, alignment and pointers are checked on the host."""
+    assert iq4.iq4_xs_bytes(6144, 2560) == 6144 * 10 * 136
+    assert iq4.iq4_xs_bytes(1, 256) == 136
+    assert iq4.iq4_xs_bytes(4, 128) == -1 and iq4.iq4_xs_bytes(0, 256) == -1
+    q = "iq4_xs_qmv_multi"
+    assert _rc(q, FAKE, 16, 256, FAKE, 256, 0, FAKE, 16, None) == iq4.IQ4_E_ARG
+    assert "T must be" in iq4.iq4_last_error()
+    assert _rc(q, FAKE, 16, 256, FAKE, 256, 9, FAKE, 16, None) == iq4.IQ4_E_ARG
+    assert _rc(q, FAKE, 16, 384, FAKE, 384, 1, FAKE, 16, None) == iq4.IQ4_E_UNSUPPORTED
+    assert _rc(q, FAKE, 0, 256, FAKE, 256, 1, FAKE, 16, None) == iq4.IQ4_E_ARG
+    assert _rc(q, FAKE, 16, 256, FAKE, 252, 1, FAKE, 16, None) == iq4.IQ4_E_ARG       # ldx < k
+    assert _rc(q, FAKE, 16, 256, FAKE, 256, 1, FAKE, 15, None) == iq4.IQ4_E_ARG       # ldy < n
+    assert _rc(q, FAKE + 4, 16, 256, FAKE, 256, 1, FAKE, 16, None) == iq4.IQ4_E_ALIGN
+    assert _rc(q, FAKE, 16, 256, FAKE + 8, 256, 1, FAKE, 16, None) == iq4.IQ4_E_ALIGN
+    assert _rc(q, FAKE, 16, 256, FAKE, 258, 1, FAKE, 16, None) == iq4.IQ4_E_ALIGN     # ldx % 4
+    assert _rc(q, None, 16, 256, FAKE, 256, 1, FAKE, 16, None) == iq4.IQ4_E_ARG
+    d = "iq4_xs_dequant"
+    assert _rc(d, FAKE, 4, 7, FAKE, None) == iq4.IQ4_E_ARG
+    assert _rc(d, FAKE, -1, 0, FAKE, None) == iq4.IQ4_E_ARG
+    assert _rc(d, FAKE + 4, 4, 0, FAKE, None) == iq4.IQ4_E_ALIGN
+    assert _rc(d, FAKE, 4, 0, FAKE + 8, None) == iq4.IQ4_E_ALIGN
+    assert _rc(d, FAKE, 0, 0, None, None) == iq4.IQ4_OK                                # nothing to do

@@ -18,6 +18,13 @@ def dense_weights(seed: int, n: int, k: int, tag: int = synth.TAG_WEIGHT):
 
 
 @functools.lru_cache(maxsize=None)
+def xs_weights(seed: int, n: int, k: int):
+    """(source float32 [n, k], oracle-encoded IQ4_XS super-blocks [n*k/256, 136])."""
+    w = synth.weights_f32(seed, synth.TAG_WEIGHT, n, k)
+    return w, oracle.encode_xs(w.reshape(-1, 256))
+
+
+@functools.lru_cache(maxsize=None)
 def acts32(seed: int, t: int, k: int):
     return synth.acts_f32(seed, synth.TAG_X, t, k)
 
