@@ -481,6 +481,46 @@ def main():
     deq_ms = per_launch_ms(lambda s: [iq4.iq4_dequant_blocks(c, n * k // 32, iq4.IQ4_F16, deq_out, s)
                                       for c in deq_copies], len(deq_copies))
     del deq_copies
+    # ---- IQ4_XS super-block matvec on page 2's two shapes, cold (rotating copies past
+    # twice the Infinity Cache), medians of 5 interleaved rounds; weights are random
+    # valid super-blocks (uniform bytes, binary16 scales of the workload's magnitude):
+    # the kernel's time does not depend on the values ----------------------------------
+    log("IQ4_XS matvec")
+    xs_gen = torch.Generator(device="cuda")
+    xs_gen.manual_seed(synth.SEED_XS_Z)
+    xs_T, xs_bytes, xs_deq_ms = {}, {}, None
+    for name, (xn, xk) in (("6144x2560", (6144, 2560)), ("2560x6144", (2560, 6144))):
+        xb = iq4.iq4_xs_bytes(xn, xk)
+        nsb = xb // 136
+        base = torch.randint(0, 256, (xb,), dtype=torch.uint8, device="cuda", generator=xs_gen)
+        dsc = (torch.randn(nsb, device="cuda", generator=xs_gen) * 2e-4).half()
+        base.view(nsb, 136)[:, 0:2] = dsc.view(torch.uint8).view(nsb, 2)
+        n_copies = (2 * (256 << 20)) // xb + 1
+        xs_copies = [base] + [base.clone() for _ in range(n_copies - 1)]
+        xs_x = synth.acts_f32_torch(synth.SEED_XS_Z, synth.TAG_X, 4, xk, device="cuda")
+        xs_y = torch.empty((4, xn), dtype=torch.float32, device="cuda")
+        gs = {T: capture(lambda s, T=T: [iq4.iq4_xs_qmv_multi(c, xn, xk, xs_x, xk, T, xs_y, xn, s)
+                                         for c in xs_copies]) for T in (1, 2, 3, 4)}
+        t_end = time.perf_counter() + 0.1
+        while time.perf_counter() < t_end:
+            for g in gs.values():
+                g.replay()
+            torch.cuda.synchronize()
+        rounds = {T: [] for T in gs}
+        for _ in range(ROUNDS):
+            for T in gs:
+                rounds[T].append(replay_ms(gs[T], n_copies))
+        xs_T[name] = {T: statistics.median(v) for T, v in rounds.items()}
+        xs_bytes[name] = (xb, xn, xk)
+        if name == "6144x2560":
+            xs_out = torch.empty(nsb * 256, dtype=torch.float16, device="cuda")
+            xs_deq_ms = per_launch_ms(lambda s: [iq4.iq4_xs_dequant(c, nsb, iq4.IQ4_F16, xs_out, s)
+                                                 for c in xs_copies], n_copies)
+            xs_deq_bytes = xb + nsb * 256 * 2
+            del xs_out
+        del gs, xs_copies, base
+    xs_alg = sum(xb + 4 * T * (xn + xk) for xb, xn, xk in xs_bytes.values() for T in (1, 2, 3, 4))
+    xs_achieved = xs_alg / (sum(sum(v.values()) for v in xs_T.values()) * 1e-3) / 1e9
     q8_alg = sum(wb + T * k + T * (k // 32) * 2 + 4 * T * n for T in (1, 2, 3, 4))  # W + codes + scales + Y
     q8_achieved = q8_alg / (sum(per_T_q8.values()) * 1e-3) / 1e9
     # ---- MoE decode step device time: one graph of N_BANKS steps back to back, so a
@@ -579,6 +619,10 @@ def main():
             "quantize_q8_us_4x4096": round(quant_ms * 1e3, 3),
             "dense_ms_26_chunks": round(comp["dense"], 4),
             "dense_tflops": round(dense_flop / (comp["dense"] * 1e-3) / 1e12, 2),
+            "xs_mmvq_us_per_call": {nm: {str(T): round(v * 1e3, 3) for T, v in d.items()} for nm, d in xs_T.items()},
+            "xs_mmvq_weight_gbs_per_T": {nm: {str(T): round(xs_bytes[nm][0] / (v * 1e-3) / 1e9, 1)
+                                              for T, v in d.items()} for nm, d in xs_T.items()},
+            "xs_dequant_us_6144x2560_f16": round(xs_deq_ms * 1e3, 2),
             "dequant_us": round(deq_ms * 1e3, 2),
             "dequant_us_in_step": round(comp["dequant"] * 1e3, 2),
             "prefill_expert_tokens_max_min": [int(counts.max()), int(counts.min())],
@@ -610,6 +654,13 @@ def main():
                             "qmv_q8_kernel: verify-window matvec on 8-bit activations, bytes = W + codes + "
                             "scales + Y per call, mean over T=1..4; traffic = HBM bytes per launch",
                             traffic=measured_traffic("qmv_q8_4096x4096_T1-4")),
+            "xs_mmvq": roof("hbm", xs_achieved, HBM_PEAK_GBS, "GB/s",
+                            "xs_qmv_kernel: IQ4_XS super-block matvec, 6144x2560 and 2560x6144, bytes = W + X + Y "
+                            "per call, mean over both shapes and T=1..4 (cold copies)",
+                            traffic=None, ceiling=stream_ceiling_gbs),
+            "xs_dequant": roof("hbm", xs_deq_bytes / (xs_deq_ms * 1e-3) / 1e9, HBM_PEAK_GBS, "GB/s",
+                               "xs_dequant_kernel<f16>: 8.4 MB of super-blocks in, 31.5 MB of f16 out per launch "
+                               "(graph of launches over cold copies)", traffic=None),
             "dequant": roof("hbm", deq_bytes / (deq_ms * 1e-3) / 1e9, HBM_PEAK_GBS, "GB/s",
                             "dequant_staged_kernel<f16>: 9.4 MB of blocks in, 33.5 MB of f16 out, per launch "
                             "(graph of 32 launches over cold copies); traffic = HBM bytes per launch",
