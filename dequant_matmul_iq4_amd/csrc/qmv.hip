@@ -347,11 +347,12 @@ __global__ void __launch_bounds__(64 * kDenseWaves) qmv_dense_kernel(QmvArgs a) 
     nib[u] = *reinterpret_cast<const uint4*>(tp + (int64_t)q * kTileNibbleBytes);
     scl[u] = *reinterpret_cast<const uint2*>(sp + (int64_t)q * kTileScaleBytes);
   }
-  // ---- level table: with NT = 64 kDenseWaves threads, 16-byte chunk q = tid + NT j
-  // holds copies 4(q mod 16) .. +3 of entry q / 16, whose low index is (tid / 16) mod 16
-  // for every j and whose high index (tid / 256) + (NT / 256) j is the same for the whole
-  // wave; consecutive lanes write consecutive chunks (no bank conflicts).
-  {
+  // ---- level table: 16-byte chunk q (0 .. 4095) holds copies 4(q mod 16) .. +3 of entry
+  // q / 16; thread tid writes chunks tid, tid + NT, ... (consecutive lanes, consecutive
+  // chunks: no bank conflicts).  With all NT = 64 kDenseWaves threads, a thread's chunks
+  // share the low index (tid / 16) mod 16 and a wave's the high index (tid / 256) +
+  // (NT / 256) j; a smaller workgroup (short K) takes the general loop.
+  if (nwaves == kDenseWaves) {
     constexpr int NT = 64 * kDenseWaves;
     const uint32_t lo = bf16_level((uint32_t)(tid >> 4) & 15u);
     const uint32_t hsel = (uint32_t)__builtin_amdgcn_readfirstlane(tid >> 8);
@@ -360,6 +361,13 @@ __global__ void __launch_bounds__(64 * kDenseWaves) qmv_dense_kernel(QmvArgs a) 
     for (int j = 0; j < 4096 / NT; ++j) {
       const uint32_t v = lo | (bf16_level(hsel + (uint32_t)(NT / 256) * j) << 16);
       dst[NT * j] = uint4{v, v, v, v};
+    }
+  } else {
+    uint4* dst = reinterpret_cast<uint4*>(smem);
+    for (int q = tid; q < 4096; q += 64 * nwaves) {
+      const uint32_t e = (uint32_t)q >> 4;
+      const uint32_t v = bf16_level(e & 15u) | (bf16_level(e >> 4) << 16);
+      dst[q] = uint4{v, v, v, v};
     }
   }
   // A lookup: byte b of index word w -> the lane's copy of entry w.byte[b]

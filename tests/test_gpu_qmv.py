@@ -179,3 +179,30 @@ def test_split_k_two_passes():
             assert bits_equal(y[t], single[t]), (T, t)
     # the workspace is left ready: a 1-column call after them still matches
     assert bits_equal(run_qmv(packed, n, k, x[2:3])[0], single[2])
+
+
+@pytest.mark.parametrize("n,k,T", [(16, 128, 1), (48, 384, 3), (32, 640, 4), (64, 896, 2)])
+def test_short_k_after_other_kernels(n, k, T):
+    """K of 1 to 7 quads runs a workgroup of fewer than 8 waves, which must build the
+    whole level table itself.  Before each call another kernel (the 8-bit matvec, the
+    IQ4_XS decode) leaves different contents in LDS, so a table built only in part would
+    read their leftovers and show here (right after a full-size float matvec the
+    leftovers happen to be a complete table)."""
+    note(f"qmv: short K after other kernels n={n} k={k} T={T}")
+    rng = np.random.default_rng(3 * n + k)
+    b = integer_exact_blocks(rng, n * k // 32, 6)
+    x = rng.integers(-8, 9, (T, k)).astype(np.float32)
+    packed = pack(b, n, k)
+    ref = oracle.qmv(b, n, k, x)
+    # other kernels first: the 8-bit matvec of the same shape, an IQ4_XS decode
+    xq = rng.integers(-127, 128, (T, k)).astype(np.float32)
+    q = torch.from_numpy(xq.astype(np.int8)).cuda()
+    d = torch.ones((T, k // 32), dtype=torch.float16, device="cuda")
+    yq = torch.empty((T, n), dtype=torch.float32, device="cuda")
+    ws, wsb = qmv_workspace(n, k)
+    for rep in range(3):
+        iq4.iq4_qmv_q8(packed, n, k, q, d.view(torch.int16), T, yq, n, ws, wsb)
+        sb = dev(rng.integers(0, 256, (64, 136), dtype=np.uint8).reshape(-1))
+        out = torch.empty(64 * 256, dtype=torch.float32, device="cuda")
+        iq4.iq4_xs_dequant(sb, 64, iq4.IQ4_F32, out)
+        assert bits_equal(run_qmv(packed, n, k, x), ref), rep
