@@ -711,14 +711,16 @@ __global__ void __launch_bounds__(512) qmv_grouped_kernel(QmvArgs a) {
     if (NRED == 1) __syncthreads();  // the partials are read; the slots can be reused
   };
 
-  // ---- prologue: first row group's weights, then the columns, the table -------------
+  // ---- prologue: the columns, then the first row group's weights, the table --------
+  // (the columns first: loads complete in order, so staging them waits for them alone
+  // and runs while the weights are in flight)
   WSet wa, wb;
-  load_w(wa, rg0);
   const bool one_pass = ncols <= kCols;
   if (one_pass) {
     load_x(0, (int)ncols);
     load_cols(0, (int)ncols);
   }
+  load_w(wa, rg0);
   for (int e = tid; e < 256; e += blockDim.x) {
     const uint32_t v = bf16_of_level(level_of(e & 15)) | (bf16_of_level(level_of(e >> 4)) << 16);
     uint4* dst = reinterpret_cast<uint4*>(lut + e * kLutCopies);
@@ -728,8 +730,13 @@ __global__ void __launch_bounds__(512) qmv_grouped_kernel(QmvArgs a) {
   __syncthreads();  // the table (LDS only: no wait on the loads in flight)
   if (one_pass) store_x((int)ncols);
 
+  // Every step requests the next group's weights (in flight during this group's work);
+  // the last group requests itself again (an L2 hit).  With the same loads issued on
+  // every path the compiler's waits for `cur` count exactly past them: issued under a
+  // branch, the waits merged from both paths also waited for the next group's loads,
+  // and each group's work waited for the next group's weights.
   auto step = [&](const WSet& cur, WSet& nxt, int64_t rg) {
-    if (rg + 1 < rg1) load_w(nxt, rg + 1);  // in flight during this group's work
+    load_w(nxt, min(rg + 1, rg1 - 1));
     for (int64_t t0 = 0; t0 < ncols; t0 += kCols) {
       const int T = (int)min((int64_t)kCols, ncols - t0);
       if (!one_pass) {  // more than kCols columns: stage each pass (rare in decode)
@@ -744,7 +751,7 @@ __global__ void __launch_bounds__(512) qmv_grouped_kernel(QmvArgs a) {
   };
   for (int64_t rg = rg0; rg < rg1; rg += 2) {
     step(wa, wb, rg);
-    if (rg + 1 < rg1) step(wb, wa, rg + 1);
+    step(wb, wa, min(rg + 1, rg1 - 1));  // an odd count repeats its last group (same values)
   }
 }
 
@@ -786,10 +793,24 @@ __global__ void __launch_bounds__(512) qmv_down_tiles_kernel(QmvArgs a) {
       w.scl[q] = *reinterpret_cast<const uint2*>(W + a.nibble_bytes + (rt * KQ + q) * kTileScaleBytes + c * 8);
     }
   };
+  // The first pass's columns are requested before the weights (loads complete in order,
+  // so staging them then waits for them alone): one staging task per thread.
+  constexpr int NTASK = kCols * NB * 4;  // (column, block, k-group) staging tasks of a pass
+  static_assert(NTASK <= 512, "one staging task per thread");
+  const int task_t = tid / (NB * 4), task_bl = (tid >> 2) % NB, task_gg = tid & 3;
+  const int T0 = (int)min((int64_t)kCols, ncols);
+  float4 x0a = float4{0.f, 0.f, 0.f, 0.f}, x0b = x0a;
+  if (tid < NTASK && task_t < T0) {
+    const float* p = a.x + (seg0 + task_t) * a.ldx + task_bl * kQK + 8 * task_gg;
+    x0a = *reinterpret_cast<const float4*>(p);
+    x0b = *reinterpret_cast<const float4*>(p + 4);
+  }
+  // the wave's first two tiles (a wave without them requests the last tile again, an L2
+  // hit, so that every wave issues the same loads and the waits stay exact)
   WSet wa, wb;
   const int64_t r0 = t0 + wave;
-  if (r0 < t1) load_w(wa, r0);
-  if (r0 + nwaves < t1) load_w(wb, r0 + nwaves);
+  load_w(wa, min(r0, t1 - 1));
+  load_w(wb, min(r0 + nwaves, t1 - 1));
 
   for (int i = tid; i < 512; i += blockDim.x) {  // level table: entry i / 2, 16 copies each
     const int le = i >> 1;
@@ -803,9 +824,11 @@ __global__ void __launch_bounds__(512) qmv_down_tiles_kernel(QmvArgs a) {
   // the pass's columns: h rows seg0 + p0 + t (pair-sorted), their pair ids and gate
   // weights (scalar loads: the lists are not written during the call)
   const __attribute__((address_space(4))) float* cgate = (const __attribute__((address_space(4))) float*)a.gate_w;
-  constexpr int NTASK = kCols * NB * 4;  // (column, block, k-group) staging tasks of a pass
 
-  for (int64_t p0 = 0; p0 < ncols; p0 += kCols) {
+  // A pass: the columns p0 .. p0 + 3.  The first pass is its own instantiation, so no
+  // branch around a load lies between the entry's requests and the waits for them.
+  auto pass = [&](int64_t p0, auto first_tag) {
+    constexpr bool FIRST = decltype(first_tag)::value;
     const int T = (int)min((int64_t)kCols, ncols - p0);
     int32_t pc[kCols];
     float gw[kCols];
@@ -814,13 +837,16 @@ __global__ void __launch_bounds__(512) qmv_down_tiles_kernel(QmvArgs a) {
       pc[t] = pair_of(a, si, p0 + min(t, T - 1));
       gw[t] = cgate[pc[t]];
     }
-    if (p0 > 0) __syncthreads();  // every wave is done with the previous pass's columns
-    for (int task = tid; task < NTASK; task += (int)blockDim.x) {
-      const int t = task / (NB * 4), bl = (task >> 2) % NB, gg = task & 3;
-      if (t < T) {
-        const float* p = a.x + (seg0 + p0 + t) * a.ldx + bl * kQK + 8 * gg;
-        const float4 xa = *reinterpret_cast<const float4*>(p);
-        const float4 xb = *reinterpret_cast<const float4*>(p + 4);
+    if (!FIRST) __syncthreads();  // every wave is done with the previous pass's columns
+    {
+      const int task = tid, t = task_t, bl = task_bl, gg = task_gg;
+      if (task < NTASK && t < T) {
+        float4 xa = x0a, xb = x0b;  // the first pass's, loaded at entry
+        if (!FIRST) {
+          const float* p = a.x + (seg0 + p0 + t) * a.ldx + bl * kQK + 8 * gg;
+          xa = *reinterpret_cast<const float4*>(p);
+          xb = *reinterpret_cast<const float4*>(p + 4);
+        }
         uint32_t q0[3], q1[3], q2[3], q3[3];
         split_pair(xa.x, xa.y, q0);
         split_pair(xa.z, xa.w, q1);
@@ -885,10 +911,12 @@ __global__ void __launch_bounds__(512) qmv_down_tiles_kernel(QmvArgs a) {
         if (rt + 3 * nwaves < t1) load_w(wb, rt + 3 * nwaves);
       }
     }
-    if (p0 + kCols < ncols) {  // a further pass walks the tiles again
-      if (r0 < t1) load_w(wa, r0);
-      if (r0 + nwaves < t1) load_w(wb, r0 + nwaves);
-    }
+  };
+  pass(0, std::true_type{});
+  for (int64_t p0 = kCols; p0 < ncols; p0 += kCols) {  // a further pass walks the tiles again
+    load_w(wa, min(r0, t1 - 1));
+    load_w(wb, min(r0 + nwaves, t1 - 1));
+    pass(p0, std::false_type{});
   }
 }
 
