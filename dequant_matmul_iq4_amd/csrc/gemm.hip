@@ -505,10 +505,15 @@ qgemm_kernel(GemmArgs a) {
           for (int r = 0; r < kWaveRT; ++r)
             if (rt_ok[r]) atomicAdd(orow + 16 * r, gw * acc[mt][r][i]);
         } else {
-          float* yrow = a.C + (int64_t)p * a.ldc + n0 + 64 * cg + c;
+          // the row rounded to binary16 (half the bytes of the write and of the
+          // combine's read); the product is rounded to binary32 first
+          uint16_t* yrow = a.R + (int64_t)p * a.ldc + n0 + 64 * cg + c;
 #pragma unroll
-          for (int r = 0; r < kWaveRT; ++r)
-            if (rt_ok[r]) yrow[16 * r] = gw * acc[mt][r][i];
+          for (int r = 0; r < kWaveRT; ++r) {
+            float v = gw * acc[mt][r][i];
+            asm volatile("" : "+v"(v));  // no fused multiply-and-convert (it would drop a -0)
+            if (rt_ok[r]) yrow[16 * r] = __half_as_ushort(__float2half_rn(v));
+          }
         }
       }
   }

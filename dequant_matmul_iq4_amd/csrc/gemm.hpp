@@ -17,7 +17,8 @@ struct GemmArgs {
   const uint8_t* S1;
   int64_t N, K;             // weight rows and reduction length of one matrix
   int64_t M;                // DENSE: rows of A in this launch
-  float* C;                 // DENSE: output [M][ldc]; DOWN: per-pair rows [pairs][ldc]
+  float* C;                 // DENSE: output [M][ldc]
+  uint16_t* R;              // DOWN: per-pair rows w * (Wd h) as binary16 [pairs][ldc]
   int64_t ldc;
   uint16_t* H;              // GATEUP: h = silu(g) * u as binary16 [pairs][ldh] (sorted order)
   int64_t ldh;

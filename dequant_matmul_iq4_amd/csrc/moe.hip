@@ -3,7 +3,7 @@
 //
 // Prefill (binary16 activations):
 //   gather (+ tile list) -> GEMM gate|up (+SwiGLU, h binary16) -> GEMM down (x gate
-//   weight) -> combine.
+//   weight, slot rows binary16) -> combine (fp32 sums).
 // Decode (fp32 activations, few tokens):
 //   gather -> grouped matvec gate|up (+SwiGLU, h fp32) -> grouped matvec down (x gate
 //   weight) -> combine; with at most 64 pairs there is no gather launch: each matvec
@@ -23,21 +23,33 @@ namespace iq4 {
 constexpr int kTileM = 128;  // rows per GEMM tile (gemm.hip kBM)
 constexpr int kMaxTopK = 16;  // the largest top_k the call accepts
 
-// out[t][h] = sum_j rows[t * K + j][h], j ascending; one thread per 4 outputs, K = top_k
-// fixed at compile time.  Every slot row is requested at once, with non-temporal loads
-// (each is read once), then added in slot order.
-template <int K>
-__global__ void __launch_bounds__(256) combine_kernel(const float* __restrict__ rows, int64_t ldr,
+// Four consecutive row elements: fp32 rows (decode) as they are, binary16 rows (prefill)
+// widened to fp32 (exact).  Non-temporal: each row is read once.
+__device__ __forceinline__ f32x4 load_row4(const float* p) {
+  return __builtin_nontemporal_load(reinterpret_cast<const f32x4*>(p));
+}
+__device__ __forceinline__ f32x4 load_row4(const uint16_t* p) {
+  typedef uint32_t u32x2 __attribute__((ext_vector_type(2)));
+  const u32x2 w = __builtin_nontemporal_load(reinterpret_cast<const u32x2*>(p));
+  return f32x4{h2f((uint16_t)(w.x & 0xFFFFu)), h2f((uint16_t)(w.x >> 16)), h2f((uint16_t)(w.y & 0xFFFFu)),
+               h2f((uint16_t)(w.y >> 16))};
+}
+
+// out[t][h] = sum_j rows[t * K + j][h], j ascending, in fp32; one thread per 4 outputs,
+// K = top_k fixed at compile time.  Every slot row is requested at once, then added in
+// slot order.
+template <int K, typename RowT>
+__global__ void __launch_bounds__(256) combine_kernel(const RowT* __restrict__ rows, int64_t ldr,
                                                       int64_t n_tok, int64_t hidden,
                                                       float* __restrict__ out, int64_t ldo) {
   const int64_t per_tok = hidden / 4;
   const int64_t i = (int64_t)blockIdx.x * blockDim.x + threadIdx.x;
   if (i >= n_tok * per_tok) return;
   const int64_t t = i / per_tok, h = (i % per_tok) * 4;
-  const float* r = rows + t * K * ldr + h;
+  const RowT* r = rows + t * K * ldr + h;
   f32x4 v[K];
 #pragma unroll
-  for (int j = 0; j < K; ++j) v[j] = __builtin_nontemporal_load(reinterpret_cast<const f32x4*>(r + j * ldr));
+  for (int j = 0; j < K; ++j) v[j] = load_row4(r + j * ldr);
   f32x4 acc = v[0];
 #pragma unroll
   for (int j = 1; j < K; ++j) {
@@ -49,18 +61,19 @@ __global__ void __launch_bounds__(256) combine_kernel(const float* __restrict__ 
   *reinterpret_cast<f32x4*>(out + t * ldo + h) = acc;
 }
 
-template <int K>
-static int launch_combine_k(const float* rows, int64_t n_tok, int64_t hidden, float* out, int64_t ldo,
+template <int K, typename RowT>
+static int launch_combine_k(const RowT* rows, int64_t n_tok, int64_t hidden, float* out, int64_t ldo,
                             hipStream_t s) {
   const int64_t n4 = n_tok * (hidden / 4);
   // a decode step's few outputs spread over more CUs (64-thread workgroups)
   const int64_t cb = n4 < 65536 ? 64 : 256;
-  hipLaunchKernelGGL(combine_kernel<K>, dim3((unsigned)((n4 + cb - 1) / cb)), dim3((unsigned)cb), 0, s, rows,
-                     hidden, n_tok, hidden, out, ldo);
+  hipLaunchKernelGGL((combine_kernel<K, RowT>), dim3((unsigned)((n4 + cb - 1) / cb)), dim3((unsigned)cb), 0, s,
+                     rows, hidden, n_tok, hidden, out, ldo);
   return check_launch("combine_kernel");
 }
 
-static int launch_combine(const float* rows, int64_t n_tok, int top_k, int64_t hidden, float* out,
+template <typename RowT>
+static int launch_combine(const RowT* rows, int64_t n_tok, int top_k, int64_t hidden, float* out,
                           int64_t ldo, hipStream_t s) {
   switch (top_k) {
     case 1: return launch_combine_k<1>(rows, n_tok, hidden, out, ldo, s);
@@ -129,7 +142,7 @@ MoeLayout moe_layout(int64_t n_tok, int top_k, int n_expert, int64_t hidden, int
   L.num_tiles = off; off += 256;
   L.tiles = off;     off += align256(8 * L.max_tiles);
   L.h = off;         off += align256(P * inter * (f16 ? 2 : 4));
-  L.rows = off;      off += align256(P * hidden * 4);
+  L.rows = off;      off += align256(P * hidden * (f16 ? 2 : 4));  // binary16 rows for the prefill
   L.ids2 = off;      off += shared ? align256(4 * P) : 0;
   L.w2 = off;        off += shared ? align256(4 * P) : 0;
   L.g = keep ? off : -1; off += keep ? align256(P * inter * 4) : 0;
@@ -150,7 +163,8 @@ int launch_moe(const MoeCall& m, hipStream_t s) {
   int32_t* slot_row = reinterpret_cast<int32_t*>(ws + L.slot_row);
   int32_t* num_tiles = reinterpret_cast<int32_t*>(ws + L.num_tiles);
   int32_t* tiles = reinterpret_cast<int32_t*>(ws + L.tiles);
-  float* rows = reinterpret_cast<float*>(ws + L.rows);
+  float* rows = reinterpret_cast<float*>(ws + L.rows);          // decode: fp32 rows
+  uint16_t* rows16 = reinterpret_cast<uint16_t*>(ws + L.rows);  // prefill: binary16 rows
   if (m.n_tok == 0) return 0;
   // the routing the products see: with a shared expert, one more expert and slot
   const int32_t* ids = m.ids;
@@ -220,7 +234,7 @@ int launch_moe(const MoeCall& m, hipStream_t s) {
     d.S0 = static_cast<const uint8_t*>(m.s_down);
     d.N = m.hidden;
     d.K = m.inter;
-    d.C = rows;
+    d.R = rows16;
     d.ldc = m.hidden;
     d.tiles = tiles;
     d.num_tiles = num_tiles;
@@ -274,7 +288,9 @@ int launch_moe(const MoeCall& m, hipStream_t s) {
   }
 
   if (!atomic) {
-    if (int e = launch_combine(rows, m.n_tok, top_k, m.hidden, m.out, m.ldo, s)) return e;
+    if (int e = m.f16 ? launch_combine(rows16, m.n_tok, top_k, m.hidden, m.out, m.ldo, s)
+                      : launch_combine(rows, m.n_tok, top_k, m.hidden, m.out, m.ldo, s))
+      return e;
   }
   return 0;
 }

@@ -101,14 +101,14 @@ __device__ __forceinline__ SlotInfo slot_from_offsets(const QmvArgs& a, int64_t 
   return s;
 }
 
-// From the routed ids themselves (at most 64 pairs, one per lane), so that no gather has
-// to run first: the wave marks the experts present in a bitmap (bm: 32 words of LDS of
-// its own, 1024 experts), counts them per word with a prefix sum over lanes, and picks
-// the slot's word and bit.  An id outside [0, n_expert) marks nothing.
-__device__ __forceinline__ SlotInfo slot_from_ids(const QmvArgs& a, int64_t slot, uint32_t* bm,
+// From the routed ids themselves (at most 64 pairs, one per lane, v = this lane's id, -1
+// past the pairs), so that no gather has to run first: the wave marks the experts
+// present in a bitmap (bm: 32 words of LDS of its own, 1024 experts), counts them per
+// word with a prefix sum over lanes, and picks the slot's word and bit.  An id outside
+// [0, n_expert) marks nothing.
+__device__ __forceinline__ SlotInfo slot_from_ids(int v, int n_expert, int64_t slot, uint32_t* bm,
                                                   int lane) {
-  const int v = (lane < a.n_pairs) ? a.ids[lane] : -1;
-  const bool valid = (unsigned)v < (unsigned)a.n_expert;
+  const bool valid = (unsigned)v < (unsigned)n_expert;
   if (lane < 32) bm[lane] = 0u;
   // a wave's LDS accesses execute in order; the fences only keep the compiler from
   // moving them
@@ -197,6 +197,19 @@ __device__ __forceinline__ void split_pair(float v0, float v1, uint32_t out[3]) 
 // matvec, one workgroup per CU, builds the table once for all of its row groups; 8
 // copies measured 5 % slower on the MoE decode step.
 constexpr int kLutCopies = 32;
+
+// The level table of the grouped kernels: entry e (0..255) holds the bf16 levels of its
+// two nibbles (low nibble in the low half), kLutCopies copies side by side.  Consecutive
+// threads write consecutive 16-byte pieces, so the stores meet no bank conflict.
+__device__ __forceinline__ void build_pair_table(uint32_t* lut, int tid, int nthreads) {
+  constexpr int PER = kLutCopies / 4;  // 16-byte pieces per entry
+  uint4* dst = reinterpret_cast<uint4*>(lut);
+  for (int q = tid; q < 256 * PER; q += nthreads) {
+    const int e = q / PER;
+    const uint32_t v = bf16_of_level(level_of(e & 15)) | (bf16_of_level(level_of(e >> 4)) << 16);
+    dst[q] = uint4{v, v, v, v};
+  }
+}
 
 template <int N>
 struct ColsC {  // a column count as a type (compile-time pass width)
@@ -506,7 +519,7 @@ __global__ void __launch_bounds__(512) qmv_grouped_kernel(QmvArgs a) {
   constexpr int ROWS = RG * kTileRows;
   constexpr int XBYTES = kWaves * WQ * 4 * kFragBytes;
   constexpr int REDN = kWaves * NMAT * RG * 64;  // one f32x4 partial per (wave, matrix, tile, lane)
-  __shared__ uint32_t lut[256 * kLutCopies];
+  __shared__ __attribute__((aligned(16))) uint32_t lut[256 * kLutCopies];
   __shared__ __attribute__((aligned(16))) uint8_t xs[XBYTES + 256];  // + room for padding-row reads
   // two reduction buffers where they fit (a buffer is then reused two calls later)
   constexpr int NRED = (XBYTES + 256 + 256 * kLutCopies * 4 + 2 * REDN * 16 + kWaves * 32 * 4 <= 160 * 1024) ? 2 : 1;
@@ -517,6 +530,28 @@ __global__ void __launch_bounds__(512) qmv_grouped_kernel(QmvArgs a) {
   const int lane = tid & 63, wave = tid >> 6, nwaves = (int)(blockDim.x >> 6);
   const int c = lane & 15, g = lane >> 4;
 
+  // Every kernel argument this kernel reads, loaded at entry.  Left to itself the
+  // compiler loads some of them where they are first used, and each such load is a
+  // scalar round trip on the way to the first weight request.
+  {
+    const uint8_t *W0 = a.W0, *W1 = a.W1, *S0 = a.S0, *S1 = a.S1;
+    const float *X = a.x, *GW = a.gate_w;
+    float *Y = a.y, *G = a.G, *U = a.U;
+    const int32_t *ids = a.ids, *offsets = a.offsets, *pairs = a.pairs;
+    const int64_t wes = a.w_expert_stride, ldx = a.ldx, ldy = a.ldy, n = a.n, nt = a.nt, rg_n = a.rg_n,
+                  nib = a.nibble_bytes, rgc = a.rg_chunks;
+    const int she = a.shared_e, n_pairs = a.n_pairs, top_k = a.top_k, n_expert = a.n_expert, kq_n = a.kq_n,
+              wave_quads = a.wave_quads, rg_per_wg = a.rg_per_wg;
+    asm volatile("" ::"s"(W0), "s"(W1), "s"(S0), "s"(S1), "s"(X), "s"(GW), "s"(Y), "s"(G), "s"(U), "s"(ids),
+                 "s"(offsets), "s"(pairs), "s"(wes), "s"(ldx), "s"(ldy), "s"(n), "s"(nt), "s"(rg_n), "s"(nib),
+                 "s"(rgc), "s"(she), "s"(n_pairs), "s"(top_k), "s"(n_expert), "s"(kq_n), "s"(wave_quads),
+                 "s"(rg_per_wg));
+  }
+  // The routed ids (when given) are requested first and the level table is built while
+  // they are in flight: the slot, and with it every weight address, waits for them.
+  const int idv = (a.ids != nullptr && lane < a.n_pairs) ? a.ids[lane] : -1;
+  build_pair_table(lut, tid, (int)blockDim.x);
+
   // ---- expert slot and row groups of this workgroup ---------------------------------
   // Slot i takes the i-th expert (ascending id) that has pairs, found in every wave from
   // the routed ids (at most 64 pairs) or the gather's offsets; slots past the routed
@@ -524,7 +559,8 @@ __global__ void __launch_bounds__(512) qmv_grouped_kernel(QmvArgs a) {
   const int64_t slot = blockIdx.x / a.rg_chunks;
   const int64_t rg0 = (blockIdx.x % a.rg_chunks) * a.rg_per_wg;
   const int64_t rg1 = min(rg0 + (int64_t)a.rg_per_wg, a.rg_n);
-  const SlotInfo si = a.ids ? slot_from_ids(a, slot, bm + 32 * wave, lane) : slot_from_offsets(a, slot, lane);
+  const SlotInfo si = a.ids ? slot_from_ids(idv, a.n_expert, slot, bm + 32 * wave, lane)
+                            : slot_from_offsets(a, slot, lane);
   const int64_t e = si.e, seg0 = si.seg0, ncols = si.ncols;
   if (e < 0 || rg0 >= rg1) return;
   const bool sh = a.S0 != nullptr && e == a.shared_e;  // the shared expert, routed to every token by the caller
@@ -711,7 +747,7 @@ __global__ void __launch_bounds__(512) qmv_grouped_kernel(QmvArgs a) {
     if (NRED == 1) __syncthreads();  // the partials are read; the slots can be reused
   };
 
-  // ---- prologue: the columns, then the first row group's weights, the table --------
+  // ---- prologue: the columns, then the first row group's weights ---------------------
   // (the columns first: loads complete in order, so staging them waits for them alone
   // and runs while the weights are in flight)
   WSet wa, wb;
@@ -721,12 +757,6 @@ __global__ void __launch_bounds__(512) qmv_grouped_kernel(QmvArgs a) {
     load_cols(0, (int)ncols);
   }
   load_w(wa, rg0);
-  for (int e = tid; e < 256; e += blockDim.x) {
-    const uint32_t v = bf16_of_level(level_of(e & 15)) | (bf16_of_level(level_of(e >> 4)) << 16);
-    uint4* dst = reinterpret_cast<uint4*>(lut + e * kLutCopies);
-#pragma unroll
-    for (int w4 = 0; w4 < kLutCopies / 4; ++w4) dst[w4] = uint4{v, v, v, v};
-  }
   __syncthreads();  // the table (LDS only: no wait on the loads in flight)
   if (one_pass) store_x((int)ncols);
 
@@ -765,7 +795,7 @@ __global__ void __launch_bounds__(512) qmv_grouped_kernel(QmvArgs a) {
 template <int KQ>
 __global__ void __launch_bounds__(512) qmv_down_tiles_kernel(QmvArgs a) {
   constexpr int NB = 4 * KQ;  // blocks of K
-  __shared__ uint32_t lut[256 * kLutCopies];
+  __shared__ __attribute__((aligned(16))) uint32_t lut[256 * kLutCopies];
   __shared__ __attribute__((aligned(16))) uint8_t xs[NB * kFragBytes + 256];
   __shared__ uint32_t bm[kWaves * 32];  // slot lookup from the ids: a bitmap per wave
 
@@ -773,11 +803,30 @@ __global__ void __launch_bounds__(512) qmv_down_tiles_kernel(QmvArgs a) {
   const int lane = tid & 63, wave = tid >> 6, nwaves = (int)(blockDim.x >> 6);
   const int c = lane & 15, g = lane >> 4;
 
+  // Every kernel argument, loaded at entry (as in the grouped kernel).
+  {
+    const uint8_t *W0 = a.W0, *S0 = a.S0;
+    const float *X = a.x, *GW = a.gate_w;
+    float* Y = a.y;
+    const int32_t *ids = a.ids, *offsets = a.offsets, *pairs = a.pairs;
+    const int64_t wes = a.w_expert_stride, ldx = a.ldx, ldy = a.ldy, n = a.n, nt = a.nt,
+                  nib = a.nibble_bytes, rgc = a.rg_chunks;
+    const int she = a.shared_e, n_pairs = a.n_pairs, n_expert = a.n_expert, rg_per_wg = a.rg_per_wg;
+    asm volatile("" ::"s"(W0), "s"(S0), "s"(X), "s"(GW), "s"(Y), "s"(ids), "s"(offsets), "s"(pairs),
+                 "s"(wes), "s"(ldx), "s"(ldy), "s"(n), "s"(nt), "s"(nib), "s"(rgc), "s"(she), "s"(n_pairs),
+                 "s"(n_expert), "s"(rg_per_wg));
+  }
+  // the routed ids first, the level table while they are in flight
+  const int idv = (a.ids != nullptr && lane < a.n_pairs) ? a.ids[lane] : -1;
+  build_pair_table(lut, tid, (int)blockDim.x);
+  const uint32_t* lutl = lut + (lane & (kLutCopies - 1));
+
   // ---- expert slot (as the grouped kernel) and this workgroup's row tiles ------------
   const int64_t slot = blockIdx.x / a.rg_chunks;
   const int64_t t0 = (blockIdx.x % a.rg_chunks) * a.rg_per_wg;
   const int64_t t1 = min(t0 + (int64_t)a.rg_per_wg, a.nt);
-  const SlotInfo si = a.ids ? slot_from_ids(a, slot, bm + 32 * wave, lane) : slot_from_offsets(a, slot, lane);
+  const SlotInfo si = a.ids ? slot_from_ids(idv, a.n_expert, slot, bm + 32 * wave, lane)
+                            : slot_from_offsets(a, slot, lane);
   const int64_t e = si.e, seg0 = si.seg0, ncols = si.ncols;
   if (e < 0 || t0 >= t1) return;  // uniform over the workgroup
   const uint8_t* W = (a.S0 != nullptr && e == a.shared_e) ? a.S0 : a.W0 + e * a.w_expert_stride;  // shared expert
@@ -812,14 +861,6 @@ __global__ void __launch_bounds__(512) qmv_down_tiles_kernel(QmvArgs a) {
   load_w(wa, min(r0, t1 - 1));
   load_w(wb, min(r0 + nwaves, t1 - 1));
 
-  for (int i = tid; i < 512; i += blockDim.x) {  // level table: entry i / 2, 16 copies each
-    const int le = i >> 1;
-    const uint32_t v = bf16_of_level(level_of(le & 15)) | (bf16_of_level(level_of(le >> 4)) << 16);
-    uint4* dst = reinterpret_cast<uint4*>(lut + le * kLutCopies + (i & 1) * 16);
-#pragma unroll
-    for (int w4 = 0; w4 < 4; ++w4) dst[w4] = uint4{v, v, v, v};
-  }
-  const uint32_t* lutl = lut + (lane & (kLutCopies - 1));
 
   // the pass's columns: h rows seg0 + p0 + t (pair-sorted), their pair ids and gate
   // weights (scalar loads: the lists are not written during the call)

@@ -248,9 +248,10 @@ int iq4_moe_workspace_size(int64_t n_tok, int32_t top_k, int32_t n_expert, int64
  *   G, U      g = Wg_e x_t and u = Wu_e x_t, float32 [P][inter], P = n_tok * top_k,
  *             in pair-sorted order: row i belongs to pair PAIRS[i] (p = t * top_k + j);
  *   H         h = silu(g) * u in the same order: binary16 (IQ4_F16) or float32 (IQ4_F32);
- *   ROWS      the per-slot rows w[t][j] * (Wd_e h), float32 [P][hidden], row p = pair p
- *             (token-major: the (n_tok * top_k, hidden) layout); not written by a call
- *             with IQ4_MOE_ATOMIC_COMBINE.
+ *   ROWS      the per-slot rows w[t][j] * (Wd_e h), [P][hidden], row p = pair p
+ *             (token-major: the (n_tok * top_k, hidden) layout): float32 (IQ4_F32) or
+ *             binary16 (IQ4_F16: the fp32 product rounded to nearest even); not written
+ *             by a call with IQ4_MOE_ATOMIC_COMBINE.
  * shared != 0: the layout of iq4_moe_expert_gemm_shared, whose pairs include the shared
  * expert as slot top_k of every token (P = n_tok * (top_k + 1)).
  * Errors: IQ4_E_ARG (sizes as for the calls).
@@ -279,7 +280,8 @@ int iq4_moe_intermediate_layout(int64_t n_tok, int32_t top_k, int32_t n_expert, 
  *               T-column matvec, an expert's columns 4 at a time; hidden and inter
  *               <= 4096) or IQ4_F16 (prefill path:
  *               grouped GEMM on the matrix cores, weights decoded to f16, fp32
- *               accumulation, h rounded to f16 for the down product).
+ *               accumulation, h rounded to f16 for the down product, each slot row
+ *               w[t][j] * y_tj rounded to f16 and the rows summed in fp32).
  *   ids, w      [n_tok][top_k] int32 / float32 (ids in [0, n_expert), not checked);
  *               1 <= top_k <= min(n_expert, 16), n_expert <= 1024.
  *   w_gate, w_up  n_expert packed inter x hidden matrices, expert e at

@@ -82,7 +82,8 @@ def test_qmv_workspace_rules():
 
 def test_moe_and_gemm_validation():
     ws = iq4.iq4_moe_workspace_size(3256, 8, 128, 2048, 768, iq4.IQ4_F16)
-    assert ws > 3256 * 8 * 2048 * 4
+    assert ws > 3256 * 8 * (2048 + 768) * 2  # binary16 slot rows and h (prefill)
+    assert iq4.iq4_moe_workspace_size(4, 8, 128, 2048, 768, iq4.IQ4_F32) > 4 * 8 * (2048 + 768) * 4  # fp32 (decode)
     rc = _rc("iq4_moe_expert_gemm", FAKE, iq4.IQ4_F16, 16, 2048, FAKE, FAKE, 8, 128, 2048, 768,
              FAKE, FAKE, FAKE, FAKE, 2048, FAKE, 16, 0, None)
     assert rc == iq4.IQ4_E_WORKSPACE

@@ -244,14 +244,26 @@ def test_prefill_batch_invariance(small_bank):
 
 
 def test_prefill_atomic_combine(small_bank):
+    """The atomic combine adds the fp32 slot rows r_j; the ordered combine adds them
+    rounded to binary16.  Elementwise the two differ by at most that rounding, 2^-11 |r_j|
+    per row (2^-25 where r_j is subnormal), plus the two fp32 summations' rounding, at
+    most 2 (k - 1) 2^-24 sum_j |r_j|.  The kept binary16 rows give sum_j |r_j| to within
+    a factor 1 + 2^-11.  Both results are within the f16 tolerance of the oracle."""
     note("moe prefill: atomic combine")
     B = small_bank
     rng = np.random.default_rng(8)
-    ids, w = routing(rng, 150, B["E"], 3)
-    x = rng.standard_normal((150, B["H"])).astype(np.float16)
+    n_tok, k = 150, 3
+    ids, w = routing(rng, n_tok, B["E"], k)
+    x = rng.standard_normal((n_tok, B["H"])).astype(np.float16)
     det, _ = run_moe(x, ids, w, B["banks"], B["H"], B["I"], B["E"])
     atom, _ = run_moe(x, ids, w, B["banks"], B["H"], B["I"], B["E"], flags=iq4.IQ4_MOE_ATOMIC_COMBINE)
-    assert normwise(atom, det) <= 1e-5
+    kept_out, r = run_moe_keep(x, ids, w, B["banks"], B["H"], B["I"], B["E"])
+    assert bits_equal(kept_out, det)
+    row_abs = np.abs(r["rows"].astype(np.float64)).reshape(n_tok, k, B["H"]).sum(axis=1) * (1 + 2.0 ** -11)
+    bound = 2.0 ** -11 * row_abs + 2 * (k - 1) * 2.0 ** -24 * row_abs + k * 2.0 ** -25
+    assert np.all(np.abs(atom.astype(np.float64) - det) <= bound)
+    ref = oracle.moe(x, ids, w, B["gate"], B["up"], B["down"], B["H"], B["I"])
+    assert normwise(atom, ref) <= 5e-3 and normwise(det, ref) <= 5e-3
 
 
 def test_prefill_deterministic(small_bank):
@@ -370,7 +382,7 @@ def run_moe_keep(x, ids, w, banks, H, I, E, dtype="f16"):
          "offsets": region("offsets", E + 1, np.int32, (E + 1,)),
          "g": region("g", P * I, np.float32, (P, I)), "u": region("u", P * I, np.float32, (P, I)),
          "h": region("h", P * I, np.float16 if f16 else np.float32, (P, I)),
-         "rows": region("rows", P * H, np.float32, (P, H))}
+         "rows": region("rows", P * H, np.float16 if f16 else np.float32, (P, H))}
     return host(out), r
 
 
@@ -393,8 +405,15 @@ def check_kept(x, ids, w, blocks, H, I, E, out, r, dtype):
     assert normwise(r["h"].astype(np.float64), h[rp]) <= (5e-3 if dtype == "f16" else 1e-3)
     ref_out, y = oracle.moe(x, ids, w, gate, up, down, H, I, return_pair_rows=True)
     rows_ref = (np.asarray(w, dtype=np.float64)[:, :, None] * y).reshape(P, H)
-    assert normwise(r["rows"], rows_ref) <= (5e-3 if dtype == "f16" else 1e-3)
+    assert normwise(r["rows"].astype(np.float64), rows_ref) <= (5e-3 if dtype == "f16" else 1e-3)
     assert normwise(out, ref_out) <= (5e-3 if dtype == "f16" else 1e-3)
+    # the output is the kept rows (binary16 for the prefill, widened exactly) added in
+    # fp32 in slot order, bit for bit
+    rows = r["rows"].astype(np.float32).reshape(ids.shape[0], ids.shape[1], H)
+    acc = rows[:, 0].copy()
+    for j in range(1, ids.shape[1]):
+        acc = (acc + rows[:, j]).astype(np.float32)
+    assert bits_equal(out, acc), "combine"
 
 
 def test_keep_intermediate_prefill_full_size_integer_exact():
