@@ -174,6 +174,13 @@ constexpr int kFragRows = 12;
 constexpr int kFragStride = 13;
 static_assert(kFragStride > kFragRows, "a slot holds its rows");
 constexpr int kFragBytes = 4 * kFragStride * 16;  // 832 B per block
+// The grouped kernel's fragment store puts a column's parts in consecutive rows:
+// [block][k-group g][row 4t+s], 16 rows of 16 B per slot (rows 4t+3 unused), so that
+// MFMA output lane (g, c) receives column g's three parts in its four entries and adds
+// them in-lane.  Staging stores meet bank conflicts (all slots start on the same bank);
+// they run once per pass.
+constexpr int kGSlot = 16 * 16;           // one (block, k-group) slot: 16 rows of 16 B
+constexpr int kGFragBytes = 4 * kGSlot;   // 1 KiB per block
 
 // Exact three-way bf16 split of two values, packed per part: word s holds part s of v0
 // in its low and of v1 in its high half.  Part 0 (hi) is the top 16 bits of v; part 1
@@ -199,10 +206,11 @@ __device__ __forceinline__ void split_pair(float v0, float v1, uint32_t out[3]) 
 constexpr int kLutCopies = 32;
 
 // The level table of the grouped kernels: entry e (0..255) holds the bf16 levels of its
-// two nibbles (low nibble in the low half), kLutCopies copies side by side.  Consecutive
+// two nibbles (low nibble in the low half), LC copies side by side.  Consecutive
 // threads write consecutive 16-byte pieces, so the stores meet no bank conflict.
+template <int LC = kLutCopies>
 __device__ __forceinline__ void build_pair_table(uint32_t* lut, int tid, int nthreads) {
-  constexpr int PER = kLutCopies / 4;  // 16-byte pieces per entry
+  constexpr int PER = LC / 4;  // 16-byte pieces per entry
   uint4* dst = reinterpret_cast<uint4*>(lut);
   for (int q = tid; q < 256 * PER; q += nthreads) {
     const int e = q / PER;
@@ -509,25 +517,40 @@ __global__ void __launch_bounds__(64 * kDenseWaves) qmv_dense_kernel(QmvArgs a) 
 
 // ---------------------------------------------------------------------------------
 // Grouped matvec (MoE decode): one workgroup per (routed expert slot, run of row groups).
-// It finds its expert and stages the expert's columns once, then walks its row groups,
-// loading the next group's weights while the current one is multiplied and reduced
-// (two register sets).  Per output the arithmetic is the dense kernel's: the same plan
-// (a function of K only), block order, wave order and part order.
+// It finds its expert and stages the expert's columns, then walks its row groups,
+// loading the next group's weights while the current one is multiplied (two register
+// sets).  Each wave adds its three parts in-wave ((hi + mid) + lo, per column) and
+// leaves the group's partial sums in LDS without waiting for the other waves; once a
+// batch of up to GB groups is done, one barrier, and the workgroup adds the waves'
+// partials in wave order and applies the mode's epilogue.  A column's arithmetic is a
+// function of K and the plan only (the T-column invariance).
 template <int MODE, int RG, int WQ>
 __global__ void __launch_bounds__(512) qmv_grouped_kernel(QmvArgs a) {
   constexpr int NMAT = (MODE == kQmvGateUp) ? 2 : 1;
   constexpr int ROWS = RG * kTileRows;
-  constexpr int XBYTES = kWaves * WQ * 4 * kFragBytes;
-  constexpr int REDN = kWaves * NMAT * RG * 64;  // one f32x4 partial per (wave, matrix, tile, lane)
-  __shared__ __attribute__((aligned(16))) uint32_t lut[256 * kLutCopies];
-  __shared__ __attribute__((aligned(16))) uint8_t xs[XBYTES + 256];  // + room for padding-row reads
-  // two reduction buffers where they fit (a buffer is then reused two calls later)
-  constexpr int NRED = (XBYTES + 256 + 256 * kLutCopies * 4 + 2 * REDN * 16 + kWaves * 32 * 4 <= 160 * 1024) ? 2 : 1;
-  __shared__ f32x4 red[NRED * REDN];
-  __shared__ uint32_t bm[kWaves * 32];  // slot lookup from the ids: a bitmap per wave
+  constexpr int XBYTES = kWaves * WQ * 4 * kGFragBytes;
+  // table copies: 64 (every lane its own copy, and the lookup address is one byte
+  // permute: index byte in bits 8..15, the lane's copy in bits 0..7) where the LDS has
+  // room; 32 for 3 quads per wave, 16 for 4 (a staged K of 4,096)
+  constexpr int LC = (WQ <= 2) ? 64 : (WQ == 3) ? 32 : 16;
+  // partials of one row group: [wave][matrix][tile][column][row], fp32
+  constexpr int SLOT = kWaves * NMAT * RG * kCols * kTileRows;
+  constexpr int OTHER = 256 * LC * 4 + XBYTES + 256 + kWaves * 32 * 4;
+  constexpr int GB_FIT = (160 * 1024 - OTHER) / (SLOT * 4);
+  constexpr int GB = GB_FIT >= 8 ? 8 : (GB_FIT & ~1);  // row groups per batch (even)
+  static_assert(GB >= 2, "two row groups' partials fit the LDS");
+  // one LDS block: the table at offset 0 (its lookup address then needs no base), the
+  // staged columns (+ room for padding-row reads), the partials, the slot bitmaps
+  constexpr int XOFF = 256 * LC * 4, POFF = XOFF + XBYTES + 256, BOFF = POFF + GB * SLOT * 4;
+  __shared__ __attribute__((aligned(256))) uint8_t smem[BOFF + kWaves * 32 * 4];
+  uint32_t* const lut = reinterpret_cast<uint32_t*>(smem);
+  uint8_t* const xs = smem + XOFF;
+  float* const part = reinterpret_cast<float*>(smem + POFF);
+  uint32_t* const bm = reinterpret_cast<uint32_t*>(smem + BOFF);  // slot lookup: a bitmap per wave
 
   const int tid = threadIdx.x;
-  const int lane = tid & 63, wave = tid >> 6, nwaves = (int)(blockDim.x >> 6);
+  // the wave index as a scalar: per-wave addresses are then computed once, in SGPRs
+  const int lane = tid & 63, wave = __builtin_amdgcn_readfirstlane(tid >> 6), nwaves = (int)(blockDim.x >> 6);
   const int c = lane & 15, g = lane >> 4;
 
   // Every kernel argument this kernel reads, loaded at entry.  Left to itself the
@@ -550,7 +573,7 @@ __global__ void __launch_bounds__(512) qmv_grouped_kernel(QmvArgs a) {
   // The routed ids (when given) are requested first and the level table is built while
   // they are in flight: the slot, and with it every weight address, waits for them.
   const int idv = (a.ids != nullptr && lane < a.n_pairs) ? a.ids[lane] : -1;
-  build_pair_table(lut, tid, (int)blockDim.x);
+  build_pair_table<LC>(lut, tid, (int)blockDim.x);
 
   // ---- expert slot and row groups of this workgroup ---------------------------------
   // Slot i takes the i-th expert (ascending id) that has pairs, found in every wave from
@@ -571,9 +594,20 @@ __global__ void __launch_bounds__(512) qmv_grouped_kernel(QmvArgs a) {
 
   // ---- this wave's activations (blocks [4 wq0, 4 wq1)), staged by the wave itself ----
   const int wblk = 4 * (wq1 - wq0);
-  uint8_t* xw = xs + wave * (4 * WQ) * kFragBytes;
+  uint8_t* xw = xs + wave * (4 * WQ) * kGFragBytes;
   constexpr int SLOTS = 16 * WQ;  // staging tasks: (t, bl, gg) = task (t SLOTS + 4 bl + gg)
-  const uint32_t* lutl = lut + (lane & (kLutCopies - 1));  // this lane's table copy
+  const uint32_t* lutl = lut + (lane & (LC - 1));  // this lane's table copy
+  typedef __attribute__((address_space(3))) const uint8_t lds_u8;
+  lds_u8* const lutb = (lds_u8*)(__attribute__((address_space(3))) uint8_t*)lut;
+  const uint32_t lane_copy = (uint32_t)lane * 4u;
+  // entry `byte b of w` in this lane's copy
+  auto lookup = [&](uint32_t w, int b) -> uint32_t {
+    if (LC == 64) {
+      const uint32_t addr = __builtin_amdgcn_perm(lane_copy, w, 0x0c0c0004u | ((uint32_t)b << 8));
+      return *reinterpret_cast<__attribute__((address_space(3))) const uint32_t*>(lutb + addr);
+    }
+    return lutl[((w >> (8 * b)) & 0xFF) * LC];
+  };
   float4 xr[WQ][2];
   auto load_x = [&](int64_t t0, int T) {  // tasks (column t, block, k-group gg), 64 lanes
     const float* col[kCols];
@@ -603,10 +637,10 @@ __global__ void __launch_bounds__(512) qmv_grouped_kernel(QmvArgs a) {
         split_pair(xa.z, xa.w, p1);
         split_pair(xb.x, xb.y, p2);
         split_pair(xb.z, xb.w, p3);
-        uint8_t* dst = xw + (bl * 4 + gg) * (kFragStride * 16) + t * 16;
+        uint8_t* dst = xw + (bl * 4 + gg) * kGSlot + t * 64;  // rows 4t + s
 #pragma unroll
         for (int sp = 0; sp < 3; ++sp)
-          *reinterpret_cast<uint4*>(dst + sp * 4 * 16) = uint4{p0[sp], p1[sp], p2[sp], p3[sp]};
+          *reinterpret_cast<uint4*>(dst + sp * 16) = uint4{p0[sp], p1[sp], p2[sp], p3[sp]};
       }
     }
     // LDS accesses of one wave execute in order: the wave's reads below see these
@@ -651,12 +685,14 @@ __global__ void __launch_bounds__(512) qmv_grouped_kernel(QmvArgs a) {
       }
   };
   // the wave's quads, one block at a time; lanes of padding rows (s = 3 or a column
-  // >= T) read whatever lies there: an MFMA output row depends on its own A row only
-  auto multiply = [&](const WSet& ws, f32x4 (&acc)[NMAT][RG]) {
+  // >= T) read whatever lies there: an MFMA output row depends on its own A row only.
+  // Lane (g, c) gets D[4g + s][c], part s of column g for weight row c: per block it
+  // adds the parts, (hi + mid) + lo, and accumulates d times that sum.
+  auto multiply = [&](const WSet& ws, float (&acc)[NMAT][RG]) {
 #pragma unroll
     for (int m = 0; m < NMAT; ++m)
 #pragma unroll
-      for (int r = 0; r < RG; ++r) acc[m][r] = f32x4{0.f, 0.f, 0.f, 0.f};
+      for (int r = 0; r < RG; ++r) acc[m][r] = 0.f;
 #pragma unroll
     for (int u = 0; u < WQ; ++u) {
       if (wq0 + u >= wq1) break;
@@ -664,7 +700,7 @@ __global__ void __launch_bounds__(512) qmv_grouped_kernel(QmvArgs a) {
 #pragma unroll
       for (int j = 0; j < 4; ++j) {
         const int bl = 4 * u + j;
-        const u32x4 xf = *reinterpret_cast<const u32x4*>(xw + (bl * 4 + g) * (kFragStride * 16) + c * 16);
+        const u32x4 xf = *reinterpret_cast<const u32x4*>(xw + (bl * 4 + g) * kGSlot + c * 16);
         u32x4 bf[NMAT][RG];
 #pragma unroll
         for (int m = 0; m < NMAT; ++m)
@@ -672,10 +708,8 @@ __global__ void __launch_bounds__(512) qmv_grouped_kernel(QmvArgs a) {
           for (int r = 0; r < RG; ++r) {
             const uint4 nb = ws.nib[u][m][r];
             const uint32_t w = (j == 0) ? nb.x : (j == 1) ? nb.y : (j == 2) ? nb.z : nb.w;
-            bf[m][r][0] = lutl[(w & 0xFF) * kLutCopies];
-            bf[m][r][1] = lutl[((w >> 8) & 0xFF) * kLutCopies];
-            bf[m][r][2] = lutl[((w >> 16) & 0xFF) * kLutCopies];
-            bf[m][r][3] = lutl[(w >> 24) * kLutCopies];
+#pragma unroll
+            for (int b = 0; b < 4; ++b) bf[m][r][b] = lookup(w, b);
           }
 #pragma unroll
         for (int m = 0; m < NMAT; ++m)
@@ -685,48 +719,41 @@ __global__ void __launch_bounds__(512) qmv_grouped_kernel(QmvArgs a) {
             const uint2 sc = ws.scl[u][m][r];
             const uint32_t sw = (j < 2) ? sc.x : sc.y;
             const float d = h2f((uint16_t)(sw >> (16 * (j & 1))));
-#pragma unroll
-            for (int i = 0; i < 4; ++i) acc[m][r][i] = __builtin_fmaf(d, pr[i], acc[m][r][i]);
+            acc[m][r] = __builtin_fmaf(d, (pr[0] + pr[1]) + pr[2], acc[m][r]);
           }
       }
     }
   };
-  // reduction over the waves' K runs, then the three parts, then the mode's epilogue.
-  // Lane (g, c) holds D[4g + i][c]: part s = g, column i, weight row c.
-  int rbuf = 0;  // the reduction buffer of the next call
-  auto reduce_store = [&](int64_t rg, int64_t t0, int T, const f32x4 (&acc)[NMAT][RG]) {
+  // A group's partials: lane (g, c) holds column g's sum for weight row c.
+  auto write_part = [&](int gi, int T, const float (&acc)[NMAT][RG]) {
 #pragma unroll
     for (int m = 0; m < NMAT; ++m)
 #pragma unroll
-      for (int r = 0; r < RG; ++r) red[rbuf * REDN + ((wave * NMAT + m) * RG + r) * 64 + lane] = acc[m][r];
-    __syncthreads();
-    const float* redf = reinterpret_cast<const float*>(red + rbuf * REDN);
-    if (NRED == 2) rbuf ^= 1;
-    const int nout = T * ROWS;
+      for (int r = 0; r < RG; ++r)
+        if (g < T) part[(((gi * kWaves + wave) * NMAT + m) * RG + r) * (kCols * kTileRows) + g * kTileRows + c] = acc[m][r];
+  };
+  // A batch's outputs: the waves' partials added in wave order, then the epilogue.
+  auto reduce_batch = [&](int64_t b0, int nb, int64_t t0, int T) {
+    const int per_group = T * ROWS;
+    const int nout = nb * per_group;
     for (int idx0 = 0; idx0 < nout; idx0 += (int)blockDim.x) {  // uniform trip count
       const int idx = idx0 + tid;
-      const int t = idx / ROWS, rr = idx % ROWS;
+      const int gi = idx / per_group, rem = idx % per_group;
+      const int t = rem / ROWS, rr = rem % ROWS;
       const int r = rr >> 4, row = rr & 15;
-      const int64_t col = rg * ROWS + rr;  // output row index (weight row)
+      const int64_t col = (b0 + gi) * ROWS + rr;  // output row index (weight row)
       if (idx < nout && col < a.n) {
         float v[NMAT];
 #pragma unroll
         for (int m = 0; m < NMAT; ++m) {
-          float pv[3][kWaves];  // every slot read at once (absent waves' slots unused)
+          float pv[kWaves];  // every slot read at once (absent waves' slots unused)
 #pragma unroll
-          for (int p = 0; p < 3; ++p)
+          for (int w2 = 0; w2 < kWaves; ++w2)
+            pv[w2] = part[(((gi * kWaves + w2) * NMAT + m) * RG + r) * (kCols * kTileRows) + t * kTileRows + row];
+          float sum = pv[0];
 #pragma unroll
-            for (int w2 = 0; w2 < kWaves; ++w2)
-              pv[p][w2] = redf[(((w2 * NMAT + m) * RG + r) * 64 + 16 * p + row) * 4 + t];
-          float part[3];
-#pragma unroll
-          for (int p = 0; p < 3; ++p) {
-            float sum = pv[p][0];
-#pragma unroll
-            for (int w2 = 1; w2 < kWaves; ++w2) sum = (w2 < nwaves) ? sum + pv[p][w2] : sum;
-            part[p] = sum;
-          }
-          v[m] = (part[0] + part[1]) + part[2];
+          for (int w2 = 1; w2 < kWaves; ++w2) sum = (w2 < nwaves) ? sum + pv[w2] : sum;
+          v[m] = sum;
         }
         if (MODE == kQmvGateUp) {
           const float gv = v[0], uv = v[NMAT - 1];
@@ -742,46 +769,52 @@ __global__ void __launch_bounds__(512) qmv_grouped_kernel(QmvArgs a) {
         }
       }
     }
-    // with two buffers the next call writes the other one, and this one is written again
-    // only after the next call's barrier, which every wave passes after its reads
-    if (NRED == 1) __syncthreads();  // the partials are read; the slots can be reused
   };
 
-  // ---- prologue: the columns, then the first row group's weights ---------------------
+  // ---- prologue: the first pass's columns, then the first row group's weights --------
   // (the columns first: loads complete in order, so staging them waits for them alone
   // and runs while the weights are in flight)
   WSet wa, wb;
-  const bool one_pass = ncols <= kCols;
-  if (one_pass) {
-    load_x(0, (int)ncols);
-    load_cols(0, (int)ncols);
-  }
+  const int T0 = (int)min((int64_t)kCols, ncols);
+  load_x(0, T0);
+  load_cols(0, T0);
   load_w(wa, rg0);
   __syncthreads();  // the table (LDS only: no wait on the loads in flight)
-  if (one_pass) store_x((int)ncols);
+  store_x(T0);
 
   // Every step requests the next group's weights (in flight during this group's work);
   // the last group requests itself again (an L2 hit).  With the same loads issued on
   // every path the compiler's waits for `cur` count exactly past them: issued under a
   // branch, the waits merged from both paths also waited for the next group's loads,
   // and each group's work waited for the next group's weights.
-  auto step = [&](const WSet& cur, WSet& nxt, int64_t rg) {
+  auto step = [&](const WSet& cur, WSet& nxt, int64_t rg, int64_t b0, int T) {
     load_w(nxt, min(rg + 1, rg1 - 1));
-    for (int64_t t0 = 0; t0 < ncols; t0 += kCols) {
-      const int T = (int)min((int64_t)kCols, ncols - t0);
-      if (!one_pass) {  // more than kCols columns: stage each pass (rare in decode)
-        load_x(t0, T);
-        load_cols(t0, T);
-        store_x(T);
-      }
-      f32x4 acc[NMAT][RG];
-      multiply(cur, acc);
-      reduce_store(rg, t0, T, acc);
-    }
+    float acc[NMAT][RG];
+    multiply(cur, acc);
+    write_part((int)(rg - b0), T, acc);
   };
-  for (int64_t rg = rg0; rg < rg1; rg += 2) {
-    step(wa, wb, rg);
-    step(wb, wa, min(rg + 1, rg1 - 1));  // an odd count repeats its last group (same values)
+  // Passes of up to kCols columns (more than one only past 4 pairs per expert); each
+  // walks the row groups in batches of GB.  Batches other than a pass's last hold an
+  // even count, so the steps go in pairs and only the last group of the range can be
+  // repeated (same weights, same slot, same values).
+  for (int64_t t0 = 0; t0 < ncols; t0 += kCols) {
+    const int T = (int)min((int64_t)kCols, ncols - t0);
+    if (t0 > 0) {  // the wave's own staging region: no barrier needed
+      load_x(t0, T);
+      load_cols(t0, T);
+      load_w(wa, rg0);
+      store_x(T);
+    }
+    for (int64_t b0 = rg0; b0 < rg1; b0 += GB) {
+      const int64_t b1 = min(b0 + (int64_t)GB, rg1);
+      for (int64_t rg = b0; rg < b1; rg += 2) {
+        step(wa, wb, rg, b0, T);
+        step(wb, wa, min(rg + 1, b1 - 1), b0, T);
+      }
+      __syncthreads();  // every wave's partials of the batch
+      reduce_batch(b0, (int)(b1 - b0), t0, T);
+      if (b1 < rg1 || t0 + kCols < ncols) __syncthreads();  // the slots are written again
+    }
   }
 }
 
