@@ -596,6 +596,14 @@ __global__ void __launch_bounds__(512) qmv_grouped_kernel(QmvArgs a) {
   const int wblk = 4 * (wq1 - wq0);
   uint8_t* xw = xs + wave * (4 * WQ) * kGFragBytes;
   constexpr int SLOTS = 16 * WQ;  // staging tasks: (t, bl, gg) = task (t SLOTS + 4 bl + gg)
+  // the lane's A fragments, read back once per pass and kept in registers for all row
+  // groups (up to 2 quads per wave; with more the registers run out and every group
+  // reads them from LDS)
+  constexpr bool XREG = WQ <= 2;
+  u32x4 xf[XREG ? 4 * WQ : 1];
+  auto frag = [&](int bl) -> u32x4 {
+    return *reinterpret_cast<const u32x4*>(xw + (min(bl, wblk - 1) * 4 + g) * kGSlot + c * 16);
+  };
   const uint32_t* lutl = lut + (lane & (LC - 1));  // this lane's table copy
   typedef __attribute__((address_space(3))) const uint8_t lds_u8;
   lds_u8* const lutb = (lds_u8*)(__attribute__((address_space(3))) uint8_t*)lut;
@@ -648,6 +656,10 @@ __global__ void __launch_bounds__(512) qmv_grouped_kernel(QmvArgs a) {
     __builtin_amdgcn_fence(__ATOMIC_RELEASE, "wavefront");
     __builtin_amdgcn_wave_barrier();
     __builtin_amdgcn_fence(__ATOMIC_ACQUIRE, "wavefront");
+    if (XREG) {
+#pragma unroll
+      for (int bl = 0; bl < 4 * WQ; ++bl) xf[bl] = frag(bl);
+    }
   };
   // DOWN: each column's pair id and gate weight (scalar loads through the constant
   // address space: the lists are not written during the call)
@@ -700,7 +712,6 @@ __global__ void __launch_bounds__(512) qmv_grouped_kernel(QmvArgs a) {
 #pragma unroll
       for (int j = 0; j < 4; ++j) {
         const int bl = 4 * u + j;
-        const u32x4 xf = *reinterpret_cast<const u32x4*>(xw + (bl * 4 + g) * kGSlot + c * 16);
         u32x4 bf[NMAT][RG];
 #pragma unroll
         for (int m = 0; m < NMAT; ++m)
@@ -715,7 +726,7 @@ __global__ void __launch_bounds__(512) qmv_grouped_kernel(QmvArgs a) {
         for (int m = 0; m < NMAT; ++m)
 #pragma unroll
           for (int r = 0; r < RG; ++r) {
-            const f32x4 pr = mfma_bf16(xf, bf[m][r], f32x4{0.f, 0.f, 0.f, 0.f});
+            const f32x4 pr = mfma_bf16(XREG ? xf[bl] : frag(bl), bf[m][r], f32x4{0.f, 0.f, 0.f, 0.f});
             const uint2 sc = ws.scl[u][m][r];
             const uint32_t sw = (j < 2) ? sc.x : sc.y;
             const float d = h2f((uint16_t)(sw >> (16 * (j & 1))));
