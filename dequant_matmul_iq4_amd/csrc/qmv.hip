@@ -574,6 +574,7 @@ __global__ void __launch_bounds__(512) qmv_grouped_kernel(QmvArgs a) {
   // they are in flight: the slot, and with it every weight address, waits for them.
   const int idv = (a.ids != nullptr && lane < a.n_pairs) ? a.ids[lane] : -1;
   build_pair_table<LC>(lut, tid, (int)blockDim.x);
+  asm volatile("" ::"v"(idv));  // the ids' wait here, on every path (as in the down kernel)
 
   // ---- expert slot and row groups of this workgroup ---------------------------------
   // Slot i takes the i-th expert (ascending id) that has pairs, found in every wave from
@@ -864,6 +865,10 @@ __global__ void __launch_bounds__(512) qmv_down_tiles_kernel(QmvArgs a) {
   const int idv = (a.ids != nullptr && lane < a.n_pairs) ? a.ids[lane] : -1;
   build_pair_table(lut, tid, (int)blockDim.x);
   const uint32_t* lutl = lut + (lane & (kLutCopies - 1));
+  // the ids' wait here, on every path: left to a later reuse of its register, the
+  // compiler's merged wait there also waited for the columns requested after it, and
+  // the weight requests went out only once the columns had arrived
+  asm volatile("" ::"v"(idv));
 
   // ---- expert slot (as the grouped kernel) and this workgroup's row tiles ------------
   const int64_t slot = blockIdx.x / a.rg_chunks;
