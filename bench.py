@@ -51,14 +51,14 @@ N_BANKS = 8                 # expert banks the decode step rotates over
 # at the time: a kernel changed since then reports traffic null.  Commands and raw
 # figures: profiles/<name>.txt.
 MEASURED_TRAFFIC = {
-    "dequant_staged_4096x4096_f16": (43014176, "b7a9db4683211408", ("format.hip", "common.hpp")),
-    "qmv_dense_4096x4096_T1-4": (9929739, "f14631106fc06a90", ("qmv.hip", "qmv.hpp", "common.hpp")),
-    "qmv_q8_4096x4096_T1-4": (9672483, "f14631106fc06a90", ("qmv.hip", "qmv.hpp", "common.hpp")),
-    "qmv_grouped_gateup_moe_decode_4tok": (55509919, "f14631106fc06a90", ("qmv.hip", "qmv.hpp", "common.hpp")),
-    "qmv_down_moe_decode_4tok": (28738823, "f14631106fc06a90", ("qmv.hip", "qmv.hpp", "common.hpp")),
-    "qgemm_gateup_moe_prefill_3256tok": (588766084, "a2bf14d3011a2459", ("gemm.hip", "gemm.hpp", "common.hpp")),
-    "qgemm_down_moe_prefill_3256tok": (507669300, "a2bf14d3011a2459", ("gemm.hip", "gemm.hpp", "common.hpp")),
-    "qgemm_dense_13056x4096x14336_chunk512": (94965099, "a2bf14d3011a2459", ("gemm.hip", "gemm.hpp", "common.hpp")),
+    "dequant_staged_4096x4096_f16": (43014226, "b7a9db4683211408", ("format.hip", "common.hpp")),
+    "qmv_dense_4096x4096_T1-4": (9928746, "d188ea4bd290b573", ("qmv.hip", "qmv.hpp", "common.hpp")),
+    "qmv_q8_4096x4096_T1-4": (9674048, "d188ea4bd290b573", ("qmv.hip", "qmv.hpp", "common.hpp")),
+    "qmv_grouped_gateup_moe_decode_4tok": (55434765, "d188ea4bd290b573", ("qmv.hip", "qmv.hpp", "common.hpp")),
+    "qmv_down_moe_decode_4tok": (28727809, "d188ea4bd290b573", ("qmv.hip", "qmv.hpp", "common.hpp")),
+    "qgemm_gateup_moe_prefill_3256tok": (589542843, "1abc4fb091a45333", ("gemm.hip", "gemm.hpp", "common.hpp")),
+    "qgemm_down_moe_prefill_3256tok": (400079717, "1abc4fb091a45333", ("gemm.hip", "gemm.hpp", "common.hpp")),
+    "qgemm_dense_13056x4096x14336_chunk512": (94965258, "1abc4fb091a45333", ("gemm.hip", "gemm.hpp", "common.hpp")),
 }
 
 
