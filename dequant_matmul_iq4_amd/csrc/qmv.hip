@@ -64,9 +64,6 @@ constexpr int kDenseRG = 1;            // row tiles per workgroup (dense)
 constexpr int kGateUpRG = 1;           // row tiles per matrix (gate + up)
 constexpr int kDownRG = 2;             // row tiles per workgroup (down)
 
-__device__ __forceinline__ uint32_t bf16_of_level(int c) {
-  return __float_as_uint((float)c) >> 16;  // exact: |c| <= 127
-}
 
 // The expert of a grouped workgroup's slot: slot i takes the i-th smallest expert id that
 // has routed pairs.  seg0 = its first position in the pair list sorted by (expert, pair
@@ -254,23 +251,6 @@ constexpr int kDenseLutCopies = 64;
 constexpr int kDenseLutBytes = 256 * kDenseLutCopies * 4;  // 64 KiB
 constexpr int kDenseSlot = 9 * 16;                         // 8 rows + 1 row of padding
 constexpr int kDenseBlockStage = 4 * kDenseSlot;           // 576 B per block
-
-// hi and lo parts of two values, packed per part: hi = (bf16(v0), bf16(v1)), lo likewise
-// for the residuals.  The residual v - hi is formed by a bf16 dot product whose only
-// non-zero term is -1 * hi (fused with v, rounded once): exact, since v - hi is
-// representable.
-// The two constants (-1, 0) and (0, -1) are passed in scalar registers: as an inline
-// constant, a packed bf16 operand's halves are not placed unambiguously.
-__device__ __forceinline__ void split_hi_lo(float v0, float v1, uint32_t& hi, uint32_t& lo) {
-  const bf16x2 h = {(__bf16)v0, (__bf16)v1};
-  uint32_t k_lo = 0x0000BF80u, k_hi = 0xBF800000u;  // (-1, 0) and (0, -1) as bf16 pairs
-  asm("" : "+s"(k_lo), "+s"(k_hi));                  // opaque: kept in registers
-  const float r0 = __builtin_amdgcn_fdot2_f32_bf16(h, __builtin_bit_cast(bf16x2, k_lo), v0, false);
-  const float r1 = __builtin_amdgcn_fdot2_f32_bf16(h, __builtin_bit_cast(bf16x2, k_hi), v1, false);
-  const bf16x2 l = {(__bf16)r0, (__bf16)r1};
-  hi = __builtin_bit_cast(uint32_t, h);
-  lo = __builtin_bit_cast(uint32_t, l);
-}
 
 // bf16 bit pattern of codebook level q (exact: |level| <= 127)
 __device__ __forceinline__ uint32_t bf16_level(uint32_t q) { return bf16_of_level(level_of(q)); }

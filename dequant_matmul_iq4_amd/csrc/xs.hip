@@ -28,6 +28,11 @@ constexpr int kXsBytes = 136;
 constexpr int kXsChunks = 16;           // chunks per super-block
 constexpr int kXsMaxWaves = 8;          // the matvec's workgroup covers K in <= 8 waves
 
+template <int N>
+struct ColsXs {  // a column count as a type (compile-time pass width)
+  static constexpr int value = N;
+};
+
 // d * (ls_i - 32) from the super-block's first 8 bytes (lo = bytes 0-3, hi = bytes 4-7).
 __device__ __forceinline__ float xs_subscale(uint32_t lo, uint32_t hi, int i) {
   const uint32_t ls = ((hi >> (4 * i)) & 0xFu) | (((lo >> (16 + 2 * i)) & 0x3u) << 4);
@@ -228,6 +233,266 @@ __global__ void __launch_bounds__(64 * kXsMaxWaves) xs_qmv_kernel(XsQmvArgs a) {
 }
 
 // ---------------------------------------------------------------------------------
+// T-column matvec on the matrix cores (K up to 24 super-blocks), the dense matvec's
+// scheme on the raw super-blocks: one workgroup per 16 rows, all of K; each of up to NWV
+// waves (8, or 4 so that two workgroups share a CU when there are more row tiles than
+// CUs) owns a run of WS super-blocks.  A sub-block (32 weights, one scale d (ls - 32))
+// is one v_mfma_f32_16x16x32_bf16:
+//   B  lane (g, c) needs index bytes 4g .. 4g+3 of row c's sub-block: byte 4g + j holds
+//      elements 4g + j (low nibble) and 4g + j + 16 (high), which a byte-indexed level
+//      table turns into the bf16 pair at MFMA k = 8g + 2j, 8g + 2j + 1;
+//   A  the activations in the same k order: each fp32 x goes in as two bf16 parts, hi =
+//      bf16(x) and lo = bf16(x - hi) (x to within 2^-18 |x|), rows 4s + t of the operand
+//      (s = 0 hi, 1 lo; t the column within a pass of 4), staged in LDS per wave;
+//   the product, exact per term, is scaled by the sub-block scale (exact in fp32) with
+//   one FMA per column; the waves' sums are added in wave order, hi parts and lo parts
+//   apart, then hi + lo.  A column's arithmetic depends on K only, not on T.
+constexpr int kXmWaves = 8;               // waves per workgroup, at most
+constexpr int kXmSlot = 9 * 16;          // 8 rows of 16 B + 1 of padding (staging banks)
+constexpr int kXmSubStage = 4 * kXmSlot;  // one sub-block's A operand: 576 B
+constexpr int kXmMaxWS = 3;              // super-blocks per wave (K <= 24 super-blocks)
+
+template <int WS, int NWV>
+struct XmShape {
+  static constexpr int kStage = NWV * WS * 8 * kXmSubStage;
+  static constexpr int kRed = NWV * 64 * 16;
+  static constexpr int kBudget = (NWV == 4 ? 80 : 160) * 1024;  // 4 waves: two workgroups per CU
+  // table copies: 64 (each lane its own; the lookup address is one byte permute) where
+  // the LDS has room, else 32 or 16
+  static constexpr int kLC = (256 * 64 * 4 + kStage + kRed <= kBudget)   ? 64
+                             : (256 * 32 * 4 + kStage + kRed <= kBudget) ? 32
+                                                                         : 16;
+  static constexpr int kLutBytes = 256 * kLC * 4;
+  static_assert(kLutBytes + kStage + kRed <= kBudget, "LDS budget");
+};
+
+struct XmArgs {
+  const uint8_t* W;
+  const float* X;
+  float* Y;
+  int64_t n, ldx, ldy, row_bytes;
+  int T, nsb;  // columns; super-blocks per row
+  int ws;      // super-blocks per wave (the template's WS)
+};
+
+// (4 waves: registers for two workgroups per CU, i.e. two waves per SIMD)
+template <int WS, int NWV, int TP>
+__global__ void __launch_bounds__(64 * NWV, NWV == 4 ? 2 : 1) xs_qmv_mfma_kernel(XmArgs a) {
+  using S = XmShape<WS, NWV>;
+  constexpr int LC = S::kLC;
+  __shared__ __attribute__((aligned(256))) uint8_t smem[S::kLutBytes + S::kStage + S::kRed];
+  // every kernel argument at entry (one scalar wait)
+  const uint8_t* const W = a.W;
+  const float* const X = a.X;
+  float* const Y = a.Y;
+  const int64_t n = a.n, ldx = a.ldx, ldy = a.ldy, row_bytes = a.row_bytes;
+  const int T_all = a.T, nsb = a.nsb;
+  asm volatile("" ::"s"(W), "s"(X), "s"(Y), "s"(n), "s"(ldx), "s"(ldy), "s"(row_bytes), "s"(T_all), "s"(nsb));
+  uint8_t* const xs = smem + S::kLutBytes;
+  f32x4* const red = reinterpret_cast<f32x4*>(smem + S::kLutBytes + S::kStage);
+  typedef __attribute__((address_space(3))) const uint8_t lds_u8;
+  lds_u8* const lds = (lds_u8*)(__attribute__((address_space(3))) uint8_t*)smem;
+
+  const int tid = threadIdx.x;
+  const int lane = tid & 63, wave = __builtin_amdgcn_readfirstlane(tid >> 6), nwaves = (int)(blockDim.x >> 6);
+  const int c = lane & 15, g = lane >> 4;
+  const int64_t r0 = (int64_t)blockIdx.x * kTileRows;
+  const int s0 = wave * WS, s1 = min(s0 + WS, nsb);  // this wave's super-blocks
+  const int nsub = 8 * (s1 - s0);                     // its sub-blocks (>= 8 for a launched wave)
+  uint8_t* const xw = xs + wave * (WS * 8) * kXmSubStage;
+
+  // ---- staging tasks: (column t, sub-block sl, k-group gg) = task t SL + 4 sl + gg ---
+  constexpr int SL = 32 * WS;  // tasks per column
+  constexpr int NI = 2 * WS;   // 4 SL / 64 task rounds
+  float4 xr[NI][2];
+  auto load_x = [&](int64_t t0, int T) {
+#pragma unroll
+    for (int i = 0; i < NI; ++i) {
+      const int task = lane + 64 * i;
+      const int t = task / SL, sl = (task % SL) >> 2, gg = task & 3;
+      if (t < T && sl < nsub) {
+        const float* p = X + (t0 + t) * ldx + (int64_t)s0 * kXsQK + 32 * sl + 4 * gg;
+        xr[i][0] = *reinterpret_cast<const float4*>(p);       // elements 4gg .. 4gg+3
+        xr[i][1] = *reinterpret_cast<const float4*>(p + 16);  // elements 4gg+16 .. 4gg+19
+      }
+    }
+  };
+  // word j of a k-group slot row pairs elements 4gg + j and 4gg + j + 16 (the index
+  // byte order); part s of column t in row 4s + t
+  auto store_x = [&](int T) {
+#pragma unroll
+    for (int i = 0; i < NI; ++i) {
+      const int task = lane + 64 * i;
+      const int t = task / SL, sl = (task % SL) >> 2, gg = task & 3;
+      if (t < T && sl < nsub) {
+        uint32_t h[4], l[4];
+        split_hi_lo(xr[i][0].x, xr[i][1].x, h[0], l[0]);
+        split_hi_lo(xr[i][0].y, xr[i][1].y, h[1], l[1]);
+        split_hi_lo(xr[i][0].z, xr[i][1].z, h[2], l[2]);
+        split_hi_lo(xr[i][0].w, xr[i][1].w, h[3], l[3]);
+        uint8_t* dst = xw + (sl * 4 + gg) * kXmSlot + t * 16;
+        *reinterpret_cast<uint4*>(dst) = uint4{h[0], h[1], h[2], h[3]};
+        *reinterpret_cast<uint4*>(dst + 4 * 16) = uint4{l[0], l[1], l[2], l[3]};
+      }
+    }
+    __builtin_amdgcn_fence(__ATOMIC_RELEASE, "wavefront", "local");
+    __builtin_amdgcn_wave_barrier();
+    __builtin_amdgcn_fence(__ATOMIC_ACQUIRE, "wavefront", "local");
+  };
+
+  // ---- requests: the first pass's activations, then every weight of the wave ----------
+  // (rows past n read row n - 1; their outputs are dropped)
+  const uint8_t* const rowp = W + min(r0 + c, n - 1) * row_bytes;
+  constexpr int T0 = TP;
+  load_x(0, T0);
+  // Lane (g, c) loads the index bytes of sub-blocks g and 4 + g of row c (16 bytes
+  // each, so a row's 64 bytes per load), and a 4 x 4 transpose across the lane groups
+  // (two 32-lane and two 16-lane swaps per set of four) leaves in its register q[u][i]
+  // dword g of sub-block i, the lane's B operand.
+  typedef uint32_t u32x4a8 __attribute__((ext_vector_type(4), aligned(8)));
+  uint2 hdr[WS];
+  uint32_t q[WS][8];
+#pragma unroll
+  for (int u = 0; u < WS; ++u) {
+    const int sb = min(s0 + u, s1 - 1);  // idle slots reload a valid super-block
+    const uint8_t* p = rowp + (int64_t)sb * kXsBytes;
+    hdr[u] = *reinterpret_cast<const uint2*>(p);
+#pragma unroll
+    for (int h = 0; h < 2; ++h) {
+      const u32x4a8 v = *reinterpret_cast<const u32x4a8*>(p + 8 + 16 * (4 * h + g));
+#pragma unroll
+      for (int j = 0; j < 4; ++j) q[u][4 * h + j] = v[j];
+    }
+  }
+  // register j of lane group g: word j of the group's load -> word g of group j's load
+  auto transpose4 = [](uint32_t& r0, uint32_t& r1, uint32_t& r2, uint32_t& r3) {
+    const auto a = __builtin_amdgcn_permlane32_swap(r0, r2, false, false);  // rows: [r0 r0 r2 r2], [r0 r0 r2 r2]
+    const auto b = __builtin_amdgcn_permlane32_swap(r1, r3, false, false);
+    const auto c0 = __builtin_amdgcn_permlane16_swap(a[0], b[0], false, false);
+    const auto c1 = __builtin_amdgcn_permlane16_swap(a[1], b[1], false, false);
+    r0 = c0[0];
+    r1 = c0[1];
+    r2 = c1[0];
+    r3 = c1[1];
+  };
+  // ---- level table: 16-byte chunk qq of LC / 4 per entry, consecutive threads write
+  // consecutive chunks (no bank conflicts) --------------------------------------------
+  {
+    constexpr int PER = LC / 4;
+    uint4* dst = reinterpret_cast<uint4*>(smem);
+    for (int qq = tid; qq < 256 * PER; qq += 64 * nwaves) {
+      const int e = qq / PER;
+      const uint32_t v = bf16_of_level(level_of((uint32_t)e & 15u)) | (bf16_of_level(level_of((uint32_t)e >> 4)) << 16);
+      dst[qq] = uint4{v, v, v, v};
+    }
+  }
+  const uint32_t lane_copy = (uint32_t)lane * 4u;
+  auto lookup = [&](uint32_t w, int b) -> uint32_t {
+    uint32_t addr;
+    if (LC == 64) {
+      addr = __builtin_amdgcn_perm(lane_copy, w, 0x0c0c0004u | ((uint32_t)b << 8));
+    } else {
+      addr = ((w >> (8 * b)) & 0xFFu) * (LC * 4) + (lane_copy & (LC * 4 - 1));
+    }
+    return *reinterpret_cast<__attribute__((address_space(3))) const uint32_t*>(lds + addr);
+  };
+  lds_u8* const arow_p = lds + S::kLutBytes + (wave * (WS * 8) * kXmSubStage + g * kXmSlot + c * 16);
+
+  // NC columns in this pass: accumulator entry i of a lane in k-group g holds row 4g + i
+  // (g = 0 hi, 1 lo; column i), so the scale FMAs of columns past NC are skipped
+  constexpr int XG = (WS >= 3) ? 2 : 4;  // sub-blocks in flight per step (registers)
+  auto multiply = [&](f32x4& acc, auto nc) {
+    constexpr int NC = decltype(nc)::value;
+    const bool arow = c < 8 && (c & 3) < NC;
+    acc = f32x4{0.f, 0.f, 0.f, 0.f};
+#pragma unroll
+    for (int u = 0; u < WS; ++u) {
+      if (s0 + u >= s1) break;
+      __builtin_amdgcn_sched_barrier(0);  // super-block u's work waits for its own weights
+      uint32_t qt[8];
+#pragma unroll
+      for (int i = 0; i < 8; ++i) qt[i] = q[u][i];
+      transpose4(qt[0], qt[1], qt[2], qt[3]);
+      transpose4(qt[4], qt[5], qt[6], qt[7]);
+#pragma unroll
+      for (int h4 = 0; h4 < 8 / XG; ++h4) {  // sub-blocks XG h4 .. XG h4 + XG - 1
+        u32x4 xf[XG], bf[XG];
+#pragma unroll
+        for (int j = 0; j < XG; ++j) {
+          const int i = XG * h4 + j;
+          if (arow)
+            xf[j] = *reinterpret_cast<__attribute__((address_space(3))) const u32x4*>(arow_p + (u * 8 + i) * kXmSubStage);
+#pragma unroll
+          for (int b = 0; b < 4; ++b) bf[j][b] = lookup(qt[i], b);
+        }
+        f32x4 prod[XG];
+#pragma unroll
+        for (int j = 0; j < XG; ++j) prod[j] = mfma_bf16(xf[j], bf[j], f32x4{0.f, 0.f, 0.f, 0.f});
+#pragma unroll
+        for (int j = 0; j < XG; ++j) {
+          const float d = xs_subscale(hdr[u].x, hdr[u].y, XG * h4 + j);
+#pragma unroll
+          for (int i = 0; i < NC; ++i) acc[i] = __builtin_fmaf(d, prod[j][i], acc[i]);
+        }
+      }
+    }
+  };
+  // cross-wave sums in wave order, hi and lo apart, then hi + lo
+  auto reduce_store = [&](int64_t t0, int T, const f32x4& acc) {
+    red[wave * 64 + lane] = acc;
+    lds_barrier();
+    const int t = tid >> 4, row = tid & 15;
+    if (tid < T * kTileRows && r0 + row < n) {
+      const float* redf = reinterpret_cast<const float*>(red);
+      float pv[2][NWV];
+#pragma unroll
+      for (int p = 0; p < 2; ++p)
+#pragma unroll
+        for (int w2 = 0; w2 < NWV; ++w2) pv[p][w2] = redf[(w2 * 64 + 16 * p + row) * 4 + t];
+      float part[2];
+#pragma unroll
+      for (int p = 0; p < 2; ++p) {
+        float sum = pv[p][0];
+#pragma unroll
+        for (int w2 = 1; w2 < NWV; ++w2) sum = (w2 < nwaves) ? sum + pv[p][w2] : sum;
+        part[p] = sum;
+      }
+      Y[(t0 + t) * ldy + r0 + row] = part[0] + part[1];
+    }
+  };
+
+  // ---- the first pass (up to 4 columns), then passes of 4 -----------------------------
+  store_x(T0);    // waits for the activations only
+  lds_barrier();  // the table
+  f32x4 acc;
+  multiply(acc, ColsXs<T0>{});
+  reduce_store(0, T0, acc);
+  for (int64_t t0 = 4; t0 < T_all; t0 += 4) {
+    const int T = (int)min((int64_t)4, (int64_t)T_all - t0);
+    lds_barrier();  // every wave is done with red
+    load_x(t0, T);
+    store_x(T);
+    multiply(acc, ColsXs<4>{});
+    reduce_store(t0, T, acc);
+  }
+}
+
+template <int WS, int NWV, int TP>
+static int launch_xm_t(const XmArgs& a, int64_t grid, int waves, hipStream_t s) {
+  hipLaunchKernelGGL((xs_qmv_mfma_kernel<WS, NWV, TP>), dim3((unsigned)grid), dim3(64 * waves), 0, s, a);
+  return check_launch("xs_qmv_mfma_kernel");
+}
+template <int WS, int NWV>
+static int launch_xm(const XmArgs& a, int64_t grid, int waves, hipStream_t s) {
+  switch (a.T < 4 ? a.T : 4) {
+    case 1: return launch_xm_t<WS, NWV, 1>(a, grid, waves, s);
+    case 2: return launch_xm_t<WS, NWV, 2>(a, grid, waves, s);
+    case 3: return launch_xm_t<WS, NWV, 3>(a, grid, waves, s);
+    default: return launch_xm_t<WS, NWV, 4>(a, grid, waves, s);
+  }
+}
+
+// ---------------------------------------------------------------------------------
 
 int launch_xs_dequant(const void* sb, int64_t nsb, bool f16, void* out, hipStream_t s) {
   if (nsb == 0) return 0;
@@ -253,6 +518,38 @@ static int launch_xs_qmv_t(const XsQmvArgs& a, int64_t n, int waves, hipStream_t
 
 int launch_xs_qmv(const void* W, int64_t n, int64_t k, const float* x, int64_t ldx, int T, float* y,
                   int64_t ldy, hipStream_t s) {
+  const int64_t nsb = k / kXsQK;
+  if (nsb <= (int64_t)kXmWaves * kXmMaxWS) {  // the matrix-core form (by the shape alone, never T)
+    XmArgs m;
+    m.W = static_cast<const uint8_t*>(W);
+    m.X = x;
+    m.Y = y;
+    m.n = n;
+    m.ldx = ldx;
+    m.ldy = ldy;
+    m.row_bytes = nsb * kXsBytes;
+    m.T = T;
+    m.nsb = (int)nsb;
+    const int64_t grid = (n + kTileRows - 1) / kTileRows;
+    // more row tiles than CUs and K within 4 waves' reach: 4-wave workgroups, two per
+    // CU, so that every tile runs in the first round; else up to 8 waves (shape only)
+    const bool four = grid > 256 && nsb <= 4 * kXmMaxWS;
+    const int nwv = four ? 4 : kXmWaves;
+    m.ws = (int)((nsb + nwv - 1) / nwv);
+    const int waves = (int)((nsb + m.ws - 1) / m.ws);
+    if (four) {
+      switch (m.ws) {
+        case 1: return launch_xm<1, 4>(m, grid, waves, s);
+        case 2: return launch_xm<2, 4>(m, grid, waves, s);
+        default: return launch_xm<3, 4>(m, grid, waves, s);
+      }
+    }
+    switch (m.ws) {
+      case 1: return launch_xm<1, kXmWaves>(m, grid, waves, s);
+      case 2: return launch_xm<2, kXmWaves>(m, grid, waves, s);
+      default: return launch_xm<3, kXmWaves>(m, grid, waves, s);
+    }
+  }
   XsQmvArgs a;
   a.W = static_cast<const uint8_t*>(W);
   a.X = x;
