@@ -148,6 +148,24 @@ def test_qmv_small_and_ragged(n, k):
         assert normwise(got, ref[:T]) <= TOL, T
 
 
+@pytest.mark.parametrize("n,k", [(4112, 1024), (4128, 2048), (4100, 3072), (2500, 6144), (33, 6400), (17, 256)])
+def test_qmv_launch_shapes(n, k):
+    """The matrix-core form's launch shapes: more row tiles than CUs with 1, 2 and 3
+    super-blocks per wave (4-wave workgroups, two per CU), 24 super-blocks with a
+    partial last row tile, and the first K past it (the vector form); each at T = 1, 4, 8
+    against the oracle, columns bitwise equal to their T = 1 call."""
+    note(f"xs qmv: launch shape {n} x {k}, T = 1, 4, 8")
+    rng = np.random.default_rng(n * 7 + k)
+    sb = random_superblocks(rng, n * k // 256)
+    x = rng.standard_normal((8, k)).astype(np.float32)
+    ref = oracle.qmv_xs(sb, n, k, x)
+    one = run_xs_qmv(sb, n, k, x[:1], 1, ldx=k + 4, ldy=n + 3)
+    for T in (1, 4, 8):
+        got = run_xs_qmv(sb, n, k, x, T, ldx=k + 4, ldy=n + 3)
+        assert normwise(got, ref[:T]) <= TOL, T
+        assert bits_equal(got[0], one[0]), T
+
+
 def test_qmv_integer_exact_bitwise():
     """d = 2^-s, every code, integer activations in [-4, 4], K = 1024: every product and
     partial sum is an exact binary32 value (|sum| <= 4064 * 4 * 1024 < 2^24), so the
