@@ -7,7 +7,8 @@
 // Decode (fp32 activations, few tokens):
 //   gather -> grouped matvec gate|up (+SwiGLU, h fp32) -> grouped matvec down (x gate
 //   weight) -> combine; with at most 64 pairs there is no gather launch: each matvec
-//   workgroup finds its expert and that expert's pairs from the ids.
+//   workgroup finds its expert and that expert's pairs from the ids, and the down
+//   product and the combine run as one launch (one workgroup per output tile and token).
 // The combine adds each token's top_k weighted slot rows in slot order j = 0..k-1, so
 // the result does not depend on how pairs were scheduled (page 1's PoolMultiFn:
 // per-slot rows (n_tok * k, n_embd), then summed per token).  The atomic variant adds
@@ -284,6 +285,12 @@ int launch_moe(const MoeCall& m, hipStream_t s) {
     d.gate_w = w;
     d.top_k = top_k;
     d.stream = s;
+    if (direct && qmv_down_combine_fits(m.inter, top_k, P)) {
+      // down product and ordered combine in one launch, straight into the output
+      d.y = m.out;
+      d.ldy = m.ldo;
+      return launch_qmv_down_combine(d, m.hidden, m.inter, n_expert, m.n_tok);
+    }
     if (int e = launch_qmv_grouped(kQmvDown, d, m.hidden, m.inter, n_expert, P)) return e;
   }
 

@@ -990,6 +990,143 @@ __global__ void __launch_bounds__(512) qmv_down_tiles_kernel(QmvArgs a) {
   }
 }
 
+// Down product and ordered combine in one launch, for a decode call with at most 64
+// routed pairs (the ids given): one workgroup per (16-row output tile, token) and one
+// wave per slot j of the token.  The wave finds its pair's expert and h row from the
+// ids (the h rows are in (expert, pair id) order), stages that row (all of K, three
+// bf16 parts in rows 0..2 of the A operand) and multiplies the expert's row tile; lane
+// (0, c) then holds the three parts of weight row c and adds them, (hi + mid) + lo.
+// The gate-weighted slot rows meet in LDS and the token's outputs are their sum in slot
+// order.  Per value this is the arithmetic of the whole-tile down kernel followed by
+// the combine (the same products, block order, part order and slot order), so the
+// result is bitwise that of the separate launches.
+constexpr int kDcSlot = 3 * 16;  // one (block, k-group) slot: the three parts of one column
+
+// (8 waves: registers for two workgroups per CU, four waves per SIMD)
+template <int KQ, int NW>
+__global__ void __launch_bounds__(64 * NW, NW == 8 ? 4 : 1) qmv_down_combine_kernel(QmvArgs a) {
+  constexpr int NB = 4 * KQ;                   // blocks of K
+  constexpr int XW = NB * 4 * kDcSlot + 256;   // a wave's staging area (+ room for pad-row reads)
+  __shared__ __attribute__((aligned(16))) uint32_t lut[256 * kLutCopies];
+  __shared__ __attribute__((aligned(16))) uint8_t xs[NW * XW];
+  __shared__ float slot_rows[NW * kTileRows];
+
+  // every kernel argument at entry (one scalar wait)
+  const uint8_t *const W0 = a.W0, *const S0 = a.S0;
+  const float* const X = a.x;
+  const float* const GW = a.gate_w;
+  float* const Y = a.y;
+  const int32_t* const ids = a.ids;
+  const int64_t wes = a.w_expert_stride, ldx = a.ldx, ldy = a.ldy, nt = a.nt, nib_bytes = a.nibble_bytes;
+  const int she = a.shared_e, n_pairs = a.n_pairs, n_expert = a.n_expert, top_k = a.top_k;
+  asm volatile("" ::"s"(W0), "s"(S0), "s"(X), "s"(GW), "s"(Y), "s"(ids), "s"(wes), "s"(ldx), "s"(ldy), "s"(nt),
+               "s"(nib_bytes), "s"(she), "s"(n_pairs), "s"(n_expert), "s"(top_k));
+
+  const int tid = threadIdx.x;
+  const int lane = tid & 63, wave = __builtin_amdgcn_readfirstlane(tid >> 6);
+  const int c = lane & 15, g = lane >> 4;
+  const int64_t tok = blockIdx.x % (a.n_pairs / top_k), rt = blockIdx.x / (a.n_pairs / top_k);
+
+  // the routed ids (one per lane) first, the level table while they are in flight
+  const int idv = (lane < n_pairs) ? ids[lane] : -1;
+  build_pair_table(lut, tid, (int)blockDim.x);
+  const uint32_t* lutl = lut + (lane & (kLutCopies - 1));
+  asm volatile("" ::"v"(idv));
+
+  // this wave's pair: its expert and its h row (the pair's rank in (expert, pair id)
+  // order).  A pair whose id is outside [0, n_expert) has no h row: it reads expert 0
+  // and row 0 and adds zero.
+  const int p = (int)tok * top_k + wave;
+  const int e = __builtin_amdgcn_readfirstlane(__shfl(idv, p));
+  const bool valid = (unsigned)idv < (unsigned)n_expert;
+  const bool e_ok = (unsigned)e < (unsigned)n_expert;
+  const int pos = e_ok ? __popcll(__ballot(valid && idv < e)) + __popcll(__ballot(valid && idv == e && lane < p)) : 0;
+  const float gw = GW[p];
+  const uint8_t* const W = (S0 != nullptr && e == she) ? S0 : W0 + (int64_t)(e_ok ? e : 0) * wes;
+
+  // requests: the h row (tasks (block, k-group), 8 floats each), then the tile's weights
+  constexpr int NI = (4 * NB + 63) / 64;
+  float4 xr[NI][2];
+  const float* const xrow = X + (int64_t)pos * ldx;
+#pragma unroll
+  for (int i = 0; i < NI; ++i) {
+    const int task = min(lane + 64 * i, 4 * NB - 1);  // clamped: every lane issues the same loads
+    const float* q = xrow + (task >> 2) * kQK + 8 * (task & 3);
+    xr[i][0] = *reinterpret_cast<const float4*>(q);
+    xr[i][1] = *reinterpret_cast<const float4*>(q + 4);
+  }
+  uint4 nib[KQ];
+  uint2 scl[KQ];
+#pragma unroll
+  for (int q = 0; q < KQ; ++q) {
+    nib[q] = *reinterpret_cast<const uint4*>(W + (rt * KQ + q) * kTileNibbleBytes + lane * 16);
+    scl[q] = *reinterpret_cast<const uint2*>(W + nib_bytes + (rt * KQ + q) * kTileScaleBytes + c * 8);
+  }
+  __syncthreads();  // the table (LDS only: no wait on the loads in flight)
+
+  // stage the h row: part s of elements 8gg .. 8gg+7 of block bl in row s of slot
+  // (bl, gg) (the wave's own area; its LDS accesses execute in order)
+  uint8_t* const xw = xs + wave * XW;
+#pragma unroll
+  for (int i = 0; i < NI; ++i) {
+    const int task = lane + 64 * i;
+    if (task < 4 * NB) {
+      uint32_t q0[3], q1[3], q2[3], q3[3];
+      split_pair(xr[i][0].x, xr[i][0].y, q0);
+      split_pair(xr[i][0].z, xr[i][0].w, q1);
+      split_pair(xr[i][1].x, xr[i][1].y, q2);
+      split_pair(xr[i][1].z, xr[i][1].w, q3);
+      uint8_t* dst = xw + task * kDcSlot;
+#pragma unroll
+      for (int sp = 0; sp < 3; ++sp) *reinterpret_cast<uint4*>(dst + sp * 16) = uint4{q0[sp], q1[sp], q2[sp], q3[sp]};
+    }
+  }
+  __builtin_amdgcn_fence(__ATOMIC_RELEASE, "wavefront");
+  __builtin_amdgcn_wave_barrier();
+  __builtin_amdgcn_fence(__ATOMIC_ACQUIRE, "wavefront");
+
+  // the tile: lane (0, c) receives D[s][c] = part s of the column for weight row c
+  float acc0 = 0.f, acc1 = 0.f, acc2 = 0.f;
+#pragma unroll
+  for (int q = 0; q < KQ; ++q) {
+    __builtin_amdgcn_sched_barrier(0);  // quad q's work waits for quad q's weights only
+#pragma unroll
+    for (int j2 = 0; j2 < 4; j2 += 2) {  // two blocks at a time (registers)
+      u32x4 xf[2], bf[2];
+#pragma unroll
+      for (int jj = 0; jj < 2; ++jj) {
+        const int j = j2 + jj;
+        xf[jj] = *reinterpret_cast<const u32x4*>(xw + ((4 * q + j) * 4 + g) * kDcSlot + c * 16);
+        const uint32_t wd = (j == 0) ? nib[q].x : (j == 1) ? nib[q].y : (j == 2) ? nib[q].z : nib[q].w;
+        bf[jj][0] = lutl[(wd & 0xFF) * kLutCopies];
+        bf[jj][1] = lutl[((wd >> 8) & 0xFF) * kLutCopies];
+        bf[jj][2] = lutl[((wd >> 16) & 0xFF) * kLutCopies];
+        bf[jj][3] = lutl[(wd >> 24) * kLutCopies];
+      }
+      f32x4 prod[2];
+#pragma unroll
+      for (int jj = 0; jj < 2; ++jj) prod[jj] = mfma_bf16(xf[jj], bf[jj], f32x4{0.f, 0.f, 0.f, 0.f});
+#pragma unroll
+      for (int jj = 0; jj < 2; ++jj) {
+        const int j = j2 + jj;
+        const uint32_t sw = (j < 2) ? scl[q].x : scl[q].y;
+        const float d = h2f((uint16_t)(sw >> (16 * (j & 1))));
+        acc0 = __builtin_fmaf(d, prod[jj][0], acc0);
+        acc1 = __builtin_fmaf(d, prod[jj][1], acc1);
+        acc2 = __builtin_fmaf(d, prod[jj][2], acc2);
+      }
+    }
+  }
+  if (g == 0) slot_rows[wave * kTileRows + c] = e_ok ? gw * ((acc0 + acc1) + acc2) : 0.f;
+  __syncthreads();
+  // the token's outputs: its slot rows added in slot order
+  if (tid < kTileRows) {
+    float sum = slot_rows[tid];
+    for (int j = 1; j < top_k; ++j) sum += slot_rows[j * kTileRows + tid];
+    Y[tok * ldy + rt * kTileRows + tid] = sum;
+  }
+}
+
 // Shape-only launch plan (never depends on T): K is cut into slices of at most
 // kSliceQuads quads (more than one slice only for K > 4096), each wave of a workgroup
 // owns a contiguous run of at most kMaxWaveQuads quads of the slice.
@@ -1191,6 +1328,37 @@ int launch_qmv_grouped(int mode, QmvArgs a, int64_t n, int64_t k, int n_expert, 
   if (a.S != 1) return set_error(-3, "grouped matvec: K above 4096 is not supported");
   grouped_split(a, slots);
   return launch_grouped_sized<kQmvDown, kDownRG>(a, slots * a.rg_chunks);
+}
+
+template <int KQ, int NW>
+static int launch_dc(const QmvArgs& a, int64_t grid) {
+  hipLaunchKernelGGL((qmv_down_combine_kernel<KQ, NW>), dim3((unsigned)grid), dim3(64 * a.top_k), 0, a.stream, a);
+  return check_launch("qmv_down_combine_kernel");
+}
+template <int NW>
+static int launch_dc_nw(const QmvArgs& a, int64_t grid) {
+  switch (a.kq_n) {
+    case 1: return launch_dc<1, NW>(a, grid);
+    case 2: return launch_dc<2, NW>(a, grid);
+    case 3: return launch_dc<3, NW>(a, grid);
+    case 4: return launch_dc<4, NW>(a, grid);
+    case 5: return launch_dc<5, NW>(a, grid);
+    case 6: return launch_dc<6, NW>(a, grid);
+    default: return launch_dc<7, NW>(a, grid);
+  }
+}
+
+bool qmv_down_combine_fits(int64_t k, int top_k, int64_t n_pairs) {
+  return k <= kMaxDownTilesK && top_k >= 1 && top_k <= 16 && n_pairs <= kDirectMaxPairs;
+}
+
+int launch_qmv_down_combine(QmvArgs a, int64_t n, int64_t k, int n_expert, int64_t n_tok) {
+  a.n_expert = n_expert;
+  qmv_plan(a, n, k, 1);
+  a.n_pairs = (int)(n_tok * a.top_k);
+  const int64_t grid = a.nt * n_tok;
+  if (grid == 0) return 0;
+  return a.top_k <= 8 ? launch_dc_nw<8>(a, grid) : launch_dc_nw<16>(a, grid);
 }
 
 // ---------------------------------------------------------------------------------

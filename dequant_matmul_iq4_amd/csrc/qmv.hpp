@@ -51,5 +51,10 @@ int launch_quantize_q8(const float* x, int64_t T, int64_t k, int64_t ldx, int8_t
 int launch_qmv_q8(const uint8_t* packed, int64_t n, int64_t k, const int8_t* q, const uint16_t* d, int T,
                   float* y, int64_t ldy, void* workspace, hipStream_t s);
 int launch_qmv_grouped(int mode, QmvArgs a, int64_t n, int64_t k, int n_expert, int64_t n_pairs);
+// The decode call's down product and ordered combine in one launch (ids given, at most
+// kDirectMaxPairs pairs, K at most 896): a.y = the output [n_tok][ldy], a.top_k = pairs
+// per token.
+bool qmv_down_combine_fits(int64_t k, int top_k, int64_t n_pairs);
+int launch_qmv_down_combine(QmvArgs a, int64_t n, int64_t k, int n_expert, int64_t n_tok);
 
 }  // namespace iq4
