@@ -51,14 +51,17 @@ N_BANKS = 8                 # expert banks the decode step rotates over
 # at the time: a kernel changed since then reports traffic null.  Commands and raw
 # figures: profiles/<name>.txt.
 MEASURED_TRAFFIC = {
-    "dequant_staged_4096x4096_f16": (43014226, "b7a9db4683211408", ("format.hip", "common.hpp")),
-    "qmv_dense_4096x4096_T1-4": (9928746, "d188ea4bd290b573", ("qmv.hip", "qmv.hpp", "common.hpp")),
-    "qmv_q8_4096x4096_T1-4": (9674048, "d188ea4bd290b573", ("qmv.hip", "qmv.hpp", "common.hpp")),
-    "qmv_grouped_gateup_moe_decode_4tok": (55434765, "d188ea4bd290b573", ("qmv.hip", "qmv.hpp", "common.hpp")),
-    "qmv_down_moe_decode_4tok": (28727809, "d188ea4bd290b573", ("qmv.hip", "qmv.hpp", "common.hpp")),
-    "qgemm_gateup_moe_prefill_3256tok": (589542843, "1abc4fb091a45333", ("gemm.hip", "gemm.hpp", "common.hpp")),
-    "qgemm_down_moe_prefill_3256tok": (400079717, "1abc4fb091a45333", ("gemm.hip", "gemm.hpp", "common.hpp")),
-    "qgemm_dense_13056x4096x14336_chunk512": (94965258, "1abc4fb091a45333", ("gemm.hip", "gemm.hpp", "common.hpp")),
+    "dequant_staged_4096x4096_f16": (43014203, "e3942b4ed3176003", ("format.hip", "common.hpp")),
+    "qmv_dense_4096x4096_T1-4": (9927978, "1fe64e0eda936e0f", ("qmv.hip", "qmv.hpp", "common.hpp")),
+    "qmv_q8_4096x4096_T1-4": (9673792, "1fe64e0eda936e0f", ("qmv.hip", "qmv.hpp", "common.hpp")),
+    "qmv_grouped_gateup_moe_decode_4tok": (55434926, "1fe64e0eda936e0f", ("qmv.hip", "qmv.hpp", "common.hpp")),
+    "qmv_down_combine_moe_decode_4tok": (28657194, "1fe64e0eda936e0f", ("qmv.hip", "qmv.hpp", "common.hpp")),
+    "xs_qmv_mfma_6144x2560_T1-4": (8760989, "8ee5d998706eda98", ("xs.hip", "common.hpp")),
+    "xs_qmv_mfma_2560x6144_T1-4": (9015369, "8ee5d998706eda98", ("xs.hip", "common.hpp")),
+    "xs_dequant_6144x2560_f16": (39844061, "8ee5d998706eda98", ("xs.hip", "common.hpp")),
+    "qgemm_gateup_moe_prefill_3256tok": (589913067, "51f83209bc6a6ef8", ("gemm.hip", "gemm.hpp", "common.hpp")),
+    "qgemm_down_moe_prefill_3256tok": (400177404, "51f83209bc6a6ef8", ("gemm.hip", "gemm.hpp", "common.hpp")),
+    "qgemm_dense_13056x4096x14336_chunk512": (94965278, "51f83209bc6a6ef8", ("gemm.hip", "gemm.hpp", "common.hpp")),
 }
 
 
@@ -75,6 +78,11 @@ def measured_traffic(name):
 def sum_traffic(*names):
     parts = [measured_traffic(nm) for nm in names]
     return None if any(p is None for p in parts) else sum(parts)
+
+
+def mean_traffic(*names):
+    total = sum_traffic(*names)
+    return None if total is None else total / len(names)
 
 
 def log(msg):
@@ -646,21 +654,25 @@ def main():
                                      traffic=sum_traffic(*["qgemm_dense_13056x4096x14336_chunk512"] * 26),
                                      ceiling=mfma_ceiling_tfs),
             "moe_decode_step": roof("hbm", unique_bytes / (dec_ms * 1e-3) / 1e9, HBM_PEAK_GBS,
-                                    "GB/s", f"gather + qmv<gateup> + qmv_down_tiles + combine, {n_unique} "
-                                    "unique experts' weights; traffic = HBM bytes of the two matvec launches",
+                                    "GB/s", f"qmv<gateup> + qmv_down_combine (down product and ordered "
+                                    f"combine in one launch), {n_unique} unique experts' weights; traffic = "
+                                    "HBM bytes of the two launches",
                                     traffic=sum_traffic("qmv_grouped_gateup_moe_decode_4tok",
-                                                        "qmv_down_moe_decode_4tok")),
+                                                        "qmv_down_combine_moe_decode_4tok")),
             "mmvq_q8": roof("hbm", q8_achieved, HBM_PEAK_GBS, "GB/s",
                             "qmv_q8_kernel: verify-window matvec on 8-bit activations, bytes = W + codes + "
                             "scales + Y per call, mean over T=1..4; traffic = HBM bytes per launch",
                             traffic=measured_traffic("qmv_q8_4096x4096_T1-4")),
             "xs_mmvq": roof("hbm", xs_achieved, HBM_PEAK_GBS, "GB/s",
-                            "xs_qmv_kernel: IQ4_XS super-block matvec, 6144x2560 and 2560x6144, bytes = W + X + Y "
-                            "per call, mean over both shapes and T=1..4 (cold copies)",
-                            traffic=None, ceiling=stream_ceiling_gbs),
+                            "xs_qmv_mfma_kernel: IQ4_XS super-block matvec on the matrix cores, 6144x2560 and "
+                            "2560x6144, bytes = W + X + Y per call, mean over both shapes and T=1..4 (cold copies); "
+                            "traffic = HBM bytes per launch, mean over both shapes",
+                            traffic=mean_traffic("xs_qmv_mfma_6144x2560_T1-4", "xs_qmv_mfma_2560x6144_T1-4"),
+                            ceiling=stream_ceiling_gbs),
             "xs_dequant": roof("hbm", xs_deq_bytes / (xs_deq_ms * 1e-3) / 1e9, HBM_PEAK_GBS, "GB/s",
                                "xs_dequant_kernel<f16>: 8.4 MB of super-blocks in, 31.5 MB of f16 out per launch "
-                               "(graph of launches over cold copies)", traffic=None),
+                               "(graph of launches over cold copies); traffic = HBM bytes per launch",
+                               traffic=measured_traffic("xs_dequant_6144x2560_f16")),
             "dequant": roof("hbm", deq_bytes / (deq_ms * 1e-3) / 1e9, HBM_PEAK_GBS, "GB/s",
                             "dequant_staged_kernel<f16>: 9.4 MB of blocks in, 33.5 MB of f16 out, per launch "
                             "(graph of 32 launches over cold copies); traffic = HBM bytes per launch",
