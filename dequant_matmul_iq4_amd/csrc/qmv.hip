@@ -342,11 +342,13 @@ __global__ void __launch_bounds__(64 * kDenseWaves) qmv_dense_kernel(QmvArgs a) 
   // ---- requests: the first pass's activations, then every weight of the wave --------
   constexpr int T0 = TP;  // columns of the first pass, min(T, 4): fixed per instantiation
   load_x(0, T0);
+  // (the weights are read once per call: non-temporal loads stream them past the L2, so
+  // that they do not evict the activations, which every workgroup reads)
 #pragma unroll
   for (int u = 0; u < WQ; ++u) {
     const int q = min(wq0 + u, max(wq1 - 1, 0));  // idle slots reload a valid quad
-    nib[u] = *reinterpret_cast<const uint4*>(tp + (int64_t)q * kTileNibbleBytes);
-    scl[u] = *reinterpret_cast<const uint2*>(sp + (int64_t)q * kTileScaleBytes);
+    nib[u] = load_nt16(tp + (int64_t)q * kTileNibbleBytes);
+    scl[u] = load_nt8(sp + (int64_t)q * kTileScaleBytes);
   }
   // ---- level table: 16-byte chunk q (0 .. 4095) holds copies 4(q mod 16) .. +3 of entry
   // q / 16; thread tid writes chunks tid, tid + NT, ... (consecutive lanes, consecutive
@@ -672,8 +674,8 @@ __global__ void __launch_bounds__(512) qmv_grouped_kernel(QmvArgs a) {
           const uint8_t* tp = W[m] + rt * kq_n * kTileNibbleBytes + lane * 16;
           const uint8_t* sp = W[m] + a.nibble_bytes + rt * kq_n * kTileScaleBytes + c * 8;
           const int q = min(wq0 + u, max(wq1 - 1, 0));  // clamped; unused when past the range
-          ws.nib[u][m][r] = *reinterpret_cast<const uint4*>(tp + (int64_t)q * kTileNibbleBytes);
-          ws.scl[u][m][r] = *reinterpret_cast<const uint2*>(sp + (int64_t)q * kTileScaleBytes);
+          ws.nib[u][m][r] = load_nt16(tp + (int64_t)q * kTileNibbleBytes);  // read once: streamed
+          ws.scl[u][m][r] = load_nt8(sp + (int64_t)q * kTileScaleBytes);
         }
       }
   };
@@ -867,8 +869,8 @@ __global__ void __launch_bounds__(512) qmv_down_tiles_kernel(QmvArgs a) {
   auto load_w = [&](WSet& w, int64_t rt) {
 #pragma unroll
     for (int q = 0; q < KQ; ++q) {
-      w.nib[q] = *reinterpret_cast<const uint4*>(W + (rt * KQ + q) * kTileNibbleBytes + lane * 16);
-      w.scl[q] = *reinterpret_cast<const uint2*>(W + a.nibble_bytes + (rt * KQ + q) * kTileScaleBytes + c * 8);
+      w.nib[q] = load_nt16(W + (rt * KQ + q) * kTileNibbleBytes + lane * 16);  // read once: streamed
+      w.scl[q] = load_nt8(W + a.nibble_bytes + (rt * KQ + q) * kTileScaleBytes + c * 8);
     }
   };
   // The first pass's columns are requested before the weights (loads complete in order,
@@ -1059,8 +1061,8 @@ __global__ void __launch_bounds__(64 * NW, NW == 8 ? 4 : 1) qmv_down_combine_ker
   uint2 scl[KQ];
 #pragma unroll
   for (int q = 0; q < KQ; ++q) {
-    nib[q] = *reinterpret_cast<const uint4*>(W + (rt * KQ + q) * kTileNibbleBytes + lane * 16);
-    scl[q] = *reinterpret_cast<const uint2*>(W + nib_bytes + (rt * KQ + q) * kTileScaleBytes + c * 8);
+    nib[q] = load_nt16(W + (rt * KQ + q) * kTileNibbleBytes + lane * 16);  // read once: streamed
+    scl[q] = load_nt8(W + nib_bytes + (rt * KQ + q) * kTileScaleBytes + c * 8);
   }
   __syncthreads();  // the table (LDS only: no wait on the loads in flight)
 
@@ -1468,8 +1470,8 @@ __global__ void __launch_bounds__(512) qmv_q8_kernel(QmvArgs a) {
 #pragma unroll
   for (int u = 0; u < WQ; ++u) {
     const int q = min(wq0 + u, max(wq1 - 1, 0));
-    nib[u] = *reinterpret_cast<const uint4*>(tp + (int64_t)q * kTileNibbleBytes);
-    scl[u] = *reinterpret_cast<const uint2*>(sp + (int64_t)q * kTileScaleBytes);
+    nib[u] = load_nt16(tp + (int64_t)q * kTileNibbleBytes);  // read once: streamed
+    scl[u] = load_nt8(sp + (int64_t)q * kTileScaleBytes);
   }
   for (int i = tid; i < 512; i += blockDim.x) {
     const int e = i >> 1;
