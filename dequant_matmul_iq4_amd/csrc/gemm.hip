@@ -390,14 +390,14 @@ qgemm_kernel(GemmArgs a) {
 #pragma unroll
           for (int mt = 0; mt < kMT; ++mt)
 #pragma unroll
-            for (int r = 0; r < kWaveRT; ++r) acc[mt][r] = mfma_f16(af[mt], bf[r], acc[mt][r]);
+            for (int r = 0; r < kWaveRT; ++r) acc[mt][r] = mfma_f16(bf[r], af[mt], acc[mt][r]);
         } else {
 #pragma unroll
           for (int mt = 0; mt < kMT; ++mt) {
             if (mt >= nfr) break;  // fragment rows wholly past the tile's rows
             const u32x4 af = *reinterpret_cast<const u32x4*>(ab + mt * 1024);
 #pragma unroll
-            for (int r = 0; r < kWaveRT; ++r) acc[mt][r] = mfma_f16(af, bf[r], acc[mt][r]);
+            for (int r = 0; r < kWaveRT; ++r) acc[mt][r] = mfma_f16(bf[r], af, acc[mt][r]);
           }
         }
         if constexpr (PB) {
@@ -456,66 +456,82 @@ qgemm_kernel(GemmArgs a) {
     if (kp != 0) return;  // the kp = 0 waves store
   }
 
-  // ---- epilogue: lane holds D[4g + i][c] of each (mt, r) fragment -------------------
+  // ---- epilogue ------------------------------------------------------------------------
+  // The weights are the matrix core's first operand, so every fragment holds its 16 x 16
+  // piece of the tile transposed: lane (g, c) has row 16 mt + c and the four consecutive
+  // columns 16 r + 4 g .. 16 r + 4 g + 3 of its column group, stored with one vector write.
   if (MODE == kGemmDense) {
 #pragma unroll
-    for (int mt = 0; mt < kMT; ++mt)
+    for (int mt = 0; mt < kMT; ++mt) {
+      const int rr = 16 * mt + c;
+      if (rr >= rows) continue;
+      float* crow = a.C + (m0 + rr) * a.ldc + n0 + 64 * cg + 4 * g;
 #pragma unroll
-      for (int i = 0; i < 4; ++i) {
-        const int rr = 16 * mt + 4 * g + i;
-        if (rr >= rows) continue;
-        float* crow = a.C + (m0 + rr) * a.ldc + n0 + 64 * cg + c;
+      for (int r = 0; r < kWaveRT; ++r) {
+        if (!rt_ok[r]) continue;
+        if (a.vec_c) {
+          *reinterpret_cast<f32x4*>(crow + 16 * r) = acc[mt][r];
+        } else {
 #pragma unroll
-        for (int r = 0; r < kWaveRT; ++r)
-          if (rt_ok[r]) crow[16 * r] = acc[mt][r][i];
+          for (int i = 0; i < 4; ++i) crow[16 * r + i] = acc[mt][r][i];
+        }
       }
+    }
   } else if (MODE == kGemmGateUp) {
 #pragma unroll
-    for (int mt = 0; mt < kMT; ++mt)
+    for (int mt = 0; mt < kMT; ++mt) {
+      const int rr = 16 * mt + c;
+      if (rr >= rows) continue;
+      const int64_t o = (seg0 + m0 + rr) * a.ldh + n0 + 32 * cg + 4 * g;
 #pragma unroll
-      for (int i = 0; i < 4; ++i) {
-        const int rr = 16 * mt + 4 * g + i;
-        if (rr >= rows) continue;
-        uint16_t* hrow = a.H + (seg0 + m0 + rr) * a.ldh + n0 + 32 * cg + c;
+      for (int r = 0; r < 2; ++r) {
+        if (!rt_ok[r]) continue;
+        const f32x4 gv = acc[mt][r], uv = acc[mt][r + 2];
+        uint32_t hb[4];
 #pragma unroll
-        for (int r = 0; r < 2; ++r) {
-          if (!rt_ok[r]) continue;
-          const float gv = acc[mt][r][i], uv = acc[mt][r + 2][i];
-          const float h = gv / (1.0f + __expf(-gv)) * uv;
-          hrow[16 * r] = __half_as_ushort(__float2half_rn(h));
-          if (a.G) {  // the intermediates kept (tests): g and u in the same place as h
-            const int64_t o = (seg0 + m0 + rr) * a.ldh + n0 + 32 * cg + c + 16 * r;
-            a.G[o] = gv;
-            a.U[o] = uv;
-          }
+        for (int i = 0; i < 4; ++i) {
+          const float h = gv[i] / (1.0f + __expf(-gv[i])) * uv[i];
+          hb[i] = __half_as_ushort(__float2half_rn(h));
+        }
+        *reinterpret_cast<u32x2*>(a.H + o + 16 * r) = u32x2{hb[0] | (hb[1] << 16), hb[2] | (hb[3] << 16)};
+        if (a.G) {  // the intermediates kept (tests): g and u in the same place as h
+          *reinterpret_cast<f32x4*>(a.G + o + 16 * r) = gv;
+          *reinterpret_cast<f32x4*>(a.U + o + 16 * r) = uv;
         }
       }
+    }
   } else {  // DOWN
 #pragma unroll
-    for (int mt = 0; mt < kMT; ++mt)
+    for (int mt = 0; mt < kMT; ++mt) {
+      const int rr = 16 * mt + c;
+      if (rr >= rows) continue;
+      const int p = tile_pair[rr];
+      const float gw = tile_gw[rr];
+      if (a.atomic) {
+        float* orow = a.out + (int64_t)(p / a.top_k) * a.ldo + n0 + 64 * cg + 4 * g;
 #pragma unroll
-      for (int i = 0; i < 4; ++i) {
-        const int rr = 16 * mt + 4 * g + i;
-        if (rr >= rows) continue;
-        const int p = tile_pair[rr];
-        const float gw = tile_gw[rr];
-        if (a.atomic) {
-          float* orow = a.out + (int64_t)(p / a.top_k) * a.ldo + n0 + 64 * cg + c;
+        for (int r = 0; r < kWaveRT; ++r)
+          if (rt_ok[r])
 #pragma unroll
-          for (int r = 0; r < kWaveRT; ++r)
-            if (rt_ok[r]) atomicAdd(orow + 16 * r, gw * acc[mt][r][i]);
-        } else {
-          // the row rounded to binary16 (half the bytes of the write and of the
-          // combine's read); the product is rounded to binary32 first
-          uint16_t* yrow = a.R + (int64_t)p * a.ldc + n0 + 64 * cg + c;
+            for (int i = 0; i < 4; ++i) atomicAdd(orow + 16 * r + i, gw * acc[mt][r][i]);
+      } else {
+        // the row rounded to binary16 (half the bytes of the write and of the combine's
+        // read); the product is rounded to binary32 first
+        uint16_t* yrow = a.R + (int64_t)p * a.ldc + n0 + 64 * cg + 4 * g;
 #pragma unroll
-          for (int r = 0; r < kWaveRT; ++r) {
+        for (int r = 0; r < kWaveRT; ++r) {
+          if (!rt_ok[r]) continue;
+          uint32_t hb[4];
+#pragma unroll
+          for (int i = 0; i < 4; ++i) {
             float v = gw * acc[mt][r][i];
             asm volatile("" : "+v"(v));  // no fused multiply-and-convert (it would drop a -0)
-            if (rt_ok[r]) yrow[16 * r] = __half_as_ushort(__float2half_rn(v));
+            hb[i] = __half_as_ushort(__float2half_rn(v));
           }
+          *reinterpret_cast<u32x2*>(yrow + 16 * r) = u32x2{hb[0] | (hb[1] << 16), hb[2] | (hb[3] << 16)};
         }
       }
+    }
   }
 }
 
@@ -545,6 +561,7 @@ int launch_qgemm_dense(const uint8_t* packed, int64_t n, int64_t k, const uint16
     a.M = (m - c0 < chunk) ? (m - c0) : chunk;
     a.C = y + c0 * ldy;
     a.ldc = ldy;
+    a.vec_c = (reinterpret_cast<uintptr_t>(y) % 16 == 0) && (ldy % 4 == 0);  // 16-byte row pieces
     const int64_t grid = round8(((a.M + kBM - 1) / kBM) * ((n + kBN - 1) / kBN));
     hipLaunchKernelGGL((qgemm_kernel<kGemmDense, kDenseWaves, kDenseKS, kDenseSA, kDenseSB, false>), dim3((unsigned)grid),
                        dim3(64 * kDenseWaves), 0, s, a);

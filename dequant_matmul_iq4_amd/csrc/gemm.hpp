@@ -18,6 +18,7 @@ struct GemmArgs {
   int64_t N, K;             // weight rows and reduction length of one matrix
   int64_t M;                // DENSE: rows of A in this launch
   float* C;                 // DENSE: output [M][ldc]
+  int vec_c;                // DENSE: C and ldc allow 16-byte stores of 4 consecutive columns
   uint16_t* R;              // DOWN: per-pair rows w * (Wd h) as binary16 [pairs][ldc]
   int64_t ldc;
   uint16_t* H;              // GATEUP: h = silu(g) * u as binary16 [pairs][ldh] (sorted order)
