@@ -225,9 +225,13 @@ qgemm_kernel(GemmArgs a) {
   const int f0 = wave * kAPerWave;
   constexpr int kAB = kMT / NW;  // PB: this wave's copies per block
   auto a_frag = [&](int i) -> int { return PB ? kMT * (i / kAB) + kAB * wave + i % kAB : f0 + i; };
-  uint32_t a_off[kAPerWave];  // byte offsets from A (the launcher checks they fit in 32 bits)
+  // Byte offsets from A (the launcher checks they fit in 32 bits).  PB: the copies of
+  // block j are this wave's fragment rows of that block, at block 0's offsets plus the
+  // block's 64 bytes (added to the scalar base), so only kAB offsets are kept.
+  constexpr int kAOff = PB ? kAB : kAPerWave;
+  uint32_t a_off[kAOff];
 #pragma unroll
-  for (int i = 0; i < kAPerWave; ++i) {
+  for (int i = 0; i < kAOff; ++i) {
     const int f = a_frag(i), mt = f % kMT, j = f / kMT;
     const int64_t r = min((int64_t)(16 * mt + c), rows - 1);
     int64_t src_row;
@@ -269,13 +273,15 @@ qgemm_kernel(GemmArgs a) {
   auto copy_a = [&](int q) {
     const uint32_t st = ring_a0 + (uint32_t)((q % SA) * kABytes);
 #pragma unroll
-    for (int i = 0; i < kAPerWave; ++i)
-      copy16(a.A + (int64_t)q * kTileK, a_off[i], st + (uint32_t)(a_frag(i) * 1024));
+    for (int i = 0; i < kAPerWave; ++i) {
+      if constexpr (PB) copy16(a.A + (int64_t)q * kTileK + 32 * (i / kAB), a_off[i % kAB], st + (uint32_t)(a_frag(i) * 1024));
+      else copy16(a.A + (int64_t)q * kTileK, a_off[i], st + (uint32_t)(a_frag(i) * 1024));
+    }
   };
   auto copy_a_block = [&](int q, int j) {  // PB: this wave's kAB fragments of block j
 #pragma unroll
-    for (int i = kAB * j; i < kAB * j + kAB; ++i)
-      copy16(a.A + (int64_t)q * kTileK, a_off[i], ring_a0 + (uint32_t)(a_frag(i) * 1024));
+    for (int k = 0; k < kAB; ++k)
+      copy16(a.A + (int64_t)q * kTileK + 32 * j, a_off[k], ring_a0 + (uint32_t)(a_frag(kAB * j + k) * 1024));
   };
   auto copy_b = [&](int q) {
     const uint32_t sb = ring_b0 + (uint32_t)((q % SB) * kBStageBytes + cg * kWaveBBytes);
