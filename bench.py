@@ -51,17 +51,17 @@ N_BANKS = 8                 # expert banks the decode step rotates over
 # at the time: a kernel changed since then reports traffic null.  Commands and raw
 # figures: profiles/<name>.txt.
 MEASURED_TRAFFIC = {
-    "dequant_staged_4096x4096_f16": (43014212, "41dc1ace9141cd08", ("format.hip", "common.hpp")),
-    "qmv_dense_4096x4096_T1-4": (9927971, "6a2fa7d6d7b1b8ad", ("qmv.hip", "qmv.hpp", "common.hpp")),
-    "qmv_q8_4096x4096_T1-4": (9674810, "6a2fa7d6d7b1b8ad", ("qmv.hip", "qmv.hpp", "common.hpp")),
-    "qmv_grouped_gateup_moe_decode_4tok": (59734140, "6a2fa7d6d7b1b8ad", ("qmv.hip", "qmv.hpp", "common.hpp")),
-    "qmv_down_combine_moe_decode_4tok": (28656220, "6a2fa7d6d7b1b8ad", ("qmv.hip", "qmv.hpp", "common.hpp")),
-    "xs_qmv_mfma_6144x2560_T1-4": (8760983, "83810f3202cde74d", ("xs.hip", "common.hpp")),
-    "xs_qmv_mfma_2560x6144_T1-4": (9015364, "83810f3202cde74d", ("xs.hip", "common.hpp")),
-    "xs_dequant_6144x2560_f16": (39844063, "83810f3202cde74d", ("xs.hip", "common.hpp")),
-    "qgemm_gateup_moe_prefill_3256tok": (588822107, "71b68082b27a9d12", ("gemm.hip", "gemm.hpp", "common.hpp")),
-    "qgemm_down_moe_prefill_3256tok": (400169826, "71b68082b27a9d12", ("gemm.hip", "gemm.hpp", "common.hpp")),
-    "qgemm_dense_13056x4096x14336_chunk512": (94965206, "71b68082b27a9d12", ("gemm.hip", "gemm.hpp", "common.hpp")),
+    "dequant_staged_4096x4096_f16": (43014205, "41dc1ace9141cd08", ("format.hip", "common.hpp")),
+    "qmv_dense_4096x4096_T1-4": (9927972, "6a2fa7d6d7b1b8ad", ("qmv.hip", "qmv.hpp", "common.hpp")),
+    "qmv_q8_4096x4096_T1-4": (9674811, "6a2fa7d6d7b1b8ad", ("qmv.hip", "qmv.hpp", "common.hpp")),
+    "qmv_grouped_gateup_moe_decode_4tok": (59952873, "6a2fa7d6d7b1b8ad", ("qmv.hip", "qmv.hpp", "common.hpp")),
+    "qmv_down_combine_moe_decode_4tok": (28656195, "6a2fa7d6d7b1b8ad", ("qmv.hip", "qmv.hpp", "common.hpp")),
+    "xs_qmv_mfma_6144x2560_T1-4": (8760985, "83810f3202cde74d", ("xs.hip", "common.hpp")),
+    "xs_qmv_mfma_2560x6144_T1-4": (9015365, "83810f3202cde74d", ("xs.hip", "common.hpp")),
+    "xs_dequant_6144x2560_f16": (39844042, "83810f3202cde74d", ("xs.hip", "common.hpp")),
+    "qgemm_gateup_moe_prefill_3256tok": (590123568, "0db542cbc5ab776d", ("gemm.hip", "gemm.hpp", "common.hpp")),
+    "qgemm_down_moe_prefill_3256tok": (400111105, "0db542cbc5ab776d", ("gemm.hip", "gemm.hpp", "common.hpp")),
+    "qgemm_dense_13056x4096x14336_chunk512": (94901830, "0db542cbc5ab776d", ("gemm.hip", "gemm.hpp", "common.hpp")),
 }
 
 
