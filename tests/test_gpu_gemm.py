@@ -54,6 +54,30 @@ def test_integer_exact_bitwise(n, k, m):
     assert bits_equal(y, oracle.gemm(b, n, k, x))
 
 
+def test_unaligned_output_rows_bitwise():
+    """Output rows that do not allow 16-byte stores (ldy not a multiple of 4, base 4 bytes
+    past a 16-byte boundary) take the scalar stores: the same values, and nothing
+    written outside the n columns of each row."""
+    note("qgemm: unaligned output rows (ldy = n + 3, base + 4 bytes)")
+    n, k, m = 48, 256, 37
+    rng = np.random.default_rng(23)
+    b = oracle.encode_blocks((rng.standard_normal((n * k // 32, 32)) * 0.02).astype(np.float32))
+    x = rng.standard_normal((m, k)).astype(np.float16)
+    packed = pack(b, n, k)
+    ref = run_qgemm(packed, n, k, x)  # ldy = n: 16-byte stores
+    ldy = n + 3
+    xd = dev(x)
+    buf = torch.full((m * ldy + 4,), float("nan"), dtype=torch.float32, device="cuda")
+    y = buf[1:1 + m * ldy]  # 4 bytes past the (256-byte aligned) allocation
+    iq4.iq4_qgemm(packed, n, k, xd, m, k, y, ldy, 512)
+    out = host(buf)
+    assert np.isnan(out[0]) and np.all(np.isnan(out[1 + m * ldy:]))
+    rows = out[1:1 + m * ldy].reshape(m, ldy)
+    assert np.all(np.isnan(rows[:, n:])), "wrote outside [0, n)"
+    assert bits_equal(rows[:, :n], ref)
+    assert normwise(rows[:, :n], oracle.gemm(b, n, k, x)) <= TOL
+
+
 def test_chunk_invariance_bitwise():
     note("qgemm: chunk 512 / 256 / 100 / one launch, bitwise")
     n, k, m = 512, 512, 1100
