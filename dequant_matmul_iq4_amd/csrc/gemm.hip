@@ -33,7 +33,10 @@
 //     byte, one packed binary16 multiply by the block scale gives the binary16
 //     rounding of the exact decoded weight.  No decoded weight goes through LDS or HBM;
 //   * per block a wave issues its 16 table reads for the next block and its 8 A-fragment
-//     reads, then 8 x 4 MFMAs (the table reads complete under them).
+//     reads, then 8 x 4 MFMAs (the table reads complete under them); the weight
+//     fragment is the instruction's first operand and the activation fragment its
+//     second (both have the same lane layout), so each accumulator holds its 16 x 16
+//     output piece transposed: a lane ends with four consecutive columns of one row.
 // The copies are issued from inline assembly so that the compiler, which cannot tell
 // the ring stages apart, does not drain every copy in flight before each LDS read; the
 // kernel waits for them itself: per quad one s_waitcnt for this wave's copies of the
