@@ -59,9 +59,9 @@ MEASURED_TRAFFIC = {
     "xs_qmv_mfma_6144x2560_T1-4": (8760985, "83810f3202cde74d", ("xs.hip", "common.hpp")),
     "xs_qmv_mfma_2560x6144_T1-4": (9015365, "83810f3202cde74d", ("xs.hip", "common.hpp")),
     "xs_dequant_6144x2560_f16": (39844042, "83810f3202cde74d", ("xs.hip", "common.hpp")),
-    "qgemm_gateup_moe_prefill_3256tok": (590123568, "0db542cbc5ab776d", ("gemm.hip", "gemm.hpp", "common.hpp")),
-    "qgemm_down_moe_prefill_3256tok": (400111105, "0db542cbc5ab776d", ("gemm.hip", "gemm.hpp", "common.hpp")),
-    "qgemm_dense_13056x4096x14336_chunk512": (94901830, "0db542cbc5ab776d", ("gemm.hip", "gemm.hpp", "common.hpp")),
+    "qgemm_gateup_moe_prefill_3256tok": (590123568, "91b289d98fd124c6", ("gemm.hip", "gemm.hpp", "common.hpp")),
+    "qgemm_down_moe_prefill_3256tok": (400111105, "91b289d98fd124c6", ("gemm.hip", "gemm.hpp", "common.hpp")),
+    "qgemm_dense_13056x4096x14336_chunk512": (94901830, "91b289d98fd124c6", ("gemm.hip", "gemm.hpp", "common.hpp")),
 }
 
 
