@@ -105,25 +105,41 @@ __global__ void __launch_bounds__(256) dequant_kernel(const uint16_t* __restrict
   decode8<F16>(blk[0], v, p, out, i);
 }
 
-// 16-byte-aligned blocks, 64 per workgroup: the workgroup's 1,152 bytes come in with
-// 72 coalesced 16-byte loads and each thread reads its block's bytes back from LDS
-// (the direct form issues five 2-byte loads per thread).
+// 16-byte-aligned blocks, G groups of 64 per workgroup: the groups' 72 G 16-byte pieces
+// come in with coalesced loads, all issued before any is waited for (four groups keep
+// about 37 KB of loads in flight per CU), and each thread reads its blocks' bytes back
+// from LDS (the direct form issues five 2-byte loads per thread).
 constexpr int kStagedBlocks = 64;
 constexpr int kStagedChunks = kStagedBlocks * kBlockBytes / 16;  // 72
+constexpr int kStagedGroups = 4;
 
-template <bool F16>
+template <bool F16, int G>
 __global__ void __launch_bounds__(256) dequant_staged_kernel(const uint4* __restrict__ blocks,
                                                              void* __restrict__ out) {
-  __shared__ uint4 st[kStagedChunks];
+  constexpr int NC = G * kStagedChunks;
+  static_assert(NC <= 3 * 256, "three loads per thread at most");
+  __shared__ uint4 st[NC];
   const int tid = threadIdx.x;
-  if (tid < kStagedChunks) st[tid] = blocks[(int64_t)blockIdx.x * kStagedChunks + tid];
+  const uint4* src = blocks + (int64_t)blockIdx.x * NC;
+  // (separate variables, not an array: an array of them was placed in LDS or scratch)
+  const int i0 = tid, i1 = tid + 256, i2 = tid + 512;
+  uint4 r0 = {0u, 0u, 0u, 0u}, r1 = {0u, 0u, 0u, 0u}, r2 = {0u, 0u, 0u, 0u};
+  if (i0 < NC) r0 = src[i0];
+  if (i1 < NC) r1 = src[i1];
+  if (i2 < NC) r2 = src[i2];
+  if (i0 < NC) st[i0] = r0;
+  if (i1 < NC) st[i1] = r1;
+  if (i2 < NC) st[i2] = r2;
   __syncthreads();
   const int b = tid >> 2, p = tid & 3;
-  const uint16_t* blk = reinterpret_cast<const uint16_t*>(st) + b * (kBlockBytes / 2);
-  uint16_t v[4];
 #pragma unroll
-  for (int j = 0; j < 4; ++j) v[j] = blk[1 + 4 * (p & 1) + j];
-  decode8<F16>(blk[0], v, p, out, (int64_t)blockIdx.x * 256 + tid);
+  for (int gg = 0; gg < G; ++gg) {
+    const uint16_t* blk = reinterpret_cast<const uint16_t*>(st + gg * kStagedChunks) + b * (kBlockBytes / 2);
+    uint16_t v[4];
+#pragma unroll
+    for (int j = 0; j < 4; ++j) v[j] = blk[1 + 4 * (p & 1) + j];
+    decode8<F16>(blk[0], v, p, out, ((int64_t)blockIdx.x * G + gg) * 256 + tid);
+  }
 }
 
 // One thread per packed entry (64 per tile).  Entry l = 16g + j of tile (rt, kq) holds,
@@ -184,12 +200,23 @@ int launch_dequant(const void* blocks, int64_t nb, bool f16, void* out, hipStrea
   // whole groups of 64 blocks through the staged kernel when the blocks are 16-byte
   // aligned; the rest (or everything, if unaligned) through the direct one
   const int64_t groups = aligned(blocks, 16) ? nb / kStagedBlocks : 0;
-  if (groups > 0) {
-    const uint4* b16 = static_cast<const uint4*>(blocks);
+  const int64_t wide = groups / kStagedGroups;  // workgroups of kStagedGroups groups
+  const uint4* b16 = static_cast<const uint4*>(blocks);
+  if (wide > 0) {
     if (f16)
-      hipLaunchKernelGGL(dequant_staged_kernel<true>, dim3((unsigned)groups), dim3(256), 0, s, b16, out);
+      hipLaunchKernelGGL((dequant_staged_kernel<true, kStagedGroups>), dim3((unsigned)wide), dim3(256), 0, s, b16, out);
     else
-      hipLaunchKernelGGL(dequant_staged_kernel<false>, dim3((unsigned)groups), dim3(256), 0, s, b16, out);
+      hipLaunchKernelGGL((dequant_staged_kernel<false, kStagedGroups>), dim3((unsigned)wide), dim3(256), 0, s, b16, out);
+    if (int e = check_launch("dequant_staged_kernel")) return e;
+  }
+  if (groups > wide * kStagedGroups) {  // the last groups, one per workgroup
+    const int64_t g0 = wide * kStagedGroups;
+    const uint4* bg = b16 + g0 * kStagedChunks;
+    void* og = static_cast<uint8_t*>(out) + g0 * kStagedBlocks * kQK * (f16 ? 2 : 4);
+    if (f16)
+      hipLaunchKernelGGL((dequant_staged_kernel<true, 1>), dim3((unsigned)(groups - g0)), dim3(256), 0, s, bg, og);
+    else
+      hipLaunchKernelGGL((dequant_staged_kernel<false, 1>), dim3((unsigned)(groups - g0)), dim3(256), 0, s, bg, og);
     if (int e = check_launch("dequant_staged_kernel")) return e;
   }
   const int64_t done = groups * kStagedBlocks, rest = nb - done;

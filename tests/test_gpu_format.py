@@ -25,7 +25,7 @@ def gpu_quantize(w32: np.ndarray) -> np.ndarray:
 def gpu_dequant(blocks: np.ndarray, f16: bool) -> np.ndarray:
     b = dev(blocks.reshape(-1))
     nb = blocks.reshape(-1, 18).shape[0]
-    out = torch.empty(nb * 32, dtype=torch.float16 if f16 else torch.float32, device="cuda")
+    out = torch.full((nb * 32,), float("nan"), dtype=torch.float16 if f16 else torch.float32, device="cuda")
     iq4.iq4_dequant_blocks(b, nb, iq4.IQ4_F16 if f16 else iq4.IQ4_F32, out)
     return host(out).reshape(nb, 32)
 
@@ -82,16 +82,18 @@ def test_dequant_odd_count():
     assert bits_equal(gpu_dequant(b, False), oracle.decode_blocks(b))
 
 
-def test_dequant_staged_and_direct_paths():
-    """197 blocks: three staged groups of 64 plus a direct tail when 16-byte aligned,
-    and all direct when the same blocks start 2 bytes into an allocation."""
-    note("dequant: 197 blocks, aligned and at a 2-byte offset (f32 and f16)")
-    rng = np.random.default_rng(21)
-    b = oracle.encode_blocks((rng.standard_normal((197, 32)) * 0.02).astype(np.float32))
+@pytest.mark.parametrize("nb", [197, 453])
+def test_dequant_staged_and_direct_paths(nb):
+    """197 blocks: three one-group workgroups of 64 blocks plus a direct tail when 16-byte
+    aligned; 453 blocks: one four-group workgroup, three one-group workgroups and a
+    direct tail; all direct when the same blocks start 2 bytes into an allocation."""
+    note(f"dequant: {nb} blocks, aligned and at a 2-byte offset (f32 and f16)")
+    rng = np.random.default_rng(21 + nb)
+    b = oracle.encode_blocks((rng.standard_normal((nb, 32)) * 0.02).astype(np.float32))
     for f16, ref in ((False, oracle.decode_blocks(b)), (True, oracle.decode_blocks_f16(b))):
         assert bits_equal(gpu_dequant(b, f16), ref)
         raw = torch.zeros(b.size + 16, dtype=torch.uint8, device="cuda")
         raw[2:2 + b.size] = dev(b.reshape(-1))
-        out = torch.empty(197 * 32, dtype=torch.float16 if f16 else torch.float32, device="cuda")
-        iq4.iq4_dequant_blocks(raw.data_ptr() + 2, 197, iq4.IQ4_F16 if f16 else iq4.IQ4_F32, out)
+        out = torch.full((nb * 32,), float("nan"), dtype=torch.float16 if f16 else torch.float32, device="cuda")
+        iq4.iq4_dequant_blocks(raw.data_ptr() + 2, nb, iq4.IQ4_F16 if f16 else iq4.IQ4_F32, out)
         assert bits_equal(host(out).reshape(ref.shape), ref)
