@@ -51,7 +51,7 @@ N_BANKS = 8                 # expert banks the decode step rotates over
 # at the time: a kernel changed since then reports traffic null.  Commands and raw
 # figures: profiles/<name>.txt.
 MEASURED_TRAFFIC = {
-    "dequant_staged_4096x4096_f16": (43014205, "41dc1ace9141cd08", ("format.hip", "common.hpp")),
+    "dequant_staged_4096x4096_f16": (43046990, "23a9b127dfaa11ea", ("format.hip", "common.hpp")),
     "qmv_dense_4096x4096_T1-4": (9927972, "6a2fa7d6d7b1b8ad", ("qmv.hip", "qmv.hpp", "common.hpp")),
     "qmv_q8_4096x4096_T1-4": (9674811, "6a2fa7d6d7b1b8ad", ("qmv.hip", "qmv.hpp", "common.hpp")),
     "qmv_grouped_gateup_moe_decode_4tok": (59952873, "6a2fa7d6d7b1b8ad", ("qmv.hip", "qmv.hpp", "common.hpp")),
